@@ -1,0 +1,136 @@
+/*
+ * rr.h — C ABI of librr.so: RouteRelay event-triggered cross-layer routing on MI355X (gfx950).
+ *
+ * Source of the operations: "RouteRelay: Event-Triggered Cross-Layer Route Reuse for
+ * Efficient Dynamic Sparse Attention" (arXiv 2609.07306).
+ *
+ *   anchor layer  (Section 4.1; Eq. 1, Eq. 2; Section 3.1 items 1-2):
+ *       S = Q K^T for every query row, route R = top-k, near-miss sentinels = the next m,
+ *       r random sentinels drawn from the remaining allowed chunks; ledger (Eq. 4) written.
+ *   relay layer   (Sections 3.2, 4.1, 4.2; Eq. 5-8):
+ *       rescore each row's ledger candidates, alpha = min over R, beta = max over sentinels,
+ *       reuse iff alpha > beta + gamma; flagged rows are compacted (ascending h*nq+i) and only
+ *       they are routed in full and get new ledger entries (anchor layer := this layer).
+ *
+ * Conventions shared by every entry point
+ *   - Q is [heads, nq, d], K is [heads, nk, d], row-major and contiguous, fp32 or bf16
+ *     (raw IEEE bfloat16 bits) as set by rr_config.dtype.  d must be 64.
+ *   - Scores are raw dot products accumulated in fp32 (no 1/sqrt(d): that factor belongs to
+ *     attention, Eq. 3).  Ties are broken by the lower chunk index.
+ *   - Causal mode (rr_config.causal = 1, needs nq == nk): query chunk i may use key chunks
+ *     j <= i only; rows with fewer than k + m allowed chunks keep all of them.
+ *   - Random sentinels: for t = 0, 1, ...: u_t = word (t mod 4) of
+ *     Philox4x32-10(counter = (t div 4, i, layer, h), key = (seed lo32, seed hi32))
+ *     (Salmon et al., SC'11), j_t = (u_t * n_i) >> 32, accepted if j_t is allowed, not in the
+ *     route or near-miss set and not accepted before; stop at r accepted.  If at most r chunks
+ *     remain they are all taken; after 65536 draws the lowest-index remaining chunks fill up.
+ *   - Ledger layout returned by rr_ledger_get: route [heads, nq, k]; sentinels [heads, nq, m+r]
+ *     = near-miss segment (m) then random segment (r); anchor layer [heads, nq].  Each segment
+ *     ascending, padded with -1.
+ *   - Device pointers are plain HIP device addresses; `stream` is a hipStream_t (NULL = the
+ *     null stream).  Compute calls are asynchronous on `stream`; the caller keeps every buffer
+ *     alive until that stream's work is done.  Calls on one ledger must be serialised by the
+ *     caller (one stream, or explicit ordering).
+ *   - Every call validates its arguments on the host before it enqueues anything.  On any
+ *     error it returns a negative rr_status, leaves the ledger unchanged, and
+ *     rr_last_error() describes the failure (thread-local, valid until the next call).
+ *   - A failed kernel launch returns RR_EDEVICE and poisons the ledger: every call but
+ *     rr_anchor_route, rr_ledger_set and rr_ledger_destroy then returns RR_ESTATE.
+ */
+#ifndef RR_H
+#define RR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RR_ABI_VERSION 1
+
+typedef enum {
+    RR_OK = 0,
+    RR_EINVAL = -1,        /* bad argument: null pointer, negative size, k < 1, ...         */
+    RR_EUNSUPPORTED = -2,  /* valid request outside what the kernels implement (d != 64 ...) */
+    RR_ENOMEM = -3,        /* device allocation failed (only rr_ledger_create allocates)     */
+    RR_EDEVICE = -4,       /* a HIP runtime call or kernel launch failed                     */
+    RR_ESTATE = -5         /* call not allowed in the ledger's state (see each entry point)  */
+} rr_status;
+
+typedef enum { RR_F32 = 0, RR_BF16 = 1 } rr_dtype;
+
+typedef struct {
+    int32_t heads;    /* H >= 1                                                        */
+    int32_t nq;       /* query chunks per head, >= 1                                   */
+    int32_t nk;       /* key chunks per head, >= 1 (== nq when causal)                 */
+    int32_t d;        /* routing representation width; must be 64                     */
+    int32_t k;        /* route width, >= 1                                             */
+    int32_t m;        /* near-miss sentinels, >= 0                                     */
+    int32_t r;        /* random sentinels, >= 0                                        */
+    float gamma;      /* guard margin of Eq. 8, finite and >= 0                        */
+    int32_t causal;   /* 0 or 1                                                        */
+    int32_t dtype;    /* rr_dtype of Q and K                                           */
+    uint64_t seed;    /* random-sentinel key                                           */
+} rr_config;
+/* Limits: k + m <= 32, k + m + r <= 64, nq and nk <= 65536, heads * nq < 2^31.
+ * Non-causal ledgers need nk >= k + m + r. */
+
+typedef struct rr_ledger rr_ledger;   /* opaque; owns the ledger and all scratch device memory */
+
+/* Optional outputs of rr_relay_layer: caller-owned device buffers, each may be NULL. */
+typedef struct {
+    uint8_t* flags;        /* [heads*nq]  1 = row failed Eq. 8 and was rerouted                  */
+    int32_t* rows;         /* [heads*nq]  ascending h*nq+i of flagged rows; first n_rows valid   */
+    int32_t* head_counts;  /* [heads]     flagged rows per head                                  */
+    int32_t* n_rows;       /* [1]         total flagged rows (rho_l * heads * nq)                */
+    float* alpha;          /* [heads*nq]  Eq. 6 at this layer                                    */
+    float* beta;           /* [heads*nq]  Eq. 7 at this layer (-inf if the row has no sentinels)  */
+    float* cand_scores;    /* [heads*nq*(k+m+r)] score of each ledger ID entering the layer, in  *
+                            * ledger order (route, near-miss, random); NaN where the ID is -1    */
+} rr_relay_out;
+
+/* Check a configuration without touching the GPU. */
+rr_status rr_config_check(const rr_config* cfg);
+
+/* Allocate a ledger and its scratch memory on the current HIP device (the only allocating
+ * call).  The ledger starts empty: the first compute call on it must be rr_anchor_route. */
+rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out);
+
+/* Free the ledger (synchronises the device first).  NULL is ignored. */
+void rr_ledger_destroy(rr_ledger* ledger);
+
+/* Anchor layer (Section 4.1): full routing of every row at `layer` (>= 0); rebuilds the whole
+ * ledger with anchor layer = `layer`.  Allowed in any state; clears a poisoned ledger. */
+rr_status rr_anchor_route(rr_ledger* ledger, const void* q, const void* k, int32_t layer,
+                          void* stream);
+
+/* Relay layer (Sections 3.2, 4.1, 4.2) at `layer`: RR_ESTATE unless the ledger has been
+ * anchored and `layer` is greater than the last layer it saw.  `out` may be NULL. */
+rr_status rr_relay_layer(rr_ledger* ledger, const void* q, const void* k, int32_t layer,
+                         void* stream, const rr_relay_out* out);
+
+/* Copy the ledger out (layout above).  Any pointer may be NULL to skip that tensor.
+ * dst_is_host = 1: host memory, the call waits for `stream`; 0: device memory, asynchronous. */
+rr_status rr_ledger_get(const rr_ledger* ledger, int32_t* route, int32_t* sent,
+                        int32_t* anchor_layer, int32_t dst_is_host, void* stream);
+
+/* Replace the whole ledger (snapshot restore / replay): route, sent and anchor_layer are
+ * required, same layout as rr_ledger_get; `last_layer` becomes the last layer seen, so the
+ * next relay call must use a greater layer.  The IDs are trusted to be valid for this
+ * configuration (in range, allowed, distinct per row).  src_is_host as in rr_ledger_get. */
+rr_status rr_ledger_set(rr_ledger* ledger, const int32_t* route, const int32_t* sent,
+                        const int32_t* anchor_layer, int32_t last_layer, int32_t src_is_host,
+                        void* stream);
+
+/* Configuration the ledger was created with. */
+rr_status rr_ledger_config(const rr_ledger* ledger, rr_config* out);
+
+/* Message for the last failure on this thread ("" if none). */
+const char* rr_last_error(void);
+
+int32_t rr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RR_H */

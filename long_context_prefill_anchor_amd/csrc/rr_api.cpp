@@ -1,0 +1,283 @@
+// C ABI of librr.so (declared in include/rr.h): argument validation, ledger ownership and
+// the launch sequence of the anchor and relay layers (Sections 4.1-4.2 of "RouteRelay:
+// Event-Triggered Cross-Layer Route Reuse for Efficient Dynamic Sparse Attention").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "rr.h"
+#include "rr_internal.h"
+
+struct rr_ledger {
+    rr_config cfg;
+    int c;        // k + m + r
+    int sel;      // k + m
+    int G;        // blocks of 64 rows per head
+    int device;
+    int32_t* ids = nullptr;      // [H, nq, c]
+    int32_t* anchor = nullptr;   // [H, nq]
+    uint8_t* flags_ws = nullptr; // [H, nq]
+    float* hint_ws = nullptr;    // [H, nq]
+    int32_t* bcount = nullptr;   // [H, G]
+    int32_t last_layer = -1;
+    bool anchored = false;
+    bool poisoned = false;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+rr_status fail(rr_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rr_status fail(rr_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+rr_status ok() {
+    g_err.clear();
+    return RR_OK;
+}
+
+rr_status check_cfg(const rr_config* c) {
+    if (!c) return fail(RR_EINVAL, "config is NULL");
+    if (c->heads < 1 || c->nq < 1 || c->nk < 1)
+        return fail(RR_EINVAL, "heads, nq and nk must be >= 1 (got %d, %d, %d)", c->heads, c->nq, c->nk);
+    if (c->k < 1 || c->m < 0 || c->r < 0)
+        return fail(RR_EINVAL, "need k >= 1, m >= 0, r >= 0 (got %d, %d, %d)", c->k, c->m, c->r);
+    if (!(std::isfinite(c->gamma) && c->gamma >= 0.f)) return fail(RR_EINVAL, "gamma must be finite and >= 0");
+    if (c->causal != 0 && c->causal != 1) return fail(RR_EINVAL, "causal must be 0 or 1");
+    if (c->dtype != RR_F32 && c->dtype != RR_BF16) return fail(RR_EINVAL, "dtype must be RR_F32 or RR_BF16");
+    if (c->causal && c->nq != c->nk) return fail(RR_EINVAL, "causal routing needs nq == nk");
+    if ((int64_t)c->heads * c->nq >= (int64_t)1 << 31 || (int64_t)c->heads * c->nk * 64 >= (int64_t)1 << 40)
+        return fail(RR_EINVAL, "problem too large");
+    if (c->d != 64) return fail(RR_EUNSUPPORTED, "only d = 64 is implemented (got %d)", c->d);
+    if (c->k + c->m > 32) return fail(RR_EUNSUPPORTED, "k + m must be <= 32 (got %d)", c->k + c->m);
+    if (c->r > 32) return fail(RR_EUNSUPPORTED, "r must be <= 32 (got %d)", c->r);
+    if (c->nk > 4096) return fail(RR_EUNSUPPORTED, "nk must be <= 4096 (got %d)", c->nk);
+    if (c->nq > 65536) return fail(RR_EUNSUPPORTED, "nq must be <= 65536 (got %d)", c->nq);
+    return RR_OK;
+}
+
+rr_status hip_fail(rr_ledger* L, hipError_t e, const char* what) {
+    if (L) L->poisoned = true;
+    return fail(RR_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+void free_all(rr_ledger* L) {
+    (void)hipFree(L->ids);
+    (void)hipFree(L->anchor);
+    (void)hipFree(L->flags_ws);
+    (void)hipFree(L->hint_ws);
+    (void)hipFree(L->bcount);
+}
+
+rr::RouteArgs route_args(const rr_ledger* L, const void* q, const void* k, int layer) {
+    rr::RouteArgs a{};
+    a.qp = q;
+    a.kp = k;
+    a.ids = L->ids;
+    a.anchor = L->anchor;
+    a.flags = L->flags_ws;
+    a.hint = L->hint_ws;
+    a.bcount = L->bcount;
+    a.H = L->cfg.heads;
+    a.nq = L->cfg.nq;
+    a.nk = L->cfg.nk;
+    a.k = L->cfg.k;
+    a.m = L->cfg.m;
+    a.r = L->cfg.r;
+    a.c = L->c;
+    a.sel = L->sel;
+    a.layer = layer;
+    a.seed_lo = (uint32_t)(L->cfg.seed & 0xFFFFFFFFull);
+    a.seed_hi = (uint32_t)(L->cfg.seed >> 32);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t rr_abi_version(void) { return RR_ABI_VERSION; }
+
+const char* rr_last_error(void) { return g_err.c_str(); }
+
+rr_status rr_config_check(const rr_config* cfg) {
+    const rr_status st = check_cfg(cfg);
+    return st == RR_OK ? ok() : st;
+}
+
+rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
+    if (!out) return fail(RR_EINVAL, "out is NULL");
+    *out = nullptr;
+    const rr_status st = check_cfg(cfg);
+    if (st != RR_OK) return st;
+    rr_ledger* L = new (std::nothrow) rr_ledger;
+    if (!L) return fail(RR_ENOMEM, "host allocation failed");
+    L->cfg = *cfg;
+    L->c = cfg->k + cfg->m + cfg->r;
+    L->sel = cfg->k + cfg->m;
+    L->G = (cfg->nq + rr::ROUTE_ROWS - 1) / rr::ROUTE_ROWS;
+    hipError_t e = hipGetDevice(&L->device);
+    if (e != hipSuccess) {
+        delete L;
+        return fail(RR_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    }
+    const size_t rows = (size_t)cfg->heads * cfg->nq;
+    struct { void** p; size_t bytes; } allocs[] = {
+        {(void**)&L->ids, rows * L->c * sizeof(int32_t)},
+        {(void**)&L->anchor, rows * sizeof(int32_t)},
+        {(void**)&L->flags_ws, rows},
+        {(void**)&L->hint_ws, rows * sizeof(float)},
+        {(void**)&L->bcount, (size_t)cfg->heads * L->G * sizeof(int32_t)},
+    };
+    for (auto& a : allocs) {
+        e = hipMalloc(a.p, a.bytes ? a.bytes : 4);
+        if (e != hipSuccess) {
+            free_all(L);
+            delete L;
+            return fail(RR_ENOMEM, "hipMalloc(%zu): %s", a.bytes, hipGetErrorString(e));
+        }
+    }
+    e = hipMemset(L->anchor, 0xFF, rows * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMemset(L->ids, 0xFF, rows * L->c * sizeof(int32_t));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        free_all(L);
+        delete L;
+        return fail(RR_EDEVICE, "initialising the ledger: %s", hipGetErrorString(e));
+    }
+    *out = L;
+    return ok();
+}
+
+void rr_ledger_destroy(rr_ledger* L) {
+    if (!L) return;
+    (void)hipDeviceSynchronize();
+    free_all(L);
+    delete L;
+}
+
+rr_status rr_ledger_config(const rr_ledger* L, rr_config* out) {
+    if (!L || !out) return fail(RR_EINVAL, "ledger or out is NULL");
+    *out = L->cfg;
+    return ok();
+}
+
+rr_status rr_anchor_route(rr_ledger* L, const void* q, const void* k, int32_t layer, void* stream) {
+    if (!L) return fail(RR_EINVAL, "ledger is NULL");
+    if (!q || !k) return fail(RR_EINVAL, "q and k must be device pointers");
+    if (layer < 0) return fail(RR_EINVAL, "layer must be >= 0 (got %d)", layer);
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const rr::RouteArgs a = route_args(L, q, k, layer);
+    const hipError_t e = rr::launch_route(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, false, st);
+    if (e != hipSuccess) return hip_fail(L, e, "anchor route launch");
+    L->anchored = true;
+    L->poisoned = false;
+    L->last_layer = layer;
+    return ok();
+}
+
+rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t layer, void* stream,
+                         const rr_relay_out* out) {
+    if (!L) return fail(RR_EINVAL, "ledger is NULL");
+    if (L->poisoned) return fail(RR_ESTATE, "ledger is poisoned by an earlier device error; anchor first");
+    if (!L->anchored) return fail(RR_ESTATE, "relay layer before any anchor layer");
+    if (layer <= L->last_layer)
+        return fail(RR_ESTATE, "relay layer %d is not after the last layer %d", layer, L->last_layer);
+    if (!q || !k) return fail(RR_EINVAL, "q and k must be device pointers");
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+    rr::RescoreArgs s{};
+    s.qp = q;
+    s.kp = k;
+    s.ids = L->ids;
+    s.flags_ws = L->flags_ws;
+    s.hint_ws = L->hint_ws;
+    s.bcount = L->bcount;
+    s.out_flags = out ? out->flags : nullptr;
+    s.out_alpha = out ? out->alpha : nullptr;
+    s.out_beta = out ? out->beta : nullptr;
+    s.cand_scores = out ? out->cand_scores : nullptr;
+    s.H = L->cfg.heads;
+    s.nq = L->cfg.nq;
+    s.nk = L->cfg.nk;
+    s.k = L->cfg.k;
+    s.m = L->cfg.m;
+    s.r = L->cfg.r;
+    s.c = L->c;
+    s.sel = L->sel;
+    int cp = 1;
+    while (cp < L->c) cp <<= 1;
+    s.cp = cp;
+    s.gamma = L->cfg.gamma;
+    hipError_t e = rr::launch_rescore(s, L->cfg.dtype == RR_BF16, st);
+    if (e != hipSuccess) return hip_fail(L, e, "rescore launch");
+
+    rr::RouteArgs a = route_args(L, q, k, layer);
+    a.out_rows = out ? out->rows : nullptr;
+    a.out_head_counts = out ? out->head_counts : nullptr;
+    a.out_n_rows = out ? out->n_rows : nullptr;
+    e = rr::launch_route(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, true, st);
+    if (e != hipSuccess) return hip_fail(L, e, "reroute launch");
+    L->last_layer = layer;
+    return ok();
+}
+
+rr_status rr_ledger_get(const rr_ledger* L, int32_t* route, int32_t* sent, int32_t* anchor_layer,
+                        int32_t dst_is_host, void* stream) {
+    if (!L) return fail(RR_EINVAL, "ledger is NULL");
+    if (L->poisoned) return fail(RR_ESTATE, "ledger is poisoned by an earlier device error");
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const hipMemcpyKind kind = dst_is_host ? hipMemcpyDeviceToHost : hipMemcpyDeviceToDevice;
+    const size_t rows = (size_t)L->cfg.heads * L->cfg.nq;
+    const size_t pitch = (size_t)L->c * sizeof(int32_t);
+    hipError_t e = hipSuccess;
+    if (route)
+        e = hipMemcpy2DAsync(route, L->cfg.k * sizeof(int32_t), L->ids, pitch, L->cfg.k * sizeof(int32_t), rows, kind, st);
+    if (e == hipSuccess && sent && L->cfg.m + L->cfg.r > 0)
+        e = hipMemcpy2DAsync(sent, (L->cfg.m + L->cfg.r) * sizeof(int32_t), L->ids + L->cfg.k, pitch,
+                             (L->cfg.m + L->cfg.r) * sizeof(int32_t), rows, kind, st);
+    if (e == hipSuccess && anchor_layer)
+        e = hipMemcpyAsync(anchor_layer, L->anchor, rows * sizeof(int32_t), kind, st);
+    if (e == hipSuccess && dst_is_host) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(RR_EDEVICE, "ledger copy out: %s", hipGetErrorString(e));
+    return ok();
+}
+
+rr_status rr_ledger_set(rr_ledger* L, const int32_t* route, const int32_t* sent, const int32_t* anchor_layer,
+                        int32_t last_layer, int32_t src_is_host, void* stream) {
+    if (!L) return fail(RR_EINVAL, "ledger is NULL");
+    if (!route || !anchor_layer || (!sent && L->cfg.m + L->cfg.r > 0))
+        return fail(RR_EINVAL, "route, sent and anchor_layer are required");
+    if (last_layer < 0) return fail(RR_EINVAL, "last_layer must be >= 0 (got %d)", last_layer);
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const hipMemcpyKind kind = src_is_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice;
+    const size_t rows = (size_t)L->cfg.heads * L->cfg.nq;
+    const size_t pitch = (size_t)L->c * sizeof(int32_t);
+    hipError_t e = hipMemcpy2DAsync(L->ids, pitch, route, L->cfg.k * sizeof(int32_t), L->cfg.k * sizeof(int32_t),
+                                    rows, kind, st);
+    if (e == hipSuccess && L->cfg.m + L->cfg.r > 0)
+        e = hipMemcpy2DAsync(L->ids + L->cfg.k, pitch, sent, (L->cfg.m + L->cfg.r) * sizeof(int32_t),
+                             (L->cfg.m + L->cfg.r) * sizeof(int32_t), rows, kind, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(L->anchor, anchor_layer, rows * sizeof(int32_t), kind, st);
+    if (e == hipSuccess && src_is_host) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(L, e, "ledger copy in");
+    L->anchored = true;
+    L->poisoned = false;
+    L->last_layer = last_layer;
+    return ok();
+}
+
+}  // extern "C"

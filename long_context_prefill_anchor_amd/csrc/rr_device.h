@@ -1,0 +1,171 @@
+// Device-side building blocks of the RouteRelay routing kernels (gfx950 / CDNA4).
+//
+//  * 64-bit selection keys: (orderable fp32 score << 32) | (0xFFFFFFFF - chunk index), so that
+//    a larger key means "higher score, and on equal scores the lower chunk index" — the
+//    order under which the route (Eq. 2) and the near-miss sentinels (Section 3.1, item 1)
+//    are ranked.  -0.0 is folded to +0.0 before encoding so both zeros tie.
+//  * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11), the counter-based generator behind the
+//    random sentinels (Section 3.1, item 2).
+//  * Compile-time sorting networks over register arrays (Batcher odd-even merge sort and the
+//    bitonic merge), used one query row per lane.
+//  * MFMA wrappers: v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x4_f32 computing
+//    D[key][query] = sum_d K[key][d] * Q[query][d] for a 16-key x 16-query tile.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------------- keys
+
+__device__ __forceinline__ uint32_t orderable(float s) {
+    uint32_t u = __float_as_uint(s);
+    u = (u == 0x80000000u) ? 0u : u;                      // -0.0 ties with +0.0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_orderable(uint32_t o) {
+    uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t make_key(float s, uint32_t j) {
+    return ((uint64_t)orderable(s) << 32) | (uint64_t)(0xFFFFFFFFu - j);
+}
+
+__device__ __forceinline__ uint32_t key_index(uint64_t key) {
+    return 0xFFFFFFFFu - (uint32_t)key;
+}
+
+__device__ __forceinline__ float key_score(uint64_t key) {
+    return from_orderable((uint32_t)(key >> 32));
+}
+
+// Key 0 sits below every real key (the lowest real score, -inf, encodes to 0x007FFFFF).
+constexpr uint64_t EMPTY_KEY = 0ull;
+
+// ---------------------------------------------------------------------------------- Philox
+
+struct P4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ P4 philox4x32_10(P4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int rnd = 0; rnd < 10; ++rnd) {
+        if (rnd) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+        c = P4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    }
+    return c;
+}
+
+// ---------------------------------------------------------------------------------- networks
+// All indices are compile-time constants after unrolling, so the arrays stay in VGPRs.
+
+template <typename T>
+__device__ __forceinline__ void ce_desc(T& a, T& b) {       // larger first
+    const bool sw = b > a;
+    const T hi = sw ? b : a;
+    const T lo = sw ? a : b;
+    a = hi;
+    b = lo;
+}
+
+template <typename T>
+__device__ __forceinline__ void ce_asc(T& a, T& b) {        // smaller first
+    const bool sw = b < a;
+    const T lo = sw ? b : a;
+    const T hi = sw ? a : b;
+    a = lo;
+    b = hi;
+}
+
+// Batcher's odd-even merge sort, descending.
+template <int N, typename T>
+__device__ __forceinline__ void sort_desc(T (&v)[N]) {
+#pragma unroll
+    for (int p = 1; p < N; p <<= 1) {
+#pragma unroll
+        for (int k = p; k >= 1; k >>= 1) {
+#pragma unroll
+            for (int j = k % p; j + k < N; j += 2 * k) {
+#pragma unroll
+                for (int i = 0; i < k; ++i) {
+                    if (i < N - j - k && (i + j) / (2 * p) == (i + j + k) / (2 * p))
+                        ce_desc(v[i + j], v[i + j + k]);
+                }
+            }
+        }
+    }
+}
+
+// Same network, ascending.
+template <int N, typename T>
+__device__ __forceinline__ void sort_asc(T (&v)[N]) {
+#pragma unroll
+    for (int p = 1; p < N; p <<= 1) {
+#pragma unroll
+        for (int k = p; k >= 1; k >>= 1) {
+#pragma unroll
+            for (int j = k % p; j + k < N; j += 2 * k) {
+#pragma unroll
+                for (int i = 0; i < k; ++i) {
+                    if (i < N - j - k && (i + j) / (2 * p) == (i + j + k) / (2 * p))
+                        ce_asc(v[i + j], v[i + j + k]);
+                }
+            }
+        }
+    }
+}
+
+// top (sorted desc, N) <- the N largest of top U chunk, chunk sorted desc (N).
+// max(top[i], chunk[N-1-i]) keeps exactly the N largest and leaves a bitonic sequence,
+// which the half-cleaner cascade then sorts.
+template <int N, typename T>
+__device__ __forceinline__ void merge_top_desc(T (&top)[N], const T (&chunk)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const T c = chunk[N - 1 - i];
+        top[i] = c > top[i] ? c : top[i];
+    }
+#pragma unroll
+    for (int s = N / 2; s >= 1; s >>= 1) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if ((i & s) == 0) ce_desc(top[i], top[i + s]);
+    }
+}
+
+// ---------------------------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------- wave ops
+
+__device__ __forceinline__ float wave_min_in(float v, int width) {
+    for (int o = width >> 1; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_in(float v, int width) {
+    for (int o = width >> 1; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_in(int v, int width) {
+    for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace rr

@@ -1,0 +1,47 @@
+// Internal interface between the C ABI host code (rr_api.cpp) and the kernels (rr_kernels.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rr {
+
+struct RouteArgs {
+    const void* qp;             // [H, nq, 64] f32 or bf16
+    const void* kp;             // [H, nk, 64]
+    int32_t* ids;               // ledger IDs [H, nq, c]: route k | near-miss m | random r
+    int32_t* anchor;            // [H, nq]
+    const uint8_t* flags;       // reroute: refresh flags [H, nq] from the rescore kernel
+    const float* hint;          // reroute: first selection threshold per row [H, nq]
+    const int32_t* bcount;      // reroute: flagged rows per rescore block [H, G]
+    int32_t* out_rows;          // reroute, optional: compacted list (ascending h*nq+i)
+    int32_t* out_head_counts;   // reroute, optional: [H]
+    int32_t* out_n_rows;        // reroute, optional: [1]
+    int H, nq, nk, k, m, r, c, sel;
+    int layer;
+    uint32_t seed_lo, seed_hi;
+};
+
+struct RescoreArgs {
+    const void* qp;
+    const void* kp;
+    const int32_t* ids;         // [H, nq, c]
+    uint8_t* flags_ws;          // [H, nq]
+    float* hint_ws;             // [H, nq]
+    int32_t* bcount;            // [H, G] flagged rows per block of 64 rows
+    uint8_t* out_flags;         // optional
+    float* out_alpha;           // optional
+    float* out_beta;            // optional
+    float* cand_scores;         // optional [H, nq, c]
+    int H, nq, nk, k, m, r, c, sel;
+    int cp;                     // lanes per row: power of two >= c, <= 64
+    float gamma;
+};
+
+constexpr int ROUTE_ROWS = 64;   // rows per route block and per rescore block
+
+hipError_t launch_route(const RouteArgs& a, bool bf16, bool causal, bool reroute, hipStream_t st);
+hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st);
+size_t route_lds_bytes(int nk);
+
+}  // namespace rr

@@ -1,0 +1,229 @@
+"""Thin ctypes binding of librr.so (include/rr.h): same entry points, argument marshalling only.
+
+Every compute step runs in the library's HIP kernels; this module only turns torch
+tensors (or raw integers) into device pointers and the current HIP stream.  It raises
+``RuntimeError`` when ``librr.so`` is missing; there is no other implementation to fall
+back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librr.so")
+
+RR_OK, RR_EINVAL, RR_EUNSUPPORTED, RR_ENOMEM, RR_EDEVICE, RR_ESTATE = 0, -1, -2, -3, -4, -5
+RR_F32, RR_BF16 = 0, 1
+STATUS_NAMES = {0: "RR_OK", -1: "RR_EINVAL", -2: "RR_EUNSUPPORTED", -3: "RR_ENOMEM",
+                -4: "RR_EDEVICE", -5: "RR_ESTATE"}
+
+# Entry points declared in include/rr.h, in declaration order.
+ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_destroy", "rr_anchor_route",
+                "rr_relay_layer", "rr_ledger_get", "rr_ledger_set", "rr_ledger_config",
+                "rr_last_error", "rr_abi_version")
+
+
+class rr_config(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("nq", ctypes.c_int32), ("nk", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("k", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("r", ctypes.c_int32), ("gamma", ctypes.c_float), ("causal", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class rr_relay_out(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_void_p), ("rows", ctypes.c_void_p),
+                ("head_counts", ctypes.c_void_p), ("n_rows", ctypes.c_void_p),
+                ("alpha", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("cand_scores", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m long_context_prefill_anchor_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER
+        L.rr_config_check.argtypes = [P(rr_config)]
+        L.rr_ledger_create.argtypes = [P(rr_config), P(vp)]
+        L.rr_ledger_destroy.argtypes = [vp]
+        L.rr_ledger_destroy.restype = None
+        L.rr_anchor_route.argtypes = [vp, vp, vp, i32, vp]
+        L.rr_relay_layer.argtypes = [vp, vp, vp, i32, vp, P(rr_relay_out)]
+        L.rr_ledger_get.argtypes = [vp, vp, vp, vp, i32, vp]
+        L.rr_ledger_set.argtypes = [vp, vp, vp, vp, i32, i32, vp]
+        L.rr_ledger_config.argtypes = [vp, P(rr_config)]
+        L.rr_last_error.restype = ctypes.c_char_p
+        L.rr_last_error.argtypes = []
+        L.rr_abi_version.restype = i32
+        L.rr_abi_version.argtypes = []
+        for name in ENTRY_POINTS:
+            fn = getattr(L, name)
+            if fn.restype is ctypes.c_int:
+                fn.restype = i32
+        _lib = L
+    return _lib
+
+
+class RRError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().rr_last_error().decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != RR_OK:
+        raise RRError(status, where)
+
+
+def _ptr(x) -> Optional[int]:
+    """Device (or host) address of a tensor / raw int; None stays None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_config(heads, nq, nk, d=64, k=12, m=12, r=8, gamma=0.0, causal=False,
+                dtype="bf16", seed=0) -> rr_config:
+    return rr_config(heads, nq, nk, d, k, m, r, float(gamma), int(bool(causal)),
+                     RR_BF16 if dtype == "bf16" else RR_F32, int(seed) & (2**64 - 1))
+
+
+# ------------------------------------------------------------------------- raw entry points
+
+def rr_config_check(cfg: rr_config) -> int:
+    return lib().rr_config_check(ctypes.byref(cfg))
+
+
+def rr_ledger_create(cfg: rr_config) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().rr_ledger_create(ctypes.byref(cfg), ctypes.byref(h)), "rr_ledger_create")
+    return h.value
+
+
+def rr_ledger_destroy(handle: int) -> None:
+    lib().rr_ledger_destroy(handle)
+
+
+def rr_anchor_route(handle, q, k, layer: int, stream=None) -> None:
+    _check(lib().rr_anchor_route(handle, _ptr(q), _ptr(k), int(layer), _stream(stream)),
+           "rr_anchor_route")
+
+
+def rr_relay_layer(handle, q, k, layer: int, stream=None, flags=None, rows=None, head_counts=None,
+                   n_rows=None, alpha=None, beta=None, cand_scores=None, out: bool = True) -> None:
+    o = rr_relay_out(_ptr(flags), _ptr(rows), _ptr(head_counts), _ptr(n_rows), _ptr(alpha),
+                     _ptr(beta), _ptr(cand_scores))
+    _check(lib().rr_relay_layer(handle, _ptr(q), _ptr(k), int(layer), _stream(stream),
+                                ctypes.byref(o) if out else None), "rr_relay_layer")
+
+
+def rr_ledger_get(handle, route, sent, anchor_layer, dst_is_host: bool, stream=None) -> None:
+    _check(lib().rr_ledger_get(handle, _ptr(route), _ptr(sent), _ptr(anchor_layer),
+                               int(bool(dst_is_host)), _stream(stream)), "rr_ledger_get")
+
+
+def rr_ledger_set(handle, route, sent, anchor_layer, last_layer: int, src_is_host: bool,
+                  stream=None) -> None:
+    _check(lib().rr_ledger_set(handle, _ptr(route), _ptr(sent), _ptr(anchor_layer),
+                               int(last_layer), int(bool(src_is_host)), _stream(stream)),
+           "rr_ledger_set")
+
+
+def rr_last_error() -> str:
+    return lib().rr_last_error().decode()
+
+
+def rr_abi_version() -> int:
+    return lib().rr_abi_version()
+
+
+# ------------------------------------------------------------------------- convenience wrapper
+
+@dataclass
+class RelayOutputs:
+    flags: object
+    rows: object
+    head_counts: object
+    n_rows: object
+    alpha: object
+    beta: object
+    cand_scores: object
+
+
+class Ledger:
+    """Owns one rr_ledger handle; torch tensors in, torch tensors out (device memory only)."""
+
+    def __init__(self, heads, nq, nk, d=64, k=12, m=12, r=8, gamma=0.0, causal=False,
+                 dtype="bf16", seed=0):
+        self.cfg = make_config(heads, nq, nk, d, k, m, r, gamma, causal, dtype, seed)
+        self.heads, self.nq, self.nk, self.k, self.m, self.r = heads, nq, nk, k, m, r
+        self.c = k + m + r
+        self.handle = rr_ledger_create(self.cfg)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            rr_ledger_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def anchor(self, q, k, layer, stream=None):
+        rr_anchor_route(self.handle, q, k, layer, stream)
+
+    def alloc_outputs(self, device="cuda", with_scores=True) -> RelayOutputs:
+        import torch
+        H, nq = self.heads, self.nq
+        return RelayOutputs(
+            flags=torch.zeros(H * nq, dtype=torch.uint8, device=device),
+            rows=torch.full((H * nq,), -1, dtype=torch.int32, device=device),
+            head_counts=torch.zeros(H, dtype=torch.int32, device=device),
+            n_rows=torch.zeros(1, dtype=torch.int32, device=device),
+            alpha=torch.zeros(H * nq, dtype=torch.float32, device=device),
+            beta=torch.zeros(H * nq, dtype=torch.float32, device=device),
+            cand_scores=(torch.zeros(H * nq * self.c, dtype=torch.float32, device=device)
+                         if with_scores else None))
+
+    def relay(self, q, k, layer, out: Optional[RelayOutputs] = None, stream=None):
+        if out is None:
+            rr_relay_layer(self.handle, q, k, layer, stream, out=False)
+        else:
+            rr_relay_layer(self.handle, q, k, layer, stream, out.flags, out.rows, out.head_counts,
+                           out.n_rows, out.alpha, out.beta, out.cand_scores)
+
+    def get(self, stream=None):
+        """(route [H,nq,k], sent [H,nq,m+r], anchor [H,nq]) as device int32 tensors."""
+        import torch
+        H, nq = self.heads, self.nq
+        route = torch.empty((H, nq, self.k), dtype=torch.int32, device="cuda")
+        sent = torch.empty((H, nq, self.m + self.r), dtype=torch.int32, device="cuda")
+        anchor = torch.empty((H, nq), dtype=torch.int32, device="cuda")
+        rr_ledger_get(self.handle, route, sent if self.m + self.r else None, anchor, False, stream)
+        return route, sent, anchor
+
+    def set(self, route, sent, anchor, last_layer, stream=None):
+        rr_ledger_set(self.handle, route, sent if self.m + self.r else None, anchor, last_layer,
+                      False, stream)

@@ -1,0 +1,186 @@
+"""Helpers for the GPU parity tests: upload inputs, run the C-ABI path, compare with the oracle.
+
+Comparison rule: route / sentinel / anchor IDs, refresh flags and the compacted row list
+must be bit-equal, except rows whose oracle score gap at a decision boundary is below
+``tol`` (1e-5 absolute; 0 for integer-valued inputs, whose scores are exact on both sides),
+which are excluded and counted.  Scores (alpha, beta, candidate scores) must agree within
+``rel`` * (|s_ref| + rms of the row's candidate scores): 1e-5 for fp32 inputs, 1e-3 for bf16.
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle as O
+from long_context_prefill_anchor_amd import rr
+
+GAP_TOL = 1e-5
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def upload(x: np.ndarray):
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def oracle_cfg(led: rr.Ledger, dtype: str, gamma=0.0, causal=False, seed=0):
+    return O.RouteConfig(heads=led.heads, nq=led.nq, nk=led.nk, d=64, k=led.k, m=led.m, r=led.r,
+                         gamma=gamma, causal=causal, seed=seed, dtype=dtype)
+
+
+def ledger_np(led: rr.Ledger):
+    route, sent, anchor = led.get()
+    import torch
+    torch.cuda.synchronize()
+    return route.cpu().numpy(), sent.cpu().numpy(), anchor.cpu().numpy()
+
+
+def set_ledger(led: rr.Ledger, ol: O.Ledger, last_layer: int):
+    import torch
+    led.set(torch.from_numpy(ol.route).cuda(), torch.from_numpy(ol.sent).cuda(),
+            torch.from_numpy(ol.anchor).cuda(), last_layer)
+
+
+def oracle_scores(cfg: O.RouteConfig, q, k) -> np.ndarray:
+    Q, K = O.decode(q, cfg.dtype), O.decode(k, cfg.dtype)
+    return np.stack([O.score_rows(Q[h], K[h]) for h in range(cfg.heads)])
+
+
+def selection_excluded(cfg: O.RouteConfig, S: np.ndarray, tol: float, rows=None) -> np.ndarray:
+    """bool [H, nq]: rows whose route / near-miss boundary gap is below tol."""
+    ex = np.zeros((cfg.heads, cfg.nq), bool)
+    if tol <= 0:
+        return ex
+    it = rows if rows is not None else [(h, i) for h in range(cfg.heads) for i in range(cfg.nq)]
+    for h, i in it:
+        ex[h, i] = O.selection_gap(S[h, i], O.n_allowed(i, cfg), cfg.k, cfg.m) < tol
+    return ex
+
+
+@dataclass
+class Report:
+    rows: int = 0
+    excluded: int = 0
+    max_score_err: float = 0.0
+    notes: list = field(default_factory=list)
+
+
+def compare_ledgers(gpu, ora: O.Ledger, mask: np.ndarray, what: str):
+    """Bit-equality of route / sent / anchor on rows where mask is True."""
+    g_route, g_sent, g_anchor = gpu
+    for name, g, o in (("route", g_route, ora.route), ("sent", g_sent, ora.sent),
+                       ("anchor", g_anchor, ora.anchor)):
+        gm, om = g[mask], o[mask]
+        if not np.array_equal(gm, om):
+            bad = np.argwhere(mask)[np.flatnonzero((gm != om).reshape(len(gm), -1).any(axis=1))]
+            h, i = bad[0]
+            raise AssertionError(f"{what}: {name} differs on {len(bad)} rows, first (h={h}, i={i}): "
+                                 f"gpu={g[h, i]} oracle={o[h, i]}")
+
+
+def check_scores(got, ref, rel, rms, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    both_nan = np.isnan(got) & np.isnan(ref)
+    both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
+    ok = both_nan | both_inf
+    err = np.where(ok, 0.0, np.abs(got - ref))
+    lim = rel * (np.abs(np.where(ok, 0, ref)) + rms)
+    bad = ~(ok | (err <= lim))
+    if bad.any():
+        idx = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} values out of tolerance, first {tuple(idx)}: "
+                             f"gpu={got[tuple(idx)]} oracle={ref[tuple(idx)]}")
+    finite = np.isfinite(err)
+    return float(err[finite].max()) if finite.any() else 0.0
+
+
+def run_anchor(led: rr.Ledger, q, k, layer: int):
+    import torch
+    led.anchor(upload(q), upload(k), layer)
+    torch.cuda.synchronize()
+    return ledger_np(led)
+
+
+def anchor_parity(led, cfg, q, k, layer, tol, rep: Report, rows=None):
+    """GPU anchor layer vs oracle on all rows (or the given (h, i) sample)."""
+    gpu = run_anchor(led, q, k, layer)
+    S = oracle_scores(cfg, q, k)
+    if rows is None:
+        ora = O.anchor_layer(cfg, q, k, layer)
+        mask = ~selection_excluded(cfg, S, tol)
+    else:
+        ora = O.Ledger.empty(cfg)
+        for h, i in rows:
+            O.rebuild_row(cfg, ora, h, layer, i, S[h, i])
+        mask = np.zeros((cfg.heads, cfg.nq), bool)
+        for h, i in rows:
+            mask[h, i] = True
+        mask &= ~selection_excluded(cfg, S, tol, rows)
+    total = len(rows) if rows is not None else cfg.heads * cfg.nq
+    rep.rows += total
+    rep.excluded += total - int(mask.sum())
+    compare_ledgers(gpu, ora, mask, f"anchor layer {layer}")
+    return gpu, ora
+
+
+def relay_parity(led, cfg, q, k, layer, ledger_in: O.Ledger, tol, rel, rep: Report, excluded_in=None):
+    """GPU relay layer (started from ``ledger_in``) vs oracle.  Returns the GPU ledger, the
+    oracle result and the rows excluded from here on."""
+    import torch
+    set_ledger(led, ledger_in, layer - 1)
+    out = led.alloc_outputs()
+    led.relay(upload(q), upload(k), layer, out)
+    torch.cuda.synchronize()
+    gpu = ledger_np(led)
+    res = O.relay_layer(cfg, q, k, layer, ledger_in)
+    H, nq = cfg.heads, cfg.nq
+    g_flags = out.flags.cpu().numpy().reshape(H, nq)
+    g_alpha = out.alpha.cpu().numpy().reshape(H, nq)
+    g_beta = out.beta.cpu().numpy().reshape(H, nq)
+    g_cand = out.cand_scores.cpu().numpy().reshape(H, nq, cfg.c)
+    n_rows = int(out.n_rows.cpu().numpy()[0])
+    g_rows = out.rows.cpu().numpy()[:n_rows]
+    g_counts = out.head_counts.cpu().numpy()
+
+    # the compacted list is exactly the GPU's own flagged rows, ascending, with matching counts
+    assert np.array_equal(g_rows, np.flatnonzero(g_flags.reshape(-1))), "compacted list"
+    assert np.array_equal(g_counts, g_flags.sum(axis=1)), "head counts"
+
+    # scores: alpha, beta, and every candidate score, within tolerance
+    rms = np.sqrt(np.nanmean(res.cand_scores.astype(np.float64) ** 2, axis=2))
+    e1 = check_scores(g_cand, res.cand_scores, rel, rms[:, :, None], f"layer {layer} candidate scores")
+    e2 = check_scores(g_alpha, res.alpha, rel, rms, f"layer {layer} alpha")
+    e3 = check_scores(g_beta, res.beta, rel, rms, f"layer {layer} beta")
+    rep.max_score_err = max(rep.max_score_err, e1, e2, e3)
+
+    # exclusions: relay decision gap, then (for refreshed rows) the selection gap at this layer
+    ex = np.zeros((H, nq), bool) if excluded_in is None else excluded_in.copy()
+    if tol > 0:
+        for h in range(H):
+            for i in range(nq):
+                if O.relay_gap(res.alpha[h, i], res.beta[h, i], cfg.gamma) < tol:
+                    ex[h, i] = True
+        S = None
+        for h, i in np.argwhere(res.flags == 1):
+            if S is None:
+                S = oracle_scores(cfg, q, k)
+            if O.selection_gap(S[h, i], O.n_allowed(i, cfg), cfg.k, cfg.m) < tol:
+                ex[h, i] = True
+    mask = ~ex
+    rep.rows += H * nq
+    rep.excluded += int(ex.sum())
+    if not np.array_equal(g_flags[mask], res.flags[mask]):
+        bad = np.argwhere(mask & (g_flags != res.flags))[0]
+        raise AssertionError(f"layer {layer}: flags differ, first {tuple(bad)}: gpu={g_flags[tuple(bad)]} "
+                             f"oracle={res.flags[tuple(bad)]} alpha={res.alpha[tuple(bad)]} beta={res.beta[tuple(bad)]}")
+    compare_ledgers(gpu, res.ledger, mask, f"relay layer {layer}")
+    return gpu, res, ex

@@ -1,0 +1,103 @@
+"""Host-side checks of the C ABI: librr.so loads, exports every entry point of include/rr.h,
+and rejects bad arguments before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_prefill_anchor_amd import rr
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "rr.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:rr_status|void|const char\*|int32_t)\s+(rr_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_and_binding_agree():
+    names = declared_functions()
+    assert len(names) == len(set(names)) >= 10
+    assert set(names) == set(rr.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = rr.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert rr.rr_abi_version() == 1
+
+
+def cfg(**kw):
+    base = dict(heads=2, nq=64, nk=64, d=64, k=12, m=12, r=8, gamma=0.0, causal=False,
+                dtype="bf16", seed=0)
+    base.update(kw)
+    return rr.make_config(**base)
+
+
+def test_config_check_accepts_every_named_workload():
+    from long_context_prefill_anchor_amd import workloads as W
+    for w in W.all_named():
+        c = rr.make_config(w.heads, w.n, w.n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
+        assert rr.rr_config_check(c) == rr.RR_OK, (w.name, rr.rr_last_error())
+    # the full-routing comparator: m = r = 0
+    assert rr.rr_config_check(cfg(m=0, r=0)) == rr.RR_OK
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(heads=0), rr.RR_EINVAL, "heads"),
+    (dict(nq=0), rr.RR_EINVAL, "nq"),
+    (dict(nk=-5), rr.RR_EINVAL, "nk"),
+    (dict(k=0), rr.RR_EINVAL, "k >= 1"),
+    (dict(m=-1), rr.RR_EINVAL, "m >= 0"),
+    (dict(r=-1), rr.RR_EINVAL, "r >= 0"),
+    (dict(gamma=-0.5), rr.RR_EINVAL, "gamma"),
+    (dict(gamma=float("inf")), rr.RR_EINVAL, "gamma"),
+    (dict(gamma=float("nan")), rr.RR_EINVAL, "gamma"),
+    (dict(causal=True, nk=32), rr.RR_EINVAL, "causal"),
+    (dict(d=128), rr.RR_EUNSUPPORTED, "d = 64"),
+    (dict(k=20, m=13), rr.RR_EUNSUPPORTED, "k + m"),
+    (dict(r=33), rr.RR_EUNSUPPORTED, "r must"),
+    (dict(nk=8192), rr.RR_EUNSUPPORTED, "nk"),
+])
+def test_config_check_rejects(kw, status, needle):
+    assert rr.rr_config_check(cfg(**kw)) == status
+    assert needle in rr.rr_last_error()
+
+
+def test_bad_dtype_and_causal_flag():
+    c = cfg()
+    c.dtype = 7
+    assert rr.rr_config_check(c) == rr.RR_EINVAL
+    c = cfg()
+    c.causal = 2
+    assert rr.rr_config_check(c) == rr.RR_EINVAL
+
+
+def test_create_rejects_bad_config_without_touching_the_device():
+    h = ctypes.c_void_p(1234)
+    st = rr.lib().rr_ledger_create(ctypes.byref(cfg(k=0)), ctypes.byref(h))
+    assert st == rr.RR_EINVAL and h.value is None
+    assert rr.lib().rr_ledger_create(None, ctypes.byref(h)) == rr.RR_EINVAL
+    assert rr.lib().rr_ledger_create(ctypes.byref(cfg()), None) == rr.RR_EINVAL
+
+
+def test_null_ledger_is_rejected_by_every_call():
+    L = rr.lib()
+    assert L.rr_anchor_route(None, 1, 1, 0, None) == rr.RR_EINVAL
+    assert L.rr_relay_layer(None, 1, 1, 1, None, None) == rr.RR_EINVAL
+    assert L.rr_ledger_get(None, None, None, None, 1, None) == rr.RR_EINVAL
+    assert L.rr_ledger_set(None, 1, 1, 1, 0, 1, None) == rr.RR_EINVAL
+    assert L.rr_ledger_config(None, None) == rr.RR_EINVAL
+    assert "NULL" in rr.rr_last_error()
+    L.rr_ledger_destroy(None)     # ignored
+
+
+def test_last_error_clears_on_success():
+    assert rr.rr_config_check(cfg(k=0)) == rr.RR_EINVAL
+    assert rr.rr_last_error() != ""
+    assert rr.rr_config_check(cfg()) == rr.RR_OK
+    assert rr.rr_last_error() == ""

@@ -218,9 +218,6 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
     s.r = L->cfg.r;
     s.c = L->c;
     s.sel = L->sel;
-    int cp = 1;
-    while (cp < L->c) cp <<= 1;
-    s.cp = cp;
     s.gamma = L->cfg.gamma;
     hipError_t e = rr::launch_rescore(s, L->cfg.dtype == RR_BF16, st);
     if (e != hipSuccess) return hip_fail(L, e, "rescore launch");

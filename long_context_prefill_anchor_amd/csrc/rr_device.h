@@ -153,6 +153,43 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 
 // ---------------------------------------------------------------------------------- wave ops
 
+// Cross-lane moves that stay in the VALU (no LDS round trip, no wait): DPP within 16-lane rows
+// and the gfx950 row swaps across rows.
+enum : int {
+    DPP_XOR1 = 0xB1,          // quad_perm [1,0,3,2]
+    DPP_XOR2 = 0x4E,          // quad_perm [2,3,0,1]
+    DPP_HALF_MIRROR = 0x141,  // lane i of each 8-lane half-row <- lane 7 - i
+    DPP_ROR8 = 0x128,         // lane i of each row <- lane (i + 8) mod 16
+};
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over aligned groups of G consecutive lanes (G = 8 or 16); every lane of a group ends with
+// the bit-identical total (each step adds the same two partial sums in either order).
+template <int G> __device__ __forceinline__ float group_sum(float s) {
+    static_assert(G == 8 || G == 16, "group of 8 or 16 lanes");
+    s += dpp_f<DPP_XOR1>(s);
+    s += dpp_f<DPP_XOR2>(s);
+    s += dpp_f<DPP_HALF_MIRROR>(s);
+    if (G == 16) s += dpp_f<DPP_ROR8>(s);
+    return s;
+}
+
+// Reduce over the 64 / G groups of G lanes whose members already agree (G = 8 or 16): the
+// partner group sits at lane offset 8 (within a row), then 16 and 32 (row swaps).
+template <int G, typename F> __device__ __forceinline__ uint32_t across_groups(uint32_t v, F op) {
+    static_assert(G == 8 || G == 16, "group of 8 or 16 lanes");
+    if (G == 8) v = op(v, (uint32_t)dpp_i<DPP_ROR8>((int)v));
+    auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op(a[0], a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return op(b[0], b[1]);
+}
+
 __device__ __forceinline__ float wave_min_in(float v, int width) {
     for (int o = width >> 1; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
     return v;

@@ -34,7 +34,6 @@ struct RescoreArgs {
     float* out_beta;            // optional
     float* cand_scores;         // optional [H, nq, c]
     int H, nq, nk, k, m, r, c, sel;
-    int cp;                     // lanes per row: power of two >= c, <= 64
     float gamma;
 };
 

@@ -47,6 +47,7 @@ constexpr int TOPW = 32;           // register top list width (k + m <= TOPW)
 constexpr int CAP = 31;            // per-wave per-row buffer: <= 15 held + 16 slots appended
 constexpr int CSTRIDE = CAP;       // row stride in entries (odd: spreads rows over LDS banks)
 constexpr int GSTRIDE = 33;        // f32 row stride of the pass-1 group maxima table
+constexpr int XSTRIDE = TOPW + 1;  // u64 row stride of the cross-wave exchange lists
 constexpr uint64_t NO_PASS_KEY = ~0ull;   // threshold whose score part is NaN: nothing passes
 
 struct bf16_t { uint16_t bits; };
@@ -61,6 +62,7 @@ template <typename DT> struct Tile;
 
 template <> struct Tile<bf16_t> {
     typedef bf16x8 KReg[4];
+    static constexpr int NBUF = 3;        // K register ring: loads run two tiles ahead
     bf16x8 q[2][4];                       // B operand: group g, k-step s: d = 16s + 8(L/32) + t
     __device__ __forceinline__ void load_q(const uint16_t* Q, int row0, int row1, int lane) {
         const int sub = lane >> 5;
@@ -77,18 +79,13 @@ template <> struct Tile<bf16_t> {
                 }
             }
     }
+    // Rows past nk read row nk-1 instead: those keys are masked out of every row afterwards.
     __device__ __forceinline__ void load_k(KReg& dst, const uint16_t* K, int key0, int nk, int lane) const {
-        const int key = key0 + (lane & 31);
+        const int key = min(key0 + (lane & 31), nk - 1);
         const int sub = lane >> 5;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (key < nk) {
-                dst[s] = *reinterpret_cast<const bf16x8*>(K + (size_t)key * 64 + 16 * s + 8 * sub);
-            } else {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                dst[s] = __builtin_bit_cast(bf16x8, z);
-            }
-        }
+        for (int s = 0; s < 4; ++s)
+            dst[s] = *reinterpret_cast<const bf16x8*>(K + (size_t)key * 64 + 16 * s + 8 * sub);
     }
     __device__ __forceinline__ void mma(const KReg& ka, f32x16& acc0, f32x16& acc1) const {
         acc0 = f32x16{};
@@ -103,6 +100,7 @@ template <> struct Tile<bf16_t> {
 
 template <> struct Tile<float> {
     typedef float KReg[32];
+    static constexpr int NBUF = 2;        // 32-register tiles: one tile ahead
     float q[2][32];                       // k-step s: d = 32(L/32) + s
     __device__ __forceinline__ void load_q(const float* Q, int row0, int row1, int lane) {
         const int sub = lane >> 5;
@@ -123,18 +121,13 @@ template <> struct Tile<float> {
         }
     }
     __device__ __forceinline__ void load_k(KReg& dst, const float* K, int key0, int nk, int lane) const {
-        const int key = key0 + (lane & 31);
+        const int key = min(key0 + (lane & 31), nk - 1);
         const int sub = lane >> 5;
-        if (key < nk) {
-            const float4* src = reinterpret_cast<const float4*>(K + (size_t)key * 64 + 32 * sub);
+        const float4* src = reinterpret_cast<const float4*>(K + (size_t)key * 64 + 32 * sub);
 #pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                const float4 x = src[v];
-                dst[4 * v] = x.x; dst[4 * v + 1] = x.y; dst[4 * v + 2] = x.z; dst[4 * v + 3] = x.w;
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < 32; ++s) dst[s] = 0.f;
+        for (int v = 0; v < 8; ++v) {
+            const float4 x = src[v];
+            dst[4 * v] = x.x; dst[4 * v + 1] = x.y; dst[4 * v + 2] = x.z; dst[4 * v + 3] = x.w;
         }
     }
     __device__ __forceinline__ void mma(const KReg& ka, f32x16& acc0, f32x16& acc1) const {
@@ -147,12 +140,6 @@ template <> struct Tile<float> {
         }
     }
 };
-
-template <typename KR>
-__device__ __forceinline__ void copy_k(KR& dst, const KR& src) {
-#pragma unroll
-    for (int s = 0; s < (int)(sizeof(KR) / sizeof(src[0])); ++s) dst[s] = src[s];
-}
 
 // After the swap every lane holds its own row: lo[v] is key lo_key(v) of the tile, hi[v] is
 // key hi_key(v).  (v_permlane32_swap exchanges lanes 32-63 of its first operand with lanes
@@ -194,7 +181,8 @@ __device__ __forceinline__ void merge16_into_top(uint64_t (&top)[TOPW], const ui
 }
 
 // Sort the lane's buffered (score bits, index) pairs and merge them into its top list.
-__device__ __forceinline__ void drain(uint64_t (&top)[TOPW], const uint2* buf, int cnt) {
+// `fresh`: every lane's list is still empty, so the first sorted chunk is copied in.
+__device__ __forceinline__ void drain(uint64_t (&top)[TOPW], const uint2* buf, int cnt, bool& fresh) {
     int maxc = cnt;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) maxc = max(maxc, __shfl_xor(maxc, o, 64));
@@ -210,9 +198,29 @@ __device__ __forceinline__ void drain(uint64_t (&top)[TOPW], const uint2* buf, i
             }
         }
         sort_desc<16>(x);
-        merge16_into_top(top, x);
+        if (fresh) {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) top[s] = x[s];
+            fresh = false;
+        } else {
+            merge16_into_top(top, x);
+        }
     }
 }
+
+// Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8), and each XCD
+// has its own L2.  Renumbering so that XCD x runs the contiguous logical range
+// [x * per, (x + 1) * per) keeps all blocks of a head, which share that head's K, on one XCD.
+// The grid is padded to a multiple of 8; padding blocks get -1.
+constexpr int XCDS = 8;
+
+__device__ __forceinline__ int xcd_block(int nlogical) {
+    const int per = (int)gridDim.x / XCDS;
+    const int l = ((int)blockIdx.x % XCDS) * per + (int)blockIdx.x / XCDS;
+    return l < nlogical ? l : -1;
+}
+
+__host__ __forceinline__ int xcd_grid(int nlogical) { return (nlogical + XCDS - 1) / XCDS * XCDS; }
 
 struct RouteShared {
     uint64_t thr[ROWS];      // shared threshold key per row (max over the waves' lower bounds)
@@ -220,10 +228,88 @@ struct RouteShared {
     int32_t redo;
 };
 
+// Random sentinels (Section 3.1, item 2) and the ledger write of one row (lane-per-row).
+// cmb: route (segment 0) and near-miss (segment 1) indices, ascending, padded with ~0.
+// RW >= r is the register width of the random list.
+template <int RW>
+__device__ __forceinline__ void emit_row(const RouteArgs& p, const uint32_t (&cmb)[TOPW], int ki, int mi,
+                                         int my_row, int my_n, int h, unsigned char* lds, int lane) {
+    // Bitmap over allowed chunks: route + near-miss + accepted draws are set.
+    const int words = (p.nk + 31) >> 5;
+    uint32_t* bm = reinterpret_cast<uint32_t*>(lds) + (size_t)lane * (words + 1);
+    for (int w = 0; w < words; ++w) bm[w] = 0u;
+#pragma unroll
+    for (int s = 0; s < TOPW; ++s) {
+        if (s < ki + mi) {
+            const uint32_t j = cmb[s] & 0xFFFFu;
+            bm[j >> 5] |= 1u << (j & 31);
+        }
+    }
+    uint32_t rnd[RW];
+#pragma unroll
+    for (int s = 0; s < RW; ++s) rnd[s] = 0xFFFFFFFFu;
+    int nr = 0;
+    const int pool = my_n - ki - mi;
+    const int rwant = (my_row < 0) ? 0 : min(p.r, pool);
+    if (p.r > 0) {
+        // Draws only for rows whose pool exceeds r; smaller pools are taken whole by the fill.
+        bool drawing = (my_row >= 0) && pool > p.r;
+        P4 w4 = {0u, 0u, 0u, 0u};
+        for (int t = 0; t < 65536 && __ballot(drawing); ++t) {
+            if ((t & 3) == 0) {
+                P4 c = {(uint32_t)(t >> 2), (uint32_t)my_row, (uint32_t)p.layer, (uint32_t)h};
+                w4 = philox4x32_10(c, p.seed_lo, p.seed_hi);
+            }
+            const uint32_t u = ((t & 3) == 0) ? w4.x : ((t & 3) == 1) ? w4.y : ((t & 3) == 2) ? w4.z : w4.w;
+            if (drawing) {
+                const uint32_t j = __umulhi(u, (uint32_t)my_n);
+                const uint32_t bit = 1u << (j & 31);
+                if (!(bm[j >> 5] & bit)) {
+                    bm[j >> 5] |= bit;
+#pragma unroll
+                    for (int s = 0; s < RW; ++s) rnd[s] = (s == nr) ? j : rnd[s];
+                    ++nr;
+                    drawing = nr < p.r;
+                }
+            }
+        }
+        // Fill: lowest-index chunks still free (whole pool when pool <= r; draw cap reached).
+        if (my_row >= 0 && nr < rwant) {
+            for (int w = 0; w < words && nr < rwant; ++w) {
+                uint32_t free_bits = ~bm[w];
+                while (free_bits && nr < rwant) {
+                    const uint32_t j = (uint32_t)(w * 32 + __builtin_ctz(free_bits));
+                    free_bits &= free_bits - 1u;
+                    if ((int)j >= my_n) { free_bits = 0; break; }
+#pragma unroll
+                    for (int s = 0; s < RW; ++s) rnd[s] = (s == nr) ? j : rnd[s];
+                    ++nr;
+                }
+            }
+        }
+        sort_asc<RW>(rnd);
+    }
+
+    if (my_row >= 0) {
+        int32_t* dst = p.ids + ((size_t)h * p.nq + my_row) * p.c;
+#pragma unroll
+        for (int s = 0; s < TOPW; ++s) {
+            if (s < ki) dst[s] = (int32_t)cmb[s];
+            else if (s < ki + mi) dst[p.k + (s - ki)] = (int32_t)(cmb[s] & 0xFFFFu);
+        }
+        for (int s = ki; s < p.k; ++s) dst[s] = -1;
+        for (int s = mi; s < p.m; ++s) dst[p.k + s] = -1;
+#pragma unroll
+        for (int s = 0; s < RW; ++s)
+            if (s < p.r) dst[p.k + p.m + s] = (s < nr) ? (int32_t)rnd[s] : -1;
+        p.anchor[(size_t)h * p.nq + my_row] = p.layer;
+    }
+}
+
 // ------------------------------------------------------------------------------ route kernel
 
 template <typename DT, bool CAUSAL, bool REROUTE>
-__global__ __launch_bounds__(ROWS * SPLIT) void k_route(RouteArgs p) {
+__global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2))) void k_route(RouteArgs p) {
     typedef typename Elem<DT>::type E;
     extern __shared__ __align__(16) unsigned char dyn_lds[];
     __shared__ RouteShared sh;
@@ -231,8 +317,10 @@ __global__ __launch_bounds__(ROWS * SPLIT) void k_route(RouteArgs p) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int G = (p.nq + ROWS - 1) / ROWS;
-    const int h = blockIdx.x / G;
-    const int g = blockIdx.x % G;
+    const int lb = xcd_block(p.H * G);
+    if (lb < 0) return;
+    const int h = lb / G;
+    const int g = lb % G;
 
     // ------------------------------------------------------------------ rows of this block
     if constexpr (REROUTE) {
@@ -316,31 +404,42 @@ __global__ __launch_bounds__(ROWS * SPLIT) void k_route(RouteArgs p) {
         float top8[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) top8[s] = -INFINITY;
-        typename Tile<DT>::KReg ka, kb;
-        if (wave < ntiles) tile.load_k(kb, Kh, TK * wave, p.nk, lane);
-        for (int t = wave; t < ntiles; t += SPLIT) {
-            copy_k(ka, kb);
-            if (t + SPLIT < ntiles) tile.load_k(kb, Kh, TK * (t + SPLIT), p.nk, lane);
-            f32x16 lo, hi;
-            tile.mma(ka, lo, hi);
-            rows_per_lane(lo, hi);
-            const int key0 = TK * t;
-            if (key0 + TK > nmin) {
+        // K tiles stream through a ring of NBUF register buffers, NBUF - 1 tiles ahead (a
+        // statically indexed ring: copying registers would make the loop wait on the newest load).
+        constexpr int NB = Tile<DT>::NBUF;
+        typename Tile<DT>::KReg kbuf[NB];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    if (key0 + lo_key(v) >= my_n) lo[v] = -INFINITY;
-                    if (key0 + hi_key(v) >= my_n) hi[v] = -INFINITY;
+        for (int u = 0; u < NB; ++u) tile.load_k(kbuf[u], Kh, TK * (wave + u * SPLIT), p.nk, lane);
+        for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int t = t0 + u * SPLIT;
+                const bool live = t < ntiles;                        // uniform
+                f32x16 lo, hi;
+                if (live) tile.mma(kbuf[u], lo, hi);
+                // Issued on every path (past the end it rereads the last key row), so the load
+                // counter sees one fixed sequence and waits only for the oldest buffer.
+                tile.load_k(kbuf[u], Kh, TK * (t + NB * SPLIT), p.nk, lane);
+                if (live) {
+                rows_per_lane(lo, hi);
+                const int key0 = TK * t;
+                if (key0 + TK > nmin) {
+                    const int lim = my_n - key0;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        lo[v] = (lo_key(v) < lim) ? lo[v] : -INFINITY;
+                        hi[v] = (hi_key(v) < lim) ? hi[v] : -INFINITY;
+                    }
                 }
-            }
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                float x = fmaxf(fmaxf(fmaxf(lo[4 * a], lo[4 * a + 1]), fmaxf(lo[4 * a + 2], lo[4 * a + 3])),
-                                fmaxf(fmaxf(hi[4 * a], hi[4 * a + 1]), fmaxf(hi[4 * a + 2], hi[4 * a + 3])));
+                for (int a = 0; a < 4; ++a) {
+                    const float x = fmaxf(fmaxf(fmaxf(lo[4 * a], lo[4 * a + 1]), fmaxf(lo[4 * a + 2], lo[4 * a + 3])),
+                                          fmaxf(fmaxf(hi[4 * a], hi[4 * a + 1]), fmaxf(hi[4 * a + 2], hi[4 * a + 3])));
+                    // insert x into the sorted list: entry s becomes med3(top[s-1], top[s], x)
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const float up = fmaxf(top8[s], x);
-                    x = fminf(top8[s], x);
-                    top8[s] = up;
+                    for (int s = 7; s >= 1; --s) top8[s] = __builtin_amdgcn_fmed3f(top8[s - 1], top8[s], x);
+                    top8[0] = fmaxf(top8[0], x);
+                }
                 }
             }
         }
@@ -368,65 +467,83 @@ __global__ __launch_bounds__(ROWS * SPLIT) void k_route(RouteArgs p) {
 
     for (int attempt = 0; attempt < 2; ++attempt) {
         int cnt = 0;
+        bool fresh = (attempt == 0);                                    // list empty in every lane
         float ts = key_score(sh.thr[lane]);
-        typename Tile<DT>::KReg ka, kb;
-        if (wave < ntiles) tile.load_k(kb, Kh, TK * wave, p.nk, lane);
-        for (int t = wave; t < ntiles; t += SPLIT) {
-            copy_k(ka, kb);
-            if (t + SPLIT < ntiles) tile.load_k(kb, Kh, TK * (t + SPLIT), p.nk, lane);
-            f32x16 lo, hi;
-            tile.mma(ka, lo, hi);
-            rows_per_lane(lo, hi);
-            const int key0 = TK * t;
-            const bool edge = key0 + TK > nmin;
+        constexpr int NB = Tile<DT>::NBUF;
+        typename Tile<DT>::KReg kbuf[NB];
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
+        for (int u = 0; u < NB; ++u) tile.load_k(kbuf[u], Kh, TK * (wave + u * SPLIT), p.nk, lane);
+        for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
 #pragma unroll
-                for (int v = 8 * half; v < 8 * half + 8; ++v) {
-                    const uint32_t jl = (uint32_t)(key0 + lo_key(v));
-                    const uint32_t jh = (uint32_t)(key0 + hi_key(v));
-                    const bool pl = lo[v] >= ts && (!edge || (int)jl < my_n);
-                    const bool ph = hi[v] >= ts && (!edge || (int)jh < my_n);
-                    if (pl) my_buf[cnt] = make_uint2(__float_as_uint(lo[v]), jl);
-                    cnt += pl;
-                    if (ph) my_buf[cnt] = make_uint2(__float_as_uint(hi[v]), jh);
-                    cnt += ph;
+            for (int u = 0; u < NB; ++u) {
+                const int t = t0 + u * SPLIT;
+                const bool live = t < ntiles;                        // uniform
+                f32x16 lo, hi;
+                if (live) tile.mma(kbuf[u], lo, hi);
+                // Issued on every path (past the end it rereads the last key row), so the load
+                // counter sees one fixed sequence and waits only for the oldest buffer.
+                tile.load_k(kbuf[u], Kh, TK * (t + NB * SPLIT), p.nk, lane);
+                if (live) {
+                rows_per_lane(lo, hi);
+                const int key0 = TK * t;
+                if (key0 + TK > nmin) {                                 // keys past a row's end
+                    const int lim = my_n - key0;
+                    const float nan = __builtin_nanf("");
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        lo[v] = (lo_key(v) < lim) ? lo[v] : nan;            // NaN never passes >=
+                        hi[v] = (hi_key(v) < lim) ? hi[v] : nan;
+                    }
                 }
-                if (__ballot(cnt >= 16)) {
-                    drain(top, my_buf, cnt);
-                    cnt = 0;
-                    const uint64_t own = pick(top, p.sel - 1);
-                    if (own != EMPTY_KEY && my_row >= 0) atomicMax((unsigned long long*)&sh.thr[lane], own);
+                // Branch-free append: every slot stores its (score, index) at the row's current
+                // count and the count advances only when the score passes, so a failing slot's
+                // store is overwritten by the next one (<= 15 held + 16 slots: index <= 30).
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                    for (int v = 8 * half; v < 8 * half + 8; ++v) {
+                        my_buf[cnt] = make_uint2(__float_as_uint(lo[v]), (uint32_t)(key0 + lo_key(v)));
+                        cnt += (lo[v] >= ts) ? 1 : 0;
+                        my_buf[cnt] = make_uint2(__float_as_uint(hi[v]), (uint32_t)(key0 + hi_key(v)));
+                        cnt += (hi[v] >= ts) ? 1 : 0;
+                    }
+                    if (__ballot(cnt >= 16)) {
+                        drain(top, my_buf, cnt, fresh);
+                        cnt = 0;
+                        const uint64_t own = pick(top, p.sel - 1);
+                        if (own != EMPTY_KEY && my_row >= 0) atomicMax((unsigned long long*)&sh.thr[lane], own);
+                    }
+                }
+                ts = key_score(sh.thr[lane]);
                 }
             }
-            ts = key_score(sh.thr[lane]);
         }
-        drain(top, my_buf, cnt);
+        drain(top, my_buf, cnt, fresh);
 
         // Merge the four waves' lists through two LDS slots: 1 -> 0 and 3 -> 2, then 2 -> 0.
-        uint64_t* xchg = reinterpret_cast<uint64_t*>(dyn_lds);          // [2][ROWS][TOPW]
+        uint64_t* xchg = reinterpret_cast<uint64_t*>(dyn_lds);          // [2][ROWS][XSTRIDE]
         __syncthreads();                                                // every buffer is drained
         if (wave & 1) {
 #pragma unroll
-            for (int s = 0; s < TOPW; ++s) xchg[((size_t)(wave >> 1) * ROWS + lane) * TOPW + s] = top[s];
+            for (int s = 0; s < TOPW; ++s) xchg[((size_t)(wave >> 1) * ROWS + lane) * XSTRIDE + s] = top[s];
         }
         __syncthreads();
         if (!(wave & 1)) {
             uint64_t y[TOPW];
 #pragma unroll
-            for (int s = 0; s < TOPW; ++s) y[s] = xchg[((size_t)(wave >> 1) * ROWS + lane) * TOPW + s];
+            for (int s = 0; s < TOPW; ++s) y[s] = xchg[((size_t)(wave >> 1) * ROWS + lane) * XSTRIDE + s];
             merge_top_desc<TOPW>(top, y);
         }
         __syncthreads();
         if (wave == 2) {
 #pragma unroll
-            for (int s = 0; s < TOPW; ++s) xchg[(size_t)lane * TOPW + s] = top[s];
+            for (int s = 0; s < TOPW; ++s) xchg[(size_t)lane * XSTRIDE + s] = top[s];
         }
         __syncthreads();
         if (wave == 0) {
             uint64_t y[TOPW];
 #pragma unroll
-            for (int s = 0; s < TOPW; ++s) y[s] = xchg[(size_t)lane * TOPW + s];
+            for (int s = 0; s < TOPW; ++s) y[s] = xchg[(size_t)lane * XSTRIDE + s];
             merge_top_desc<TOPW>(top, y);
             // Each row must now hold min(sel, n) keys.  Only a reroute threshold taken from the
             // rescore kernel's arithmetic can miss (rounding); such rows are redone from -inf.
@@ -467,156 +584,127 @@ __global__ __launch_bounds__(ROWS * SPLIT) void k_route(RouteArgs p) {
     }
     sort_asc<TOPW>(cmb);
 
-    // Sampler bitmap over allowed chunks: route + near-miss + accepted draws are set.
-    const int words = (p.nk + 31) >> 5;
-    uint32_t* bm = reinterpret_cast<uint32_t*>(dyn_lds) + (size_t)lane * (words + 1);
-    for (int w = 0; w < words; ++w) bm[w] = 0u;
-#pragma unroll
-    for (int s = 0; s < TOPW; ++s) {
-        if (s < ki + mi) {
-            const uint32_t j = cmb[s] & 0xFFFFu;
-            bm[j >> 5] |= 1u << (j & 31);
-        }
-    }
-    uint32_t rnd[TOPW];
-#pragma unroll
-    for (int s = 0; s < TOPW; ++s) rnd[s] = 0xFFFFFFFFu;
-    int nr = 0;
-    const int pool = my_n - ki - mi;
-    const int rwant = (my_row < 0) ? 0 : min(p.r, pool);
-    if (p.r > 0) {
-        // Draws only for rows whose pool exceeds r; smaller pools are taken whole by the fill.
-        bool drawing = (my_row >= 0) && pool > p.r;
-        P4 w4 = {0u, 0u, 0u, 0u};
-        for (int t = 0; t < 65536 && __ballot(drawing); ++t) {
-            if ((t & 3) == 0) {
-                P4 c = {(uint32_t)(t >> 2), (uint32_t)my_row, (uint32_t)p.layer, (uint32_t)h};
-                w4 = philox4x32_10(c, p.seed_lo, p.seed_hi);
-            }
-            const uint32_t u = ((t & 3) == 0) ? w4.x : ((t & 3) == 1) ? w4.y : ((t & 3) == 2) ? w4.z : w4.w;
-            if (drawing) {
-                const uint32_t j = __umulhi(u, (uint32_t)my_n);
-                const uint32_t bit = 1u << (j & 31);
-                if (!(bm[j >> 5] & bit)) {
-                    bm[j >> 5] |= bit;
-#pragma unroll
-                    for (int s = 0; s < TOPW; ++s) rnd[s] = (s == nr) ? j : rnd[s];
-                    ++nr;
-                    drawing = nr < p.r;
-                }
-            }
-        }
-        // Fill: lowest-index chunks still free (whole pool when pool <= r; draw cap reached).
-        if (my_row >= 0 && nr < rwant) {
-            for (int w = 0; w < words && nr < rwant; ++w) {
-                uint32_t free_bits = ~bm[w];
-                while (free_bits && nr < rwant) {
-                    const uint32_t j = (uint32_t)(w * 32 + __builtin_ctz(free_bits));
-                    free_bits &= free_bits - 1u;
-                    if ((int)j >= my_n) { free_bits = 0; break; }
-#pragma unroll
-                    for (int s = 0; s < TOPW; ++s) rnd[s] = (s == nr) ? j : rnd[s];
-                    ++nr;
-                }
-            }
-        }
-        sort_asc<TOPW>(rnd);
-    }
-
-    if (my_row >= 0) {
-        int32_t* dst = p.ids + ((size_t)h * p.nq + my_row) * p.c;
-#pragma unroll
-        for (int s = 0; s < TOPW; ++s) {
-            if (s < ki) dst[s] = (int32_t)cmb[s];
-            else if (s < ki + mi) dst[p.k + (s - ki)] = (int32_t)(cmb[s] & 0xFFFFu);
-        }
-        for (int s = ki; s < p.k; ++s) dst[s] = -1;
-        for (int s = mi; s < p.m; ++s) dst[p.k + s] = -1;
-#pragma unroll
-        for (int s = 0; s < TOPW; ++s)
-            if (s < p.r) dst[p.k + p.m + s] = (s < nr) ? (int32_t)rnd[s] : -1;
-        p.anchor[(size_t)h * p.nq + my_row] = p.layer;
-    }
+    if (p.r <= 8) emit_row<8>(p, cmb, ki, mi, my_row, my_n, h, dyn_lds, lane);
+    else emit_row<TOPW>(p, cmb, ki, mi, my_row, my_n, h, dyn_lds, lane);
 }
 
 // ------------------------------------------------------------------------------ rescore
 
-template <typename DT>
-__device__ __forceinline__ float dot_row(const typename Elem<DT>::type* q, const typename Elem<DT>::type* k);
-
-template <>
-__device__ __forceinline__ float dot_row<bf16_t>(const uint16_t* q, const uint16_t* k) {
-    // 32 packed bf16 pairs; v_dot2 adds two exact bf16 products into the fp32 sum.
-    const uint4* qa = reinterpret_cast<const uint4*>(q);
-    const uint4* ka = reinterpret_cast<const uint4*>(k);
-    uint32_t qw[32], kw[32];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-        const uint4 a = qa[v], b = ka[v];
-        qw[4 * v + 0] = a.x; qw[4 * v + 1] = a.y; qw[4 * v + 2] = a.z; qw[4 * v + 3] = a.w;
-        kw[4 * v + 0] = b.x; kw[4 * v + 1] = b.y; kw[4 * v + 2] = b.z; kw[4 * v + 3] = b.w;
+// Lanes per candidate key row: each lane loads one 16-byte chunk, so a row is one contiguous
+// run of CL lanes (one or two cache lines) rather than one lane reading it whole, which would
+// make every load instruction touch 64 different lines.
+template <typename DT> struct Gather;
+template <> struct Gather<bf16_t> {
+    static constexpr int CL = 8;          // 8 lanes x 8 bf16
+    __device__ __forceinline__ static float dot(const uint4& q, const uint4& k) {
+        float acc = 0.f;
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x), __builtin_bit_cast(bf16x2, k.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y), __builtin_bit_cast(bf16x2, k.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z), __builtin_bit_cast(bf16x2, k.z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w), __builtin_bit_cast(bf16x2, k.w), acc, false);
+        return acc;
     }
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[e]),
-                                              __builtin_bit_cast(bf16x2, kw[e]), acc, false);
-    return acc;
-}
-
-template <>
-__device__ __forceinline__ float dot_row<float>(const float* q, const float* k) {
-    const float4* qa = reinterpret_cast<const float4*>(q);
-    const float4* ka = reinterpret_cast<const float4*>(k);
-    float acc = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const float4 a = qa[v], b = ka[v];
-        acc = fmaf(a.x, b.x, acc);
-        acc = fmaf(a.y, b.y, acc);
-        acc = fmaf(a.z, b.z, acc);
-        acc = fmaf(a.w, b.w, acc);
+};
+template <> struct Gather<float> {
+    static constexpr int CL = 16;         // 16 lanes x 4 fp32
+    __device__ __forceinline__ static float dot(const uint4& q, const uint4& k) {
+        float acc = __uint_as_float(q.x) * __uint_as_float(k.x);
+        acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+        acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+        acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+        return acc;
     }
-    return acc;
-}
+};
 
 constexpr int RESCORE_THREADS = 1024;     // 16 waves x 4 rows: rows 64b..64b+63 of head h
 
-// Block (h, b): rows 64b..64b+63 of head h; `cp` lanes per row (power of two >= c).
-template <typename DT>
+// Block (h, b): rows 64b..64b+63 of head h; wave w takes rows 4w..4w+3.  Per row, the c
+// candidate IDs are scored in NP passes of 64 / CL candidates; lanes g*CL .. g*CL+CL-1 share
+// candidate g of a pass.  Rows go in batches of 8 / NP so that each lane has 8 independent
+// 16-byte K loads in flight: the kernel moves few bytes, so its time is set by how many memory
+// round trips each wave waits for, not by bandwidth.  At NP = 4 that fits 64 VGPRs, so two
+// 1024-thread blocks share a CU and a 32-head layer runs in a single round of blocks.  Loads are unconditional with clamped
+// addresses; lanes without a candidate mask their score to NaN, which min/max then ignore.
+template <typename DT, int NP>
 __global__ __launch_bounds__(RESCORE_THREADS) void k_rescore(RescoreArgs p) {
     typedef typename Elem<DT>::type E;
+    constexpr int CL = Gather<DT>::CL;
+    constexpr int CPP = 64 / CL;                      // candidates per pass
+    constexpr int RB = (8 / NP) > 0 ? 8 / NP : 1;   // rows per batch
+    static_assert(4 % RB == 0, "rows per batch must divide 4");
+    constexpr int EPC = 16 / (int)sizeof(E);          // elements per 16-byte chunk
     __shared__ int32_t wave_flags[RESCORE_THREADS / 64];
     const int G = (p.nq + ROWS - 1) / ROWS;
-    const int h = blockIdx.x / G;
-    const int b = blockIdx.x % G;
+    const int lb = xcd_block(p.H * G);
+    if (lb < 0) return;
+    const int h = lb / G;
+    const int b = lb % G;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int cp = p.cp;
-    const int rpp = 64 / cp;                          // rows per wave pass
-    const int slot = lane & (cp - 1);
+    const int ch = lane % CL;                         // 16-byte chunk of the key / query row
+    const int grp = lane / CL;                        // candidate slot within a pass
     const E* Qh = reinterpret_cast<const E*>(p.qp) + (size_t)h * p.nq * 64;
     const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
+    const int32_t* Ih = p.ids + (size_t)h * p.nq * p.c;
     const float nan = __builtin_nanf("");
     int flagged = 0;
-    for (int r0 = 0; r0 < 4; r0 += rpp) {
-        const int rl = r0 + lane / cp;                // row within this wave's 4
-        const int i = b * ROWS + wave * 4 + rl;
-        const bool row_ok = rl < 4 && i < p.nq;
-        const size_t flat = (size_t)h * p.nq + (row_ok ? i : 0);
-        int id = (row_ok && slot < p.c) ? p.ids[flat * p.c + slot] : -1;
-        id = (id < p.nk) ? id : -1;                   // never gather outside K, whatever the ledger holds
-        float s = nan;
-        if (id >= 0) s = dot_row<DT>(Qh + (size_t)i * 64, Kh + (size_t)id * 64);
-        const float alpha = wave_min_in(slot < p.k ? s : nan, cp);
-        const float nmin = wave_min_in((slot >= p.k && slot < p.sel) ? s : nan, cp);
-        float beta = wave_max_in((slot >= p.k && slot < p.c) ? s : nan, cp);
-        const int nsel = wave_sum_in((slot < p.sel && id >= 0) ? 1 : 0, cp);
-        beta = (beta != beta) ? -INFINITY : beta;
-        const bool reuse = alpha > (beta + p.gamma);
-        if (row_ok) {
-            if (p.cand_scores && slot < p.c) p.cand_scores[flat * p.c + slot] = s;
-            if (slot == 0) {
+#pragma unroll
+    for (int r0 = 0; r0 < 4; r0 += RB) {
+        const int ibase = b * ROWS + wave * 4 + r0;
+        uint4 qv[RB];
+        int ids[RB][NP];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+            const int i = ibase + rr;
+            const int ic = i < p.nq ? i : p.nq - 1;
+            qv[rr] = *reinterpret_cast<const uint4*>(Qh + (size_t)ic * 64 + ch * EPC);
+#pragma unroll
+            for (int ps = 0; ps < NP; ++ps) {
+                const int c = grp + CPP * ps;
+                const bool ok = (i < p.nq) & (c < p.c);
+                const int id = Ih[ok ? (size_t)i * p.c + c : 0];
+                // The select's condition reads the loaded value, so the load cannot be sunk into a
+                // branch (one wait per load); the unsigned compare also drops -1 padding and any
+                // index outside K, whatever the ledger holds.
+                ids[rr][ps] = (ok & ((unsigned)id < (unsigned)p.nk)) ? id : -1;
+            }
+        }
+        uint4 kv[RB][NP];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+            for (int ps = 0; ps < NP; ++ps) {
+                const int id = ids[rr][ps] >= 0 ? ids[rr][ps] : 0;
+                kv[rr][ps] = *reinterpret_cast<const uint4*>(Kh + (size_t)id * 64 + ch * EPC);
+            }
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+            const int i = ibase + rr;
+            float alpha = nan, nmin = nan, beta = nan;
+            int nsel = 0;
+#pragma unroll
+            for (int ps = 0; ps < NP; ++ps) {
+                float s = group_sum<CL>(Gather<DT>::dot(qv[rr], kv[rr][ps]));
+                const int c = grp + CPP * ps;
+                s = (ids[rr][ps] >= 0) ? s : nan;
+                if (p.cand_scores && ch == 0 && c < p.c && i < p.nq)
+                    p.cand_scores[((size_t)h * p.nq + i) * p.c + c] = s;
+                alpha = fminf(alpha, c < p.k ? s : nan);
+                nmin = fminf(nmin, (c >= p.k && c < p.sel) ? s : nan);
+                beta = fmaxf(beta, (c >= p.k && c < p.c) ? s : nan);
+                nsel += (c < p.sel && ids[rr][ps] >= 0) ? 1 : 0;
+            }
+            auto fmin_u = [](uint32_t a, uint32_t b) { return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b))); };
+            auto fmax_u = [](uint32_t a, uint32_t b) { return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); };
+            auto add_u = [](uint32_t a, uint32_t b) { return a + b; };
+            alpha = __uint_as_float(across_groups<CL>(__float_as_uint(alpha), fmin_u));
+            nmin = __uint_as_float(across_groups<CL>(__float_as_uint(nmin), fmin_u));
+            beta = __uint_as_float(across_groups<CL>(__float_as_uint(beta), fmax_u));
+            nsel = (int)across_groups<CL>((uint32_t)nsel, add_u);
+            beta = (beta != beta) ? -INFINITY : beta;
+            const bool reuse = alpha > (beta + p.gamma);
+            if (lane == 0 && i < p.nq) {
+                const size_t flat = (size_t)h * p.nq + i;
                 p.flags_ws[flat] = reuse ? 0 : 1;
                 p.hint_ws[flat] = (nsel == p.sel) ? fminf(alpha, nmin) : -INFINITY;
                 if (p.out_flags) p.out_flags[flat] = reuse ? 0 : 1;
@@ -626,16 +714,13 @@ __global__ __launch_bounds__(RESCORE_THREADS) void k_rescore(RescoreArgs p) {
             }
         }
     }
-    int wsum = flagged;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
-    if (lane == 0) wave_flags[wave] = wsum;
+    if (lane == 0) wave_flags[wave] = flagged;
     __syncthreads();
     if (threadIdx.x == 0) {
         int tot = 0;
 #pragma unroll
         for (int w = 0; w < RESCORE_THREADS / 64; ++w) tot += wave_flags[w];
-        p.bcount[blockIdx.x] = tot;
+        p.bcount[lb] = tot;
     }
 }
 
@@ -643,7 +728,7 @@ __global__ __launch_bounds__(RESCORE_THREADS) void k_rescore(RescoreArgs p) {
 
 size_t route_lds_bytes(int nk) {
     const size_t cand = (size_t)SPLIT * ROWS * CSTRIDE * sizeof(uint2);
-    const size_t xchg = (size_t)2 * ROWS * TOPW * sizeof(uint64_t);
+    const size_t xchg = (size_t)2 * ROWS * XSTRIDE * sizeof(uint64_t);
     const size_t gm = (size_t)ROWS * GSTRIDE * sizeof(float);
     const size_t bm = (size_t)ROWS * ((nk + 31) / 32 + 1) * sizeof(uint32_t);
     size_t m = cand > xchg ? cand : xchg;
@@ -655,7 +740,7 @@ template <typename DT, bool CAUSAL, bool REROUTE>
 static hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
     const int G = (a.nq + ROWS - 1) / ROWS;
     const size_t lds = route_lds_bytes(a.nk);
-    hipLaunchKernelGGL((k_route<DT, CAUSAL, REROUTE>), dim3(a.H * G), dim3(ROWS * SPLIT), lds, st, a);
+    hipLaunchKernelGGL((k_route<DT, CAUSAL, REROUTE>), dim3(xcd_grid(a.H * G)), dim3(ROWS * SPLIT), lds, st, a);
     return hipGetLastError();
 }
 
@@ -669,9 +754,16 @@ hipError_t launch_route(const RouteArgs& a, bool bf16, bool causal, bool reroute
 }
 
 hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st) {
-    const int G = (a.nq + ROWS - 1) / ROWS;
-    if (bf16) hipLaunchKernelGGL((k_rescore<bf16_t>), dim3(a.H * G), dim3(RESCORE_THREADS), 0, st, a);
-    else hipLaunchKernelGGL((k_rescore<float>), dim3(a.H * G), dim3(RESCORE_THREADS), 0, st, a);
+    const dim3 grid(xcd_grid(a.H * ((a.nq + ROWS - 1) / ROWS)));
+    const int passes = (a.c + (bf16 ? 7 : 3)) / (bf16 ? 8 : 4);   // candidates per pass: 64 / lanes per row
+    if (bf16) {
+        if (passes <= 4) hipLaunchKernelGGL((k_rescore<bf16_t, 4>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        else hipLaunchKernelGGL((k_rescore<bf16_t, 8>), grid, dim3(RESCORE_THREADS), 0, st, a);
+    } else {
+        if (passes <= 4) hipLaunchKernelGGL((k_rescore<float, 4>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        else if (passes <= 8) hipLaunchKernelGGL((k_rescore<float, 8>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        else hipLaunchKernelGGL((k_rescore<float, 16>), grid, dim3(RESCORE_THREADS), 0, st, a);
+    }
     return hipGetLastError();
 }
 

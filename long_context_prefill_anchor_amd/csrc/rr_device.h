@@ -160,12 +160,23 @@ enum : int {
     DPP_XOR2 = 0x4E,          // quad_perm [2,3,0,1]
     DPP_HALF_MIRROR = 0x141,  // lane i of each 8-lane half-row <- lane 7 - i
     DPP_ROR8 = 0x128,         // lane i of each row <- lane (i + 8) mod 16
+    DPP_REVERSE = 0x1B,       // quad_perm [3,2,1,0]
+    DPP_BCAST0 = 0x00,        // quad_perm [0,0,0,0]: every lane of a quad <- its lane 0
+    DPP_BCAST1 = 0x55,        // quad_perm [1,1,1,1]
+    DPP_BCAST2 = 0xAA,        // quad_perm [2,2,2,2]
+    DPP_BCAST3 = 0xFF,        // quad_perm [3,3,3,3]
 };
 template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL> __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Sum over aligned groups of G consecutive lanes (G = 8 or 16); every lane of a group ends with

@@ -242,7 +242,7 @@ __device__ __forceinline__ void emit_row(const RouteArgs& p, const uint32_t (&cm
     for (int s = 0; s < TOPW; ++s) {
         if (s < ki + mi) {
             const uint32_t j = cmb[s] & 0xFFFFu;
-            bm[j >> 5] |= 1u << (j & 31);
+            atomicOr(&bm[j >> 5], 1u << (j & 31));
         }
     }
     uint32_t rnd[RW];
@@ -307,6 +307,160 @@ __device__ __forceinline__ void emit_row(const RouteArgs& p, const uint32_t (&cm
 }
 
 // ------------------------------------------------------------------------------ route kernel
+
+// Per-lane state of the route kernel shared by the selection pass and the redo path.
+template <typename DT>
+struct RowCtx {
+    typedef typename Elem<DT>::type E;
+    int lane, wave, h, my_row, my_n, nmin, ntiles;
+    const E* Qh;
+    const E* Kh;
+    uint2* my_buf;
+    bool redo_row;
+};
+
+// Streaming selection pass from the rows' shared thresholds (sh.thr), merge of the four waves'
+// lists and ledger write (wave 0).  Attempt 0 emits every row that holds min(k+m, n) keys; in
+// reroute mode the others are marked for a redo from -inf (attempt 1, which emits only them).
+template <typename DT, bool CAUSAL, bool REROUTE>
+__device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared& sh, unsigned char* dyn_lds,
+                                                Tile<DT>& tile, RowCtx<DT>& cx, int attempt) {
+    const int lane = cx.lane, wave = cx.wave, h = cx.h, my_row = cx.my_row, my_n = cx.my_n;
+    const int nmin = cx.nmin, ntiles = cx.ntiles;
+    const auto* Kh = cx.Kh;
+    uint2* my_buf = cx.my_buf;
+    if constexpr (REROUTE) tile.load_q(cx.Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
+    uint64_t top[TOPW];
+#pragma unroll
+    for (int s = 0; s < TOPW; ++s) top[s] = EMPTY_KEY;
+    int cnt = 0;
+    bool fresh = true;                                                  // list empty in every lane
+    float ts = key_score(sh.thr[lane]);
+    constexpr int NB = Tile<DT>::NBUF;
+    typename Tile<DT>::KReg kbuf[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) tile.load_k(kbuf[u], Kh, TK * (wave + u * SPLIT), p.nk, lane);
+    for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int t = t0 + u * SPLIT;
+            const bool live = t < ntiles;                        // uniform
+            f32x16 lo, hi;
+            if (live) tile.mma(kbuf[u], lo, hi);
+            // Issued on every path (past the end it rereads the last key row), so the load
+            // counter sees one fixed sequence and waits only for the oldest buffer.
+            tile.load_k(kbuf[u], Kh, TK * (t + NB * SPLIT), p.nk, lane);
+            if (live) {
+            rows_per_lane(lo, hi);
+            const int key0 = TK * t;
+            if (key0 + TK > nmin) {                                 // keys past a row's end
+                const int lim = my_n - key0;
+                const float nan = __builtin_nanf("");
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    lo[v] = (lo_key(v) < lim) ? lo[v] : nan;            // NaN never passes >=
+                    hi[v] = (hi_key(v) < lim) ? hi[v] : nan;
+                }
+            }
+            // Branch-free append: every slot stores its (score, index) at the row's current
+            // count and the count advances only when the score passes, so a failing slot's
+            // store is overwritten by the next one (<= 15 held + 16 slots: index <= 30).
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                for (int v = 8 * half; v < 8 * half + 8; ++v) {
+                    my_buf[cnt] = make_uint2(__float_as_uint(lo[v]), (uint32_t)(key0 + lo_key(v)));
+                    cnt += (lo[v] >= ts) ? 1 : 0;
+                    my_buf[cnt] = make_uint2(__float_as_uint(hi[v]), (uint32_t)(key0 + hi_key(v)));
+                    cnt += (hi[v] >= ts) ? 1 : 0;
+                }
+                if (__ballot(cnt >= 16)) {
+                    drain(top, my_buf, cnt, fresh);
+                    cnt = 0;
+                    const uint64_t own = pick(top, p.sel - 1);
+                    if (own != EMPTY_KEY && my_row >= 0) atomicMax((unsigned long long*)&sh.thr[lane], own);
+                }
+            }
+            ts = key_score(sh.thr[lane]);
+            }
+        }
+    }
+    drain(top, my_buf, cnt, fresh);
+
+    // Merge the four waves' lists through two LDS slots: 1 -> 0 and 3 -> 2, then 2 -> 0.
+    uint64_t* xchg = reinterpret_cast<uint64_t*>(dyn_lds);          // [2][ROWS][XSTRIDE]
+    __syncthreads();                                                // every buffer is drained
+    if (wave & 1) {
+#pragma unroll
+        for (int s = 0; s < TOPW; ++s) xchg[((size_t)(wave >> 1) * ROWS + lane) * XSTRIDE + s] = top[s];
+    }
+    __syncthreads();
+    if (!(wave & 1)) {
+        uint64_t y[TOPW];
+#pragma unroll
+        for (int s = 0; s < TOPW; ++s) y[s] = xchg[((size_t)(wave >> 1) * ROWS + lane) * XSTRIDE + s];
+        merge_top_desc<TOPW>(top, y);
+    }
+    __syncthreads();
+    if (wave == 2) {
+#pragma unroll
+        for (int s = 0; s < TOPW; ++s) xchg[(size_t)lane * XSTRIDE + s] = top[s];
+    }
+    __syncthreads();
+    if (wave == 0) {
+        uint64_t y[TOPW];
+#pragma unroll
+        for (int s = 0; s < TOPW; ++s) y[s] = xchg[(size_t)lane * XSTRIDE + s];
+        merge_top_desc<TOPW>(top, y);
+        bool emit_now = my_row >= 0;
+        if constexpr (REROUTE) {
+            // Each row must now hold min(sel, n) keys.  Only a reroute threshold taken from the
+            // rescore kernel's arithmetic can miss (rounding); such rows are redone from -inf
+            // while every other row keeps the result it emits now.
+            if (attempt == 0) {
+                int have = 0;
+#pragma unroll
+                for (int s = 0; s < TOPW; ++s) have += (top[s] != EMPTY_KEY);
+                const bool redo = (my_row >= 0) && have < min(p.sel, my_n);
+                cx.redo_row = redo;
+                if (__ballot(redo)) {
+                    sh.thr[lane] = redo ? make_key(-INFINITY, 0xFFFFFFFFu) : NO_PASS_KEY;
+                    if (lane == 0) sh.redo = 1;
+                }
+                emit_now = emit_now && !redo;
+            } else {
+                emit_now = emit_now && cx.redo_row;
+            }
+        }
+        // Route = entries [0, ki), near-miss = [ki, ki+mi) of the sorted list; both emitted
+        // ascending by chunk index via one ascending sort of (segment << 16 | index).
+        const int ki = min(p.k, my_n);
+        const int mi = min(p.m, my_n - ki);
+        uint32_t cmb[TOPW];
+#pragma unroll
+        for (int s = 0; s < TOPW; ++s) {
+            const uint32_t j = key_index(top[s]);
+            cmb[s] = (s < ki) ? j : ((s < ki + mi) ? (0x10000u | j) : 0xFFFFFFFFu);
+        }
+        sort_asc<TOPW>(cmb);
+        const int erow = emit_now ? my_row : -1;
+        if (p.r <= 8) emit_row<8>(p, cmb, ki, mi, erow, my_n, h, dyn_lds, lane);
+        else emit_row<TOPW>(p, cmb, ki, mi, erow, my_n, h, dyn_lds, lane);
+    }
+    __syncthreads();                                                    // LDS free, sh.redo final
+}
+
+// Rows whose reroute threshold missed (see select_and_emit) are selected again from -inf.  It
+// runs only when a row needs it.  The context goes through an empty asm so the compiler cannot
+// share address arithmetic with the first pass, which would keep that pass's registers alive
+// through the merge.
+template <typename DT, bool CAUSAL>
+__device__ __forceinline__ void redo_rows(const RouteArgs& p, RouteShared& sh, unsigned char* dyn_lds, RowCtx<DT>& cx) {
+    asm volatile("" : "+v"(cx.my_n), "+v"(cx.nmin), "+v"(cx.my_row), "+v"(cx.ntiles));
+    asm volatile("" : "+v"(cx.Kh), "+v"(cx.Qh), "+v"(cx.my_buf));
+    Tile<DT> tile;
+    select_and_emit<DT, CAUSAL, true>(p, sh, dyn_lds, tile, cx, 1);
+}
 
 template <typename DT, bool CAUSAL, bool REROUTE>
 __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2))) void k_route(RouteArgs p) {
@@ -389,7 +543,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     const E* Qh = reinterpret_cast<const E*>(p.qp) + (size_t)h * p.nq * 64;
     const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
     Tile<DT> tile;
-    tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
+    if constexpr (!REROUTE) tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
 
     uint2* my_buf = reinterpret_cast<uint2*>(dyn_lds) + ((size_t)wave * ROWS + lane) * CSTRIDE;
 
@@ -461,131 +615,11 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     __syncthreads();
 
     // ------------------------------------------------------------------ streaming pass
-    uint64_t top[TOPW];
-#pragma unroll
-    for (int s = 0; s < TOPW; ++s) top[s] = EMPTY_KEY;
-
-    for (int attempt = 0; attempt < 2; ++attempt) {
-        int cnt = 0;
-        bool fresh = (attempt == 0);                                    // list empty in every lane
-        float ts = key_score(sh.thr[lane]);
-        constexpr int NB = Tile<DT>::NBUF;
-        typename Tile<DT>::KReg kbuf[NB];
-#pragma unroll
-        for (int u = 0; u < NB; ++u) tile.load_k(kbuf[u], Kh, TK * (wave + u * SPLIT), p.nk, lane);
-        for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
-#pragma unroll
-            for (int u = 0; u < NB; ++u) {
-                const int t = t0 + u * SPLIT;
-                const bool live = t < ntiles;                        // uniform
-                f32x16 lo, hi;
-                if (live) tile.mma(kbuf[u], lo, hi);
-                // Issued on every path (past the end it rereads the last key row), so the load
-                // counter sees one fixed sequence and waits only for the oldest buffer.
-                tile.load_k(kbuf[u], Kh, TK * (t + NB * SPLIT), p.nk, lane);
-                if (live) {
-                rows_per_lane(lo, hi);
-                const int key0 = TK * t;
-                if (key0 + TK > nmin) {                                 // keys past a row's end
-                    const int lim = my_n - key0;
-                    const float nan = __builtin_nanf("");
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        lo[v] = (lo_key(v) < lim) ? lo[v] : nan;            // NaN never passes >=
-                        hi[v] = (hi_key(v) < lim) ? hi[v] : nan;
-                    }
-                }
-                // Branch-free append: every slot stores its (score, index) at the row's current
-                // count and the count advances only when the score passes, so a failing slot's
-                // store is overwritten by the next one (<= 15 held + 16 slots: index <= 30).
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-#pragma unroll
-                    for (int v = 8 * half; v < 8 * half + 8; ++v) {
-                        my_buf[cnt] = make_uint2(__float_as_uint(lo[v]), (uint32_t)(key0 + lo_key(v)));
-                        cnt += (lo[v] >= ts) ? 1 : 0;
-                        my_buf[cnt] = make_uint2(__float_as_uint(hi[v]), (uint32_t)(key0 + hi_key(v)));
-                        cnt += (hi[v] >= ts) ? 1 : 0;
-                    }
-                    if (__ballot(cnt >= 16)) {
-                        drain(top, my_buf, cnt, fresh);
-                        cnt = 0;
-                        const uint64_t own = pick(top, p.sel - 1);
-                        if (own != EMPTY_KEY && my_row >= 0) atomicMax((unsigned long long*)&sh.thr[lane], own);
-                    }
-                }
-                ts = key_score(sh.thr[lane]);
-                }
-            }
-        }
-        drain(top, my_buf, cnt, fresh);
-
-        // Merge the four waves' lists through two LDS slots: 1 -> 0 and 3 -> 2, then 2 -> 0.
-        uint64_t* xchg = reinterpret_cast<uint64_t*>(dyn_lds);          // [2][ROWS][XSTRIDE]
-        __syncthreads();                                                // every buffer is drained
-        if (wave & 1) {
-#pragma unroll
-            for (int s = 0; s < TOPW; ++s) xchg[((size_t)(wave >> 1) * ROWS + lane) * XSTRIDE + s] = top[s];
-        }
-        __syncthreads();
-        if (!(wave & 1)) {
-            uint64_t y[TOPW];
-#pragma unroll
-            for (int s = 0; s < TOPW; ++s) y[s] = xchg[((size_t)(wave >> 1) * ROWS + lane) * XSTRIDE + s];
-            merge_top_desc<TOPW>(top, y);
-        }
-        __syncthreads();
-        if (wave == 2) {
-#pragma unroll
-            for (int s = 0; s < TOPW; ++s) xchg[(size_t)lane * XSTRIDE + s] = top[s];
-        }
-        __syncthreads();
-        if (wave == 0) {
-            uint64_t y[TOPW];
-#pragma unroll
-            for (int s = 0; s < TOPW; ++s) y[s] = xchg[(size_t)lane * XSTRIDE + s];
-            merge_top_desc<TOPW>(top, y);
-            // Each row must now hold min(sel, n) keys.  Only a reroute threshold taken from the
-            // rescore kernel's arithmetic can miss (rounding); such rows are redone from -inf.
-            int have = 0;
-#pragma unroll
-            for (int s = 0; s < TOPW; ++s) have += (top[s] != EMPTY_KEY);
-            const bool redo = (my_row >= 0) && have < min(p.sel, my_n);
-            if (__ballot(redo) && attempt == 0) {
-                sh.thr[lane] = redo ? make_key(-INFINITY, 0xFFFFFFFFu) : NO_PASS_KEY;
-                if (lane == 0) sh.redo = 1;
-                if (redo) {
-#pragma unroll
-                    for (int s = 0; s < TOPW; ++s) top[s] = EMPTY_KEY;
-                }
-            }
-        }
-        __syncthreads();
-        if (!sh.redo) break;                                            // uniform over the block
-        if (wave != 0) {
-#pragma unroll
-            for (int s = 0; s < TOPW; ++s) top[s] = EMPTY_KEY;
-        }
-        __syncthreads();                                                // everyone has read sh.redo
-        if (threadIdx.x == 0) sh.redo = 0;
+    RowCtx<DT> cx{lane, wave, h, my_row, my_n, nmin, ntiles, Qh, Kh, my_buf, false};
+    select_and_emit<DT, CAUSAL, REROUTE>(p, sh, dyn_lds, tile, cx, 0);
+    if constexpr (REROUTE) {
+        if (sh.redo) redo_rows<DT, CAUSAL>(p, sh, dyn_lds, cx);         // uniform; rare
     }
-    if (wave != 0) return;                                              // no barriers below
-
-    // ------------------------------------------------------------------ ledger update (wave 0)
-    // Route = entries [0, ki), near-miss = [ki, ki+mi) of the sorted list; both emitted
-    // ascending by chunk index via one ascending sort of (segment << 16 | index).
-    const int ki = min(p.k, my_n);
-    const int mi = min(p.m, my_n - ki);
-    uint32_t cmb[TOPW];
-#pragma unroll
-    for (int s = 0; s < TOPW; ++s) {
-        const uint32_t j = key_index(top[s]);
-        cmb[s] = (s < ki) ? j : ((s < ki + mi) ? (0x10000u | j) : 0xFFFFFFFFu);
-    }
-    sort_asc<TOPW>(cmb);
-
-    if (p.r <= 8) emit_row<8>(p, cmb, ki, mi, my_row, my_n, h, dyn_lds, lane);
-    else emit_row<TOPW>(p, cmb, ki, mi, my_row, my_n, h, dyn_lds, lane);
 }
 
 // ------------------------------------------------------------------------------ rescore

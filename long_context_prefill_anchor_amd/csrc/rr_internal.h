@@ -41,6 +41,6 @@ constexpr int ROUTE_ROWS = 64;   // rows per route block and per rescore block
 
 hipError_t launch_route(const RouteArgs& a, bool bf16, bool causal, bool reroute, hipStream_t st);
 hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st);
-size_t route_lds_bytes(int nk);
+size_t route_lds_bytes(int nk, int c);
 
 }  // namespace rr

@@ -228,82 +228,210 @@ struct RouteShared {
     int32_t redo;
 };
 
-// Random sentinels (Section 3.1, item 2) and the ledger write of one row (lane-per-row).
-// cmb: route (segment 0) and near-miss (segment 1) indices, ascending, padded with ~0.
-// RW >= r is the register width of the random list.
-template <int RW>
-__device__ __forceinline__ void emit_row(const RouteArgs& p, const uint32_t (&cmb)[TOPW], int ki, int mi,
-                                         int my_row, int my_n, int h, unsigned char* lds, int lane) {
-    // Bitmap over allowed chunks: route + near-miss + accepted draws are set.
-    const int words = (p.nk + 31) >> 5;
-    uint32_t* bm = reinterpret_cast<uint32_t*>(lds) + (size_t)lane * (words + 1);
-    for (int w = 0; w < words; ++w) bm[w] = 0u;
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a > b ? b : a; }
+
+// Sort a bitonic sequence descending (half-cleaner cascade).
+template <int N, typename T>
+__device__ __forceinline__ void bitonic_clean_desc(T (&v)[N]) {
 #pragma unroll
-    for (int s = 0; s < TOPW; ++s) {
-        if (s < ki + mi) {
-            const uint32_t j = cmb[s] & 0xFFFFu;
-            atomicOr(&bm[j >> 5], 1u << (j & 31));
+    for (int st = N / 2; st >= 1; st >>= 1) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if ((i & st) == 0) ce_desc(v[i], v[i + st]);
+    }
+}
+
+// Merge the four sorted lists (descending, TOPW = 32 keys) held by the lanes of a quad into
+// the quad's best 32, split between lanes: lanes 0 and 3 end with entries [0, 16) and lanes 1
+// and 2 with entries [16, 32), each sorted descending.  Level 1 merges lists 0+1 and 2+3
+// (partners lane ^ 1), level 2 merges the two results (partners lane ^ 3, then lane ^ 1).
+// Each step is a bitonic merge: the element-wise max of one list and the other reversed holds
+// exactly the best half, as a bitonic sequence; a half-cleaner splits it between two lanes.
+// Keys are distinct (the index is part of the key), so partners agree on every split.
+__device__ __forceinline__ void quad_merge_split(const uint64_t (&a)[TOPW], uint64_t (&hv)[16], int sub) {
+    static_assert(TOPW == 32, "the split merge is written for 32-key lists");
+    {
+        uint64_t b[32];
+#pragma unroll
+        for (int s = 0; s < 32; ++s) b[s] = dpp_u64<DPP_XOR1>(a[s]);
+        const bool keep_max = (sub & 1) == 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint64_t x = max_u64(a[i], b[31 - i]);
+            const uint64_t y = max_u64(a[i + 16], b[15 - i]);
+            hv[i] = keep_max ? max_u64(x, y) : min_u64(x, y);
+        }
+        bitonic_clean_desc<16>(hv);
+    }
+    {
+        uint64_t b[16], d[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) b[s] = dpp_u64<DPP_REVERSE>(hv[s]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) d[i] = max_u64(hv[i], b[15 - i]);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) b[s] = dpp_u64<DPP_XOR1>(d[s]);
+        const bool keep_max = (sub == 0) || (sub == 3);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) hv[i] = keep_max ? max_u64(d[i], b[i]) : min_u64(d[i], b[i]);
+        bitonic_clean_desc<16>(hv);
+    }
+}
+
+// Sum of x over the quad lanes below this one; *total gets the sum over all four.
+__device__ __forceinline__ int quad_excl_sum(int x, int sub, int* total) {
+    const int x0 = dpp_i<DPP_BCAST0>(x), x1 = dpp_i<DPP_BCAST1>(x);
+    const int x2 = dpp_i<DPP_BCAST2>(x), x3 = dpp_i<DPP_BCAST3>(x);
+    *total = x0 + x1 + x2 + x3;
+    return (sub > 0 ? x0 : 0) + (sub > 1 ? x1 : 0) + (sub > 2 ? x2 : 0);
+}
+
+// Random sentinels (Section 3.1, item 2) and the ledger write of one row, split over the row's
+// quad of lanes (sub = lane & 3).  hv: this lane's half of the row's final list (see
+// quad_merge_split).  LDS per row slot: route and near-miss bitmaps of W = (nk + 31) / 32 + 1
+// words each, then a staging row of c IDs.  Route and near-miss chunks come out in ascending
+// index order by scanning the bitmaps; each lane scans a quarter of the words.
+template <int RW>
+__device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&hv)[16], int slot, int sub,
+                                           int my_row, int my_n, int h, unsigned char* lds) {
+    const int ki = min(p.k, my_n);
+    const int mi = min(p.m, my_n - ki);
+    const int words = (p.nk + 31) >> 5;
+    const int W = words + 1;
+    uint32_t* bmr = reinterpret_cast<uint32_t*>(lds) + (size_t)slot * 2 * W;
+    uint32_t* bmn = bmr + W;
+    int32_t* stage = reinterpret_cast<int32_t*>(lds) + (size_t)ROWS * 2 * W + (size_t)slot * p.c;
+    for (int w = sub; w < 2 * W; w += 4) bmr[w] = 0u;
+    if (sub < 2) {                                    // lanes 0 / 1 own positions [0,16) / [16,32)
+        const int base = 16 * sub;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int pos = base + i;
+            const uint32_t j = key_index(hv[i]);
+            if (pos < ki + mi && hv[i] != EMPTY_KEY)
+                atomicOr(pos < ki ? &bmr[j >> 5] : &bmn[j >> 5], 1u << (j & 31));
         }
     }
-    uint32_t rnd[RW];
+
+    // Draws t = 0..15 come from Philox blocks 0..3, one block per lane of the quad.
+    const P4 w4 = philox4x32_10(P4{(uint32_t)sub, (uint32_t)my_row, (uint32_t)p.layer, (uint32_t)h},
+                                p.seed_lo, p.seed_hi);
+    uint32_t u[16];
+    u[0] = dpp_i<DPP_BCAST0>((int)w4.x); u[1] = dpp_i<DPP_BCAST0>((int)w4.y);
+    u[2] = dpp_i<DPP_BCAST0>((int)w4.z); u[3] = dpp_i<DPP_BCAST0>((int)w4.w);
+    u[4] = dpp_i<DPP_BCAST1>((int)w4.x); u[5] = dpp_i<DPP_BCAST1>((int)w4.y);
+    u[6] = dpp_i<DPP_BCAST1>((int)w4.z); u[7] = dpp_i<DPP_BCAST1>((int)w4.w);
+    u[8] = dpp_i<DPP_BCAST2>((int)w4.x); u[9] = dpp_i<DPP_BCAST2>((int)w4.y);
+    u[10] = dpp_i<DPP_BCAST2>((int)w4.z); u[11] = dpp_i<DPP_BCAST2>((int)w4.w);
+    u[12] = dpp_i<DPP_BCAST3>((int)w4.x); u[13] = dpp_i<DPP_BCAST3>((int)w4.y);
+    u[14] = dpp_i<DPP_BCAST3>((int)w4.z); u[15] = dpp_i<DPP_BCAST3>((int)w4.w);
+
+    if (sub == 0) {
+        uint32_t rnd[RW];
 #pragma unroll
-    for (int s = 0; s < RW; ++s) rnd[s] = 0xFFFFFFFFu;
-    int nr = 0;
-    const int pool = my_n - ki - mi;
-    const int rwant = (my_row < 0) ? 0 : min(p.r, pool);
-    if (p.r > 0) {
-        // Draws only for rows whose pool exceeds r; smaller pools are taken whole by the fill.
-        bool drawing = (my_row >= 0) && pool > p.r;
-        P4 w4 = {0u, 0u, 0u, 0u};
-        for (int t = 0; t < 65536 && __ballot(drawing); ++t) {
-            if ((t & 3) == 0) {
-                P4 c = {(uint32_t)(t >> 2), (uint32_t)my_row, (uint32_t)p.layer, (uint32_t)h};
-                w4 = philox4x32_10(c, p.seed_lo, p.seed_hi);
+        for (int s = 0; s < RW; ++s) rnd[s] = 0xFFFFFFFFu;
+        int nr = 0;
+        const int pool = my_n - ki - mi;
+        const int rwant = min(p.r, pool);
+        if (p.r > 0) {
+            // A draw is taken when its chunk is in neither the route nor the near-miss set and
+            // not drawn before; only rows whose pool exceeds r draw, smaller pools are filled.
+            bool drawing = pool > p.r;
+            uint32_t jj[16], inrn[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                jj[t] = __umulhi(u[t], (uint32_t)my_n);
+                inrn[t] = (bmr[jj[t] >> 5] | bmn[jj[t] >> 5]) & (1u << (jj[t] & 31));
             }
-            const uint32_t u = ((t & 3) == 0) ? w4.x : ((t & 3) == 1) ? w4.y : ((t & 3) == 2) ? w4.z : w4.w;
-            if (drawing) {
-                const uint32_t j = __umulhi(u, (uint32_t)my_n);
-                const uint32_t bit = 1u << (j & 31);
-                if (!(bm[j >> 5] & bit)) {
-                    bm[j >> 5] |= bit;
 #pragma unroll
-                    for (int s = 0; s < RW; ++s) rnd[s] = (s == nr) ? j : rnd[s];
+            for (int t = 0; t < 16; ++t) {
+                bool dup = false;
+#pragma unroll
+                for (int s = 0; s < RW; ++s) dup = dup || (rnd[s] == jj[t]);
+                if (drawing && !inrn[t] && !dup) {
+#pragma unroll
+                    for (int s = 0; s < RW; ++s) rnd[s] = (s == nr) ? jj[t] : rnd[s];
                     ++nr;
                     drawing = nr < p.r;
                 }
             }
-        }
-        // Fill: lowest-index chunks still free (whole pool when pool <= r; draw cap reached).
-        if (my_row >= 0 && nr < rwant) {
-            for (int w = 0; w < words && nr < rwant; ++w) {
-                uint32_t free_bits = ~bm[w];
-                while (free_bits && nr < rwant) {
-                    const uint32_t j = (uint32_t)(w * 32 + __builtin_ctz(free_bits));
-                    free_bits &= free_bits - 1u;
-                    if ((int)j >= my_n) { free_bits = 0; break; }
+            // Rarely more than 16 draws are needed: continue one draw at a time.
+            P4 v4 = {0u, 0u, 0u, 0u};
+            for (int t = 16; t < 65536 && __ballot(drawing); ++t) {
+                if ((t & 3) == 0) {
+                    P4 c = {(uint32_t)(t >> 2), (uint32_t)my_row, (uint32_t)p.layer, (uint32_t)h};
+                    v4 = philox4x32_10(c, p.seed_lo, p.seed_hi);
+                }
+                const uint32_t uu = ((t & 3) == 0) ? v4.x : ((t & 3) == 1) ? v4.y : ((t & 3) == 2) ? v4.z : v4.w;
+                if (drawing) {
+                    const uint32_t j = __umulhi(uu, (uint32_t)my_n);
+                    bool dup = ((bmr[j >> 5] | bmn[j >> 5]) & (1u << (j & 31))) != 0u;
 #pragma unroll
-                    for (int s = 0; s < RW; ++s) rnd[s] = (s == nr) ? j : rnd[s];
-                    ++nr;
+                    for (int s = 0; s < RW; ++s) dup = dup || (rnd[s] == j);
+                    if (!dup) {
+#pragma unroll
+                        for (int s = 0; s < RW; ++s) rnd[s] = (s == nr) ? j : rnd[s];
+                        ++nr;
+                        drawing = nr < p.r;
+                    }
                 }
             }
-        }
-        sort_asc<RW>(rnd);
-    }
-
-    if (my_row >= 0) {
-        int32_t* dst = p.ids + ((size_t)h * p.nq + my_row) * p.c;
+            // Fill: lowest-index chunks still free (whole pool when pool <= r; draw cap reached).
+            if (nr < rwant) {
+                for (int w = 0; w < words && nr < rwant; ++w) {
+                    uint32_t free_bits = ~(bmr[w] | bmn[w]);
+                    while (free_bits && nr < rwant) {
+                        const uint32_t j = (uint32_t)(w * 32 + __builtin_ctz(free_bits));
+                        free_bits &= free_bits - 1u;
+                        if ((int)j >= my_n) { free_bits = 0; break; }
+                        bool dup = false;
 #pragma unroll
-        for (int s = 0; s < TOPW; ++s) {
-            if (s < ki) dst[s] = (int32_t)cmb[s];
-            else if (s < ki + mi) dst[p.k + (s - ki)] = (int32_t)(cmb[s] & 0xFFFFu);
+                        for (int s = 0; s < RW; ++s) dup = dup || (rnd[s] == j);
+                        if (dup) continue;
+#pragma unroll
+                        for (int s = 0; s < RW; ++s) rnd[s] = (s == nr) ? j : rnd[s];
+                        ++nr;
+                    }
+                }
+            }
+            sort_asc<RW>(rnd);
         }
-        for (int s = ki; s < p.k; ++s) dst[s] = -1;
-        for (int s = mi; s < p.m; ++s) dst[p.k + s] = -1;
 #pragma unroll
         for (int s = 0; s < RW; ++s)
-            if (s < p.r) dst[p.k + p.m + s] = (s < nr) ? (int32_t)rnd[s] : -1;
+            if (s < p.r) stage[p.k + p.m + s] = (s < nr) ? (int32_t)rnd[s] : -1;
         p.anchor[(size_t)h * p.nq + my_row] = p.layer;
     }
+
+    // Route and near-miss chunks in ascending index order: each lane counts the set bits of its
+    // quarter of the words, an exclusive sum over the quad gives its output offsets.
+    const int wq = (words + 3) >> 2;
+    const int w0 = sub * wq;
+    const int w1 = min(words, w0 + wq);
+    int cr = 0, cn = 0;
+    for (int w = w0; w < w1; ++w) {
+        cr += __popc(bmr[w]);
+        cn += __popc(bmn[w]);
+    }
+    int tr, tn;
+    int pr = quad_excl_sum(cr, sub, &tr);
+    int pn = p.k + quad_excl_sum(cn, sub, &tn);
+    for (int w = w0; w < w1; ++w) {
+        uint32_t br = bmr[w], bn = bmn[w];
+        while (br) {
+            stage[pr++] = w * 32 + __builtin_ctz(br);
+            br &= br - 1u;
+        }
+        while (bn) {
+            stage[pn++] = w * 32 + __builtin_ctz(bn);
+            bn &= bn - 1u;
+        }
+    }
+    for (int s = tr + sub; s < p.k; s += 4) stage[s] = -1;
+    for (int s = tn + sub; s < p.m; s += 4) stage[p.k + s] = -1;
+    // The quad copies the staged row out: four consecutive IDs per instruction and row.
+    int32_t* dst = p.ids + ((size_t)h * p.nq + my_row) * p.c;
+    for (int e = sub; e < p.c; e += 4) dst[e] = stage[e];
 }
 
 // ------------------------------------------------------------------------------ route kernel
@@ -316,103 +444,96 @@ struct RowCtx {
     const E* Qh;
     const E* Kh;
     uint2* my_buf;
-    bool redo_row;
+    int qslot, qsub, q_row, q_n;
+    bool q_redo;
 };
 
-// Streaming selection pass from the rows' shared thresholds (sh.thr), merge of the four waves'
-// lists and ledger write (wave 0).  Attempt 0 emits every row that holds min(k+m, n) keys; in
-// reroute mode the others are marked for a redo from -inf (attempt 1, which emits only them).
+// Streaming selection pass from the rows' shared thresholds (sh.thr), final merge and ledger
+// write.  attempt 0 emits every row that holds min(k+m, n) keys; in reroute mode the others are
+// marked for a redo from -inf (attempt 1, which emits only them).
 template <typename DT, bool CAUSAL, bool REROUTE>
 __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared& sh, unsigned char* dyn_lds,
                                                 Tile<DT>& tile, RowCtx<DT>& cx, int attempt) {
     const int lane = cx.lane, wave = cx.wave, h = cx.h, my_row = cx.my_row, my_n = cx.my_n;
     const int nmin = cx.nmin, ntiles = cx.ntiles;
+    const auto* Qh = cx.Qh;
     const auto* Kh = cx.Kh;
     uint2* my_buf = cx.my_buf;
-    if constexpr (REROUTE) tile.load_q(cx.Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
+    const int qslot = cx.qslot, qsub = cx.qsub, q_row = cx.q_row, q_n = cx.q_n;
+    if constexpr (REROUTE) tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
+    else (void)Qh;
     uint64_t top[TOPW];
 #pragma unroll
     for (int s = 0; s < TOPW; ++s) top[s] = EMPTY_KEY;
-    int cnt = 0;
-    bool fresh = true;                                                  // list empty in every lane
-    float ts = key_score(sh.thr[lane]);
-    constexpr int NB = Tile<DT>::NBUF;
-    typename Tile<DT>::KReg kbuf[NB];
+    {
+        int cnt = 0;
+        bool fresh = true;                                              // list empty in every lane
+        float ts = key_score(sh.thr[lane]);
+        constexpr int NB = Tile<DT>::NBUF;
+        typename Tile<DT>::KReg kbuf[NB];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) tile.load_k(kbuf[u], Kh, TK * (wave + u * SPLIT), p.nk, lane);
-    for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
+        for (int u = 0; u < NB; ++u) tile.load_k(kbuf[u], Kh, TK * (wave + u * SPLIT), p.nk, lane);
+        for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            const int t = t0 + u * SPLIT;
-            const bool live = t < ntiles;                        // uniform
-            f32x16 lo, hi;
-            if (live) tile.mma(kbuf[u], lo, hi);
-            // Issued on every path (past the end it rereads the last key row), so the load
-            // counter sees one fixed sequence and waits only for the oldest buffer.
-            tile.load_k(kbuf[u], Kh, TK * (t + NB * SPLIT), p.nk, lane);
-            if (live) {
-            rows_per_lane(lo, hi);
-            const int key0 = TK * t;
-            if (key0 + TK > nmin) {                                 // keys past a row's end
-                const int lim = my_n - key0;
-                const float nan = __builtin_nanf("");
+            for (int u = 0; u < NB; ++u) {
+                const int t = t0 + u * SPLIT;
+                const bool live = t < ntiles;                        // uniform
+                f32x16 lo, hi;
+                if (live) tile.mma(kbuf[u], lo, hi);
+                // Issued on every path (past the end it rereads the last key row), so the load
+                // counter sees one fixed sequence and waits only for the oldest buffer.
+                tile.load_k(kbuf[u], Kh, TK * (t + NB * SPLIT), p.nk, lane);
+                if (live) {
+                rows_per_lane(lo, hi);
+                const int key0 = TK * t;
+                if (key0 + TK > nmin) {                                 // keys past a row's end
+                    const int lim = my_n - key0;
+                    const float nan = __builtin_nanf("");
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    lo[v] = (lo_key(v) < lim) ? lo[v] : nan;            // NaN never passes >=
-                    hi[v] = (hi_key(v) < lim) ? hi[v] : nan;
+                    for (int v = 0; v < 16; ++v) {
+                        lo[v] = (lo_key(v) < lim) ? lo[v] : nan;            // NaN never passes >=
+                        hi[v] = (hi_key(v) < lim) ? hi[v] : nan;
+                    }
                 }
-            }
-            // Branch-free append: every slot stores its (score, index) at the row's current
-            // count and the count advances only when the score passes, so a failing slot's
-            // store is overwritten by the next one (<= 15 held + 16 slots: index <= 30).
+                // Branch-free append: every slot stores its (score, index) at the row's current
+                // count and the count advances only when the score passes, so a failing slot's
+                // store is overwritten by the next one (<= 15 held + 16 slots: index <= 30).
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
+                for (int half = 0; half < 2; ++half) {
 #pragma unroll
-                for (int v = 8 * half; v < 8 * half + 8; ++v) {
-                    my_buf[cnt] = make_uint2(__float_as_uint(lo[v]), (uint32_t)(key0 + lo_key(v)));
-                    cnt += (lo[v] >= ts) ? 1 : 0;
-                    my_buf[cnt] = make_uint2(__float_as_uint(hi[v]), (uint32_t)(key0 + hi_key(v)));
-                    cnt += (hi[v] >= ts) ? 1 : 0;
+                    for (int v = 8 * half; v < 8 * half + 8; ++v) {
+                        my_buf[cnt] = make_uint2(__float_as_uint(lo[v]), (uint32_t)(key0 + lo_key(v)));
+                        cnt += (lo[v] >= ts) ? 1 : 0;
+                        my_buf[cnt] = make_uint2(__float_as_uint(hi[v]), (uint32_t)(key0 + hi_key(v)));
+                        cnt += (hi[v] >= ts) ? 1 : 0;
+                    }
+                    if (__ballot(cnt >= 16)) {
+                        drain(top, my_buf, cnt, fresh);
+                        cnt = 0;
+                        const uint64_t own = pick(top, p.sel - 1);
+                        if (own != EMPTY_KEY && my_row >= 0) atomicMax((unsigned long long*)&sh.thr[lane], own);
+                    }
                 }
-                if (__ballot(cnt >= 16)) {
-                    drain(top, my_buf, cnt, fresh);
-                    cnt = 0;
-                    const uint64_t own = pick(top, p.sel - 1);
-                    if (own != EMPTY_KEY && my_row >= 0) atomicMax((unsigned long long*)&sh.thr[lane], own);
+                ts = key_score(sh.thr[lane]);
                 }
-            }
-            ts = key_score(sh.thr[lane]);
             }
         }
-    }
-    drain(top, my_buf, cnt, fresh);
+        drain(top, my_buf, cnt, fresh);
 
-    // Merge the four waves' lists through two LDS slots: 1 -> 0 and 3 -> 2, then 2 -> 0.
-    uint64_t* xchg = reinterpret_cast<uint64_t*>(dyn_lds);          // [2][ROWS][XSTRIDE]
-    __syncthreads();                                                // every buffer is drained
-    if (wave & 1) {
+        // Final merge, one row per quad: wave w takes rows 16w .. 16w+15 and lane 4j + s of it
+        // holds wave s's list of row 16w + j.
+        uint64_t* xl = reinterpret_cast<uint64_t*>(dyn_lds);            // [SPLIT][ROWS][XSTRIDE]
+        __syncthreads();                                                // every buffer is drained
 #pragma unroll
-        for (int s = 0; s < TOPW; ++s) xchg[((size_t)(wave >> 1) * ROWS + lane) * XSTRIDE + s] = top[s];
-    }
-    __syncthreads();
-    if (!(wave & 1)) {
-        uint64_t y[TOPW];
+        for (int s = 0; s < TOPW; ++s) xl[((size_t)wave * ROWS + lane) * XSTRIDE + s] = top[s];
+        __syncthreads();
 #pragma unroll
-        for (int s = 0; s < TOPW; ++s) y[s] = xchg[((size_t)(wave >> 1) * ROWS + lane) * XSTRIDE + s];
-        merge_top_desc<TOPW>(top, y);
-    }
-    __syncthreads();
-    if (wave == 2) {
-#pragma unroll
-        for (int s = 0; s < TOPW; ++s) xchg[(size_t)lane * XSTRIDE + s] = top[s];
-    }
-    __syncthreads();
-    if (wave == 0) {
-        uint64_t y[TOPW];
-#pragma unroll
-        for (int s = 0; s < TOPW; ++s) y[s] = xchg[(size_t)lane * XSTRIDE + s];
-        merge_top_desc<TOPW>(top, y);
-        bool emit_now = my_row >= 0;
+        for (int s = 0; s < TOPW; ++s) top[s] = xl[((size_t)qsub * ROWS + qslot) * XSTRIDE + s];
+        uint64_t hv[16];
+        quad_merge_split(top, hv, qsub);
+        __syncthreads();                                                // xl is free again
+
+        bool emit_now = q_row >= 0;
         if constexpr (REROUTE) {
             // Each row must now hold min(sel, n) keys.  Only a reroute threshold taken from the
             // rescore kernel's arithmetic can miss (rounding); such rows are redone from -inf
@@ -420,34 +541,22 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
             if (attempt == 0) {
                 int have = 0;
 #pragma unroll
-                for (int s = 0; s < TOPW; ++s) have += (top[s] != EMPTY_KEY);
-                const bool redo = (my_row >= 0) && have < min(p.sel, my_n);
-                cx.redo_row = redo;
-                if (__ballot(redo)) {
-                    sh.thr[lane] = redo ? make_key(-INFINITY, 0xFFFFFFFFu) : NO_PASS_KEY;
-                    if (lane == 0) sh.redo = 1;
-                }
-                emit_now = emit_now && !redo;
+                for (int s = 0; s < 16; ++s) have += (hv[s] != EMPTY_KEY);
+                have += dpp_i<DPP_XOR1>(have);                          // the other half's count
+                cx.q_redo = (q_row >= 0) && have < min(p.sel, q_n);
+                if (cx.q_redo) sh.redo = 1;
+                if (qsub == 0) sh.thr[qslot] = cx.q_redo ? make_key(-INFINITY, 0xFFFFFFFFu) : NO_PASS_KEY;
+                emit_now = emit_now && !cx.q_redo;
             } else {
-                emit_now = emit_now && cx.redo_row;
+                emit_now = emit_now && cx.q_redo;
             }
         }
-        // Route = entries [0, ki), near-miss = [ki, ki+mi) of the sorted list; both emitted
-        // ascending by chunk index via one ascending sort of (segment << 16 | index).
-        const int ki = min(p.k, my_n);
-        const int mi = min(p.m, my_n - ki);
-        uint32_t cmb[TOPW];
-#pragma unroll
-        for (int s = 0; s < TOPW; ++s) {
-            const uint32_t j = key_index(top[s]);
-            cmb[s] = (s < ki) ? j : ((s < ki + mi) ? (0x10000u | j) : 0xFFFFFFFFu);
+        if (emit_now) {
+            if (p.r <= 8) emit_split<8>(p, hv, qslot, qsub, q_row, q_n, h, dyn_lds);
+            else emit_split<TOPW>(p, hv, qslot, qsub, q_row, q_n, h, dyn_lds);
         }
-        sort_asc<TOPW>(cmb);
-        const int erow = emit_now ? my_row : -1;
-        if (p.r <= 8) emit_row<8>(p, cmb, ki, mi, erow, my_n, h, dyn_lds, lane);
-        else emit_row<TOPW>(p, cmb, ki, mi, erow, my_n, h, dyn_lds, lane);
+        __syncthreads();                                                // LDS free, sh.redo final
     }
-    __syncthreads();                                                    // LDS free, sh.redo final
 }
 
 // Rows whose reroute threshold missed (see select_and_emit) are selected again from -inf.  It
@@ -456,8 +565,11 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
 // through the merge.
 template <typename DT, bool CAUSAL>
 __device__ __forceinline__ void redo_rows(const RouteArgs& p, RouteShared& sh, unsigned char* dyn_lds, RowCtx<DT>& cx) {
+    __syncthreads();                                                    // everyone has read sh.redo
+    if (threadIdx.x == 0) sh.redo = 0;
     asm volatile("" : "+v"(cx.my_n), "+v"(cx.nmin), "+v"(cx.my_row), "+v"(cx.ntiles));
     asm volatile("" : "+v"(cx.Kh), "+v"(cx.Qh), "+v"(cx.my_buf));
+    asm volatile("" : "+v"(cx.q_row), "+v"(cx.q_n), "+v"(cx.qslot), "+v"(cx.qsub));
     Tile<DT> tile;
     select_and_emit<DT, CAUSAL, true>(p, sh, dyn_lds, tile, cx, 1);
 }
@@ -546,6 +658,11 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     if constexpr (!REROUTE) tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
 
     uint2* my_buf = reinterpret_cast<uint2*>(dyn_lds) + ((size_t)wave * ROWS + lane) * CSTRIDE;
+    // Final merge and ledger write run one row per quad of lanes over all four waves.
+    const int qslot = 16 * wave + (lane >> 2);
+    const int qsub = lane & 3;
+    const int q_row = sh.rows[qslot];
+    const int q_n = (q_row < 0) ? 0 : (CAUSAL ? q_row + 1 : p.nk);
 
     // ------------------------------------------------------------------ first threshold
     uint64_t base_thr;
@@ -615,7 +732,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     __syncthreads();
 
     // ------------------------------------------------------------------ streaming pass
-    RowCtx<DT> cx{lane, wave, h, my_row, my_n, nmin, ntiles, Qh, Kh, my_buf, false};
+    RowCtx<DT> cx{lane, wave, h, my_row, my_n, nmin, ntiles, Qh, Kh, my_buf, qslot, qsub, q_row, q_n, false};
     select_and_emit<DT, CAUSAL, REROUTE>(p, sh, dyn_lds, tile, cx, 0);
     if constexpr (REROUTE) {
         if (sh.redo) redo_rows<DT, CAUSAL>(p, sh, dyn_lds, cx);         // uniform; rare
@@ -760,20 +877,20 @@ __global__ __launch_bounds__(RESCORE_THREADS) void k_rescore(RescoreArgs p) {
 
 // ------------------------------------------------------------------------------ launchers
 
-size_t route_lds_bytes(int nk) {
+size_t route_lds_bytes(int nk, int c) {
     const size_t cand = (size_t)SPLIT * ROWS * CSTRIDE * sizeof(uint2);
-    const size_t xchg = (size_t)2 * ROWS * XSTRIDE * sizeof(uint64_t);
+    const size_t xl = (size_t)SPLIT * ROWS * XSTRIDE * sizeof(uint64_t);
     const size_t gm = (size_t)ROWS * GSTRIDE * sizeof(float);
-    const size_t bm = (size_t)ROWS * ((nk + 31) / 32 + 1) * sizeof(uint32_t);
-    size_t m = cand > xchg ? cand : xchg;
+    const size_t em = (size_t)ROWS * (2 * ((nk + 31) / 32 + 1) + c) * sizeof(uint32_t);
+    size_t m = cand > xl ? cand : xl;
     m = m > gm ? m : gm;
-    return m > bm ? m : bm;
+    return m > em ? m : em;
 }
 
 template <typename DT, bool CAUSAL, bool REROUTE>
 static hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
     const int G = (a.nq + ROWS - 1) / ROWS;
-    const size_t lds = route_lds_bytes(a.nk);
+    const size_t lds = route_lds_bytes(a.nk, a.c);
     hipLaunchKernelGGL((k_route<DT, CAUSAL, REROUTE>), dim3(xcd_grid(a.H * G)), dim3(ROWS * SPLIT), lds, st, a);
     return hipGetLastError();
 }

@@ -7,13 +7,18 @@ routing at every layer (top-12 only).  Inputs for all 32 layers are resident in 
 timing starts.
 
 Headline: relay-layer query-row routes per second = heads * nq * (relay layers) / (time spent
-in relay layers), timed with HIP events on the launch stream around every layer call.
+in relay layers), timed with HIP events on the launch stream around every layer call.  Each
+kernel is also timed on its own, in a second timed region of the same steps (events the
+library records around its launches), and set against its roofline: the reroute kernel (dominant in relay layers) and full routing against
+the bf16 MFMA peak on algorithmic flops, the rescore kernel against HBM bandwidth on
+algorithmic bytes.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--graph]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--calib-copy]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,8 +31,11 @@ sys.path.insert(0, ROOT)
 
 from long_context_prefill_anchor_amd import rr, synth, workloads as W  # noqa: E402
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+KERNEL_SRC = os.path.join(ROOT, "long_context_prefill_anchor_amd", "csrc", "rr_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_route_reroute_batched_heads.txt")
+CALIB_BYTES = 256 << 20         # plain copy used to calibrate the HBM byte counters
 
 
 def log(msg):
@@ -36,16 +44,15 @@ def log(msg):
 
 def upload_layers(w):
     import torch
-    qs, ks, sig = [], [], []
+    qs, ks = [], []
     for li in synth.generate(w):
         qs.append(torch.from_numpy(li.q.view(np.int16)).cuda())
         ks.append(torch.from_numpy(li.k.view(np.int16)).cuda())
-        sig.append(li.sigma)
     torch.cuda.synchronize()
-    return qs, ks, sig
+    return qs, ks
 
 
-def run_relay_chain(w, led, qs, ks, outs=None, ev=None):
+def run_relay_chain(w, led, qs, ks, ev=None):
     """Anchor or relay per layer; optional per-layer events (start, end) lists."""
     for l in range(w.layers):
         if ev is not None:
@@ -53,7 +60,7 @@ def run_relay_chain(w, led, qs, ks, outs=None, ev=None):
         if w.is_anchor(l):
             led.anchor(qs[l], ks[l], l)
         else:
-            led.relay(qs[l], ks[l], l, outs[l] if outs is not None else None)
+            led.relay(qs[l], ks[l], l)
         if ev is not None:
             ev[l][1].record()
 
@@ -69,11 +76,11 @@ def run_full_chain(w, full, qs, ks, ev=None):
 
 def quality_pass(w, led, full, qs, ks):
     """Untimed: recall of the relayed routes against full routing, rerouted fraction,
-    evaluated score-pair fraction (Section 5 metrics)."""
+    evaluated score-pair fraction (Section 5 metrics), flagged rows per relay layer."""
     import torch
     H, n = w.heads, w.n
     outs = [led.alloc_outputs(with_scores=False) if not w.is_anchor(l) else None for l in range(w.layers)]
-    recall_sum, rows_rerouted, relay_flags, pairs = 0.0, 0, [], 0
+    recall_sum, rows_rerouted, flagged, pairs = 0.0, 0, {}, 0
     for l in range(w.layers):
         if w.is_anchor(l):
             led.anchor(qs[l], ks[l], l)
@@ -85,18 +92,20 @@ def quality_pass(w, led, full, qs, ks):
         torch.cuda.synchronize()
         used = led.get()[0].cpu().numpy().reshape(-1, w.k)
         exact = full.get()[0].cpu().numpy().reshape(-1, w.k)
-        # recall per row: |used & exact| / |exact| (routes are ascending; n >= k so no padding)
+        # recall per row: |used & exact| / |exact| (non-causal, n >= k: no padding)
         inter = (used[:, :, None] == exact[:, None, :]).any(axis=2).sum(axis=1)
         recall_sum += float((inter / w.k).mean())
         if not w.is_anchor(l):
             nf = int(outs[l].n_rows.cpu().numpy()[0])
-            relay_flags.append(nf / (H * n))
+            flagged[l] = nf
             rows_rerouted += nf
             pairs += H * n * w.c + nf * n
     L = w.layers
+    relay_rho = [flagged[l] / (H * n) for l in sorted(flagged)]
     return dict(recall=recall_sum / L, reroute_fraction=rows_rerouted / (H * n * L),
-                relay_rho_mean=float(np.mean(relay_flags)), relay_rho_per_layer=[round(x, 4) for x in relay_flags],
-                pair_fraction=pairs / (H * n * n * L))
+                relay_rho_mean=float(np.mean(relay_rho)), relay_rho_per_layer=[round(x, 4) for x in relay_rho],
+                pair_fraction=pairs / (H * n * n * L), flagged=flagged,
+                relay_pairs=sum(H * n * w.c + flagged[l] * n for l in flagged))
 
 
 def cpu_baseline(w, max_seconds=20.0):
@@ -133,6 +142,35 @@ def cpu_baseline(w, max_seconds=20.0):
             "relay_over_full_time": (t_relay / n_relay) / (t_anchor / n_anchor) if n_anchor else None}
 
 
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` (reroute / rescore / route) from the committed counter
+    summary, if it was taken on the kernel source as it is now (else None)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if ":" in line and not line.startswith("#"))
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return float(fields[f"{kernel}_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calib_copy():
+    """A plain device copy of known size (CALIB_BYTES read + written), for counter calibration."""
+    import torch
+    a = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +178,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); heads shard across GPUs "
@@ -151,12 +191,14 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
     rr.lib()
+    if args.calib_copy:
+        calib_copy()
     w = W.batched_heads()
-    H, n = w.heads, w.n
-    log(f"[bench] generating + uploading {w.layers} layers of {H}x{n}x{w.d} bf16 Q and K")
-    qs, ks, _ = upload_layers(w)
-    led = rr.Ledger(H, n, n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
-    full = rr.Ledger(H, n, n, w.d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
+    H, n, d = w.heads, w.n, w.d
+    log(f"[bench] generating + uploading {w.layers} layers of {H}x{n}x{d} bf16 Q and K")
+    qs, ks = upload_layers(w)
+    led = rr.Ledger(H, n, n, d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
+    full = rr.Ledger(H, n, n, d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
 
     log("[bench] quality pass (recall, reroute fraction, pair fraction)")
     q = quality_pass(w, led, full, qs, ks)
@@ -168,7 +210,7 @@ def main():
     anchor_layers = [l for l in range(L) if w.is_anchor(l)]
 
     def step(evr=None, evf=None):
-        run_relay_chain(w, led, qs, ks, None, evr)
+        run_relay_chain(w, led, qs, ks, evr)
         run_full_chain(w, full, qs, ks, evf)
 
     log(f"[bench] warmup {args.warmup} steps")
@@ -187,6 +229,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # Second timed region, same steps, with the library's per-kernel launch events on (kept
+    # out of the headline region: each extra event record adds a gap between kernels).
+    log(f"[bench] timing {args.steps} steps with per-kernel events")
+    led.profile(True)
+    full.profile(True)
+    for s in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt_led = led.kernel_times()
+    kt_full = full.kernel_times()
+    led.profile(False)
+    full.profile(False)
+
     relay_ms = np.array([[evs[s][0][l][0].elapsed_time(evs[s][0][l][1]) for l in range(L)]
                          for s in range(args.steps)])
     full_ms = np.array([[evs[s][1][l][0].elapsed_time(evs[s][1][l][1]) for l in range(L)]
@@ -200,16 +255,46 @@ def main():
     anchor_layer_us = float(np.median(relay_ms[:, anchor_layers]) * 1e3)
     full_layer_us = float(np.median(full_ms) * 1e3)
     speedup = (t_full_layers / (L * args.steps)) / (t_relay_layers / (len(relay_layers) * args.steps))
+    pairs_per_s = q["relay_pairs"] * args.steps / (t_relay_layers / 1e3)
 
-    # Dominant kernel: full routing of a whole layer (the anchor / comparator route kernel),
-    # bound by MFMA: algorithmic flops per launch = 2 * d * heads * nq * nk.
-    flops = 2.0 * w.d * H * n * n
-    achieved_tflops = flops / (full_layer_us * 1e-6) / 1e12
-    roofline = {"kernel": "k_route (full routing, k=12)", "bound": "mfma",
-                "achieved": round(achieved_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None,
-                "per_launch": {"flops": flops, "avg_us": round(full_layer_us, 2)}}
+    # Per-kernel averages from the library's own launch events (same stream as the kernels).
+    def avg_us(kt, kind):
+        nl, ms = kt[kind]
+        return (ms * 1e3 / nl) if nl else None, nl
+    t_resc, n_resc = avg_us(kt_led, rr.RR_KERNEL_RESCORE)
+    t_rer, n_rer = avg_us(kt_led, rr.RR_KERNEL_REROUTE)
+    t_anc, n_anc = avg_us(kt_led, rr.RR_KERNEL_ROUTE)
+    t_full, n_full = avg_us(kt_full, rr.RR_KERNEL_ROUTE)
+
+    # Algorithmic work per launch.
+    #   reroute: 2*d*nk flops per flagged row (its full row is scored), averaged over the
+    #            relay layers (every timed step repeats the same flags);
+    #   full routing: 2*d*nq*nk per head;
+    #   rescore: bytes read once — Q, K (K counted once per head), the c ledger IDs per row —
+    #            plus one flag byte written per row.
+    reroute_flops = 2.0 * d * n * float(np.mean([q["flagged"][l] for l in relay_layers]))
+    full_flops = 2.0 * d * H * n * n
+    rescore_bytes = float(H * (n * d * 2 + n * d * 2 + n * w.c * 4 + n))
+
+    def mfma_line(name, flops, us, nl):
+        ach = flops / (us * 1e-6) / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "per_launch": {"flops": flops, "avg_us": round(us, 2), "launches": nl}}
+
+    rer = mfma_line("k_route<bf16, reroute> (flagged rows)", reroute_flops, t_rer, n_rer)
+    rer["traffic"] = recorded_traffic("reroute")
+    ach_resc = rescore_bytes / (t_resc * 1e-6) / 1e9
+    kernels = {
+        "rescore": {"kernel": "k_rescore<bf16, 4>", "bound": "hbm", "achieved": round(ach_resc, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_resc / HBM_PEAK_GBS, 4),
+                    "per_launch": {"bytes": rescore_bytes, "avg_us": round(t_resc, 2), "launches": n_resc},
+                    "traffic": recorded_traffic("rescore")},
+        "reroute": rer,
+        "full_routing": mfma_line("k_route<bf16, full> (k=12, m=r=0)", full_flops, t_full, n_full),
+        "anchor": mfma_line("k_route<bf16, full> (k=12, m=12, r=8)", full_flops, t_anc, n_anc),
+    }
+    roofline = dict(rer)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -229,7 +314,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "batched_heads", "heads": H, "nq": n, "nk": n, "d": w.d,
+        "config": {"workload": "batched_heads", "heads": H, "nq": n, "nk": n, "d": d,
                    "layers": L, "anchors": list(w.anchors), "k": w.k, "m": w.m, "r": w.r,
                    "gamma": w.gamma, "causal": w.causal, "drift": "sigma_l ~ U[0.01, 0.06), relative",
                    "parallelism": "single GPU"},
@@ -238,11 +323,13 @@ def main():
         "reroute_fraction": round(q["reroute_fraction"], 4),
         "relay_rho_mean": round(q["relay_rho_mean"], 4),
         "pair_fraction": round(q["pair_fraction"], 4),
+        "relay_score_pairs_per_s": round(pairs_per_s, 1),
         "full_routing_routes_per_s": round(full_value, 1),
         "relay_layer_us_median": round(relay_layer_us, 2),
         "anchor_layer_us_median": round(anchor_layer_us, 2),
         "full_layer_us_median": round(full_layer_us, 2),
         "roofline": roofline,
+        "kernels": kernels,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

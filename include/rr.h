@@ -72,8 +72,9 @@ typedef struct {
     int32_t dtype;    /* rr_dtype of Q and K                                           */
     uint64_t seed;    /* random-sentinel key                                           */
 } rr_config;
-/* Limits: k + m <= 32, k + m + r <= 64, nq and nk <= 65536, heads * nq < 2^31.
- * Non-causal ledgers need nk >= k + m + r. */
+/* Limits (RR_EUNSUPPORTED beyond them): d == 64, k + m <= 32, r <= 32, nk <= 4096,
+ * nq <= 65536; heads * nq < 2^31 (RR_EINVAL).  A row with fewer allowed chunks than
+ * k + m + r gets shorter segments, padded with -1. */
 
 typedef struct rr_ledger rr_ledger;   /* opaque; owns the ledger and all scratch device memory */
 
@@ -121,6 +122,22 @@ rr_status rr_ledger_get(const rr_ledger* ledger, int32_t* route, int32_t* sent,
 rr_status rr_ledger_set(rr_ledger* ledger, const int32_t* route, const int32_t* sent,
                         const int32_t* anchor_layer, int32_t last_layer, int32_t src_is_host,
                         void* stream);
+
+/* Per-kernel timing, for measurement.  While profiling is on, every kernel the ledger
+ * launches is bracketed by HIP events recorded on its stream (no synchronisation, no device
+ * allocation; the events are created on the host as needed, without the system-scope fence
+ * that would write back the caches at every record).  rr_ledger_kernel_times waits
+ * for the recorded events, writes per kernel kind the number of launches and their summed
+ * duration in milliseconds (arrays of RR_KERNEL_KINDS entries, indexed by rr_kernel_kind),
+ * and clears the record.  rr_ledger_profile(ledger, 1) also clears it; 0 stops recording. */
+typedef enum {
+    RR_KERNEL_ROUTE = 0,    /* full routing of every row (rr_anchor_route)               */
+    RR_KERNEL_RESCORE = 1,  /* candidate rescoring + flags (first kernel of a relay)      */
+    RR_KERNEL_REROUTE = 2,  /* full routing of the flagged rows (second kernel of a relay) */
+    RR_KERNEL_KINDS = 3
+} rr_kernel_kind;
+rr_status rr_ledger_profile(rr_ledger* ledger, int32_t enable);
+rr_status rr_ledger_kernel_times(rr_ledger* ledger, int32_t* launches, double* total_ms);
 
 /* Configuration the ledger was created with. */
 rr_status rr_ledger_config(const rr_ledger* ledger, rr_config* out);

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "rr.h"
 #include "rr_internal.h"
@@ -27,6 +28,12 @@ struct rr_ledger {
     int32_t last_layer = -1;
     bool anchored = false;
     bool poisoned = false;
+    // Kernel timing (rr_ledger_profile): recorded (kind, start, stop) triples and a pool of
+    // spare events.
+    struct Timed { int kind; hipEvent_t start, stop; };
+    bool profiling = false;
+    std::vector<Timed> timed;
+    std::vector<hipEvent_t> spare;
 };
 
 namespace {
@@ -80,6 +87,50 @@ void free_all(rr_ledger* L) {
     (void)hipFree(L->flags_ws);
     (void)hipFree(L->hint_ws);
     (void)hipFree(L->bcount);
+}
+
+hipEvent_t take_event(rr_ledger* L) {
+    hipEvent_t ev = nullptr;
+    if (!L->spare.empty()) {
+        ev = L->spare.back();
+        L->spare.pop_back();
+    } else if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) {
+        // timing only: no system-scope fence (cache writeback) when the event is recorded
+        ev = nullptr;
+    }
+    return ev;
+}
+
+// Record the start of a timed launch; returns the index of its record or -1.
+int time_begin(rr_ledger* L, int kind, hipStream_t st) {
+    if (!L->profiling) return -1;
+    hipEvent_t a = take_event(L), b = take_event(L);
+    if (!a || !b || hipEventRecord(a, st) != hipSuccess) {
+        if (a) L->spare.push_back(a);
+        if (b) L->spare.push_back(b);
+        return -1;
+    }
+    L->timed.push_back({kind, a, b});
+    return (int)L->timed.size() - 1;
+}
+
+void time_end(rr_ledger* L, int idx, hipStream_t st) {
+    if (idx < 0) return;
+    if (hipEventRecord(L->timed[idx].stop, st) != hipSuccess) {
+        L->spare.push_back(L->timed[idx].start);
+        L->spare.push_back(L->timed[idx].stop);
+        L->timed.erase(L->timed.begin() + idx);
+    }
+}
+
+void release_events(rr_ledger* L) {
+    for (auto& t : L->timed) {
+        (void)hipEventDestroy(t.start);
+        (void)hipEventDestroy(t.stop);
+    }
+    for (auto e : L->spare) (void)hipEventDestroy(e);
+    L->timed.clear();
+    L->spare.clear();
 }
 
 rr::RouteArgs route_args(const rr_ledger* L, const void* q, const void* k, int layer) {
@@ -165,8 +216,49 @@ rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
 void rr_ledger_destroy(rr_ledger* L) {
     if (!L) return;
     (void)hipDeviceSynchronize();
+    release_events(L);
     free_all(L);
     delete L;
+}
+
+rr_status rr_ledger_profile(rr_ledger* L, int32_t enable) {
+    if (!L) return fail(RR_EINVAL, "ledger is NULL");
+    if (enable != 0 && enable != 1) return fail(RR_EINVAL, "enable must be 0 or 1");
+    if (enable) {
+        for (auto& t : L->timed) {
+            (void)hipEventSynchronize(t.stop);
+            L->spare.push_back(t.start);
+            L->spare.push_back(t.stop);
+        }
+        L->timed.clear();
+    }
+    L->profiling = enable != 0;
+    return ok();
+}
+
+rr_status rr_ledger_kernel_times(rr_ledger* L, int32_t* launches, double* total_ms) {
+    if (!L || !launches || !total_ms) return fail(RR_EINVAL, "ledger, launches and total_ms are required");
+    for (int i = 0; i < RR_KERNEL_KINDS; ++i) {
+        launches[i] = 0;
+        total_ms[i] = 0.0;
+    }
+    hipError_t bad = hipSuccess;
+    for (auto& t : L->timed) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(t.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+        if (e == hipSuccess) {
+            launches[t.kind] += 1;
+            total_ms[t.kind] += ms;
+        } else {
+            bad = e;
+        }
+        L->spare.push_back(t.start);
+        L->spare.push_back(t.stop);
+    }
+    L->timed.clear();
+    if (bad != hipSuccess) return fail(RR_EDEVICE, "kernel timing events: %s", hipGetErrorString(bad));
+    return ok();
 }
 
 rr_status rr_ledger_config(const rr_ledger* L, rr_config* out) {
@@ -181,7 +273,9 @@ rr_status rr_anchor_route(rr_ledger* L, const void* q, const void* k, int32_t la
     if (layer < 0) return fail(RR_EINVAL, "layer must be >= 0 (got %d)", layer);
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const rr::RouteArgs a = route_args(L, q, k, layer);
+    const int tix = time_begin(L, RR_KERNEL_ROUTE, st);
     const hipError_t e = rr::launch_route(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, false, st);
+    time_end(L, tix, st);
     if (e != hipSuccess) return hip_fail(L, e, "anchor route launch");
     L->anchored = true;
     L->poisoned = false;
@@ -219,14 +313,18 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
     s.c = L->c;
     s.sel = L->sel;
     s.gamma = L->cfg.gamma;
+    int tix = time_begin(L, RR_KERNEL_RESCORE, st);
     hipError_t e = rr::launch_rescore(s, L->cfg.dtype == RR_BF16, st);
+    time_end(L, tix, st);
     if (e != hipSuccess) return hip_fail(L, e, "rescore launch");
 
     rr::RouteArgs a = route_args(L, q, k, layer);
     a.out_rows = out ? out->rows : nullptr;
     a.out_head_counts = out ? out->head_counts : nullptr;
     a.out_n_rows = out ? out->n_rows : nullptr;
+    tix = time_begin(L, RR_KERNEL_REROUTE, st);
     e = rr::launch_route(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, true, st);
+    time_end(L, tix, st);
     if (e != hipSuccess) return hip_fail(L, e, "reroute launch");
     L->last_layer = layer;
     return ok();

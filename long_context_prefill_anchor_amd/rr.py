@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "RR_OK", -1: "RR_EINVAL", -2: "RR_EUNSUPPORTED", -3: "RR_ENOM
 # Entry points declared in include/rr.h, in declaration order.
 ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_destroy", "rr_anchor_route",
                 "rr_relay_layer", "rr_ledger_get", "rr_ledger_set", "rr_ledger_config",
-                "rr_last_error", "rr_abi_version")
+                "rr_ledger_profile", "rr_ledger_kernel_times", "rr_last_error", "rr_abi_version")
+RR_KERNEL_ROUTE, RR_KERNEL_RESCORE, RR_KERNEL_REROUTE, RR_KERNEL_KINDS = 0, 1, 2, 3
 
 
 class rr_config(ctypes.Structure):
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.rr_ledger_get.argtypes = [vp, vp, vp, vp, i32, vp]
         L.rr_ledger_set.argtypes = [vp, vp, vp, vp, i32, i32, vp]
         L.rr_ledger_config.argtypes = [vp, P(rr_config)]
+        L.rr_ledger_profile.argtypes = [vp, i32]
+        L.rr_ledger_kernel_times.argtypes = [vp, P(i32), P(ctypes.c_double)]
         L.rr_last_error.restype = ctypes.c_char_p
         L.rr_last_error.argtypes = []
         L.rr_abi_version.restype = i32
@@ -149,6 +152,18 @@ def rr_ledger_set(handle, route, sent, anchor_layer, last_layer: int, src_is_hos
            "rr_ledger_set")
 
 
+def rr_ledger_profile(handle, enable: bool) -> None:
+    _check(lib().rr_ledger_profile(handle, int(bool(enable))), "rr_ledger_profile")
+
+
+def rr_ledger_kernel_times(handle):
+    """[(launches, total_ms)] indexed by RR_KERNEL_ROUTE / _RESCORE / _REROUTE."""
+    n = (ctypes.c_int32 * RR_KERNEL_KINDS)()
+    ms = (ctypes.c_double * RR_KERNEL_KINDS)()
+    _check(lib().rr_ledger_kernel_times(handle, n, ms), "rr_ledger_kernel_times")
+    return [(int(n[i]), float(ms[i])) for i in range(RR_KERNEL_KINDS)]
+
+
 def rr_last_error() -> str:
     return lib().rr_last_error().decode()
 
@@ -223,6 +238,12 @@ class Ledger:
         anchor = torch.empty((H, nq), dtype=torch.int32, device="cuda")
         rr_ledger_get(self.handle, route, sent if self.m + self.r else None, anchor, False, stream)
         return route, sent, anchor
+
+    def profile(self, enable=True):
+        rr_ledger_profile(self.handle, enable)
+
+    def kernel_times(self):
+        return rr_ledger_kernel_times(self.handle)
 
     def set(self, route, sent, anchor, last_layer, stream=None):
         rr_ledger_set(self.handle, route, sent if self.m + self.r else None, anchor, last_layer,

@@ -92,7 +92,9 @@ def test_null_ledger_is_rejected_by_every_call():
     assert L.rr_ledger_get(None, None, None, None, 1, None) == rr.RR_EINVAL
     assert L.rr_ledger_set(None, 1, 1, 1, 0, 1, None) == rr.RR_EINVAL
     assert L.rr_ledger_config(None, None) == rr.RR_EINVAL
-    assert "NULL" in rr.rr_last_error()
+    assert L.rr_ledger_profile(None, 1) == rr.RR_EINVAL
+    assert L.rr_ledger_kernel_times(None, None, None) == rr.RR_EINVAL
+    assert "NULL" in rr.rr_last_error() or "required" in rr.rr_last_error()
     L.rr_ledger_destroy(None)     # ignored
 
 

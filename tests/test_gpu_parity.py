@@ -280,3 +280,25 @@ def test_state_rules_on_device():
     # same inputs as the anchor: every row is stable unless it ties (alpha == beta)
     assert np.array_equal(before[0], after[0])
     led.close()
+
+
+@pytest.mark.gpu
+def test_kernel_timing_records_every_launch():
+    import torch
+    U.log("[profile] per-kernel launch events")
+    led = rr.Ledger(2, 128, 128, 64, 12, 12, 8, 0.0, False, "f32", 0)
+    q, k = synth.gaussian_inputs(2, 128, 128, 64, seed=1)
+    qd, kd = U.upload(q), U.upload(k)
+    led.profile(True)
+    led.anchor(qd, kd, 0)
+    led.relay(qd, kd, 1)
+    led.relay(qd, kd, 2)
+    kt = led.kernel_times()
+    assert [n for n, _ in kt] == [1, 2, 2]
+    assert all(ms > 0.0 for _, ms in kt)
+    assert [n for n, _ in led.kernel_times()] == [0, 0, 0]       # reading clears the record
+    led.profile(False)
+    led.anchor(qd, kd, 3)
+    torch.cuda.synchronize()
+    assert [n for n, _ in led.kernel_times()] == [0, 0, 0]
+    led.close()

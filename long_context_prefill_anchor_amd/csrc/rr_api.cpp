@@ -25,6 +25,7 @@ struct rr_ledger {
     uint8_t* flags_ws = nullptr; // [H, nq]
     float* hint_ws = nullptr;    // [H, nq]
     int32_t* bcount = nullptr;   // [H, G]
+    int32_t* blist = nullptr;    // [H, G, 64]
     int32_t last_layer = -1;
     bool anchored = false;
     bool poisoned = false;
@@ -87,6 +88,7 @@ void free_all(rr_ledger* L) {
     (void)hipFree(L->flags_ws);
     (void)hipFree(L->hint_ws);
     (void)hipFree(L->bcount);
+    (void)hipFree(L->blist);
 }
 
 hipEvent_t take_event(rr_ledger* L) {
@@ -142,6 +144,7 @@ rr::RouteArgs route_args(const rr_ledger* L, const void* q, const void* k, int l
     a.flags = L->flags_ws;
     a.hint = L->hint_ws;
     a.bcount = L->bcount;
+    a.blist = L->blist;
     a.H = L->cfg.heads;
     a.nq = L->cfg.nq;
     a.nk = L->cfg.nk;
@@ -192,6 +195,7 @@ rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
         {(void**)&L->flags_ws, rows},
         {(void**)&L->hint_ws, rows * sizeof(float)},
         {(void**)&L->bcount, (size_t)cfg->heads * L->G * sizeof(int32_t)},
+        {(void**)&L->blist, (size_t)cfg->heads * L->G * rr::ROUTE_ROWS * sizeof(int32_t)},
     };
     for (auto& a : allocs) {
         e = hipMalloc(a.p, a.bytes ? a.bytes : 4);
@@ -300,6 +304,7 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
     s.flags_ws = L->flags_ws;
     s.hint_ws = L->hint_ws;
     s.bcount = L->bcount;
+    s.blist = L->blist;
     s.out_flags = out ? out->flags : nullptr;
     s.out_alpha = out ? out->alpha : nullptr;
     s.out_beta = out ? out->beta : nullptr;

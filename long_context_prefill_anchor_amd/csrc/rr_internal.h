@@ -14,6 +14,7 @@ struct RouteArgs {
     const uint8_t* flags;       // reroute: refresh flags [H, nq] from the rescore kernel
     const float* hint;          // reroute: first selection threshold per row [H, nq]
     const int32_t* bcount;      // reroute: flagged rows per rescore block [H, G]
+    const int32_t* blist;       // reroute: per rescore block, its flagged rows (ascending) [H, G, 64]
     int32_t* out_rows;          // reroute, optional: compacted list (ascending h*nq+i)
     int32_t* out_head_counts;   // reroute, optional: [H]
     int32_t* out_n_rows;        // reroute, optional: [1]
@@ -29,6 +30,7 @@ struct RescoreArgs {
     uint8_t* flags_ws;          // [H, nq]
     float* hint_ws;             // [H, nq]
     int32_t* bcount;            // [H, G] flagged rows per block of 64 rows
+    int32_t* blist;             // [H, G, 64] those rows (row index within the head), ascending
     uint8_t* out_flags;         // optional
     float* out_alpha;           // optional
     float* out_beta;            // optional

@@ -591,46 +591,88 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     // ------------------------------------------------------------------ rows of this block
     if constexpr (REROUTE) {
         const int32_t* bc = p.bcount + (size_t)h * G;
-        int total = 0;
-        for (int b0 = 0; b0 < G; b0 += 64) total += wave_sum_in((b0 + lane < G) ? bc[b0 + lane] : 0, 64);
-        const int count_h = total;
-        if (g == 0 && wave == 0) {
-            // Compacted list output (ascending h*nq + i), per-head count and total.
-            if (p.out_head_counts && lane == 0) p.out_head_counts[h] = count_h;
-            int offset = 0;
-            if (p.out_rows || p.out_n_rows) {
-                int acc = 0;
-                for (int x = lane; x < h * G; x += 64) acc += p.bcount[x];
-                offset = wave_sum_in(acc, 64);
-                if (p.out_n_rows && h == p.H - 1 && lane == 0) p.out_n_rows[0] = offset + count_h;
+        if (G <= 64) {
+            // Ranks of flagged rows within the head: block b of the rescore kernel holds ranks
+            // [incl_b - cnt_b, incl_b), listed ascending in blist.
+            const int cnt = (lane < G) ? bc[lane] : 0;
+            int incl = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o, 64);
+                incl += (lane >= o) ? y : 0;
             }
-            if (p.out_rows) {
+            const int count_h = __shfl(incl, 63, 64);
+            const int32_t* bl = p.blist + (size_t)h * G * ROWS;
+            if (g == 0 && wave == 0) {
+                // Compacted list output (ascending h*nq + i), per-head count and total.
+                if (p.out_head_counts && lane == 0) p.out_head_counts[h] = count_h;
+                int offset = 0;
+                if (p.out_rows || p.out_n_rows) {
+                    int acc = 0;
+                    for (int x = lane; x < h * G; x += 64) acc += p.bcount[x];
+                    offset = wave_sum_in(acc, 64);
+                    if (p.out_n_rows && h == p.H - 1 && lane == 0) p.out_n_rows[0] = offset + count_h;
+                }
+                if (p.out_rows) {
+                    for (int bb = 0; bb < G; ++bb) {
+                        const int cb = __shfl(cnt, bb, 64);
+                        const int base = __shfl(incl, bb, 64) - cb;
+                        if (lane < cb) p.out_rows[offset + base + lane] = h * p.nq + bl[bb * ROWS + lane];
+                    }
+                }
+            }
+            if (g * ROWS >= count_h) return;                   // uniform over the block
+            if (wave == 0) {
+                const int rank = g * ROWS + lane;
+                int blk = 0;                                   // blocks whose ranks end at or before `rank`
+                for (int bb = 0; bb < G; ++bb) blk += (__shfl(incl, bb, 64) <= rank) ? 1 : 0;
+                const int bsel = min(blk, G - 1);
+                const int start = __shfl(incl, bsel, 64) - __shfl(cnt, bsel, 64);
+                const int ent = min(rank - start, ROWS - 1);    // < the block's count when rank < count_h
+                sh.rows[lane] = (rank < count_h) ? bl[bsel * ROWS + ent] : -1;
+            }
+        } else {
+            int total = 0;
+            for (int b0 = 0; b0 < G; b0 += 64) total += wave_sum_in((b0 + lane < G) ? bc[b0 + lane] : 0, 64);
+            const int count_h = total;
+            if (g == 0 && wave == 0) {
+                // Compacted list output (ascending h*nq + i), per-head count and total.
+                if (p.out_head_counts && lane == 0) p.out_head_counts[h] = count_h;
+                int offset = 0;
+                if (p.out_rows || p.out_n_rows) {
+                    int acc = 0;
+                    for (int x = lane; x < h * G; x += 64) acc += p.bcount[x];
+                    offset = wave_sum_in(acc, 64);
+                    if (p.out_n_rows && h == p.H - 1 && lane == 0) p.out_n_rows[0] = offset + count_h;
+                }
+                if (p.out_rows) {
+                    int run = 0;
+                    for (int b = 0; b < G; ++b) {
+                        const int i = b * ROWS + lane;
+                        const bool f = i < p.nq && p.flags[(size_t)h * p.nq + i];
+                        const uint64_t m = __ballot(f);
+                        const int pos = run + __popcll(m & ((1ull << lane) - 1ull));
+                        if (f) p.out_rows[offset + pos] = h * p.nq + i;
+                        run += __popcll(m);
+                    }
+                }
+            }
+            if (g * ROWS >= count_h) return;                       // uniform over the block
+            if (wave == 0) {
+                const int want0 = g * ROWS;
                 int run = 0;
-                for (int b = 0; b < G; ++b) {
-                    const int i = b * ROWS + lane;
-                    const bool f = i < p.nq && p.flags[(size_t)h * p.nq + i];
-                    const uint64_t m = __ballot(f);
-                    const int pos = run + __popcll(m & ((1ull << lane) - 1ull));
-                    if (f) p.out_rows[offset + pos] = h * p.nq + i;
-                    run += __popcll(m);
+                sh.rows[lane] = -1;
+                for (int b = 0; b < G && run < want0 + ROWS; ++b) {
+                    const int cb = bc[b];
+                    if (run + cb > want0) {
+                        const int i = b * ROWS + lane;
+                        const bool f = i < p.nq && p.flags[(size_t)h * p.nq + i];
+                        const uint64_t m = __ballot(f);
+                        const int pos = run + __popcll(m & ((1ull << lane) - 1ull));
+                        if (f && pos >= want0 && pos < want0 + ROWS) sh.rows[pos - want0] = i;
+                    }
+                    run += cb;
                 }
-            }
-        }
-        if (g * ROWS >= count_h) return;                       // uniform over the block
-        if (wave == 0) {
-            const int want0 = g * ROWS;
-            int run = 0;
-            sh.rows[lane] = -1;
-            for (int b = 0; b < G && run < want0 + ROWS; ++b) {
-                const int cb = bc[b];
-                if (run + cb > want0) {
-                    const int i = b * ROWS + lane;
-                    const bool f = i < p.nq && p.flags[(size_t)h * p.nq + i];
-                    const uint64_t m = __ballot(f);
-                    const int pos = run + __popcll(m & ((1ull << lane) - 1ull));
-                    if (f && pos >= want0 && pos < want0 + ROWS) sh.rows[pos - want0] = i;
-                }
-                run += cb;
             }
         }
     } else {
@@ -769,22 +811,44 @@ template <> struct Gather<float> {
 
 constexpr int RESCORE_THREADS = 1024;     // 16 waves x 4 rows: rows 64b..64b+63 of head h
 
+// Raw buffer loads: a uniform base in a buffer resource plus a 32-bit per-lane offset (one
+// VALU op of address arithmetic instead of a 64-bit add); offsets past `bytes` read zeros.
+// Word 3 is the gfx9-family raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ int buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+constexpr uint32_t OOB = 0x7FFFFFF0u;                 // offset past any buffer here: reads zeros
+
+// min / max of non-NaN values as one med3 (the median of {a, b, -inf} is the smaller of a, b).
+__device__ __forceinline__ float min_f(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -INFINITY); }
+__device__ __forceinline__ float max_f(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
 // Block (h, b): rows 64b..64b+63 of head h; wave w takes rows 4w..4w+3.  Per row, the c
 // candidate IDs are scored in NP passes of 64 / CL candidates; lanes g*CL .. g*CL+CL-1 share
 // candidate g of a pass.  Rows go in batches of 8 / NP so that each lane has 8 independent
 // 16-byte K loads in flight: the kernel moves few bytes, so its time is set by how many memory
 // round trips each wave waits for, not by bandwidth.  At NP = 4 that fits 64 VGPRs, so two
-// 1024-thread blocks share a CU and a 32-head layer runs in a single round of blocks.  Loads are unconditional with clamped
-// addresses; lanes without a candidate mask their score to NaN, which min/max then ignore.
+// 1024-thread blocks share a CU and a 32-head layer runs in a single round of blocks.
+// Loads are raw buffer loads from the head's base (out-of-range offsets read zeros), all
+// issued before any is used; candidates without an ID contribute +inf to the minima and -inf
+// to the maximum.  The block
+// ends by listing its flagged rows (ascending) for the reroute kernel.
 template <typename DT, int NP>
 __global__ __launch_bounds__(RESCORE_THREADS) void k_rescore(RescoreArgs p) {
     typedef typename Elem<DT>::type E;
     constexpr int CL = Gather<DT>::CL;
     constexpr int CPP = 64 / CL;                      // candidates per pass
-    constexpr int RB = (8 / NP) > 0 ? 8 / NP : 1;   // rows per batch
+    constexpr int RB = (8 / NP) > 0 ? 8 / NP : 1;     // rows per batch
     static_assert(4 % RB == 0, "rows per batch must divide 4");
-    constexpr int EPC = 16 / (int)sizeof(E);          // elements per 16-byte chunk
-    __shared__ int32_t wave_flags[RESCORE_THREADS / 64];
+    constexpr uint32_t ROW_BYTES = 64 * sizeof(E);
+    __shared__ uint32_t row_flag[ROWS];
     const int G = (p.nq + ROWS - 1) / ROWS;
     const int lb = xcd_block(p.H * G);
     if (lb < 0) return;
@@ -794,11 +858,21 @@ __global__ __launch_bounds__(RESCORE_THREADS) void k_rescore(RescoreArgs p) {
     const int lane = threadIdx.x & 63;
     const int ch = lane % CL;                         // 16-byte chunk of the key / query row
     const int grp = lane / CL;                        // candidate slot within a pass
-    const E* Qh = reinterpret_cast<const E*>(p.qp) + (size_t)h * p.nq * 64;
-    const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
-    const int32_t* Ih = p.ids + (size_t)h * p.nq * p.c;
-    const float nan = __builtin_nanf("");
-    int flagged = 0;
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(reinterpret_cast<const char*>(p.qp) + (size_t)h * p.nq * ROW_BYTES,
+                                                (uint32_t)p.nq * ROW_BYTES);
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(reinterpret_cast<const char*>(p.kp) + (size_t)h * p.nk * ROW_BYTES,
+                                                (uint32_t)p.nk * ROW_BYTES);
+    const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.ids + (size_t)h * p.nq * p.c, (uint32_t)(p.nq * p.c * 4));
+    const uint32_t coff = 16u * ch;
+    // Candidate categories of this lane's slot in each pass (route, near-miss, any sentinel).
+    bool isR[NP], isN[NP], isS[NP];
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps) {
+        const int c = grp + CPP * ps;
+        isR[ps] = c < p.k;
+        isN[ps] = c >= p.k && c < p.sel;
+        isS[ps] = c >= p.k && c < p.c;
+    }
 #pragma unroll
     for (int r0 = 0; r0 < 4; r0 += RB) {
         const int ibase = b * ROWS + wave * 4 + r0;
@@ -807,13 +881,12 @@ __global__ __launch_bounds__(RESCORE_THREADS) void k_rescore(RescoreArgs p) {
 #pragma unroll
         for (int rr = 0; rr < RB; ++rr) {
             const int i = ibase + rr;
-            const int ic = i < p.nq ? i : p.nq - 1;
-            qv[rr] = *reinterpret_cast<const uint4*>(Qh + (size_t)ic * 64 + ch * EPC);
+            qv[rr] = buf_load16(rQ, i < p.nq ? (uint32_t)i * ROW_BYTES + coff : OOB);
 #pragma unroll
             for (int ps = 0; ps < NP; ++ps) {
                 const int c = grp + CPP * ps;
                 const bool ok = (i < p.nq) & (c < p.c);
-                const int id = Ih[ok ? (size_t)i * p.c + c : 0];
+                const int id = buf_load4(rI, ok ? (uint32_t)(i * p.c + c) * 4u : OOB);
                 // The select's condition reads the loaded value, so the load cannot be sunk into a
                 // branch (one wait per load); the unsigned compare also drops -1 padding and any
                 // index outside K, whatever the ledger holds.
@@ -825,53 +898,55 @@ __global__ __launch_bounds__(RESCORE_THREADS) void k_rescore(RescoreArgs p) {
         for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
             for (int ps = 0; ps < NP; ++ps) {
-                const int id = ids[rr][ps] >= 0 ? ids[rr][ps] : 0;
-                kv[rr][ps] = *reinterpret_cast<const uint4*>(Kh + (size_t)id * 64 + ch * EPC);
+                const int id = ids[rr][ps];
+                kv[rr][ps] = buf_load16(rK, id >= 0 ? (uint32_t)id * ROW_BYTES + coff : OOB);
             }
 #pragma unroll
         for (int rr = 0; rr < RB; ++rr) {
             const int i = ibase + rr;
-            float alpha = nan, nmin = nan, beta = nan;
-            int nsel = 0;
+            float alpha = INFINITY, mu = INFINITY, beta = -INFINITY;
+            uint32_t bad = 0;                         // a route / near-miss slot without an ID
 #pragma unroll
             for (int ps = 0; ps < NP; ++ps) {
-                float s = group_sum<CL>(Gather<DT>::dot(qv[rr], kv[rr][ps]));
-                const int c = grp + CPP * ps;
-                s = (ids[rr][ps] >= 0) ? s : nan;
-                if (p.cand_scores && ch == 0 && c < p.c && i < p.nq)
-                    p.cand_scores[((size_t)h * p.nq + i) * p.c + c] = s;
-                alpha = fminf(alpha, c < p.k ? s : nan);
-                nmin = fminf(nmin, (c >= p.k && c < p.sel) ? s : nan);
-                beta = fmaxf(beta, (c >= p.k && c < p.c) ? s : nan);
-                nsel += (c < p.sel && ids[rr][ps] >= 0) ? 1 : 0;
+                const float s = group_sum<CL>(Gather<DT>::dot(qv[rr], kv[rr][ps]));
+                const bool valid = ids[rr][ps] >= 0;
+                alpha = min_f(alpha, (isR[ps] && valid) ? s : INFINITY);
+                mu = min_f(mu, (isN[ps] && valid) ? s : INFINITY);
+                beta = max_f(beta, (isS[ps] && valid) ? s : -INFINITY);
+                bad |= ((isR[ps] || isN[ps]) && !valid) ? 1u : 0u;
+                if (p.cand_scores && ch == 0 && grp + CPP * ps < p.c && i < p.nq)
+                    p.cand_scores[((size_t)h * p.nq + i) * p.c + grp + CPP * ps] = valid ? s : __builtin_nanf("");
             }
-            auto fmin_u = [](uint32_t a, uint32_t b) { return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b))); };
-            auto fmax_u = [](uint32_t a, uint32_t b) { return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); };
-            auto add_u = [](uint32_t a, uint32_t b) { return a + b; };
+            auto fmin_u = [](uint32_t x, uint32_t y) { return __float_as_uint(min_f(__uint_as_float(x), __uint_as_float(y))); };
+            auto fmax_u = [](uint32_t x, uint32_t y) { return __float_as_uint(max_f(__uint_as_float(x), __uint_as_float(y))); };
+            auto or_u = [](uint32_t x, uint32_t y) { return x | y; };
             alpha = __uint_as_float(across_groups<CL>(__float_as_uint(alpha), fmin_u));
-            nmin = __uint_as_float(across_groups<CL>(__float_as_uint(nmin), fmin_u));
+            mu = __uint_as_float(across_groups<CL>(__float_as_uint(mu), fmin_u));
             beta = __uint_as_float(across_groups<CL>(__float_as_uint(beta), fmax_u));
-            nsel = (int)across_groups<CL>((uint32_t)nsel, add_u);
-            beta = (beta != beta) ? -INFINITY : beta;
-            const bool reuse = alpha > (beta + p.gamma);
-            if (lane == 0 && i < p.nq) {
-                const size_t flat = (size_t)h * p.nq + i;
-                p.flags_ws[flat] = reuse ? 0 : 1;
-                p.hint_ws[flat] = (nsel == p.sel) ? fminf(alpha, nmin) : -INFINITY;
-                if (p.out_flags) p.out_flags[flat] = reuse ? 0 : 1;
-                if (p.out_alpha) p.out_alpha[flat] = alpha;
-                if (p.out_beta) p.out_beta[flat] = beta;
-                flagged += reuse ? 0 : 1;
+            bad = across_groups<CL>(bad, or_u);
+            // Eq. 8: reuse iff alpha > beta + gamma (a row without any route ID is refreshed).
+            const bool reuse = alpha < INFINITY && alpha > beta + p.gamma;
+            if (lane == 0) {
+                if (i < p.nq) {
+                    const size_t flat = (size_t)h * p.nq + i;
+                    p.flags_ws[flat] = reuse ? 0 : 1;
+                    p.hint_ws[flat] = bad ? -INFINITY : min_f(alpha, mu);
+                    if (p.out_flags) p.out_flags[flat] = reuse ? 0 : 1;
+                    if (p.out_alpha) p.out_alpha[flat] = alpha;
+                    if (p.out_beta) p.out_beta[flat] = beta;
+                }
+                row_flag[wave * 4 + r0 + rr] = (i < p.nq && !reuse) ? 1u : 0u;
             }
         }
     }
-    if (lane == 0) wave_flags[wave] = flagged;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int tot = 0;
-#pragma unroll
-        for (int w = 0; w < RESCORE_THREADS / 64; ++w) tot += wave_flags[w];
-        p.bcount[lb] = tot;
+    if (wave == 0) {
+        // This block's flagged rows, ascending, and their count (the reroute's compaction input).
+        const bool f = row_flag[lane] != 0u;
+        const uint64_t m = __ballot(f);
+        const int pos = __popcll(m & ((1ull << lane) - 1ull));
+        if (f) p.blist[(size_t)lb * ROWS + pos] = b * ROWS + lane;
+        if (lane == 0) p.bcount[lb] = __popcll(m);
     }
 }
 

@@ -289,20 +289,23 @@ __device__ __forceinline__ int quad_excl_sum(int x, int sub, int* total) {
 
 // Random sentinels (Section 3.1, item 2) and the ledger write of one row, split over the row's
 // quad of lanes (sub = lane & 3).  hv: this lane's half of the row's final list (see
-// quad_merge_split).  LDS per row slot: route and near-miss bitmaps of W = (nk + 31) / 32 + 1
-// words each, then a staging row of c IDs.  Route and near-miss chunks come out in ascending
-// index order by scanning the bitmaps; each lane scans a quarter of the words.
-template <int RW>
+// quad_merge_split).  LDS per row slot: two bitmaps A and B of W = (nk + 31) / 32 + 1 words,
+// then a staging row of c IDs.  A route chunk sets A, a near-miss chunk B, a random sentinel
+// both; so "A | B" is the set a draw must avoid, and the three segments come out in ascending
+// index order by scanning the words (each lane scans a quarter of them).
+// The first 16 draws (Philox blocks 0..3, one block per lane) are decided in parallel: draw t
+// is taken iff its chunk is not in A | B, no earlier draw hit the same chunk, and fewer than r
+// draws before it were taken.  Rows that need more draws continue one draw at a time.
 __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&hv)[16], int slot, int sub,
                                            int my_row, int my_n, int h, unsigned char* lds) {
     const int ki = min(p.k, my_n);
     const int mi = min(p.m, my_n - ki);
     const int words = (p.nk + 31) >> 5;
     const int W = words + 1;
-    uint32_t* bmr = reinterpret_cast<uint32_t*>(lds) + (size_t)slot * 2 * W;
-    uint32_t* bmn = bmr + W;
+    uint32_t* bma = reinterpret_cast<uint32_t*>(lds) + (size_t)slot * 2 * W;
+    uint32_t* bmb = bma + W;
     int32_t* stage = reinterpret_cast<int32_t*>(lds) + (size_t)ROWS * 2 * W + (size_t)slot * p.c;
-    for (int w = sub; w < 2 * W; w += 4) bmr[w] = 0u;
+    for (int w = sub; w < 2 * W; w += 4) bma[w] = 0u;
     if (sub < 2) {                                    // lanes 0 / 1 own positions [0,16) / [16,32)
         const int base = 16 * sub;
 #pragma unroll
@@ -310,53 +313,57 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
             const int pos = base + i;
             const uint32_t j = key_index(hv[i]);
             if (pos < ki + mi && hv[i] != EMPTY_KEY)
-                atomicOr(pos < ki ? &bmr[j >> 5] : &bmn[j >> 5], 1u << (j & 31));
+                atomicOr(pos < ki ? &bma[j >> 5] : &bmb[j >> 5], 1u << (j & 31));
         }
     }
 
-    // Draws t = 0..15 come from Philox blocks 0..3, one block per lane of the quad.
-    const P4 w4 = philox4x32_10(P4{(uint32_t)sub, (uint32_t)my_row, (uint32_t)p.layer, (uint32_t)h},
-                                p.seed_lo, p.seed_hi);
-    uint32_t u[16];
-    u[0] = dpp_i<DPP_BCAST0>((int)w4.x); u[1] = dpp_i<DPP_BCAST0>((int)w4.y);
-    u[2] = dpp_i<DPP_BCAST0>((int)w4.z); u[3] = dpp_i<DPP_BCAST0>((int)w4.w);
-    u[4] = dpp_i<DPP_BCAST1>((int)w4.x); u[5] = dpp_i<DPP_BCAST1>((int)w4.y);
-    u[6] = dpp_i<DPP_BCAST1>((int)w4.z); u[7] = dpp_i<DPP_BCAST1>((int)w4.w);
-    u[8] = dpp_i<DPP_BCAST2>((int)w4.x); u[9] = dpp_i<DPP_BCAST2>((int)w4.y);
-    u[10] = dpp_i<DPP_BCAST2>((int)w4.z); u[11] = dpp_i<DPP_BCAST2>((int)w4.w);
-    u[12] = dpp_i<DPP_BCAST3>((int)w4.x); u[13] = dpp_i<DPP_BCAST3>((int)w4.y);
-    u[14] = dpp_i<DPP_BCAST3>((int)w4.z); u[15] = dpp_i<DPP_BCAST3>((int)w4.w);
-
-    if (sub == 0) {
-        uint32_t rnd[RW];
+    const int pool = my_n - ki - mi;
+    const int rwant = min(p.r, pool);
+    int taken = 0;                                    // random sentinels taken so far (quad-uniform)
+    if (p.r > 0 && pool > p.r) {
+        // Draws 4 sub .. 4 sub + 3 from Philox block `sub`.
+        const P4 w4 = philox4x32_10(P4{(uint32_t)sub, (uint32_t)my_row, (uint32_t)p.layer, (uint32_t)h},
+                                    p.seed_lo, p.seed_hi);
+        uint32_t jj[4];
+        jj[0] = __umulhi(w4.x, (uint32_t)my_n);
+        jj[1] = __umulhi(w4.y, (uint32_t)my_n);
+        jj[2] = __umulhi(w4.z, (uint32_t)my_n);
+        jj[3] = __umulhi(w4.w, (uint32_t)my_n);
+        bool ok[4];
 #pragma unroll
-        for (int s = 0; s < RW; ++s) rnd[s] = 0xFFFFFFFFu;
-        int nr = 0;
-        const int pool = my_n - ki - mi;
-        const int rwant = min(p.r, pool);
-        if (p.r > 0) {
-            // A draw is taken when its chunk is in neither the route nor the near-miss set and
-            // not drawn before; only rows whose pool exceeds r draw, smaller pools are filled.
-            bool drawing = pool > p.r;
-            uint32_t jj[16], inrn[16];
+        for (int q = 0; q < 4; ++q) ok[q] = ((bma[jj[q] >> 5] | bmb[jj[q] >> 5]) & (1u << (jj[q] & 31))) == 0u;
+        // Earlier draws of the quad: blocks 0 .. sub-1 (all four words each).
+        uint32_t e[12];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                jj[t] = __umulhi(u[t], (uint32_t)my_n);
-                inrn[t] = (bmr[jj[t] >> 5] | bmn[jj[t] >> 5]) & (1u << (jj[t] & 31));
+        for (int q = 0; q < 4; ++q) {
+            e[q] = (uint32_t)dpp_i<DPP_BCAST0>((int)jj[q]);
+            e[4 + q] = (uint32_t)dpp_i<DPP_BCAST1>((int)jj[q]);
+            e[8 + q] = (uint32_t)dpp_i<DPP_BCAST2>((int)jj[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            bool dup = false;
+#pragma unroll
+            for (int t = 0; t < 12; ++t) dup = dup || (t < 4 * sub && e[t] == jj[q]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dup = dup || (t < q && jj[t] == jj[q]);
+            ok[q] = ok[q] && !dup;
+        }
+        const int mine = (int)ok[0] + (int)ok[1] + (int)ok[2] + (int)ok[3];
+        int tot;
+        int rank = quad_excl_sum(mine, sub, &tot);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (ok[q] && rank < p.r) {
+                atomicOr(&bma[jj[q] >> 5], 1u << (jj[q] & 31));
+                atomicOr(&bmb[jj[q] >> 5], 1u << (jj[q] & 31));
             }
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                bool dup = false;
-#pragma unroll
-                for (int s = 0; s < RW; ++s) dup = dup || (rnd[s] == jj[t]);
-                if (drawing && !inrn[t] && !dup) {
-#pragma unroll
-                    for (int s = 0; s < RW; ++s) rnd[s] = (s == nr) ? jj[t] : rnd[s];
-                    ++nr;
-                    drawing = nr < p.r;
-                }
-            }
+            rank += ok[q] ? 1 : 0;
+        }
+        taken = min(tot, p.r);
+        if (sub == 0) {
             // Rarely more than 16 draws are needed: continue one draw at a time.
+            bool drawing = taken < p.r;
             P4 v4 = {0u, 0u, 0u, 0u};
             for (int t = 16; t < 65536 && __ballot(drawing); ++t) {
                 if ((t & 3) == 0) {
@@ -366,72 +373,64 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
                 const uint32_t uu = ((t & 3) == 0) ? v4.x : ((t & 3) == 1) ? v4.y : ((t & 3) == 2) ? v4.z : v4.w;
                 if (drawing) {
                     const uint32_t j = __umulhi(uu, (uint32_t)my_n);
-                    bool dup = ((bmr[j >> 5] | bmn[j >> 5]) & (1u << (j & 31))) != 0u;
-#pragma unroll
-                    for (int s = 0; s < RW; ++s) dup = dup || (rnd[s] == j);
-                    if (!dup) {
-#pragma unroll
-                        for (int s = 0; s < RW; ++s) rnd[s] = (s == nr) ? j : rnd[s];
-                        ++nr;
-                        drawing = nr < p.r;
+                    const uint32_t bit = 1u << (j & 31);
+                    if (((bma[j >> 5] | bmb[j >> 5]) & bit) == 0u) {
+                        bma[j >> 5] |= bit;
+                        bmb[j >> 5] |= bit;
+                        ++taken;
+                        drawing = taken < p.r;
                     }
                 }
             }
-            // Fill: lowest-index chunks still free (whole pool when pool <= r; draw cap reached).
-            if (nr < rwant) {
-                for (int w = 0; w < words && nr < rwant; ++w) {
-                    uint32_t free_bits = ~(bmr[w] | bmn[w]);
-                    while (free_bits && nr < rwant) {
-                        const uint32_t j = (uint32_t)(w * 32 + __builtin_ctz(free_bits));
-                        free_bits &= free_bits - 1u;
-                        if ((int)j >= my_n) { free_bits = 0; break; }
-                        bool dup = false;
-#pragma unroll
-                        for (int s = 0; s < RW; ++s) dup = dup || (rnd[s] == j);
-                        if (dup) continue;
-#pragma unroll
-                        for (int s = 0; s < RW; ++s) rnd[s] = (s == nr) ? j : rnd[s];
-                        ++nr;
-                    }
-                }
-            }
-            sort_asc<RW>(rnd);
         }
-#pragma unroll
-        for (int s = 0; s < RW; ++s)
-            if (s < p.r) stage[p.k + p.m + s] = (s < nr) ? (int32_t)rnd[s] : -1;
-        p.anchor[(size_t)h * p.nq + my_row] = p.layer;
+        taken = dpp_i<DPP_BCAST0>(taken);
     }
+    if (sub == 0 && taken < rwant) {
+        // Fill: lowest-index chunks still free (whole pool when pool <= r; draw cap reached).
+        for (int w = 0; w < words && taken < rwant; ++w) {
+            uint32_t free_bits = ~(bma[w] | bmb[w]);
+            while (free_bits && taken < rwant) {
+                const uint32_t j = (uint32_t)(w * 32 + __builtin_ctz(free_bits));
+                free_bits &= free_bits - 1u;
+                if ((int)j >= my_n) { free_bits = 0; break; }
+                bma[w] |= 1u << (j & 31);
+                bmb[w] |= 1u << (j & 31);
+                ++taken;
+            }
+        }
+    }
+    if (sub == 0) p.anchor[(size_t)h * p.nq + my_row] = p.layer;
 
-    // Route and near-miss chunks in ascending index order: each lane counts the set bits of its
-    // quarter of the words, an exclusive sum over the quad gives its output offsets.
+    // The three segments in ascending index order: each lane counts route (A only), near-miss
+    // (B only) and random (A and B) bits of its quarter of the words, an exclusive sum over the
+    // quad gives its output offsets.
     const int wq = (words + 3) >> 2;
     const int w0 = sub * wq;
     const int w1 = min(words, w0 + wq);
-    int cr = 0, cn = 0;
+    int cr = 0, cn = 0, cx = 0;
     for (int w = w0; w < w1; ++w) {
-        cr += __popc(bmr[w]);
-        cn += __popc(bmn[w]);
+        const uint32_t x = bma[w], y = bmb[w];
+        cr += __popc(x & ~y);
+        cn += __popc(y & ~x);
+        cx += __popc(x & y);
     }
-    int tr, tn;
+    int tr, tn, tx;
     int pr = quad_excl_sum(cr, sub, &tr);
     int pn = p.k + quad_excl_sum(cn, sub, &tn);
+    int px = p.k + p.m + quad_excl_sum(cx, sub, &tx);
     for (int w = w0; w < w1; ++w) {
-        uint32_t br = bmr[w], bn = bmn[w];
-        while (br) {
-            stage[pr++] = w * 32 + __builtin_ctz(br);
-            br &= br - 1u;
-        }
-        while (bn) {
-            stage[pn++] = w * 32 + __builtin_ctz(bn);
-            bn &= bn - 1u;
-        }
+        const uint32_t x = bma[w], y = bmb[w];
+        uint32_t br = x & ~y, bn = y & ~x, bx = x & y;
+        while (br) { stage[pr++] = w * 32 + __builtin_ctz(br); br &= br - 1u; }
+        while (bn) { stage[pn++] = w * 32 + __builtin_ctz(bn); bn &= bn - 1u; }
+        while (bx) { stage[px++] = w * 32 + __builtin_ctz(bx); bx &= bx - 1u; }
     }
-    for (int s = tr + sub; s < p.k; s += 4) stage[s] = -1;
-    for (int s = tn + sub; s < p.m; s += 4) stage[p.k + s] = -1;
+    for (int s2 = tr + sub; s2 < p.k; s2 += 4) stage[s2] = -1;
+    for (int s2 = tn + sub; s2 < p.m; s2 += 4) stage[p.k + s2] = -1;
+    for (int s2 = tx + sub; s2 < p.r; s2 += 4) stage[p.k + p.m + s2] = -1;
     // The quad copies the staged row out: four consecutive IDs per instruction and row.
     int32_t* dst = p.ids + ((size_t)h * p.nq + my_row) * p.c;
-    for (int e = sub; e < p.c; e += 4) dst[e] = stage[e];
+    for (int e2 = sub; e2 < p.c; e2 += 4) dst[e2] = stage[e2];
 }
 
 // ------------------------------------------------------------------------------ route kernel
@@ -551,10 +550,7 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
                 emit_now = emit_now && cx.q_redo;
             }
         }
-        if (emit_now) {
-            if (p.r <= 8) emit_split<8>(p, hv, qslot, qsub, q_row, q_n, h, dyn_lds);
-            else emit_split<TOPW>(p, hv, qslot, qsub, q_row, q_n, h, dyn_lds);
-        }
+        if (emit_now) emit_split(p, hv, qslot, qsub, q_row, q_n, h, dyn_lds);
         __syncthreads();                                                // LDS free, sh.redo final
     }
 }

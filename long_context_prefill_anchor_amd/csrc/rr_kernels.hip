@@ -404,26 +404,47 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
     // The three segments in ascending index order: each lane counts route (A only), near-miss
     // (B only) and random (A and B) bits of its quarter of the words, an exclusive sum over the
     // quad gives its output offsets.
-    const int wq = (words + 3) >> 2;
+    // Words are read eight at a time (all loads of a chunk issued before any is used); the
+    // bitmaps' unused tail words are zero.
+    constexpr int SW = 8;
+    const int wq = (((words + 3) >> 2) + SW - 1) / SW * SW;   // words per lane, whole chunks
     const int w0 = sub * wq;
-    const int w1 = min(words, w0 + wq);
     int cr = 0, cn = 0, cx = 0;
-    for (int w = w0; w < w1; ++w) {
-        const uint32_t x = bma[w], y = bmb[w];
-        cr += __popc(x & ~y);
-        cn += __popc(y & ~x);
-        cx += __popc(x & y);
+    for (int c0 = 0; c0 < wq; c0 += SW) {
+        uint32_t x[SW], y[SW];
+#pragma unroll
+        for (int u = 0; u < SW; ++u) {
+            const int w = w0 + c0 + u;
+            x[u] = (w < words) ? bma[w] : 0u;
+            y[u] = (w < words) ? bmb[w] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < SW; ++u) {
+            cr += __popc(x[u] & ~y[u]);
+            cn += __popc(y[u] & ~x[u]);
+            cx += __popc(x[u] & y[u]);
+        }
     }
     int tr, tn, tx;
     int pr = quad_excl_sum(cr, sub, &tr);
     int pn = p.k + quad_excl_sum(cn, sub, &tn);
     int px = p.k + p.m + quad_excl_sum(cx, sub, &tx);
-    for (int w = w0; w < w1; ++w) {
-        const uint32_t x = bma[w], y = bmb[w];
-        uint32_t br = x & ~y, bn = y & ~x, bx = x & y;
-        while (br) { stage[pr++] = w * 32 + __builtin_ctz(br); br &= br - 1u; }
-        while (bn) { stage[pn++] = w * 32 + __builtin_ctz(bn); bn &= bn - 1u; }
-        while (bx) { stage[px++] = w * 32 + __builtin_ctz(bx); bx &= bx - 1u; }
+    for (int c0 = 0; c0 < wq; c0 += SW) {
+        uint32_t x[SW], y[SW];
+#pragma unroll
+        for (int u = 0; u < SW; ++u) {
+            const int w = w0 + c0 + u;
+            x[u] = (w < words) ? bma[w] : 0u;
+            y[u] = (w < words) ? bmb[w] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < SW; ++u) {
+            const int wb = (w0 + c0 + u) * 32;
+            uint32_t br = x[u] & ~y[u], bn = y[u] & ~x[u], bx = x[u] & y[u];
+            while (br) { stage[pr++] = wb + __builtin_ctz(br); br &= br - 1u; }
+            while (bn) { stage[pn++] = wb + __builtin_ctz(bn); bn &= bn - 1u; }
+            while (bx) { stage[px++] = wb + __builtin_ctz(bx); bx &= bx - 1u; }
+        }
     }
     for (int s2 = tr + sub; s2 < p.k; s2 += 4) stage[s2] = -1;
     for (int s2 = tn + sub; s2 < p.m; s2 += 4) stage[p.k + s2] = -1;

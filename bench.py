@@ -79,33 +79,93 @@ def quality_pass(w, led, full, qs, ks):
     evaluated score-pair fraction (Section 5 metrics), flagged rows per relay layer."""
     import torch
     H, n = w.heads, w.n
-    outs = [led.alloc_outputs(with_scores=False) if not w.is_anchor(l) else None for l in range(w.layers)]
-    recall_sum, rows_rerouted, flagged, pairs = 0.0, 0, {}, 0
+    n_i = (np.arange(n) + 1) if w.causal else np.full(n, n)          # allowed keys per row
+    c_i = np.minimum(w.c, n_i)                                          # candidates per row
+    out = led.alloc_outputs(with_scores=False)
+    recall_sum, rows_rerouted, flagged, pairs, relay_pairs = 0.0, 0, {}, 0, 0
     for l in range(w.layers):
         if w.is_anchor(l):
             led.anchor(qs[l], ks[l], l)
             rows_rerouted += H * n
-            pairs += H * n * n
+            pairs += H * int(n_i.sum())
         else:
-            led.relay(qs[l], ks[l], l, outs[l])
+            led.relay(qs[l], ks[l], l, out)
         full.anchor(qs[l], ks[l], l)
         torch.cuda.synchronize()
         used = led.get()[0].cpu().numpy().reshape(-1, w.k)
         exact = full.get()[0].cpu().numpy().reshape(-1, w.k)
-        # recall per row: |used & exact| / |exact| (non-causal, n >= k: no padding)
-        inter = (used[:, :, None] == exact[:, None, :]).any(axis=2).sum(axis=1)
-        recall_sum += float((inter / w.k).mean())
+        # recall per row: |used & exact| / |exact|, padding (-1) excluded
+        hit = ((used[:, :, None] == exact[:, None, :]) & (exact[:, None, :] >= 0)).any(axis=1).sum(axis=1)
+        recall_sum += float((hit / np.maximum((exact >= 0).sum(axis=1), 1)).mean())
         if not w.is_anchor(l):
-            nf = int(outs[l].n_rows.cpu().numpy()[0])
+            nf = int(out.n_rows.cpu().numpy()[0])
+            rows = out.rows.cpu().numpy()[:nf] % n
             flagged[l] = nf
             rows_rerouted += nf
-            pairs += H * n * w.c + nf * n
+            lp = H * int(c_i.sum()) + int(n_i[rows].sum())
+            pairs += lp
+            relay_pairs += lp
     L = w.layers
     relay_rho = [flagged[l] / (H * n) for l in sorted(flagged)]
     return dict(recall=recall_sum / L, reroute_fraction=rows_rerouted / (H * n * L),
                 relay_rho_mean=float(np.mean(relay_rho)), relay_rho_per_layer=[round(x, 4) for x in relay_rho],
-                pair_fraction=pairs / (H * n * n * L), flagged=flagged,
-                relay_pairs=sum(H * n * w.c + flagged[l] * n for l in flagged))
+                pair_fraction=pairs / (H * int(n_i.sum()) * L), flagged=flagged, relay_pairs=relay_pairs)
+
+
+def time_chains(w, led, full, qs, ks, steps, warmup):
+    """`warmup` untimed passes, then `steps` timed passes of the relay chain and the full-routing
+    chain, each layer call bracketed by events on the launch stream; returns the per-layer
+    times (ms) of both chains and the wall time of the timed passes."""
+    import torch
+    L = w.layers
+    for _ in range(warmup):
+        run_relay_chain(w, led, qs, ks)
+        run_full_chain(w, full, qs, ks)
+    torch.cuda.synchronize()
+    evs = [([[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)],
+            [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)])
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        run_relay_chain(w, led, qs, ks, evs[s][0])
+        run_full_chain(w, full, qs, ks, evs[s][1])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    relay_ms = np.array([[evs[s][0][l][0].elapsed_time(evs[s][0][l][1]) for l in range(L)] for s in range(steps)])
+    full_ms = np.array([[evs[s][1][l][0].elapsed_time(evs[s][1][l][1]) for l in range(L)] for s in range(steps)])
+    return relay_ms, full_ms, wall
+
+
+def secondary_causal(steps=3, warmup=1):
+    """The 64-head, 4096-chunk causal workload: relay vs full routing (reported beside the
+    headline, which is the 32-head 1024-chunk workload)."""
+    import torch
+    w = W.causal_large()
+    H, n = w.heads, w.n
+    log(f"[bench] secondary: {w.name} {H}x{n} causal, {w.layers} layers")
+    qs, ks = upload_layers(w)
+    led = rr.Ledger(H, n, n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
+    full = rr.Ledger(H, n, n, w.d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
+    q = quality_pass(w, led, full, qs, ks)
+    relay_ms, full_ms, _ = time_chains(w, led, full, qs, ks, steps, warmup)
+    relay_layers = [l for l in range(w.layers) if not w.is_anchor(l)]
+    t_relay = relay_ms[:, relay_layers].sum()
+    t_full = full_ms.sum()
+    out = {"workload": w.name, "heads": H, "nq": n, "nk": n, "causal": True, "layers": w.layers,
+           "relay_routes_per_s": round(H * n * len(relay_layers) * steps / (t_relay / 1e3), 1),
+           "full_routing_routes_per_s": round(H * n * w.layers * steps / (t_full / 1e3), 1),
+           "speedup_vs_full": round(float((t_full / (w.layers * steps)) / (t_relay / (len(relay_layers) * steps))), 4),
+           "relay_layer_us_median": round(float(np.median(relay_ms[:, relay_layers]) * 1e3), 2),
+           "full_layer_us_median": round(float(np.median(full_ms) * 1e3), 2),
+           "recall": round(q["recall"], 6), "reroute_fraction": round(q["reroute_fraction"], 4),
+           "relay_rho_mean": round(q["relay_rho_mean"], 4), "pair_fraction": round(q["pair_fraction"], 4),
+           "steps": steps}
+    led.close()
+    full.close()
+    del qs, ks
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, max_seconds=20.0):
@@ -178,6 +238,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the 64-head 4096-chunk causal relay-vs-full measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (counter calibration)")
     args = ap.parse_args()
@@ -209,25 +271,12 @@ def main():
     relay_layers = [l for l in range(L) if not w.is_anchor(l)]
     anchor_layers = [l for l in range(L) if w.is_anchor(l)]
 
-    def step(evr=None, evf=None):
-        run_relay_chain(w, led, qs, ks, evr)
-        run_full_chain(w, full, qs, ks, evf)
+    def step():
+        run_relay_chain(w, led, qs, ks)
+        run_full_chain(w, full, qs, ks)
 
-    log(f"[bench] warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    log(f"[bench] timing {args.steps} steps")
-    evs = [([[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)],
-            [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)])
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s][0], evs[s][1])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    log(f"[bench] warmup {args.warmup} steps, timing {args.steps} steps")
+    relay_ms, full_ms, wall = time_chains(w, led, full, qs, ks, args.steps, args.warmup)
 
     # Second timed region, same steps, with the library's per-kernel launch events on (kept
     # out of the headline region: each extra event record adds a gap between kernels).
@@ -242,10 +291,6 @@ def main():
     led.profile(False)
     full.profile(False)
 
-    relay_ms = np.array([[evs[s][0][l][0].elapsed_time(evs[s][0][l][1]) for l in range(L)]
-                         for s in range(args.steps)])
-    full_ms = np.array([[evs[s][1][l][0].elapsed_time(evs[s][1][l][1]) for l in range(L)]
-                        for s in range(args.steps)])
     t_relay_layers = relay_ms[:, relay_layers].sum()          # ms over all timed steps
     t_full_layers = full_ms.sum()
     rows_relay = H * n * len(relay_layers) * args.steps
@@ -296,6 +341,12 @@ def main():
     }
     roofline = dict(rer)
 
+    led.close()
+    full.close()
+    del qs, ks
+    torch.cuda.empty_cache()
+    secondary = None if args.no_secondary else secondary_causal()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: oracle on a bounded sample")
@@ -331,10 +382,9 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "secondary": secondary,
     }
     print(json.dumps(out), flush=True)
-    led.close()
-    full.close()
 
 
 if __name__ == "__main__":

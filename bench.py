@@ -137,6 +137,44 @@ def time_chains(w, led, full, qs, ks, steps, warmup):
     return relay_ms, full_ms, wall
 
 
+def graph_chains(w, led, full, qs, ks, reps=10):
+    """Both 32-layer chains captured once as HIP graphs (through torch's graph capture on the
+    library's stream argument) and replayed `reps` times; returns mean ms per chain and whether
+    the replayed relay chain leaves the same ledger as an eager run."""
+    import torch
+    torch.cuda.synchronize()
+    run_relay_chain(w, led, qs, ks)
+    torch.cuda.synchronize()
+    eager = [t.cpu() for t in led.get()]
+    res = {}
+    for name, fn in (("relay_chain_ms", lambda: run_relay_chain(w, led, qs, ks)),
+                     ("full_chain_ms", lambda: run_full_chain(w, full, qs, ks))):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / reps, 4)
+        if name == "relay_chain_ms":
+            replayed = [t.cpu() for t in led.get()]
+            res["replay_matches_eager"] = all(bool(torch.equal(a, b)) for a, b in zip(eager, replayed))
+        del g
+    res["speedup_vs_full_chain"] = round(res["full_chain_ms"] / res["relay_chain_ms"], 4)
+    return res
+
+
 def secondary_causal(steps=3, warmup=1):
     """The 64-head, 4096-chunk causal workload: relay vs full routing (reported beside the
     headline, which is the 32-head 1024-chunk workload)."""
@@ -278,6 +316,9 @@ def main():
     log(f"[bench] warmup {args.warmup} steps, timing {args.steps} steps")
     relay_ms, full_ms, wall = time_chains(w, led, full, qs, ks, args.steps, args.warmup)
 
+    log("[bench] chains as graph replays")
+    graph = graph_chains(w, led, full, qs, ks)
+
     # Second timed region, same steps, with the library's per-kernel launch events on (kept
     # out of the headline region: each extra event record adds a gap between kernels).
     log(f"[bench] timing {args.steps} steps with per-kernel events")
@@ -381,6 +422,7 @@ def main():
         "full_layer_us_median": round(full_layer_us, 2),
         "roofline": roofline,
         "kernels": kernels,
+        "graph": graph,
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

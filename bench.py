@@ -372,7 +372,7 @@ def main():
     rer["traffic"] = recorded_traffic("reroute")
     ach_resc = rescore_bytes / (t_resc * 1e-6) / 1e9
     kernels = {
-        "rescore": {"kernel": "k_rescore<bf16, 4>", "bound": "hbm", "achieved": round(ach_resc, 1),
+        "rescore": {"kernel": "k_rescore<bf16, 1>", "bound": "hbm", "achieved": round(ach_resc, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_resc / HBM_PEAK_GBS, 4),
                     "per_launch": {"bytes": rescore_bytes, "avg_us": round(t_resc, 2), "launches": n_resc},
                     "traffic": recorded_traffic("rescore")},

@@ -64,6 +64,12 @@ __device__ __forceinline__ P4 philox4x32_10(P4 c, uint32_t k0, uint32_t k1) {
     return c;
 }
 
+// min / max of non-NaN values as one med3 (the median of {a, b, -inf} is the smaller of a, b).
+// Unlike fminf / fmaxf these need no canonicalising of operands the compiler cannot prove
+// canonical (MFMA results, lane moves).
+__device__ __forceinline__ float min_f(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -INFINITY); }
+__device__ __forceinline__ float max_f(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
 // ---------------------------------------------------------------------------------- networks
 // All indices are compile-time constants after unrolling, so the arrays stay in VGPRs.
 
@@ -159,6 +165,7 @@ enum : int {
     DPP_XOR1 = 0xB1,          // quad_perm [1,0,3,2]
     DPP_XOR2 = 0x4E,          // quad_perm [2,3,0,1]
     DPP_HALF_MIRROR = 0x141,  // lane i of each 8-lane half-row <- lane 7 - i
+    DPP_ROR4 = 0x124,         // lane i of each row <- lane (i + 4) mod 16
     DPP_ROR8 = 0x128,         // lane i of each row <- lane (i + 8) mod 16
     DPP_REVERSE = 0x1B,       // quad_perm [3,2,1,0]
     DPP_BCAST0 = 0x00,        // quad_perm [0,0,0,0]: every lane of a quad <- its lane 0
@@ -166,11 +173,13 @@ enum : int {
     DPP_BCAST2 = 0xAA,        // quad_perm [2,2,2,2]
     DPP_BCAST3 = 0xFF,        // quad_perm [3,3,3,3]
 };
+// Lanes whose source lies outside their row (the row shifts) read 0 (bound_ctrl); every other
+// pattern here has a source for every lane, so no "old" value has to be materialised.
 template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
 template <int CTRL> __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
@@ -199,6 +208,51 @@ template <int G, typename F> __device__ __forceinline__ uint32_t across_groups(u
     v = op(a[0], a[1]);
     auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return op(b[0], b[1]);
+}
+
+// Reduce over all 64 lanes (every lane ends with the result), without an LDS round trip:
+// quad, half-row and row steps in DPP, then the row swaps.
+template <typename F> __device__ __forceinline__ int wave_reduce_i(int v, F op) {
+    v = op(v, dpp_i<DPP_XOR1>(v));
+    v = op(v, dpp_i<DPP_XOR2>(v));
+    v = op(v, dpp_i<DPP_HALF_MIRROR>(v));
+    return (int)across_groups<8>((uint32_t)v, [op](uint32_t a, uint32_t b) { return (uint32_t)op((int)a, (int)b); });
+}
+__device__ __forceinline__ int wave_max_i(int v) { return wave_reduce_i(v, [](int a, int b) { return a > b ? a : b; }); }
+__device__ __forceinline__ int wave_min_i(int v) { return wave_reduce_i(v, [](int a, int b) { return a < b ? a : b; }); }
+__device__ __forceinline__ int wave_sum_i(int v) { return wave_reduce_i(v, [](int a, int b) { return a + b; }); }
+
+// Inclusive prefix sum over the 64 lanes: shifts within rows of 16 in DPP (lanes without a
+// source add 0), then the row totals from lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+    v += dpp_i<0x111>(v);                                             // row_shr:1
+    v += dpp_i<0x112>(v);                                             // row_shr:2
+    v += dpp_i<0x114>(v);                                             // row_shr:4
+    v += dpp_i<0x118>(v);                                             // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(v, 15);
+    const int r1 = __builtin_amdgcn_readlane(v, 31);
+    const int r2 = __builtin_amdgcn_readlane(v, 47);
+    const int lane = (int)(threadIdx.x & 63);
+    return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
+// fp32 min / max of two or three values as one VALU op.  Written as instructions because the compiler
+// canonicalises both operands of fmaxf (two extra ops each) when it cannot prove them canonical,
+// as for MFMA results and lane moves; the inputs here are never NaN.
+__device__ __forceinline__ float vmax2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmin2(float a, float b) {
+    float r;
+    asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 __device__ __forceinline__ float wave_min_in(float v, int width) {

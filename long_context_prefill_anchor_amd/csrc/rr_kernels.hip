@@ -80,12 +80,16 @@ template <> struct Tile<bf16_t> {
             }
     }
     // Rows past nk read row nk-1 instead: those keys are masked out of every row afterwards.
+    // FENCED keeps the loads in program order (see fill_ring).
+    template <bool FENCED = false>
     __device__ __forceinline__ void load_k(KReg& dst, const uint16_t* K, int key0, int nk, int lane) const {
         const int key = min(key0 + (lane & 31), nk - 1);
         const int sub = lane >> 5;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
             dst[s] = *reinterpret_cast<const bf16x8*>(K + (size_t)key * 64 + 16 * s + 8 * sub);
+            if constexpr (FENCED) __builtin_amdgcn_sched_barrier(0);
+        }
     }
     __device__ __forceinline__ void mma(const KReg& ka, f32x16& acc0, f32x16& acc1) const {
         acc0 = f32x16{};
@@ -120,6 +124,7 @@ template <> struct Tile<float> {
             }
         }
     }
+    template <bool FENCED = false>
     __device__ __forceinline__ void load_k(KReg& dst, const float* K, int key0, int nk, int lane) const {
         const int key = min(key0 + (lane & 31), nk - 1);
         const int sub = lane >> 5;
@@ -128,6 +133,7 @@ template <> struct Tile<float> {
         for (int v = 0; v < 8; ++v) {
             const float4 x = src[v];
             dst[4 * v] = x.x; dst[4 * v + 1] = x.y; dst[4 * v + 2] = x.z; dst[4 * v + 3] = x.w;
+            if constexpr (FENCED) __builtin_amdgcn_sched_barrier(0);
         }
     }
     __device__ __forceinline__ void mma(const KReg& ka, f32x16& acc0, f32x16& acc1) const {
@@ -151,6 +157,17 @@ __device__ __forceinline__ void rows_per_lane(f32x16& acc0, f32x16& acc1) {
         acc0[v] = __uint_as_float(r[0]);
         acc1[v] = __uint_as_float(r[1]);
     }
+}
+
+// Fill the K register ring with tiles wave, wave + SPLIT, ... in the order in which the
+// streaming loop reissues them, oldest first.  The wait at the loop head has to hold both on
+// entry and on the back edge; if the entry issued the loads in another order (the scheduler
+// would reverse them), that wait would drain every load in flight instead of only the oldest
+// tile's.
+template <typename DT, typename E, typename KRing>
+__device__ __forceinline__ void fill_ring(const Tile<DT>& tile, KRing& kbuf, const E* Kh, int wave, int nk, int lane) {
+#pragma unroll
+    for (int u = 0; u < Tile<DT>::NBUF; ++u) tile.template load_k<true>(kbuf[u], Kh, TK * (wave + u * SPLIT), nk, lane);
 }
 
 __device__ __forceinline__ constexpr int lo_key(int v) { return 8 * (v >> 2) + (v & 3); }
@@ -183,9 +200,7 @@ __device__ __forceinline__ void merge16_into_top(uint64_t (&top)[TOPW], const ui
 // Sort the lane's buffered (score bits, index) pairs and merge them into its top list.
 // `fresh`: every lane's list is still empty, so the first sorted chunk is copied in.
 __device__ __forceinline__ void drain(uint64_t (&top)[TOPW], const uint2* buf, int cnt, bool& fresh) {
-    int maxc = cnt;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) maxc = max(maxc, __shfl_xor(maxc, o, 64));
+    const int maxc = wave_max_i(cnt);
     for (int c0 = 0; c0 < maxc; c0 += 16) {
         uint64_t x[16];
 #pragma unroll
@@ -218,6 +233,22 @@ __device__ __forceinline__ int xcd_block(int nlogical) {
     const int per = (int)gridDim.x / XCDS;
     const int l = ((int)blockIdx.x % XCDS) * per + (int)blockIdx.x / XCDS;
     return l < nlogical ? l : -1;
+}
+
+// Reroute grids are sized for every slice of 64 rows of every head, but a slice past the head's
+// flagged count exits at once.  The dispatcher deals an XCD's blocks to its CUs in turn, so in
+// head-major order the live slices (the first few of each head) would stack two to a CU while
+// others idle.  When an XCD's range holds whole heads, its blocks are handed out slice-major
+// (slice 0 of each of its heads, then slice 1, ...), which puts the live ones first.
+__device__ __forceinline__ int slice_major_block(int H, int G) {
+    const int per = (int)gridDim.x / XCDS;
+    const int l0 = ((int)blockIdx.x % XCDS) * per;
+    const int local = (int)blockIdx.x / XCDS;
+    if (per % G == 0 && l0 + per <= H * G) {
+        const int nh = per / G;
+        return l0 + (local % nh) * G + local / nh;
+    }
+    return xcd_block(H * G);
 }
 
 __host__ __forceinline__ int xcd_grid(int nlogical) { return (nlogical + XCDS - 1) / XCDS * XCDS; }
@@ -475,7 +506,8 @@ template <typename DT, bool CAUSAL, bool REROUTE>
 __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared& sh, unsigned char* dyn_lds,
                                                 Tile<DT>& tile, RowCtx<DT>& cx, int attempt) {
     const int lane = cx.lane, wave = cx.wave, h = cx.h, my_row = cx.my_row, my_n = cx.my_n;
-    const int nmin = cx.nmin, ntiles = cx.ntiles;
+    // Block-uniform by construction; readfirstlane makes the loops scalar.
+    const int nmin = __builtin_amdgcn_readfirstlane(cx.nmin), ntiles = __builtin_amdgcn_readfirstlane(cx.ntiles);
     const auto* Qh = cx.Qh;
     const auto* Kh = cx.Kh;
     uint2* my_buf = cx.my_buf;
@@ -491,8 +523,7 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
         float ts = key_score(sh.thr[lane]);
         constexpr int NB = Tile<DT>::NBUF;
         typename Tile<DT>::KReg kbuf[NB];
-#pragma unroll
-        for (int u = 0; u < NB; ++u) tile.load_k(kbuf[u], Kh, TK * (wave + u * SPLIT), p.nk, lane);
+        fill_ring<DT>(tile, kbuf, Kh, wave, p.nk, lane);
         for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
@@ -598,9 +629,9 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     __shared__ RouteShared sh;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = (p.nq + ROWS - 1) / ROWS;
-    const int lb = xcd_block(p.H * G);
+    const int lb = REROUTE ? slice_major_block(p.H, G) : xcd_block(p.H * G);
     if (lb < 0) return;
     const int h = lb / G;
     const int g = lb % G;
@@ -612,13 +643,8 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
             // Ranks of flagged rows within the head: block b of the rescore kernel holds ranks
             // [incl_b - cnt_b, incl_b), listed ascending in blist.
             const int cnt = (lane < G) ? bc[lane] : 0;
-            int incl = cnt;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(incl, o, 64);
-                incl += (lane >= o) ? y : 0;
-            }
-            const int count_h = __shfl(incl, 63, 64);
+            const int incl = wave_incl_scan_i(cnt);
+            const int count_h = __builtin_amdgcn_readlane(incl, 63);
             const int32_t* bl = p.blist + (size_t)h * G * ROWS;
             if (g == 0 && wave == 0) {
                 // Compacted list output (ascending h*nq + i), per-head count and total.
@@ -627,30 +653,39 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
                 if (p.out_rows || p.out_n_rows) {
                     int acc = 0;
                     for (int x = lane; x < h * G; x += 64) acc += p.bcount[x];
-                    offset = wave_sum_in(acc, 64);
+                    offset = wave_sum_i(acc);
                     if (p.out_n_rows && h == p.H - 1 && lane == 0) p.out_n_rows[0] = offset + count_h;
                 }
                 if (p.out_rows) {
                     for (int bb = 0; bb < G; ++bb) {
-                        const int cb = __shfl(cnt, bb, 64);
-                        const int base = __shfl(incl, bb, 64) - cb;
+                        const int cb = __builtin_amdgcn_readlane(cnt, bb);
+                        const int base = __builtin_amdgcn_readlane(incl, bb) - cb;
                         if (lane < cb) p.out_rows[offset + base + lane] = h * p.nq + bl[bb * ROWS + lane];
                     }
                 }
             }
             if (g * ROWS >= count_h) return;                   // uniform over the block
             if (wave == 0) {
+                // The rescore block holding this lane's rank, and the rank's entry in its list;
+                // only entries below that block's count are ever read.
                 const int rank = g * ROWS + lane;
-                int blk = 0;                                   // blocks whose ranks end at or before `rank`
-                for (int bb = 0; bb < G; ++bb) blk += (__shfl(incl, bb, 64) <= rank) ? 1 : 0;
-                const int bsel = min(blk, G - 1);
-                const int start = __shfl(incl, bsel, 64) - __shfl(cnt, bsel, 64);
-                const int ent = min(rank - start, ROWS - 1);    // < the block's count when rank < count_h
-                sh.rows[lane] = (rank < count_h) ? bl[bsel * ROWS + ent] : -1;
+                int start = 0, bsel = -1, csel = 0;
+                for (int bb = 0; bb < G; ++bb) {
+                    const int ib = __builtin_amdgcn_readlane(incl, bb);
+                    const int cb = __builtin_amdgcn_readlane(cnt, bb);
+                    if (ib <= rank) {
+                        start = ib;
+                    } else if (bsel < 0) {
+                        bsel = bb;
+                        csel = cb;
+                    }
+                }
+                const int ent = rank - start;
+                sh.rows[lane] = (bsel >= 0 && ent >= 0 && ent < csel) ? bl[bsel * ROWS + ent] : -1;
             }
         } else {
             int total = 0;
-            for (int b0 = 0; b0 < G; b0 += 64) total += wave_sum_in((b0 + lane < G) ? bc[b0 + lane] : 0, 64);
+            for (int b0 = 0; b0 < G; b0 += 64) total += wave_sum_i((b0 + lane < G) ? bc[b0 + lane] : 0);
             const int count_h = total;
             if (g == 0 && wave == 0) {
                 // Compacted list output (ascending h*nq + i), per-head count and total.
@@ -659,7 +694,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
                 if (p.out_rows || p.out_n_rows) {
                     int acc = 0;
                     for (int x = lane; x < h * G; x += 64) acc += p.bcount[x];
-                    offset = wave_sum_in(acc, 64);
+                    offset = wave_sum_i(acc);
                     if (p.out_n_rows && h == p.H - 1 && lane == 0) p.out_n_rows[0] = offset + count_h;
                 }
                 if (p.out_rows) {
@@ -704,12 +739,9 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     // ------------------------------------------------------------------ per-row setup
     const int my_row = sh.rows[lane];
     const int my_n = (my_row < 0) ? 0 : (CAUSAL ? my_row + 1 : p.nk);
-    int kmax = my_n, nmin = (my_row < 0) ? (1 << 30) : my_n;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        kmax = max(kmax, __shfl_xor(kmax, o, 64));
-        nmin = min(nmin, __shfl_xor(nmin, o, 64));
-    }
+    // Wave-uniform after the reductions; readfirstlane lets the compiler see it.
+    const int kmax = __builtin_amdgcn_readfirstlane(wave_max_i(my_n));
+    const int nmin = __builtin_amdgcn_readfirstlane(wave_min_i((my_row < 0) ? (1 << 30) : my_n));
     const int ntiles = (kmax + TK - 1) / TK;
     const E* Qh = reinterpret_cast<const E*>(p.qp) + (size_t)h * p.nq * 64;
     const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
@@ -738,8 +770,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
         // statically indexed ring: copying registers would make the loop wait on the newest load).
         constexpr int NB = Tile<DT>::NBUF;
         typename Tile<DT>::KReg kbuf[NB];
-#pragma unroll
-        for (int u = 0; u < NB; ++u) tile.load_k(kbuf[u], Kh, TK * (wave + u * SPLIT), p.nk, lane);
+        fill_ring<DT>(tile, kbuf, Kh, wave, p.nk, lane);
         for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
@@ -763,12 +794,13 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
                 }
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    const float x = fmaxf(fmaxf(fmaxf(lo[4 * a], lo[4 * a + 1]), fmaxf(lo[4 * a + 2], lo[4 * a + 3])),
-                                          fmaxf(fmaxf(hi[4 * a], hi[4 * a + 1]), fmaxf(hi[4 * a + 2], hi[4 * a + 3])));
+                    const float x = vmax3(vmax3(lo[4 * a], lo[4 * a + 1], lo[4 * a + 2]),
+                                          vmax3(lo[4 * a + 3], hi[4 * a], hi[4 * a + 1]),
+                                          vmax2(hi[4 * a + 2], hi[4 * a + 3]));
                     // insert x into the sorted list: entry s becomes med3(top[s-1], top[s], x)
 #pragma unroll
                     for (int s = 7; s >= 1; --s) top8[s] = __builtin_amdgcn_fmed3f(top8[s - 1], top8[s], x);
-                    top8[0] = fmaxf(top8[0], x);
+                    top8[0] = vmax2(top8[0], x);
                 }
                 }
             }
@@ -800,33 +832,30 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
 
 // ------------------------------------------------------------------------------ rescore
 
-// Lanes per candidate key row: each lane loads one 16-byte chunk, so a row is one contiguous
-// run of CL lanes (one or two cache lines) rather than one lane reading it whole, which would
-// make every load instruction touch 64 different lines.
-template <typename DT> struct Gather;
-template <> struct Gather<bf16_t> {
-    static constexpr int CL = 8;          // 8 lanes x 8 bf16
-    __device__ __forceinline__ static float dot(const uint4& q, const uint4& k) {
-        float acc = 0.f;
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x), __builtin_bit_cast(bf16x2, k.x), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y), __builtin_bit_cast(bf16x2, k.y), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z), __builtin_bit_cast(bf16x2, k.z), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w), __builtin_bit_cast(bf16x2, k.w), acc, false);
-        return acc;
+// Dot product of 16-byte chunks of a query row and a key row, accumulated into a.
+template <typename DT> struct Dot;
+template <> struct Dot<bf16_t> {
+    __device__ __forceinline__ static float acc(const uint4& q, const uint4& k, float a) {
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x), __builtin_bit_cast(bf16x2, k.x), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y), __builtin_bit_cast(bf16x2, k.y), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z), __builtin_bit_cast(bf16x2, k.z), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w), __builtin_bit_cast(bf16x2, k.w), a, false);
+        return a;
     }
 };
-template <> struct Gather<float> {
-    static constexpr int CL = 16;         // 16 lanes x 4 fp32
-    __device__ __forceinline__ static float dot(const uint4& q, const uint4& k) {
-        float acc = __uint_as_float(q.x) * __uint_as_float(k.x);
-        acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
-        acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
-        acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
-        return acc;
+template <> struct Dot<float> {
+    __device__ __forceinline__ static float acc(const uint4& q, const uint4& k, float a) {
+        a = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), a);
+        a = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), a);
+        a = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), a);
+        a = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), a);
+        return a;
     }
 };
 
 constexpr int RESCORE_THREADS = 1024;     // 16 waves x 4 rows: rows 64b..64b+63 of head h
+constexpr int RS_WAVES = RESCORE_THREADS / 64;
+constexpr int RS_ROWS = ROWS / RS_WAVES;  // rows per wave
 
 // Raw buffer loads: a uniform base in a buffer resource plus a 32-bit per-lane offset (one
 // VALU op of address arithmetic instead of a 64-bit add); offsets past `bytes` read zeros.
@@ -843,117 +872,197 @@ __device__ __forceinline__ int buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 constexpr uint32_t OOB = 0x7FFFFFF0u;                 // offset past any buffer here: reads zeros
 
-// min / max of non-NaN values as one med3 (the median of {a, b, -inf} is the smaller of a, b).
-__device__ __forceinline__ float min_f(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -INFINITY); }
-__device__ __forceinline__ float max_f(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+// Min of `lo` and max of `hi`, each over the 32 lanes of this lane's parity (every lane ends
+// with its parity's results): partners at lane offsets 2, 4 and 8 within a row of 16 (DPP),
+// then the row swaps.  The two reductions go step by step together so that each fills the
+// other's wait after a lane move.
+__device__ __forceinline__ void parity_minmax(float& lo, float& hi) {
+    lo = vmin2(lo, dpp_f<DPP_XOR2>(lo));
+    hi = vmax2(hi, dpp_f<DPP_XOR2>(hi));
+    lo = vmin2(lo, dpp_f<DPP_ROR4>(lo));
+    hi = vmax2(hi, dpp_f<DPP_ROR4>(hi));
+    lo = vmin2(lo, dpp_f<DPP_ROR8>(lo));
+    hi = vmax2(hi, dpp_f<DPP_ROR8>(hi));
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(lo), false, false);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(hi), __float_as_uint(hi), false, false);
+    lo = vmin2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    hi = vmax2(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(lo), false, false);
+    auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(hi), __float_as_uint(hi), false, false);
+    lo = vmin2(__uint_as_float(c[0]), __uint_as_float(c[1]));
+    hi = vmax2(__uint_as_float(d[0]), __uint_as_float(d[1]));
+}
 
-// Block (h, b): rows 64b..64b+63 of head h; wave w takes rows 4w..4w+3.  Per row, the c
-// candidate IDs are scored in NP passes of 64 / CL candidates; lanes g*CL .. g*CL+CL-1 share
-// candidate g of a pass.  Rows go in batches of 8 / NP so that each lane has 8 independent
-// 16-byte K loads in flight: the kernel moves few bytes, so its time is set by how many memory
-// round trips each wave waits for, not by bandwidth.  At NP = 4 that fits 64 VGPRs, so two
-// 1024-thread blocks share a CU and a 32-head layer runs in a single round of blocks.
-// Loads are raw buffer loads from the head's base (out-of-range offsets read zeros), all
-// issued before any is used; candidates without an ID contribute +inf to the minima and -inf
-// to the maximum.  The block
-// ends by listing its flagged rows (ascending) for the reroute kernel.
+// Block (h, b): rows 64b..64b+63 of head h; wave w takes rows 4w..4w+3, one at a time.
+//
+// Loads.  Each load instruction reads 8 whole key rows: lane L takes 16-byte chunk L % 8 of
+// candidate 8 j + L / 8 in instruction j, so an instruction touches 8 cache lines (the address
+// unit handles a load in about one cycle per line it touches, so spreading a row's candidates
+// over more lines per instruction would cost more than the extra lane arithmetic below).  Each
+// lane dots its chunk with the matching 16 bytes of the query row, giving partial sums for 4
+// (8 when c > 32) candidates, which a reduce-scatter over the 8-lane group turns into full dot
+// products: afterwards lane L holds candidate 8 (2 b2 + b1) + L / 8 (b2, b1: bits 2 and 1 of L),
+// and with c <= 32 lanes L and L ^ 1 hold the same candidate.
+//
+// Flags.  Even lanes fold the route scores and odd lanes the route + near-miss scores into one
+// min over their parity, which gives alpha (Eq. 6) and the reroute threshold hint together;
+// the max over sentinel scores is beta (Eq. 7).  Candidates without an ID count as +inf for the
+// minima and -inf for the max; a route or near-miss slot without one makes the hint -inf.
+//
+// The wave's query rows and candidate IDs are staged in LDS (read back by this wave only; LDS
+// operations of one wave complete in order), and the key rows of the next DEPTH rows stay in
+// flight while a row is reduced.  The block ends by listing its flagged rows (ascending) for
+// the reroute kernel.
 template <typename DT, int NP>
-__global__ __launch_bounds__(RESCORE_THREADS) void k_rescore(RescoreArgs p) {
+__global__ __launch_bounds__(RESCORE_THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(typename Elem<DT>::type) == 2 ? 8 : 4)))
+void k_rescore(RescoreArgs p) {
     typedef typename Elem<DT>::type E;
-    constexpr int CL = Gather<DT>::CL;
-    constexpr int CPP = 64 / CL;                      // candidates per pass
-    constexpr int RB = (8 / NP) > 0 ? 8 / NP : 1;     // rows per batch
-    static_assert(4 % RB == 0, "rows per batch must divide 4");
     constexpr uint32_t ROW_BYTES = 64 * sizeof(E);
+    static_assert(ROW_BYTES == 128 || ROW_BYTES == 256, "bf16 or fp32 rows");
+    constexpr int LPR = ROW_BYTES / 16;                // lanes per key row in one instruction: 8 or 16
+    constexpr int RPI = 64 / LPR;                      // key rows per instruction: 8 or 4
+    constexpr int NI = 32 * NP / RPI;                  // instructions per query row
+    constexpr int DEPTH = (NP == 1 && LPR == 8) ? 2 : 1;
     __shared__ uint32_t row_flag[ROWS];
+    __shared__ __align__(16) unsigned char sq[RS_WAVES][RS_ROWS][ROW_BYTES];
+    __shared__ int32_t sid[RS_WAVES][RS_ROWS * 32 * NP];
     const int G = (p.nq + ROWS - 1) / ROWS;
     const int lb = xcd_block(p.H * G);
     if (lb < 0) return;
     const int h = lb / G;
     const int b = lb % G;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int ch = lane % CL;                         // 16-byte chunk of the key / query row
-    const int grp = lane / CL;                        // candidate slot within a pass
+    const int i0 = b * ROWS + wave * RS_ROWS;
+    const int nrow = max(0, min(RS_ROWS, p.nq - i0));   // rows of this wave inside the head
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(reinterpret_cast<const char*>(p.qp) + (size_t)h * p.nq * ROW_BYTES,
                                                 (uint32_t)p.nq * ROW_BYTES);
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(reinterpret_cast<const char*>(p.kp) + (size_t)h * p.nk * ROW_BYTES,
                                                 (uint32_t)p.nk * ROW_BYTES);
     const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.ids + (size_t)h * p.nq * p.c, (uint32_t)(p.nq * p.c * 4));
-    const uint32_t coff = 16u * ch;
-    // Candidate categories of this lane's slot in each pass (route, near-miss, any sentinel).
-    bool isR[NP], isN[NP], isS[NP];
-#pragma unroll
-    for (int ps = 0; ps < NP; ++ps) {
-        const int c = grp + CPP * ps;
-        isR[ps] = c < p.k;
-        isN[ps] = c >= p.k && c < p.sel;
-        isS[ps] = c >= p.k && c < p.c;
+
+    // Stage the wave's query rows and its rows' candidate IDs (contiguous in the ledger).
+    {
+        constexpr int PIECES = RS_ROWS * ROW_BYTES / 16;
+        for (int x = lane; x < PIECES; x += 64) {
+            const int rr = x / (ROW_BYTES / 16), piece = x % (ROW_BYTES / 16);
+            const uint4 v = buf_load16(rQ, rr < nrow ? (uint32_t)(i0 + rr) * ROW_BYTES + 16u * piece : OOB);
+            *reinterpret_cast<uint4*>(&sq[wave][rr][16 * piece]) = v;
+        }
+        const int nid = nrow * p.c;
+        for (int x = lane; x < RS_ROWS * p.c; x += 64) {
+            const int id = buf_load4(rI, x < nid ? (uint32_t)(i0 * p.c + x) * 4u : OOB);
+            // -1 for padding, rows outside the head and any index outside K.
+            sid[wave][x] = (x < nid && (unsigned)id < (unsigned)p.nk) ? id : -1;
+        }
     }
+    const int grp = lane / LPR;                         // key row within an instruction
+    const uint32_t coff = 16u * (lane % LPR);           // this lane's chunk of it
+    // Candidate held after the reduce-scatter (pass ps adds 32 ps).
+    const int b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1, b0 = lane & 1;
+    const int b3 = (lane >> 3) & 1;
+    const int jown = (LPR == 8) ? (NP == 1 ? 2 * b2 + b1 : 4 * b2 + 2 * b1 + b0)
+                                : (NP == 1 ? 4 * b3 + 2 * b2 + b1 : 8 * b3 + 4 * b2 + 2 * b1 + b0);
+    const int cown = RPI * jown + grp;                  // candidate index 0 .. 32 NP - 1
+
+    uint4 kv[DEPTH][NI];
+    auto issue = [&](int slot, int rr) {
 #pragma unroll
-    for (int r0 = 0; r0 < 4; r0 += RB) {
-        const int ibase = b * ROWS + wave * 4 + r0;
-        uint4 qv[RB];
-        int ids[RB][NP];
+        for (int j = 0; j < NI; ++j) {
+            const int c = RPI * j + grp;
+            const int id = (c < p.c) ? sid[wave][rr * p.c + c] : -1;
+            kv[slot][j] = buf_load16(rK, id >= 0 ? (uint32_t)id * ROW_BYTES + coff : OOB);
+        }
+    };
 #pragma unroll
-        for (int rr = 0; rr < RB; ++rr) {
-            const int i = ibase + rr;
-            qv[rr] = buf_load16(rQ, i < p.nq ? (uint32_t)i * ROW_BYTES + coff : OOB);
+    for (int d = 0; d < DEPTH; ++d) issue(d, d);
+
+    const bool ownR = cown < p.k, ownSel = cown < p.sel, ownS = cown >= p.k && cown < p.c;
 #pragma unroll
-            for (int ps = 0; ps < NP; ++ps) {
-                const int c = grp + CPP * ps;
-                const bool ok = (i < p.nq) & (c < p.c);
-                const int id = buf_load4(rI, ok ? (uint32_t)(i * p.c + c) * 4u : OOB);
-                // The select's condition reads the loaded value, so the load cannot be sunk into a
-                // branch (one wait per load); the unsigned compare also drops -1 padding and any
-                // index outside K, whatever the ledger holds.
-                ids[rr][ps] = (ok & ((unsigned)id < (unsigned)p.nk)) ? id : -1;
+    for (int rr = 0; rr < RS_ROWS; ++rr) {
+        const int slot = rr % DEPTH;
+        const int i = i0 + rr;
+        const uint4 qv = *reinterpret_cast<const uint4*>(&sq[wave][rr][coff]);
+        float part[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) part[j] = Dot<DT>::acc(qv, kv[slot][j], 0.f);
+        if (rr + DEPTH < RS_ROWS) issue(slot, rr + DEPTH);
+        // Reduce-scatter over the lanes that share key rows.  Each step pairs lanes that differ
+        // in one bit of the group position; a lane keeps the half of its values selected by that
+        // bit and adds the partner's copy of the same half.
+        float s;
+        if constexpr (LPR == 8) {
+            // partners: 7 - (L % 8) (bit 2 differs), L ^ 2, L ^ 1
+            if constexpr (NP == 1) {
+                float k0 = b2 ? part[2] : part[0], k1 = b2 ? part[3] : part[1];
+                const float s0 = b2 ? part[0] : part[2], s1 = b2 ? part[1] : part[3];
+                k0 += dpp_f<DPP_HALF_MIRROR>(s0);
+                k1 += dpp_f<DPP_HALF_MIRROR>(s1);
+                s = b1 ? k1 : k0;
+                s += dpp_f<DPP_XOR2>(b1 ? k0 : k1);
+                s += dpp_f<DPP_XOR1>(s);
+            } else {
+                float k[4], t[2];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) k[u] = (b2 ? part[4 + u] : part[u]) + dpp_f<DPP_HALF_MIRROR>(b2 ? part[u] : part[4 + u]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) t[u] = (b1 ? k[2 + u] : k[u]) + dpp_f<DPP_XOR2>(b1 ? k[u] : k[2 + u]);
+                s = (b0 ? t[1] : t[0]) + dpp_f<DPP_XOR1>(b0 ? t[0] : t[1]);
+            }
+        } else {
+            // fp32 rows, 16 lanes per row: partners L ^ 8 (row rotation by 8), 7 - (L % 8), L ^ 2 [, L ^ 1]
+            if constexpr (NP == 1) {
+                float k[4], t[2];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) k[u] = (b3 ? part[4 + u] : part[u]) + dpp_f<DPP_ROR8>(b3 ? part[u] : part[4 + u]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) t[u] = (b2 ? k[2 + u] : k[u]) + dpp_f<DPP_HALF_MIRROR>(b2 ? k[u] : k[2 + u]);
+                s = (b1 ? t[1] : t[0]) + dpp_f<DPP_XOR2>(b1 ? t[0] : t[1]);
+                s += dpp_f<DPP_XOR1>(s);
+            } else {
+                float k[8], t[4], v[2];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) k[u] = (b3 ? part[8 + u] : part[u]) + dpp_f<DPP_ROR8>(b3 ? part[u] : part[8 + u]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) t[u] = (b2 ? k[4 + u] : k[u]) + dpp_f<DPP_HALF_MIRROR>(b2 ? k[u] : k[4 + u]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) v[u] = (b1 ? t[2 + u] : t[u]) + dpp_f<DPP_XOR2>(b1 ? t[u] : t[2 + u]);
+                s = (b0 ? v[1] : v[0]) + dpp_f<DPP_XOR1>(b0 ? v[0] : v[1]);
             }
         }
-        uint4 kv[RB][NP];
-#pragma unroll
-        for (int rr = 0; rr < RB; ++rr)
-#pragma unroll
-            for (int ps = 0; ps < NP; ++ps) {
-                const int id = ids[rr][ps];
-                kv[rr][ps] = buf_load16(rK, id >= 0 ? (uint32_t)id * ROW_BYTES + coff : OOB);
+        const bool valid = (cown < p.c) && sid[wave][rr * p.c + min(cown, p.c - 1)] >= 0;
+        const float vr = (ownR && valid) ? s : INFINITY;
+        const float vsel = (ownSel && valid) ? s : INFINITY;
+        float B = (ownS && valid) ? s : -INFINITY;
+        float A;
+        if constexpr (NP == 1) {
+            A = b0 ? vsel : vr;                         // lanes L and L ^ 1 hold the same candidate
+        } else {
+            // Pair up: the even lane takes the pair's route minimum, the odd lane its route +
+            // near-miss minimum.
+            A = vmin2(b0 ? vsel : vr, dpp_f<DPP_XOR1>(b0 ? vr : vsel));
+            B = vmax2(B, dpp_f<DPP_XOR1>(B));
+        }
+        const bool bad = ownSel && !valid;
+        if (p.cand_scores && i < p.nq && cown < p.c && (NP == 2 || b0 == 0))
+            p.cand_scores[((size_t)h * p.nq + i) * p.c + cown] = valid ? s : __builtin_nanf("");
+        parity_minmax(A, B);
+        const float alpha = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(A), 0));
+        const float mu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(A), 1));   // min over route + near-miss
+        const float beta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(B), 0));
+        const bool any_bad = __ballot(bad) != 0ull;
+        // Eq. 8: reuse iff alpha > beta + gamma (a row without any route ID is refreshed).
+        const bool reuse = alpha < INFINITY && alpha > beta + p.gamma;
+        if (lane == 0) {
+            if (i < p.nq) {
+                const size_t flat = (size_t)h * p.nq + i;
+                p.flags_ws[flat] = reuse ? 0 : 1;
+                p.hint_ws[flat] = any_bad ? -INFINITY : mu;
+                if (p.out_flags) p.out_flags[flat] = reuse ? 0 : 1;
+                if (p.out_alpha) p.out_alpha[flat] = alpha;
+                if (p.out_beta) p.out_beta[flat] = beta;
             }
-#pragma unroll
-        for (int rr = 0; rr < RB; ++rr) {
-            const int i = ibase + rr;
-            float alpha = INFINITY, mu = INFINITY, beta = -INFINITY;
-            uint32_t bad = 0;                         // a route / near-miss slot without an ID
-#pragma unroll
-            for (int ps = 0; ps < NP; ++ps) {
-                const float s = group_sum<CL>(Gather<DT>::dot(qv[rr], kv[rr][ps]));
-                const bool valid = ids[rr][ps] >= 0;
-                alpha = min_f(alpha, (isR[ps] && valid) ? s : INFINITY);
-                mu = min_f(mu, (isN[ps] && valid) ? s : INFINITY);
-                beta = max_f(beta, (isS[ps] && valid) ? s : -INFINITY);
-                bad |= ((isR[ps] || isN[ps]) && !valid) ? 1u : 0u;
-                if (p.cand_scores && ch == 0 && grp + CPP * ps < p.c && i < p.nq)
-                    p.cand_scores[((size_t)h * p.nq + i) * p.c + grp + CPP * ps] = valid ? s : __builtin_nanf("");
-            }
-            auto fmin_u = [](uint32_t x, uint32_t y) { return __float_as_uint(min_f(__uint_as_float(x), __uint_as_float(y))); };
-            auto fmax_u = [](uint32_t x, uint32_t y) { return __float_as_uint(max_f(__uint_as_float(x), __uint_as_float(y))); };
-            auto or_u = [](uint32_t x, uint32_t y) { return x | y; };
-            alpha = __uint_as_float(across_groups<CL>(__float_as_uint(alpha), fmin_u));
-            mu = __uint_as_float(across_groups<CL>(__float_as_uint(mu), fmin_u));
-            beta = __uint_as_float(across_groups<CL>(__float_as_uint(beta), fmax_u));
-            bad = across_groups<CL>(bad, or_u);
-            // Eq. 8: reuse iff alpha > beta + gamma (a row without any route ID is refreshed).
-            const bool reuse = alpha < INFINITY && alpha > beta + p.gamma;
-            if (lane == 0) {
-                if (i < p.nq) {
-                    const size_t flat = (size_t)h * p.nq + i;
-                    p.flags_ws[flat] = reuse ? 0 : 1;
-                    p.hint_ws[flat] = bad ? -INFINITY : min_f(alpha, mu);
-                    if (p.out_flags) p.out_flags[flat] = reuse ? 0 : 1;
-                    if (p.out_alpha) p.out_alpha[flat] = alpha;
-                    if (p.out_beta) p.out_beta[flat] = beta;
-                }
-                row_flag[wave * 4 + r0 + rr] = (i < p.nq && !reuse) ? 1u : 0u;
-            }
+            row_flag[wave * RS_ROWS + rr] = (i < p.nq && !reuse) ? 1u : 0u;
         }
     }
     __syncthreads();
@@ -998,14 +1107,13 @@ hipError_t launch_route(const RouteArgs& a, bool bf16, bool causal, bool reroute
 
 hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st) {
     const dim3 grid(xcd_grid(a.H * ((a.nq + ROWS - 1) / ROWS)));
-    const int passes = (a.c + (bf16 ? 7 : 3)) / (bf16 ? 8 : 4);   // candidates per pass: 64 / lanes per row
+    const bool two = a.c > 32;                        // candidate passes of 32
     if (bf16) {
-        if (passes <= 4) hipLaunchKernelGGL((k_rescore<bf16_t, 4>), grid, dim3(RESCORE_THREADS), 0, st, a);
-        else hipLaunchKernelGGL((k_rescore<bf16_t, 8>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        if (two) hipLaunchKernelGGL((k_rescore<bf16_t, 2>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        else hipLaunchKernelGGL((k_rescore<bf16_t, 1>), grid, dim3(RESCORE_THREADS), 0, st, a);
     } else {
-        if (passes <= 4) hipLaunchKernelGGL((k_rescore<float, 4>), grid, dim3(RESCORE_THREADS), 0, st, a);
-        else if (passes <= 8) hipLaunchKernelGGL((k_rescore<float, 8>), grid, dim3(RESCORE_THREADS), 0, st, a);
-        else hipLaunchKernelGGL((k_rescore<float, 16>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        if (two) hipLaunchKernelGGL((k_rescore<float, 2>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        else hipLaunchKernelGGL((k_rescore<float, 1>), grid, dim3(RESCORE_THREADS), 0, st, a);
     }
     return hipGetLastError();
 }

@@ -45,9 +45,13 @@ constexpr int SPLIT = 4;           // waves per block, each scoring a quarter of
 constexpr int TK = 32;             // keys per tile
 constexpr int TOPW = 32;           // register top list width (k + m <= TOPW)
 constexpr int CAP = 31;            // per-wave per-row buffer: <= 15 held + 16 slots appended
-constexpr int CSTRIDE = CAP;       // row stride in entries (odd: spreads rows over LDS banks)
+// The per-wave buffers are slot-major ([CAP][ROWS] per wave): a lane's consecutive entries are
+// ROWS apart, so whatever count each lane is at, the 32 lanes of a half-wave write 64-bit entries
+// to 32 distinct bank pairs.
 constexpr int GSTRIDE = 33;        // f32 row stride of the pass-1 group maxima table
 constexpr int XSTRIDE = TOPW + 1;  // u64 row stride of the cross-wave exchange lists
+constexpr int XWAVE = ROWS * XSTRIDE + 8;  // u64 stride between waves' exchange lists: the pad puts
+                                           // the four lists a quad reads in different banks
 constexpr uint64_t NO_PASS_KEY = ~0ull;   // threshold whose score part is NaN: nothing passes
 
 struct bf16_t { uint16_t bits; };
@@ -199,14 +203,14 @@ __device__ __forceinline__ void merge16_into_top(uint64_t (&top)[TOPW], const ui
 
 // Sort the lane's buffered (score bits, index) pairs and merge them into its top list.
 // `fresh`: every lane's list is still empty, so the first sorted chunk is copied in.
-__device__ __forceinline__ void drain(uint64_t (&top)[TOPW], const uint2* buf, int cnt, bool& fresh) {
+__device__ __forceinline__ void drain(uint64_t (&top)[TOPW], const uint2* buf, int cnt, bool& fresh) {   // buf: slot-major
     const int maxc = wave_max_i(cnt);
     for (int c0 = 0; c0 < maxc; c0 += 16) {
         uint64_t x[16];
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             if (c0 + s < cnt) {
-                const uint2 e = buf[c0 + s];
+                const uint2 e = buf[(c0 + s) * ROWS];
                 x[s] = make_key(__uint_as_float(e.x), e.y);
             } else {
                 x[s] = EMPTY_KEY;
@@ -553,9 +557,9 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
                 for (int half = 0; half < 2; ++half) {
 #pragma unroll
                     for (int v = 8 * half; v < 8 * half + 8; ++v) {
-                        my_buf[cnt] = make_uint2(__float_as_uint(lo[v]), (uint32_t)(key0 + lo_key(v)));
+                        my_buf[cnt * ROWS] = make_uint2(__float_as_uint(lo[v]), (uint32_t)(key0 + lo_key(v)));
                         cnt += (lo[v] >= ts) ? 1 : 0;
-                        my_buf[cnt] = make_uint2(__float_as_uint(hi[v]), (uint32_t)(key0 + hi_key(v)));
+                        my_buf[cnt * ROWS] = make_uint2(__float_as_uint(hi[v]), (uint32_t)(key0 + hi_key(v)));
                         cnt += (hi[v] >= ts) ? 1 : 0;
                     }
                     if (__ballot(cnt >= 16)) {
@@ -573,13 +577,13 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
 
         // Final merge, one row per quad: wave w takes rows 16w .. 16w+15 and lane 4j + s of it
         // holds wave s's list of row 16w + j.
-        uint64_t* xl = reinterpret_cast<uint64_t*>(dyn_lds);            // [SPLIT][ROWS][XSTRIDE]
+        uint64_t* xl = reinterpret_cast<uint64_t*>(dyn_lds);            // [SPLIT][XWAVE]: [ROWS][XSTRIDE] + pad
         __syncthreads();                                                // every buffer is drained
 #pragma unroll
-        for (int s = 0; s < TOPW; ++s) xl[((size_t)wave * ROWS + lane) * XSTRIDE + s] = top[s];
+        for (int s = 0; s < TOPW; ++s) xl[wave * XWAVE + lane * XSTRIDE + s] = top[s];
         __syncthreads();
 #pragma unroll
-        for (int s = 0; s < TOPW; ++s) top[s] = xl[((size_t)qsub * ROWS + qslot) * XSTRIDE + s];
+        for (int s = 0; s < TOPW; ++s) top[s] = xl[qsub * XWAVE + qslot * XSTRIDE + s];
         uint64_t hv[16];
         quad_merge_split(top, hv, qsub);
         __syncthreads();                                                // xl is free again
@@ -748,7 +752,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     Tile<DT> tile;
     if constexpr (!REROUTE) tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
 
-    uint2* my_buf = reinterpret_cast<uint2*>(dyn_lds) + ((size_t)wave * ROWS + lane) * CSTRIDE;
+    uint2* my_buf = reinterpret_cast<uint2*>(dyn_lds) + (size_t)wave * CAP * ROWS + lane;
     // Final merge and ledger write run one row per quad of lanes over all four waves.
     const int qslot = 16 * wave + (lane >> 2);
     const int qsub = lane & 3;
@@ -1079,8 +1083,8 @@ void k_rescore(RescoreArgs p) {
 // ------------------------------------------------------------------------------ launchers
 
 size_t route_lds_bytes(int nk, int c) {
-    const size_t cand = (size_t)SPLIT * ROWS * CSTRIDE * sizeof(uint2);
-    const size_t xl = (size_t)SPLIT * ROWS * XSTRIDE * sizeof(uint64_t);
+    const size_t cand = (size_t)SPLIT * CAP * ROWS * sizeof(uint2);
+    const size_t xl = (size_t)SPLIT * XWAVE * sizeof(uint64_t);
     const size_t gm = (size_t)ROWS * GSTRIDE * sizeof(float);
     const size_t em = (size_t)ROWS * (2 * ((nk + 31) / 32 + 1) + c) * sizeof(uint32_t);
     size_t m = cand > xl ? cand : xl;

@@ -897,6 +897,67 @@ __device__ __forceinline__ void parity_minmax(float& lo, float& hi) {
     hi = vmax2(__uint_as_float(d[0]), __uint_as_float(d[1]));
 }
 
+// Reduce-scatter of per-lane partial dot products over the LPR lanes that share key rows (LPR = 8
+// for bf16 rows, 16 for fp32): part[j] is this lane's share of candidate RPI j + L / LPR.  Each
+// step pairs lanes that differ in one bit of the group position; a lane keeps the half of its
+// values selected by that bit and adds the partner's copy of the same half.  Returns the full
+// dot product of candidate cand_of_lane<LPR, NP>(L); with 32 candidates (NP = 1) lanes L and
+// L ^ 1 end with the same candidate and bit-identical sums.
+template <int LPR, int NP>
+__device__ __forceinline__ float reduce_scatter(const float (&part)[32 * NP * LPR / 64], int lane) {
+    const int b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1, b0 = lane & 1;
+    (void)b3;
+    float s;
+    if constexpr (LPR == 8) {
+        // partners: 7 - (L % 8) (bit 2 differs), L ^ 2, L ^ 1
+        if constexpr (NP == 1) {
+            float k0 = b2 ? part[2] : part[0], k1 = b2 ? part[3] : part[1];
+            const float s0 = b2 ? part[0] : part[2], s1 = b2 ? part[1] : part[3];
+            k0 += dpp_f<DPP_HALF_MIRROR>(s0);
+            k1 += dpp_f<DPP_HALF_MIRROR>(s1);
+            s = b1 ? k1 : k0;
+            s += dpp_f<DPP_XOR2>(b1 ? k0 : k1);
+            s += dpp_f<DPP_XOR1>(s);
+        } else {
+            float k[4], t[2];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) k[u] = (b2 ? part[4 + u] : part[u]) + dpp_f<DPP_HALF_MIRROR>(b2 ? part[u] : part[4 + u]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) t[u] = (b1 ? k[2 + u] : k[u]) + dpp_f<DPP_XOR2>(b1 ? k[u] : k[2 + u]);
+            s = (b0 ? t[1] : t[0]) + dpp_f<DPP_XOR1>(b0 ? t[0] : t[1]);
+        }
+    } else {
+        // fp32 rows, 16 lanes per row: partners L ^ 8 (row rotation by 8), 7 - (L % 8), L ^ 2 [, L ^ 1]
+        if constexpr (NP == 1) {
+            float k[4], t[2];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) k[u] = (b3 ? part[4 + u] : part[u]) + dpp_f<DPP_ROR8>(b3 ? part[u] : part[4 + u]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) t[u] = (b2 ? k[2 + u] : k[u]) + dpp_f<DPP_HALF_MIRROR>(b2 ? k[u] : k[2 + u]);
+            s = (b1 ? t[1] : t[0]) + dpp_f<DPP_XOR2>(b1 ? t[0] : t[1]);
+            s += dpp_f<DPP_XOR1>(s);
+        } else {
+            float k[8], t[4], v[2];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) k[u] = (b3 ? part[8 + u] : part[u]) + dpp_f<DPP_ROR8>(b3 ? part[u] : part[8 + u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t[u] = (b2 ? k[4 + u] : k[u]) + dpp_f<DPP_HALF_MIRROR>(b2 ? k[u] : k[4 + u]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) v[u] = (b1 ? t[2 + u] : t[u]) + dpp_f<DPP_XOR2>(b1 ? t[u] : t[2 + u]);
+            s = (b0 ? v[1] : v[0]) + dpp_f<DPP_XOR1>(b0 ? v[0] : v[1]);
+        }
+    }
+    return s;
+}
+
+template <int LPR, int NP>
+__device__ __forceinline__ int cand_of_lane(int lane) {
+    const int b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1, b0 = lane & 1;
+    const int j = (LPR == 8) ? (NP == 1 ? 2 * b2 + b1 : 4 * b2 + 2 * b1 + b0)
+                             : (NP == 1 ? 4 * b3 + 2 * b2 + b1 : 8 * b3 + 4 * b2 + 2 * b1 + b0);
+    return (64 / LPR) * j + lane / LPR;
+}
+
 // Block (h, b): rows 64b..64b+63 of head h; wave w takes rows 4w..4w+3, one at a time.
 //
 // Loads.  Each load instruction reads 8 whole key rows: lane L takes 16-byte chunk L % 8 of
@@ -963,11 +1024,8 @@ void k_rescore(RescoreArgs p) {
     const int grp = lane / LPR;                         // key row within an instruction
     const uint32_t coff = 16u * (lane % LPR);           // this lane's chunk of it
     // Candidate held after the reduce-scatter (pass ps adds 32 ps).
-    const int b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1, b0 = lane & 1;
-    const int b3 = (lane >> 3) & 1;
-    const int jown = (LPR == 8) ? (NP == 1 ? 2 * b2 + b1 : 4 * b2 + 2 * b1 + b0)
-                                : (NP == 1 ? 4 * b3 + 2 * b2 + b1 : 8 * b3 + 4 * b2 + 2 * b1 + b0);
-    const int cown = RPI * jown + grp;                  // candidate index 0 .. 32 NP - 1
+    const int b0 = lane & 1;
+    const int cown = cand_of_lane<LPR, NP>(lane);       // candidate index 0 .. 32 NP - 1
 
     uint4 kv[DEPTH][NI];
     auto issue = [&](int slot, int rr) {
@@ -991,49 +1049,7 @@ void k_rescore(RescoreArgs p) {
 #pragma unroll
         for (int j = 0; j < NI; ++j) part[j] = Dot<DT>::acc(qv, kv[slot][j], 0.f);
         if (rr + DEPTH < RS_ROWS) issue(slot, rr + DEPTH);
-        // Reduce-scatter over the lanes that share key rows.  Each step pairs lanes that differ
-        // in one bit of the group position; a lane keeps the half of its values selected by that
-        // bit and adds the partner's copy of the same half.
-        float s;
-        if constexpr (LPR == 8) {
-            // partners: 7 - (L % 8) (bit 2 differs), L ^ 2, L ^ 1
-            if constexpr (NP == 1) {
-                float k0 = b2 ? part[2] : part[0], k1 = b2 ? part[3] : part[1];
-                const float s0 = b2 ? part[0] : part[2], s1 = b2 ? part[1] : part[3];
-                k0 += dpp_f<DPP_HALF_MIRROR>(s0);
-                k1 += dpp_f<DPP_HALF_MIRROR>(s1);
-                s = b1 ? k1 : k0;
-                s += dpp_f<DPP_XOR2>(b1 ? k0 : k1);
-                s += dpp_f<DPP_XOR1>(s);
-            } else {
-                float k[4], t[2];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) k[u] = (b2 ? part[4 + u] : part[u]) + dpp_f<DPP_HALF_MIRROR>(b2 ? part[u] : part[4 + u]);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) t[u] = (b1 ? k[2 + u] : k[u]) + dpp_f<DPP_XOR2>(b1 ? k[u] : k[2 + u]);
-                s = (b0 ? t[1] : t[0]) + dpp_f<DPP_XOR1>(b0 ? t[0] : t[1]);
-            }
-        } else {
-            // fp32 rows, 16 lanes per row: partners L ^ 8 (row rotation by 8), 7 - (L % 8), L ^ 2 [, L ^ 1]
-            if constexpr (NP == 1) {
-                float k[4], t[2];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) k[u] = (b3 ? part[4 + u] : part[u]) + dpp_f<DPP_ROR8>(b3 ? part[u] : part[4 + u]);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) t[u] = (b2 ? k[2 + u] : k[u]) + dpp_f<DPP_HALF_MIRROR>(b2 ? k[u] : k[2 + u]);
-                s = (b1 ? t[1] : t[0]) + dpp_f<DPP_XOR2>(b1 ? t[0] : t[1]);
-                s += dpp_f<DPP_XOR1>(s);
-            } else {
-                float k[8], t[4], v[2];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) k[u] = (b3 ? part[8 + u] : part[u]) + dpp_f<DPP_ROR8>(b3 ? part[u] : part[8 + u]);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) t[u] = (b2 ? k[4 + u] : k[u]) + dpp_f<DPP_HALF_MIRROR>(b2 ? k[u] : k[4 + u]);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) v[u] = (b1 ? t[2 + u] : t[u]) + dpp_f<DPP_XOR2>(b1 ? t[u] : t[2 + u]);
-                s = (b0 ? v[1] : v[0]) + dpp_f<DPP_XOR1>(b0 ? v[0] : v[1]);
-            }
-        }
+        const float s = reduce_scatter<LPR, NP>(part, lane);
         const bool valid = (cown < p.c) && sid[wave][rr * p.c + min(cown, p.c - 1)] >= 0;
         const float vr = (ownR && valid) ? s : INFINITY;
         const float vsel = (ownSel && valid) ? s : INFINITY;

@@ -86,6 +86,13 @@ RELAY_CASES = [
     ("relay_int", 2, 128, 160, 12, 12, 8, "f32", False, 0.0, "int"),
     ("relay_int_causal", 1, 140, 140, 12, 12, 8, "bf16", True, 0.0, "int"),
     ("relay_guard", 2, 128, 256, 12, 12, 8, "bf16", False, 0.02, "gauss"),
+    # c = 64 (two candidate passes)
+    ("relay_wide64_bf16", 1, 96, 512, 16, 16, 32, "bf16", False, 0.05, "gauss"),
+    ("relay_wide64_f32", 1, 70, 200, 16, 16, 32, "f32", False, 0.05, "gauss"),
+    # more keys than the main workloads (1300-1500 bf16, 600 fp32)
+    ("relay_gather_bf16", 2, 96, 1500, 12, 12, 8, "bf16", False, 0.05, "gauss"),
+    ("relay_gather_f32", 1, 100, 600, 12, 12, 8, "f32", False, 0.05, "gauss"),
+    ("relay_gather_wide", 1, 80, 1300, 16, 16, 32, "bf16", False, 0.05, "gauss"),
 ]
 
 

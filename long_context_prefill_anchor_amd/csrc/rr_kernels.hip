@@ -506,9 +506,11 @@ struct RowCtx {
 // Streaming selection pass from the rows' shared thresholds (sh.thr), final merge and ledger
 // write.  attempt 0 emits every row that holds min(k+m, n) keys; in reroute mode the others are
 // marked for a redo from -inf (attempt 1, which emits only them).
+// kbuf: the K register ring (shared with the anchor's first pass).
 template <typename DT, bool CAUSAL, bool REROUTE>
 __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared& sh, unsigned char* dyn_lds,
-                                                Tile<DT>& tile, RowCtx<DT>& cx, int attempt) {
+                                                Tile<DT>& tile, typename Tile<DT>::KReg (&kbuf)[Tile<DT>::NBUF],
+                                                RowCtx<DT>& cx, int attempt) {
     const int lane = cx.lane, wave = cx.wave, h = cx.h, my_row = cx.my_row, my_n = cx.my_n;
     // Block-uniform by construction; readfirstlane makes the loops scalar.
     const int nmin = __builtin_amdgcn_readfirstlane(cx.nmin), ntiles = __builtin_amdgcn_readfirstlane(cx.ntiles);
@@ -526,7 +528,6 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
         bool fresh = true;                                              // list empty in every lane
         float ts = key_score(sh.thr[lane]);
         constexpr int NB = Tile<DT>::NBUF;
-        typename Tile<DT>::KReg kbuf[NB];
         fill_ring<DT>(tile, kbuf, Kh, wave, p.nk, lane);
         for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
 #pragma unroll
@@ -623,7 +624,8 @@ __device__ __forceinline__ void redo_rows(const RouteArgs& p, RouteShared& sh, u
     asm volatile("" : "+v"(cx.Kh), "+v"(cx.Qh), "+v"(cx.my_buf));
     asm volatile("" : "+v"(cx.q_row), "+v"(cx.q_n), "+v"(cx.qslot), "+v"(cx.qsub));
     Tile<DT> tile;
-    select_and_emit<DT, CAUSAL, true>(p, sh, dyn_lds, tile, cx, 1);
+    typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
+    select_and_emit<DT, CAUSAL, true>(p, sh, dyn_lds, tile, kbuf, cx, 1);
 }
 
 template <typename DT, bool CAUSAL, bool REROUTE>
@@ -750,6 +752,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     const E* Qh = reinterpret_cast<const E*>(p.qp) + (size_t)h * p.nq * 64;
     const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
     Tile<DT> tile;
+    typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
     if constexpr (!REROUTE) tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
 
     uint2* my_buf = reinterpret_cast<uint2*>(dyn_lds) + (size_t)wave * CAP * ROWS + lane;
@@ -771,9 +774,9 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
         for (int s = 0; s < 8; ++s) top8[s] = -INFINITY;
         // K tiles stream through a ring of NBUF register buffers, NBUF - 1 tiles ahead (a
-        // statically indexed ring: copying registers would make the loop wait on the newest load).
+        // statically indexed ring: copying registers would make the loop wait on the newest
+        // load).
         constexpr int NB = Tile<DT>::NBUF;
-        typename Tile<DT>::KReg kbuf[NB];
         fill_ring<DT>(tile, kbuf, Kh, wave, p.nk, lane);
         for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
 #pragma unroll
@@ -828,7 +831,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
 
     // ------------------------------------------------------------------ streaming pass
     RowCtx<DT> cx{lane, wave, h, my_row, my_n, nmin, ntiles, Qh, Kh, my_buf, qslot, qsub, q_row, q_n, false};
-    select_and_emit<DT, CAUSAL, REROUTE>(p, sh, dyn_lds, tile, cx, 0);
+    select_and_emit<DT, CAUSAL, REROUTE>(p, sh, dyn_lds, tile, kbuf, cx, 0);
     if constexpr (REROUTE) {
         if (sh.redo) redo_rows<DT, CAUSAL>(p, sh, dyn_lds, cx);         // uniform; rare
     }
@@ -875,27 +878,6 @@ __device__ __forceinline__ int buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 constexpr uint32_t OOB = 0x7FFFFFF0u;                 // offset past any buffer here: reads zeros
-
-// Min of `lo` and max of `hi`, each over the 32 lanes of this lane's parity (every lane ends
-// with its parity's results): partners at lane offsets 2, 4 and 8 within a row of 16 (DPP),
-// then the row swaps.  The two reductions go step by step together so that each fills the
-// other's wait after a lane move.
-__device__ __forceinline__ void parity_minmax(float& lo, float& hi) {
-    lo = vmin2(lo, dpp_f<DPP_XOR2>(lo));
-    hi = vmax2(hi, dpp_f<DPP_XOR2>(hi));
-    lo = vmin2(lo, dpp_f<DPP_ROR4>(lo));
-    hi = vmax2(hi, dpp_f<DPP_ROR4>(hi));
-    lo = vmin2(lo, dpp_f<DPP_ROR8>(lo));
-    hi = vmax2(hi, dpp_f<DPP_ROR8>(hi));
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(lo), false, false);
-    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(hi), __float_as_uint(hi), false, false);
-    lo = vmin2(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    hi = vmax2(__uint_as_float(b[0]), __uint_as_float(b[1]));
-    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(lo), false, false);
-    auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(hi), __float_as_uint(hi), false, false);
-    lo = vmin2(__uint_as_float(c[0]), __uint_as_float(c[1]));
-    hi = vmax2(__uint_as_float(d[0]), __uint_as_float(d[1]));
-}
 
 // Reduce-scatter of per-lane partial dot products over the LPR lanes that share key rows (LPR = 8
 // for bf16 rows, 16 for fp32): part[j] is this lane's share of candidate RPI j + L / LPR.  Each
@@ -971,8 +953,9 @@ __device__ __forceinline__ int cand_of_lane(int lane) {
 //
 // Flags.  Even lanes fold the route scores and odd lanes the route + near-miss scores into one
 // min over their parity, which gives alpha (Eq. 6) and the reroute threshold hint together;
-// the max over sentinel scores is beta (Eq. 7).  Candidates without an ID count as +inf for the
-// minima and -inf for the max; a route or near-miss slot without one makes the hint -inf.
+// the max over sentinel scores is beta (Eq. 7).  Two rows are reduced together, and each wave
+// writes its rows' results with one store per output.  Candidates without an ID count as +inf
+// for the minima and -inf for the max; a route or near-miss slot without one makes the hint -inf.
 //
 // The wave's query rows and candidate IDs are staged in LDS (read back by this wave only; LDS
 // operations of one wave complete in order), and the key rows of the next DEPTH rows stay in
@@ -1040,50 +1023,88 @@ void k_rescore(RescoreArgs p) {
     for (int d = 0; d < DEPTH; ++d) issue(d, d);
 
     const bool ownR = cown < p.k, ownSel = cown < p.sel, ownS = cown >= p.k && cown < p.c;
+    static_assert(RS_ROWS % 2 == 0, "rows are reduced in pairs");
+    // Per-row results, lane rr of the wave holding row rr.
+    float res_alpha = 0.f, res_mu = 0.f, res_beta = 0.f;
+    bool res_bad = false;
 #pragma unroll
-    for (int rr = 0; rr < RS_ROWS; ++rr) {
-        const int slot = rr % DEPTH;
-        const int i = i0 + rr;
-        const uint4 qv = *reinterpret_cast<const uint4*>(&sq[wave][rr][coff]);
-        float part[NI];
+    for (int pr = 0; pr < RS_ROWS; pr += 2) {
+        float A[2], B[2];
+        bool bad[2];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) part[j] = Dot<DT>::acc(qv, kv[slot][j], 0.f);
-        if (rr + DEPTH < RS_ROWS) issue(slot, rr + DEPTH);
-        const float s = reduce_scatter<LPR, NP>(part, lane);
-        const bool valid = (cown < p.c) && sid[wave][rr * p.c + min(cown, p.c - 1)] >= 0;
-        const float vr = (ownR && valid) ? s : INFINITY;
-        const float vsel = (ownSel && valid) ? s : INFINITY;
-        float B = (ownS && valid) ? s : -INFINITY;
-        float A;
-        if constexpr (NP == 1) {
-            A = b0 ? vsel : vr;                         // lanes L and L ^ 1 hold the same candidate
-        } else {
-            // Pair up: the even lane takes the pair's route minimum, the odd lane its route +
-            // near-miss minimum.
-            A = vmin2(b0 ? vsel : vr, dpp_f<DPP_XOR1>(b0 ? vr : vsel));
-            B = vmax2(B, dpp_f<DPP_XOR1>(B));
-        }
-        const bool bad = ownSel && !valid;
-        if (p.cand_scores && i < p.nq && cown < p.c && (NP == 2 || b0 == 0))
-            p.cand_scores[((size_t)h * p.nq + i) * p.c + cown] = valid ? s : __builtin_nanf("");
-        parity_minmax(A, B);
-        const float alpha = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(A), 0));
-        const float mu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(A), 1));   // min over route + near-miss
-        const float beta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(B), 0));
-        const bool any_bad = __ballot(bad) != 0ull;
-        // Eq. 8: reuse iff alpha > beta + gamma (a row without any route ID is refreshed).
-        const bool reuse = alpha < INFINITY && alpha > beta + p.gamma;
-        if (lane == 0) {
-            if (i < p.nq) {
-                const size_t flat = (size_t)h * p.nq + i;
-                p.flags_ws[flat] = reuse ? 0 : 1;
-                p.hint_ws[flat] = any_bad ? -INFINITY : mu;
-                if (p.out_flags) p.out_flags[flat] = reuse ? 0 : 1;
-                if (p.out_alpha) p.out_alpha[flat] = alpha;
-                if (p.out_beta) p.out_beta[flat] = beta;
+        for (int t = 0; t < 2; ++t) {
+            const int rr = pr + t;
+            const int slot = rr % DEPTH;
+            const int i = i0 + rr;
+            const uint4 qv = *reinterpret_cast<const uint4*>(&sq[wave][rr][coff]);
+            float part[NI];
+#pragma unroll
+            for (int j = 0; j < NI; ++j) part[j] = Dot<DT>::acc(qv, kv[slot][j], 0.f);
+            if (rr + DEPTH < RS_ROWS) issue(slot, rr + DEPTH);
+            const float sc = reduce_scatter<LPR, NP>(part, lane);
+            const bool valid = (cown < p.c) && sid[wave][rr * p.c + min(cown, p.c - 1)] >= 0;
+            const float vr = (ownR && valid) ? sc : INFINITY;
+            const float vsel = (ownSel && valid) ? sc : INFINITY;
+            B[t] = (ownS && valid) ? sc : -INFINITY;
+            if constexpr (NP == 1) {
+                A[t] = b0 ? vsel : vr;                  // lanes L and L ^ 1 hold the same candidate
+            } else {
+                // Pair up: the even lane takes the pair's route minimum, the odd lane its route +
+                // near-miss minimum.
+                A[t] = vmin2(b0 ? vsel : vr, dpp_f<DPP_XOR1>(b0 ? vr : vsel));
+                B[t] = vmax2(B[t], dpp_f<DPP_XOR1>(B[t]));
             }
-            row_flag[wave * RS_ROWS + rr] = (i < p.nq && !reuse) ? 1u : 0u;
+            bad[t] = __ballot(ownSel && !valid) != 0ull;
+            if (p.cand_scores && i < p.nq && cown < p.c && (NP == 2 || b0 == 0))
+                p.cand_scores[((size_t)h * p.nq + i) * p.c + cown] = valid ? sc : __builtin_nanf("");
         }
+        // Min / max over each parity of lanes, two rows at once: one exchange with lane ^ 2 leaves
+        // the first row in lanes with bit 1 clear and the second in the others, then the common
+        // steps (partners 4 and 8 apart within a row of 16, then the row swaps) reduce both.
+        const bool second = (lane & 2) != 0;
+        float a = vmin2(second ? A[1] : A[0], dpp_f<DPP_XOR2>(second ? A[0] : A[1]));
+        float bb = vmax2(second ? B[1] : B[0], dpp_f<DPP_XOR2>(second ? B[0] : B[1]));
+        a = vmin2(a, dpp_f<DPP_ROR4>(a));
+        bb = vmax2(bb, dpp_f<DPP_ROR4>(bb));
+        a = vmin2(a, dpp_f<DPP_ROR8>(a));
+        bb = vmax2(bb, dpp_f<DPP_ROR8>(bb));
+        {
+            auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+            auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(bb), __float_as_uint(bb), false, false);
+            a = vmin2(__uint_as_float(x[0]), __uint_as_float(x[1]));
+            bb = vmax2(__uint_as_float(y[0]), __uint_as_float(y[1]));
+            auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+            auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(bb), __float_as_uint(bb), false, false);
+            a = vmin2(__uint_as_float(z[0]), __uint_as_float(z[1]));
+            bb = vmax2(__uint_as_float(w[0]), __uint_as_float(w[1]));
+        }
+        // Lane 0: alpha (Eq. 6) and beta (Eq. 7) of the first row, lane 1: its minimum over route
+        // + near-miss (the reroute hint); lanes 2 and 3 the same for the second row.
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float al = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 2 * t));
+            const float mu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 2 * t + 1));
+            const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bb), 2 * t));
+            const bool mine = lane == pr + t;
+            res_alpha = mine ? al : res_alpha;
+            res_mu = mine ? mu : res_mu;
+            res_beta = mine ? be : res_beta;
+            res_bad = mine ? bad[t] : res_bad;
+        }
+    }
+    // Eq. 8: reuse iff alpha > beta + gamma (a row without any route ID is refreshed).
+    if (lane < RS_ROWS) {
+        const int i = i0 + lane;
+        const bool reuse = res_alpha < INFINITY && res_alpha > res_beta + p.gamma;
+        if (i < p.nq) {
+            const size_t flat = (size_t)h * p.nq + i;
+            p.flags_ws[flat] = reuse ? 0 : 1;
+            p.hint_ws[flat] = res_bad ? -INFINITY : res_mu;
+            if (p.out_flags) p.out_flags[flat] = reuse ? 0 : 1;
+            if (p.out_alpha) p.out_alpha[flat] = res_alpha;
+            if (p.out_beta) p.out_beta[flat] = res_beta;
+        }
+        row_flag[wave * RS_ROWS + lane] = (i < p.nq && !reuse) ? 1u : 0u;
     }
     __syncthreads();
     if (wave == 0) {

@@ -322,39 +322,63 @@ __device__ __forceinline__ int quad_excl_sum(int x, int sub, int* total) {
     return (sub > 0 ? x0 : 0) + (sub > 1 ? x1 : 0) + (sub > 2 ? x2 : 0);
 }
 
+// Ascending sort of 16 32-bit keys (Batcher's network, min / max compare-exchanges).
+__device__ __forceinline__ void sort16_asc_u32(uint32_t (&v)[16]) {
+#pragma unroll
+    for (int p = 1; p < 16; p <<= 1) {
+#pragma unroll
+        for (int k = p; k >= 1; k >>= 1) {
+#pragma unroll
+            for (int j = k % p; j + k < 16; j += 2 * k) {
+#pragma unroll
+                for (int i = 0; i < k; ++i) {
+                    if (i < 16 - j - k && (i + j) / (2 * p) == (i + j + k) / (2 * p)) {
+                        const uint32_t a = v[i + j], b = v[i + j + k];
+                        v[i + j] = min(a, b);
+                        v[i + j + k] = max(a, b);
+                    }
+                }
+            }
+        }
+    }
+}
+
+constexpr int RLIST = 32;          // per-row list of drawn random sentinels (r <= 32)
+
 // Random sentinels (Section 3.1, item 2) and the ledger write of one row, split over the row's
 // quad of lanes (sub = lane & 3).  hv: this lane's half of the row's final list (see
-// quad_merge_split).  LDS per row slot: two bitmaps A and B of W = (nk + 31) / 32 + 1 words,
-// then a staging row of c IDs.  A route chunk sets A, a near-miss chunk B, a random sentinel
-// both; so "A | B" is the set a draw must avoid, and the three segments come out in ascending
-// index order by scanning the words (each lane scans a quarter of them).
+// quad_merge_split: lanes 0 and 3 hold positions [0, 16), lanes 1 and 2 [16, 32)).  LDS per row
+// slot: a bitmap of W = (nk + 31) / 32 + 1 words holding route, near-miss and drawn chunks (what
+// a draw must avoid), the list of drawn chunks in draw order, then a staging row of c IDs plus a
+// spare slot.
 // The first 16 draws (Philox blocks 0..3, one block per lane) are decided in parallel: draw t
-// is taken iff its chunk is not in A | B, no earlier draw hit the same chunk, and fewer than r
-// draws before it were taken.  Rows that need more draws continue one draw at a time.
+// is taken iff its chunk is not in the bitmap, no earlier draw hit the same chunk, and fewer
+// than r draws before it were taken.  Rows that need more draws continue one draw at a time.
+// Output order: lanes 0 and 1 sort the route and near-miss chunks by (segment, index) and
+// lanes 2 and 3 the drawn chunks by index, each pair with a 16-key network per lane and one
+// bitonic exchange between the two lanes, which leaves every segment in ascending index order.
 __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&hv)[16], int slot, int sub,
                                            int my_row, int my_n, int h, unsigned char* lds) {
     const int ki = min(p.k, my_n);
     const int mi = min(p.m, my_n - ki);
     const int words = (p.nk + 31) >> 5;
     const int W = words + 1;
-    uint32_t* bma = reinterpret_cast<uint32_t*>(lds) + (size_t)slot * 2 * W;
-    uint32_t* bmb = bma + W;
-    int32_t* stage = reinterpret_cast<int32_t*>(lds) + (size_t)ROWS * 2 * W + (size_t)slot * p.c;
-    for (int w = sub; w < 2 * W; w += 4) bma[w] = 0u;
+    uint32_t* bm = reinterpret_cast<uint32_t*>(lds) + (size_t)slot * (W + RLIST);
+    int32_t* rlist = reinterpret_cast<int32_t*>(bm + W);
+    int32_t* stage = reinterpret_cast<int32_t*>(lds) + (size_t)ROWS * (W + RLIST) + (size_t)slot * (p.c + 1);
+    for (int w = sub; w < W; w += 4) bm[w] = 0u;
     if (sub < 2) {                                    // lanes 0 / 1 own positions [0,16) / [16,32)
-        const int base = 16 * sub;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int pos = base + i;
+            const int pos = 16 * sub + i;
             const uint32_t j = key_index(hv[i]);
-            if (pos < ki + mi && hv[i] != EMPTY_KEY)
-                atomicOr(pos < ki ? &bma[j >> 5] : &bmb[j >> 5], 1u << (j & 31));
+            if (pos < ki + mi && hv[i] != EMPTY_KEY) atomicOr(&bm[j >> 5], 1u << (j & 31));
         }
     }
 
     const int pool = my_n - ki - mi;
     const int rwant = min(p.r, pool);
-    int taken = 0;                                    // random sentinels taken so far (quad-uniform)
+    int taken = 0;                                    // random sentinels taken so far
     if (p.r > 0 && pool > p.r) {
         // Draws 4 sub .. 4 sub + 3 from Philox block `sub`.
         const P4 w4 = philox4x32_10(P4{(uint32_t)sub, (uint32_t)my_row, (uint32_t)p.layer, (uint32_t)h},
@@ -366,7 +390,7 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
         jj[3] = __umulhi(w4.w, (uint32_t)my_n);
         bool ok[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ok[q] = ((bma[jj[q] >> 5] | bmb[jj[q] >> 5]) & (1u << (jj[q] & 31))) == 0u;
+        for (int q = 0; q < 4; ++q) ok[q] = (bm[jj[q] >> 5] & (1u << (jj[q] & 31))) == 0u;
         // Earlier draws of the quad: blocks 0 .. sub-1 (all four words each).
         uint32_t e[12];
 #pragma unroll
@@ -390,8 +414,8 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (ok[q] && rank < p.r) {
-                atomicOr(&bma[jj[q] >> 5], 1u << (jj[q] & 31));
-                atomicOr(&bmb[jj[q] >> 5], 1u << (jj[q] & 31));
+                atomicOr(&bm[jj[q] >> 5], 1u << (jj[q] & 31));
+                rlist[rank] = (int32_t)jj[q];
             }
             rank += ok[q] ? 1 : 0;
         }
@@ -409,81 +433,84 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
                 if (drawing) {
                     const uint32_t j = __umulhi(uu, (uint32_t)my_n);
                     const uint32_t bit = 1u << (j & 31);
-                    if (((bma[j >> 5] | bmb[j >> 5]) & bit) == 0u) {
-                        bma[j >> 5] |= bit;
-                        bmb[j >> 5] |= bit;
+                    if ((bm[j >> 5] & bit) == 0u) {
+                        bm[j >> 5] |= bit;
+                        rlist[taken] = (int32_t)j;
                         ++taken;
                         drawing = taken < p.r;
                     }
                 }
             }
         }
-        taken = dpp_i<DPP_BCAST0>(taken);
     }
     if (sub == 0 && taken < rwant) {
         // Fill: lowest-index chunks still free (whole pool when pool <= r; draw cap reached).
         for (int w = 0; w < words && taken < rwant; ++w) {
-            uint32_t free_bits = ~(bma[w] | bmb[w]);
+            uint32_t free_bits = ~bm[w];
             while (free_bits && taken < rwant) {
                 const uint32_t j = (uint32_t)(w * 32 + __builtin_ctz(free_bits));
                 free_bits &= free_bits - 1u;
                 if ((int)j >= my_n) { free_bits = 0; break; }
-                bma[w] |= 1u << (j & 31);
-                bmb[w] |= 1u << (j & 31);
+                bm[w] |= 1u << (j & 31);
+                rlist[taken] = (int32_t)j;
                 ++taken;
             }
         }
     }
+    taken = dpp_i<DPP_BCAST0>(taken);                 // lane 0 holds the final count
     if (sub == 0) p.anchor[(size_t)h * p.nq + my_row] = p.layer;
 
-    // The three segments in ascending index order: each lane counts route (A only), near-miss
-    // (B only) and random (A and B) bits of its quarter of the words, an exclusive sum over the
-    // quad gives its output offsets.
-    // Words are read eight at a time (all loads of a chunk issued before any is used); the
-    // bitmaps' unused tail words are zero.
-    constexpr int SW = 8;
-    const int wq = (((words + 3) >> 2) + SW - 1) / SW * SW;   // words per lane, whole chunks
-    const int w0 = sub * wq;
-    int cr = 0, cn = 0, cx = 0;
-    for (int c0 = 0; c0 < wq; c0 += SW) {
-        uint32_t x[SW], y[SW];
+    // Sort keys: lanes 0 / 1 take list positions [0,16) / [16,32) as (segment << 16) | index
+    // (segment 0 route, 1 near-miss, 2 none), lanes 2 / 3 the drawn chunks [0,16) / [16,32)
+    // (absent: all ones).  Indices are below 65536.
+    const int half = sub & 1;
+    uint32_t key[16];
+    int cr = 0, cn = 0;
 #pragma unroll
-        for (int u = 0; u < SW; ++u) {
-            const int w = w0 + c0 + u;
-            x[u] = (w < words) ? bma[w] : 0u;
-            y[u] = (w < words) ? bmb[w] : 0u;
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int pos = 16 * half + i;
+        const bool used = sub < 2 && pos < ki + mi && hv[i] != EMPTY_KEY;
+        const bool route = used && pos < ki;
+        cr += route ? 1 : 0;
+        cn += (used && !route) ? 1 : 0;
+        const uint32_t sel_key = used ? ((route ? 0u : 0x10000u) | key_index(hv[i])) : 0x2FFFFu;
+        const uint32_t rnd_key = (pos < taken) ? (uint32_t)rlist[pos] : 0xFFFFFFFFu;
+        key[i] = (sub < 2) ? sel_key : rnd_key;
+    }
+    sort16_asc_u32(key);
+    {
+        // Bitonic exchange with the partner lane (lane ^ 1): the even lane keeps the lower 16 of
+        // the pair's 32 keys, the odd lane the upper 16.
+        uint32_t b[16];
 #pragma unroll
-        for (int u = 0; u < SW; ++u) {
-            cr += __popc(x[u] & ~y[u]);
-            cn += __popc(y[u] & ~x[u]);
-            cx += __popc(x[u] & y[u]);
+        for (int i = 0; i < 16; ++i) b[i] = (uint32_t)dpp_i<DPP_XOR1>((int)key[15 - i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) key[i] = half ? max(key[i], b[i]) : min(key[i], b[i]);
+#pragma unroll
+        for (int st = 8; st >= 1; st >>= 1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if ((i & st) == 0) {
+                    const uint32_t x = key[i], y = key[i + st];
+                    key[i] = min(x, y);
+                    key[i + st] = max(x, y);
+                }
         }
     }
-    int tr, tn, tx;
-    int pr = quad_excl_sum(cr, sub, &tr);
-    int pn = p.k + quad_excl_sum(cn, sub, &tn);
-    int px = p.k + p.m + quad_excl_sum(cx, sub, &tx);
-    for (int c0 = 0; c0 < wq; c0 += SW) {
-        uint32_t x[SW], y[SW];
+    int tr, tn;
+    quad_excl_sum(cr, sub, &tr);
+    quad_excl_sum(cn, sub, &tn);
+    // Every lane stores all 16 keys; those past its segments go to the row's spare slot c.
 #pragma unroll
-        for (int u = 0; u < SW; ++u) {
-            const int w = w0 + c0 + u;
-            x[u] = (w < words) ? bma[w] : 0u;
-            y[u] = (w < words) ? bmb[w] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < SW; ++u) {
-            const int wb = (w0 + c0 + u) * 32;
-            uint32_t br = x[u] & ~y[u], bn = y[u] & ~x[u], bx = x[u] & y[u];
-            while (br) { stage[pr++] = wb + __builtin_ctz(br); br &= br - 1u; }
-            while (bn) { stage[pn++] = wb + __builtin_ctz(bn); bn &= bn - 1u; }
-            while (bx) { stage[px++] = wb + __builtin_ctz(bx); bx &= bx - 1u; }
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int q = 16 * half + i;
+        const int d_sel = (q < tr) ? q : (q < tr + tn) ? p.k + (q - tr) : p.c;
+        const int d_rnd = (q < taken) ? p.k + p.m + q : p.c;
+        stage[(sub < 2) ? d_sel : d_rnd] = (int32_t)((sub < 2) ? (key[i] & 0xFFFFu) : key[i]);
     }
     for (int s2 = tr + sub; s2 < p.k; s2 += 4) stage[s2] = -1;
     for (int s2 = tn + sub; s2 < p.m; s2 += 4) stage[p.k + s2] = -1;
-    for (int s2 = tx + sub; s2 < p.r; s2 += 4) stage[p.k + p.m + s2] = -1;
+    for (int s2 = taken + sub; s2 < p.r; s2 += 4) stage[p.k + p.m + s2] = -1;
     // The quad copies the staged row out: four consecutive IDs per instruction and row.
     int32_t* dst = p.ids + ((size_t)h * p.nq + my_row) * p.c;
     for (int e2 = sub; e2 < p.c; e2 += 4) dst[e2] = stage[e2];
@@ -1123,7 +1150,7 @@ size_t route_lds_bytes(int nk, int c) {
     const size_t cand = (size_t)SPLIT * CAP * ROWS * sizeof(uint2);
     const size_t xl = (size_t)SPLIT * XWAVE * sizeof(uint64_t);
     const size_t gm = (size_t)ROWS * GSTRIDE * sizeof(float);
-    const size_t em = (size_t)ROWS * (2 * ((nk + 31) / 32 + 1) + c) * sizeof(uint32_t);
+    const size_t em = (size_t)ROWS * (((nk + 31) / 32 + 1) + RLIST + c + 1) * sizeof(uint32_t);
     size_t m = cand > xl ? cand : xl;
     m = m > gm ? m : gm;
     return m > em ? m : em;

@@ -178,10 +178,29 @@ def graph_chains(w, led, full, qs, ks, reps=10):
 def secondary_causal(steps=3, warmup=1):
     """The 64-head, 4096-chunk causal workload: relay vs full routing (reported beside the
     headline, which is the 32-head 1024-chunk workload)."""
-    import torch
     w = W.causal_large()
+    log(f"[bench] secondary: {w.name} {w.heads}x{w.n} causal, {w.layers} layers")
+    return relay_vs_full(w, steps, warmup)
+
+
+def drift_sweep_batched(sigmas=(0.01, 0.03, 0.06), steps=2, warmup=1):
+    """The batched-heads shape (32 x 1024, bf16) at fixed per-layer drift: where relay layers
+    stand against full routing as the rerouted fraction grows (the headline draws each layer's
+    drift from [0.01, 0.06))."""
+    out = []
+    for s in sigmas:
+        w = W.batched_heads().with_(name=f"batched_heads_drift{s:g}", drift=(s, s))
+        log(f"[bench] drift sweep: {w.name}")
+        r = relay_vs_full(w, steps, warmup)
+        out.append({"sigma": s, **{k: r[k] for k in ("relay_layer_us_median", "full_layer_us_median",
+                                                      "speedup_vs_full", "recall", "reroute_fraction",
+                                                      "relay_rho_mean")}})
+    return out
+
+
+def relay_vs_full(w, steps, warmup):
+    import torch
     H, n = w.heads, w.n
-    log(f"[bench] secondary: {w.name} {H}x{n} causal, {w.layers} layers")
     qs, ks = upload_layers(w)
     led = rr.Ledger(H, n, n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
     full = rr.Ledger(H, n, n, w.d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
@@ -190,7 +209,7 @@ def secondary_causal(steps=3, warmup=1):
     relay_layers = [l for l in range(w.layers) if not w.is_anchor(l)]
     t_relay = relay_ms[:, relay_layers].sum()
     t_full = full_ms.sum()
-    out = {"workload": w.name, "heads": H, "nq": n, "nk": n, "causal": True, "layers": w.layers,
+    out = {"workload": w.name, "heads": H, "nq": n, "nk": n, "causal": w.causal, "layers": w.layers,
            "relay_routes_per_s": round(H * n * len(relay_layers) * steps / (t_relay / 1e3), 1),
            "full_routing_routes_per_s": round(H * n * w.layers * steps / (t_full / 1e3), 1),
            "speedup_vs_full": round(float((t_full / (w.layers * steps)) / (t_relay / (len(relay_layers) * steps))), 4),
@@ -277,7 +296,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the 64-head 4096-chunk causal relay-vs-full measurement")
+                    help="skip the side measurements (64-head 4096-chunk causal; fixed-drift sweep)")
     ap.add_argument("--calib-copy", action="store_true",
                     help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (counter calibration)")
     args = ap.parse_args()
@@ -387,6 +406,7 @@ def main():
     del qs, ks
     torch.cuda.empty_cache()
     secondary = None if args.no_secondary else secondary_causal()
+    drift_sweep = None if args.no_secondary else drift_sweep_batched()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -425,6 +445,7 @@ def main():
         "graph": graph,
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "drift_sweep": drift_sweep,
     }
     print(json.dumps(out), flush=True)
 

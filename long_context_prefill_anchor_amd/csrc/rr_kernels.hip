@@ -265,6 +265,10 @@ struct RouteShared {
 
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a > b ? b : a; }
+// keep_max ? max(a, b) : min(a, b) with one compare (the lane's choice flips the compare's mask).
+__device__ __forceinline__ uint64_t max_or_min_u64(uint64_t a, uint64_t b, bool keep_max) {
+    return ((a > b) == keep_max) ? a : b;
+}
 
 // Sort a bitonic sequence descending (half-cleaner cascade).
 template <int N, typename T>
@@ -295,7 +299,7 @@ __device__ __forceinline__ void quad_merge_split(const uint64_t (&a)[TOPW], uint
         for (int i = 0; i < 16; ++i) {
             const uint64_t x = max_u64(a[i], b[31 - i]);
             const uint64_t y = max_u64(a[i + 16], b[15 - i]);
-            hv[i] = keep_max ? max_u64(x, y) : min_u64(x, y);
+            hv[i] = max_or_min_u64(x, y, keep_max);
         }
         bitonic_clean_desc<16>(hv);
     }
@@ -309,7 +313,7 @@ __device__ __forceinline__ void quad_merge_split(const uint64_t (&a)[TOPW], uint
         for (int s = 0; s < 16; ++s) b[s] = dpp_u64<DPP_XOR1>(d[s]);
         const bool keep_max = (sub == 0) || (sub == 3);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) hv[i] = keep_max ? max_u64(d[i], b[i]) : min_u64(d[i], b[i]);
+        for (int i = 0; i < 16; ++i) hv[i] = max_or_min_u64(d[i], b[i], keep_max);
         bitonic_clean_desc<16>(hv);
     }
 }

@@ -76,13 +76,22 @@ def run_full_chain(w, full, qs, ks, ev=None):
 
 def quality_pass(w, led, full, qs, ks):
     """Untimed: recall of the relayed routes against full routing, rerouted fraction,
-    evaluated score-pair fraction (Section 5 metrics), flagged rows per relay layer."""
+    evaluated score-pair fraction (Section 5 metrics), flagged rows per relay layer; also the
+    recall of the pages' fixed-stride baseline (every row refreshed each 4th layer, the route
+    reused unchecked in between), which needs no kernel of its own."""
     import torch
     H, n = w.heads, w.n
     n_i = (np.arange(n) + 1) if w.causal else np.full(n, n)          # allowed keys per row
     c_i = np.minimum(w.c, n_i)                                          # candidates per row
     out = led.alloc_outputs(with_scores=False)
     recall_sum, rows_rerouted, flagged, pairs, relay_pairs = 0.0, 0, {}, 0, 0
+    stride4_sum, stale = 0.0, None
+
+    def recall_of(used, exact):
+        # per row: |used & exact| / |exact|, padding (-1) excluded
+        hit = ((used[:, :, None] == exact[:, None, :]) & (exact[:, None, :] >= 0)).any(axis=1).sum(axis=1)
+        return float((hit / np.maximum((exact >= 0).sum(axis=1), 1)).mean())
+
     for l in range(w.layers):
         if w.is_anchor(l):
             led.anchor(qs[l], ks[l], l)
@@ -94,9 +103,10 @@ def quality_pass(w, led, full, qs, ks):
         torch.cuda.synchronize()
         used = led.get()[0].cpu().numpy().reshape(-1, w.k)
         exact = full.get()[0].cpu().numpy().reshape(-1, w.k)
-        # recall per row: |used & exact| / |exact|, padding (-1) excluded
-        hit = ((used[:, :, None] == exact[:, None, :]) & (exact[:, None, :] >= 0)).any(axis=1).sum(axis=1)
-        recall_sum += float((hit / np.maximum((exact >= 0).sum(axis=1), 1)).mean())
+        recall_sum += recall_of(used, exact)
+        if l % 4 == 0:
+            stale = exact
+        stride4_sum += recall_of(stale, exact)
         if not w.is_anchor(l):
             nf = int(out.n_rows.cpu().numpy()[0])
             rows = out.rows.cpu().numpy()[:nf] % n
@@ -109,7 +119,8 @@ def quality_pass(w, led, full, qs, ks):
     relay_rho = [flagged[l] / (H * n) for l in sorted(flagged)]
     return dict(recall=recall_sum / L, reroute_fraction=rows_rerouted / (H * n * L),
                 relay_rho_mean=float(np.mean(relay_rho)), relay_rho_per_layer=[round(x, 4) for x in relay_rho],
-                pair_fraction=pairs / (H * int(n_i.sum()) * L), flagged=flagged, relay_pairs=relay_pairs)
+                pair_fraction=pairs / (H * int(n_i.sum()) * L), flagged=flagged, relay_pairs=relay_pairs,
+                stride4_recall=stride4_sum / L)
 
 
 def time_chains(w, led, full, qs, ks, steps, warmup):
@@ -194,7 +205,35 @@ def drift_sweep_batched(sigmas=(0.01, 0.03, 0.06), steps=2, warmup=1):
         r = relay_vs_full(w, steps, warmup)
         out.append({"sigma": s, **{k: r[k] for k in ("relay_layer_us_median", "full_layer_us_median",
                                                       "speedup_vs_full", "recall", "reroute_fraction",
-                                                      "relay_rho_mean")}})
+                                                      "relay_rho_mean", "fixed_stride4_recall")}})
+    return out
+
+
+def sentinel_ablation(seeds=5):
+    """Sentinel mixes on the pages' ablation setting (1 x 256 chunks, fp32, 24 layers, drift
+    0.003, k = 12; anchors every 8 layers, as in the other chains): mean recall against full
+    routing, rerouted fraction and score-pair fraction over the seeds.  Widths beyond
+    k + m = 32 (24 or 48 near-miss) are outside this library's limits and are not run."""
+    import torch
+    mixes = [("random only", 0, 12), ("near-miss only", 12, 0), ("12 near-miss + 12 random", 12, 12),
+             ("12 near-miss + 8 random", 12, 8)]
+    out = []
+    for name, m, r in mixes:
+        acc = np.zeros(3)
+        for seed in range(seeds):
+            w = W.drift_sweep(0.003, seed).with_(name=f"ablation_{m}nm_{r}rnd_seed{seed}", layers=24,
+                                                 anchors=W.stride_anchors(24, 8), m=m, r=r)
+            qs, ks = upload_layers(w)
+            led = rr.Ledger(w.heads, w.n, w.n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
+            full = rr.Ledger(w.heads, w.n, w.n, w.d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
+            q = quality_pass(w, led, full, qs, ks)
+            acc += [q["recall"], q["reroute_fraction"], q["pair_fraction"]]
+            led.close()
+            full.close()
+        acc /= seeds
+        out.append({"sentinels": name, "m": m, "r": r, "recall": round(float(acc[0]), 6),
+                    "reroute_fraction": round(float(acc[1]), 4), "pair_fraction": round(float(acc[2]), 4)})
+    torch.cuda.empty_cache()
     return out
 
 
@@ -217,6 +256,7 @@ def relay_vs_full(w, steps, warmup):
            "full_layer_us_median": round(float(np.median(full_ms) * 1e3), 2),
            "recall": round(q["recall"], 6), "reroute_fraction": round(q["reroute_fraction"], 4),
            "relay_rho_mean": round(q["relay_rho_mean"], 4), "pair_fraction": round(q["pair_fraction"], 4),
+           "fixed_stride4_recall": round(q["stride4_recall"], 6),
            "steps": steps}
     led.close()
     full.close()
@@ -296,7 +336,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the side measurements (64-head 4096-chunk causal; fixed-drift sweep)")
+                    help="skip the side measurements (64-head 4096-chunk causal; fixed-drift sweep; sentinel ablation)")
     ap.add_argument("--calib-copy", action="store_true",
                     help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (counter calibration)")
     args = ap.parse_args()
@@ -407,6 +447,7 @@ def main():
     torch.cuda.empty_cache()
     secondary = None if args.no_secondary else secondary_causal()
     drift_sweep = None if args.no_secondary else drift_sweep_batched()
+    ablation = None if args.no_secondary else sentinel_ablation()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -435,6 +476,7 @@ def main():
         "reroute_fraction": round(q["reroute_fraction"], 4),
         "relay_rho_mean": round(q["relay_rho_mean"], 4),
         "pair_fraction": round(q["pair_fraction"], 4),
+        "fixed_stride4_recall": round(q["stride4_recall"], 6),
         "relay_score_pairs_per_s": round(pairs_per_s, 1),
         "full_routing_routes_per_s": round(full_value, 1),
         "relay_layer_us_median": round(relay_layer_us, 2),
@@ -446,6 +488,7 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
         "drift_sweep": drift_sweep,
+        "sentinel_ablation": ablation,
     }
     print(json.dumps(out), flush=True)
 

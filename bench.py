@@ -74,6 +74,24 @@ def run_full_chain(w, full, qs, ks, ev=None):
             ev[l][1].record()
 
 
+def route_recall(used, exact):
+    """Mean over rows of |used & exact| / |exact| for [rows, k] int arrays; -1 padding in
+    `exact` is not counted (a row with no exact entries counts as 0)."""
+    hit = ((used[:, :, None] == exact[:, None, :]) & (exact[:, None, :] >= 0)).any(axis=1).sum(axis=1)
+    return float((hit / np.maximum((exact >= 0).sum(axis=1), 1)).mean())
+
+
+def stride_reuse_routes(exact_per_layer, stride=4):
+    """The fixed-stride baseline: every row refreshed at layers divisible by `stride`, the
+    route reused unchecked in between."""
+    out, stale = [], None
+    for l, exact in enumerate(exact_per_layer):
+        if l % stride == 0:
+            stale = exact
+        out.append(stale)
+    return out
+
+
 def quality_pass(w, led, full, qs, ks):
     """Untimed: recall of the relayed routes against full routing, rerouted fraction,
     evaluated score-pair fraction (Section 5 metrics), flagged rows per relay layer; also the
@@ -86,12 +104,6 @@ def quality_pass(w, led, full, qs, ks):
     out = led.alloc_outputs(with_scores=False)
     recall_sum, rows_rerouted, flagged, pairs, relay_pairs = 0.0, 0, {}, 0, 0
     stride4_sum, stale = 0.0, None
-
-    def recall_of(used, exact):
-        # per row: |used & exact| / |exact|, padding (-1) excluded
-        hit = ((used[:, :, None] == exact[:, None, :]) & (exact[:, None, :] >= 0)).any(axis=1).sum(axis=1)
-        return float((hit / np.maximum((exact >= 0).sum(axis=1), 1)).mean())
-
     for l in range(w.layers):
         if w.is_anchor(l):
             led.anchor(qs[l], ks[l], l)
@@ -103,10 +115,10 @@ def quality_pass(w, led, full, qs, ks):
         torch.cuda.synchronize()
         used = led.get()[0].cpu().numpy().reshape(-1, w.k)
         exact = full.get()[0].cpu().numpy().reshape(-1, w.k)
-        recall_sum += recall_of(used, exact)
+        recall_sum += route_recall(used, exact)
         if l % 4 == 0:
-            stale = exact
-        stride4_sum += recall_of(stale, exact)
+            stale = exact                                    # same rule as stride_reuse_routes
+        stride4_sum += route_recall(stale, exact)
         if not w.is_anchor(l):
             nf = int(out.n_rows.cpu().numpy()[0])
             rows = out.rows.cpu().numpy()[:nf] % n

@@ -93,6 +93,8 @@ RELAY_CASES = [
     ("relay_gather_bf16", 2, 96, 1500, 12, 12, 8, "bf16", False, 0.05, "gauss"),
     ("relay_gather_f32", 1, 100, 600, 12, 12, 8, "f32", False, 0.05, "gauss"),
     ("relay_gather_wide", 1, 80, 1300, 16, 16, 32, "bf16", False, 0.05, "gauss"),
+    # more than 64 rescore blocks per head (nq > 4096): the reroute finds its rows by scanning flags
+    ("relay_many_rows", 1, 4160, 96, 12, 12, 8, "bf16", False, 0.05, "gauss"),
 ]
 
 

@@ -30,6 +30,9 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # The route kernel runs two waves per SIMD (register-bound) and is latency-bound there;
+           # the ILP-first scheduler spreads independent work between dependent instructions.
+           "-mllvm", "-amdgpu-sched-strategy=max-ilp",
            "-Wno-unused-command-line-argument",
            f"-I{INCLUDE}", f"-I{CSRC}"]
     cmd += ["-x", "hip"] + [os.path.join(CSRC, s) for s in SOURCES]

@@ -33,6 +33,8 @@ def build(verbose: bool = False) -> str:
            # The route kernel runs two waves per SIMD (register-bound) and is latency-bound there;
            # the ILP-first scheduler spreads independent work between dependent instructions.
            "-mllvm", "-amdgpu-sched-strategy=max-ilp",
+           # s_setprio around VALU-heavy stretches: the wave that holds the SIMD keeps issuing.
+           "-mllvm", "-amdgpu-set-wave-priority",
            "-Wno-unused-command-line-argument",
            f"-I{INCLUDE}", f"-I{CSRC}"]
     cmd += ["-x", "hip"] + [os.path.join(CSRC, s) for s in SOURCES]

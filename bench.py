@@ -34,6 +34,7 @@ from long_context_prefill_anchor_amd import rr, synth, workloads as W  # noqa: E
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 KERNEL_SRC = os.path.join(ROOT, "long_context_prefill_anchor_amd", "csrc", "rr_kernels.hip")
+BUILD_SCRIPT = os.path.join(ROOT, "long_context_prefill_anchor_amd", "build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_route_reroute_batched_heads.txt")
 CALIB_BYTES = 256 << 20         # plain copy used to calibrate the HBM byte counters
 
@@ -311,17 +312,24 @@ def cpu_baseline(w, max_seconds=20.0):
             "relay_over_full_time": (t_relay / n_relay) / (t_anchor / n_anchor) if n_anchor else None}
 
 
+def kernel_build_hash():
+    """sha256 of the kernel source followed by the build script (its compiler flags)."""
+    h = hashlib.sha256()
+    for path in (KERNEL_SRC, BUILD_SCRIPT):
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
 def recorded_traffic(kernel):
     """HBM bytes per launch of `kernel` (reroute / rescore / route) from the committed counter
-    summary, if it was taken on the kernel source as it is now (else None)."""
+    summary, if it was taken on the kernel source and build script as they are now (else None)."""
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
         return None
     fields = dict(line.split(":", 1) for line in text.splitlines() if ":" in line and not line.startswith("#"))
     fields = {k.strip(): v.strip() for k, v in fields.items()}
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if fields.get("kernel_source_sha256") != src_hash:
+    if fields.get("kernel_build_sha256") != kernel_build_hash():
         return None
     try:
         return float(fields[f"{kernel}_hbm_bytes_per_launch"])

@@ -7,11 +7,13 @@
 //              top-(k+m) selection (Eq. 2 + near-miss sentinels, Section 3.1), random
 //              sentinels, ledger write.  Anchor mode routes rows 64g..64g+63; reroute mode
 //              routes the g-th slice of 64 flagged rows of the head (the compacted list of
-//              Sections 4.1/4.2), recovered from the rescore kernel's flags.
+//              Sections 4.1/4.2), found from the rescore kernel's per-block lists of
+//              flagged rows.
 // k_rescore  — relay candidate rescoring (Eq. 5-8): per row, gather the ledger's candidate key
 //              rows, dot them with the query row, alpha / beta / refresh flag, plus a lower
 //              bound on the row's (k+m)-th best score that the reroute uses as its first
-//              selection threshold.  Writes per-block flag counts for the compaction.
+//              selection threshold.  Lists each 64-row block's flagged rows for the
+//              compaction.
 //
 // k_route layout.  A block is SPLIT = 4 waves; all four own the same 64 rows (one row per
 // lane) and wave w scores the key tiles t = w, w+4, ... (32 keys per tile).  One tile is two
@@ -24,7 +26,7 @@
 // per-wave, per-row LDS buffer; when a buffer holds 16 or more entries the lane sorts them
 // (odd-even merge network) and merges them into its list, and publishes the list's (k+m)-th key
 // as the row's threshold (LDS atomic max shared by the four waves).  At the end the four lists
-// are merged pairwise through LDS.  A key below the threshold cannot be among the best k+m, so
+// are exchanged through LDS and merged by the row's quad of lanes (DPP bitonic exchanges).  A key below the threshold cannot be among the best k+m, so
 // the result is exact.  The first threshold is a proven lower bound on the (k+m)-th best score:
 // anchor mode — the (k+m)-th largest of 32 maxima of disjoint 8-key groups taken from a first
 // MFMA pass (each wave contributes its 8 largest group maxima); reroute mode — the smallest

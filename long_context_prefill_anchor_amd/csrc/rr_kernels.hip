@@ -47,6 +47,7 @@ constexpr int SPLIT = 4;           // waves per block, each scoring a quarter of
 constexpr int TK = 32;             // keys per tile
 constexpr int TOPW = 32;           // register top list width (k + m <= TOPW)
 constexpr int CAP = 31;            // per-wave per-row buffer: <= 15 held + 16 slots appended
+constexpr int BUF_IDX = CAP * ROWS; // words from a buffered score to its key index
 // The per-wave buffers are slot-major ([CAP][ROWS] per wave): a lane's consecutive entries are
 // ROWS apart, so whatever count each lane is at, the 32 lanes of a half-wave write 64-bit entries
 // to 32 distinct bank pairs.
@@ -207,15 +208,16 @@ __device__ __forceinline__ void merge16_into_top(uint64_t (&top)[TOPW], const ui
 
 // Sort the lane's buffered (score bits, index) pairs and merge them into its top list.
 // `fresh`: every lane's list is still empty, so the first sorted chunk is copied in.
-__device__ __forceinline__ void drain(uint64_t (&top)[TOPW], const uint2* buf, int cnt, bool& fresh) {   // buf: slot-major
+// buf: slot-major, scores at buf[j * ROWS], their key indices BUF_IDX words further on.
+__device__ __forceinline__ void drain(uint64_t (&top)[TOPW], const uint32_t* buf, int cnt, bool& fresh) {
     const int maxc = wave_max_i(cnt);
     for (int c0 = 0; c0 < maxc; c0 += 16) {
         uint64_t x[16];
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
             if (c0 + s < cnt) {
-                const uint2 e = buf[(c0 + s) * ROWS];
-                x[s] = make_key(__uint_as_float(e.x), e.y);
+                const uint32_t* e = buf + (c0 + s) * ROWS;
+                x[s] = make_key(__uint_as_float(e[0]), e[BUF_IDX]);
             } else {
                 x[s] = EMPTY_KEY;
             }
@@ -533,7 +535,7 @@ struct RowCtx {
     int lane, wave, h, my_row, my_n, nmin, ntiles;
     const E* Qh;
     const E* Kh;
-    uint2* my_buf;
+    uint32_t* my_buf;
     int qslot, qsub, q_row, q_n;
     bool q_redo;
 };
@@ -541,20 +543,25 @@ struct RowCtx {
 // Streaming selection pass from the rows' shared thresholds (sh.thr), final merge and ledger
 // write.  attempt 0 emits every row that holds min(k+m, n) keys; in reroute mode the others are
 // marked for a redo from -inf (attempt 1, which emits only them).
-// kbuf: the K register ring (shared with the anchor's first pass).
+// kbuf: the K register ring (shared with the anchor's first pass).  `primed`: the query rows
+// and the ring's first tiles are already loaded (the reroute's first attempt issues them beside
+// its threshold load).
 template <typename DT, bool CAUSAL, bool REROUTE>
 __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared& sh, unsigned char* dyn_lds,
                                                 Tile<DT>& tile, typename Tile<DT>::KReg (&kbuf)[Tile<DT>::NBUF],
-                                                RowCtx<DT>& cx, int attempt) {
+                                                bool primed, RowCtx<DT>& cx, int attempt) {
     const int lane = cx.lane, wave = cx.wave, h = cx.h, my_row = cx.my_row, my_n = cx.my_n;
     // Block-uniform by construction; readfirstlane makes the loops scalar.
     const int nmin = __builtin_amdgcn_readfirstlane(cx.nmin), ntiles = __builtin_amdgcn_readfirstlane(cx.ntiles);
     const auto* Qh = cx.Qh;
     const auto* Kh = cx.Kh;
-    uint2* my_buf = cx.my_buf;
+    uint32_t* my_buf = cx.my_buf;
     const int qslot = cx.qslot, qsub = cx.qsub, q_row = cx.q_row, q_n = cx.q_n;
-    if constexpr (REROUTE) tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
-    else (void)Qh;
+    if constexpr (REROUTE) {
+        if (!primed) tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
+    } else {
+        (void)Qh;
+    }
     uint64_t top[TOPW];
 #pragma unroll
     for (int s = 0; s < TOPW; ++s) top[s] = EMPTY_KEY;
@@ -563,7 +570,7 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
         bool fresh = true;                                              // list empty in every lane
         float ts = key_score(sh.thr[lane]);
         constexpr int NB = Tile<DT>::NBUF;
-        fill_ring<DT>(tile, kbuf, Kh, wave, p.nk, lane);
+        if (!primed) fill_ring<DT>(tile, kbuf, Kh, wave, p.nk, lane);
         for (int t0 = wave; t0 < ntiles; t0 += NB * SPLIT) {
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
@@ -586,6 +593,10 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
                         hi[v] = (hi_key(v) < lim) ? hi[v] : nan;
                     }
                 }
+                // The key index in a vector register: each slot's index is then one add, and
+                // score and index go out as one two-address store.
+                uint32_t vkey0 = (uint32_t)key0;
+                asm volatile("" : "+v"(vkey0));
                 // Branch-free append: every slot stores its (score, index) at the row's current
                 // count and the count advances only when the score passes, so a failing slot's
                 // store is overwritten by the next one (<= 15 held + 16 slots: index <= 30).
@@ -593,9 +604,11 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
                 for (int half = 0; half < 2; ++half) {
 #pragma unroll
                     for (int v = 8 * half; v < 8 * half + 8; ++v) {
-                        my_buf[cnt * ROWS] = make_uint2(__float_as_uint(lo[v]), (uint32_t)(key0 + lo_key(v)));
+                        my_buf[cnt * ROWS] = __float_as_uint(lo[v]);
+                        my_buf[cnt * ROWS + BUF_IDX] = vkey0 + lo_key(v);
                         cnt += (lo[v] >= ts) ? 1 : 0;
-                        my_buf[cnt * ROWS] = make_uint2(__float_as_uint(hi[v]), (uint32_t)(key0 + hi_key(v)));
+                        my_buf[cnt * ROWS] = __float_as_uint(hi[v]);
+                        my_buf[cnt * ROWS + BUF_IDX] = vkey0 + hi_key(v);
                         cnt += (hi[v] >= ts) ? 1 : 0;
                     }
                     if (__ballot(cnt >= 16)) {
@@ -660,7 +673,7 @@ __device__ __forceinline__ void redo_rows(const RouteArgs& p, RouteShared& sh, u
     asm volatile("" : "+v"(cx.q_row), "+v"(cx.q_n), "+v"(cx.qslot), "+v"(cx.qsub));
     Tile<DT> tile;
     typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
-    select_and_emit<DT, CAUSAL, true>(p, sh, dyn_lds, tile, kbuf, cx, 1);
+    select_and_emit<DT, CAUSAL, true>(p, sh, dyn_lds, tile, kbuf, false, cx, 1);
 }
 
 template <typename DT, bool CAUSAL, bool REROUTE>
@@ -790,7 +803,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
     if constexpr (!REROUTE) tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
 
-    uint2* my_buf = reinterpret_cast<uint2*>(dyn_lds) + (size_t)wave * CAP * ROWS + lane;
+    uint32_t* my_buf = reinterpret_cast<uint32_t*>(dyn_lds) + (size_t)wave * 2 * CAP * ROWS + lane;
     // Final merge and ledger write run one row per quad of lanes over all four waves.
     const int qslot = 16 * wave + (lane >> 2);
     const int qsub = lane & 3;
@@ -800,7 +813,12 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     // ------------------------------------------------------------------ first threshold
     uint64_t base_thr;
     if constexpr (REROUTE) {
-        const float hv = (my_row >= 0) ? p.hint[(size_t)h * p.nq + my_row] : -INFINITY;
+        // The threshold load first, then the query rows and the first key tiles: the three
+        // round trips overlap, and waiting for the threshold does not wait for the others.
+        const float hraw = p.hint[(size_t)h * p.nq + max(my_row, 0)];
+        tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
+        fill_ring<DT>(tile, kbuf, Kh, wave, p.nk, lane);
+        const float hv = (my_row >= 0) ? hraw : -INFINITY;
         const float t = (hv == -INFINITY) ? -INFINITY : hv - (fabsf(hv) * 1e-4f + 1e-6f);
         base_thr = make_key(t, 0xFFFFFFFFu);
     } else {
@@ -866,7 +884,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
 
     // ------------------------------------------------------------------ streaming pass
     RowCtx<DT> cx{lane, wave, h, my_row, my_n, nmin, ntiles, Qh, Kh, my_buf, qslot, qsub, q_row, q_n, false};
-    select_and_emit<DT, CAUSAL, REROUTE>(p, sh, dyn_lds, tile, kbuf, cx, 0);
+    select_and_emit<DT, CAUSAL, REROUTE>(p, sh, dyn_lds, tile, kbuf, REROUTE, cx, 0);
     if constexpr (REROUTE) {
         if (sh.redo) redo_rows<DT, CAUSAL>(p, sh, dyn_lds, cx);         // uniform; rare
     }

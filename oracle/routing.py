@@ -37,10 +37,16 @@ class RouteConfig:
     causal: bool = False
     seed: int = 0
     dtype: str = "f32"          # "f32" or "bf16": encoding of the Q/K arrays handed in
+    sink: int = 0               # mandatory sink sentinels: chunks 0 .. sink-1
+    recent: int = 0             # mandatory recent sentinels: the row's last `recent` allowed chunks
+
+    @property
+    def mand(self) -> int:
+        return self.sink + self.recent
 
     @property
     def c(self) -> int:
-        return self.k + self.m + self.r
+        return self.k + self.m + self.mand + self.r
 
 
 # ----------------------------------------------------------------------------- inputs
@@ -88,6 +94,23 @@ def select(s_row: np.ndarray, n: int, k: int, m: int):
     return order[:ki], order[ki:ki + mi]
 
 
+# ----------------------------------------------------------------------------- mandatory sentinels
+
+def mandatory_sentinels(n: int, sink: int, recent: int, covered: Sequence[int]) -> np.ndarray:
+    """Mandatory global candidates (Section 3.1, item 3), ascending.
+
+    Reading: the sink chunks are the first ``sink`` chunks 0 .. sink-1 and the recent
+    chunks the row's last ``recent`` allowed chunks n-recent .. n-1 (the query chunk and
+    the ones just before it under the causal mask); both are cut to the allowed range.
+    A chunk that is already in the route or the near-miss set is not repeated here: as a
+    sentinel it would sit on both sides of Eq. 8 (beta >= its score >= alpha for a route
+    chunk), so the row could never be reused.
+    """
+    wanted = set(range(min(sink, n))) | set(range(max(0, n - recent), n))
+    wanted -= set(int(j) for j in covered)
+    return np.asarray(sorted(wanted), dtype=np.int64)
+
+
 # ----------------------------------------------------------------------------- random sentinels
 
 def random_sentinels(seed: int, h: int, layer: int, i: int, n: int,
@@ -95,7 +118,8 @@ def random_sentinels(seed: int, h: int, layer: int, i: int, n: int,
     """r chunks drawn uniformly without replacement from the omitted chunks
     (Section 3.1, item 2; the residual pool of Section 3.4, Eq. 10).
 
-    Reading: "omitted" = allowed chunks outside route and near-miss set.  The page
+    Reading: "omitted" = allowed chunks outside route, near-miss set and mandatory
+    sentinels (``excluded`` holds all three).  The page
     names no sampler; this one is deterministic so results can be compared:
       * pool size N <= r: take the whole pool;
       * else for t = 0, 1, 2, ...: u_t = word (t mod 4) of
@@ -140,17 +164,18 @@ def _pad(ids: np.ndarray, width: int) -> np.ndarray:
 @dataclass
 class Ledger:
     """Route ledger (Section 3.1, Eq. 4; Section 4.1): per query row the route [k],
-    the sentinels [m + r] and the layer a of its last full routing.  Every segment
-    is ascending with -1 padding; sentinels hold the near-miss segment (width m)
-    then the random segment (width r)."""
+    the sentinels [m + sink + recent + r] and the layer a of its last full routing.
+    Every segment is ascending with -1 padding; sentinels hold the near-miss segment
+    (width m), the mandatory segment (width sink + recent), then the random segment
+    (width r)."""
     route: np.ndarray    # int32 [H, nq, k]
-    sent: np.ndarray     # int32 [H, nq, m + r]
+    sent: np.ndarray     # int32 [H, nq, c - k]
     anchor: np.ndarray   # int32 [H, nq]
 
     @staticmethod
     def empty(cfg: RouteConfig) -> "Ledger":
         return Ledger(np.full((cfg.heads, cfg.nq, cfg.k), -1, np.int32),
-                      np.full((cfg.heads, cfg.nq, cfg.m + cfg.r), -1, np.int32),
+                      np.full((cfg.heads, cfg.nq, cfg.c - cfg.k), -1, np.int32),
                       np.full((cfg.heads, cfg.nq), -1, np.int32))
 
     def copy(self) -> "Ledger":
@@ -164,15 +189,17 @@ class Ledger:
 
 def rebuild_row(cfg: RouteConfig, ledger: Ledger, h: int, layer: int, i: int,
                 s_row: np.ndarray) -> None:
-    """Full routing of one row at ``layer``: new route, near-miss and random
-    sentinels, anchor layer set to ``layer`` (Section 3.2: a failing row computes
-    all n_k scores, replaces its route and rebuilds its sentinels)."""
+    """Full routing of one row at ``layer``: new route, near-miss, mandatory and
+    random sentinels, anchor layer set to ``layer`` (Section 3.2: a failing row
+    computes all n_k scores, replaces its route and rebuilds its sentinels)."""
     n = n_allowed(i, cfg)
     route, near = select(s_row, n, cfg.k, cfg.m)
-    rnd = random_sentinels(cfg.seed, h, layer, i, n, np.concatenate([route, near]), cfg.r)
+    mand = mandatory_sentinels(n, cfg.sink, cfg.recent, np.concatenate([route, near]))
+    rnd = random_sentinels(cfg.seed, h, layer, i, n, np.concatenate([route, near, mand]), cfg.r)
     ledger.route[h, i] = _pad(route, cfg.k)
     ledger.sent[h, i, : cfg.m] = _pad(near, cfg.m)
-    ledger.sent[h, i, cfg.m:] = _pad(rnd, cfg.r)
+    ledger.sent[h, i, cfg.m: cfg.m + cfg.mand] = _pad(mand, cfg.mand)
+    ledger.sent[h, i, cfg.m + cfg.mand:] = _pad(rnd, cfg.r)
     ledger.anchor[h, i] = layer
 
 

@@ -6,6 +6,8 @@
  *
  *   anchor layer  (Section 4.1; Eq. 1, Eq. 2; Section 3.1 items 1-2):
  *       S = Q K^T for every query row, route R = top-k, near-miss sentinels = the next m,
+ *       mandatory sink / recent sentinels (Section 3.1 item 3: chunks 0 .. sink-1 and the
+ *       row's last `recent` allowed chunks, those not already in R or the near-miss set),
  *       r random sentinels drawn from the remaining allowed chunks; ledger (Eq. 4) written.
  *   relay layer   (Sections 3.2, 4.1, 4.2; Eq. 5-8):
  *       rescore each row's ledger candidates, alpha = min over R, beta = max over sentinels,
@@ -22,11 +24,12 @@
  *   - Random sentinels: for t = 0, 1, ...: u_t = word (t mod 4) of
  *     Philox4x32-10(counter = (t div 4, i, layer, h), key = (seed lo32, seed hi32))
  *     (Salmon et al., SC'11), j_t = (u_t * n_i) >> 32, accepted if j_t is allowed, not in the
- *     route or near-miss set and not accepted before; stop at r accepted.  If at most r chunks
+ *     route, near-miss or mandatory set and not accepted before; stop at r accepted.  If at most r chunks
  *     remain they are all taken; after 65536 draws the lowest-index remaining chunks fill up.
- *   - Ledger layout returned by rr_ledger_get: route [heads, nq, k]; sentinels [heads, nq, m+r]
- *     = near-miss segment (m) then random segment (r); anchor layer [heads, nq].  Each segment
- *     ascending, padded with -1.
+ *   - Ledger layout returned by rr_ledger_get: route [heads, nq, k]; sentinels
+ *     [heads, nq, m + sink + recent + r] = near-miss segment (m), mandatory segment
+ *     (sink + recent), random segment (r); anchor layer [heads, nq].  Each segment ascending,
+ *     padded with -1.
  *   - Device pointers are plain HIP device addresses; `stream` is a hipStream_t (NULL = the
  *     null stream).  Compute calls are asynchronous on `stream`; the caller keeps every buffer
  *     alive until that stream's work is done.  Calls on one ledger must be serialised by the
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-#define RR_ABI_VERSION 1
+#define RR_ABI_VERSION 2
 
 typedef enum {
     RR_OK = 0,
@@ -71,10 +74,13 @@ typedef struct {
     int32_t causal;   /* 0 or 1                                                        */
     int32_t dtype;    /* rr_dtype of Q and K                                           */
     uint64_t seed;    /* random-sentinel key                                           */
+    int32_t sink;     /* mandatory sink sentinels (chunks 0 .. sink-1), >= 0           */
+    int32_t recent;   /* mandatory recent sentinels (last `recent` allowed chunks), >= 0 */
 } rr_config;
-/* Limits (RR_EUNSUPPORTED beyond them): d == 64, k + m <= 32, r <= 32, nk <= 4096,
- * nq <= 65536; heads * nq < 2^31 (RR_EINVAL).  A row with fewer allowed chunks than
- * k + m + r gets shorter segments, padded with -1. */
+/* c = k + m + sink + recent + r ledger IDs per row.  Limits (RR_EUNSUPPORTED beyond them):
+ * d == 64, k + m <= 32, r <= 32, sink + recent <= 32, c <= 64, nk <= 4096, nq <= 65536;
+ * heads * nq < 2^31 (RR_EINVAL).  A row with fewer allowed chunks than c gets shorter
+ * segments, padded with -1. */
 
 typedef struct rr_ledger rr_ledger;   /* opaque; owns the ledger and all scratch device memory */
 
@@ -86,8 +92,8 @@ typedef struct {
     int32_t* n_rows;       /* [1]         total flagged rows (rho_l * heads * nq)                */
     float* alpha;          /* [heads*nq]  Eq. 6 at this layer                                    */
     float* beta;           /* [heads*nq]  Eq. 7 at this layer (-inf if the row has no sentinels)  */
-    float* cand_scores;    /* [heads*nq*(k+m+r)] score of each ledger ID entering the layer, in  *
-                            * ledger order (route, near-miss, random); NaN where the ID is -1    */
+    float* cand_scores;    /* [heads*nq*c] score of each ledger ID entering the layer, in ledger *
+                            * order (route, near-miss, mandatory, random); NaN where the ID is -1 */
 } rr_relay_out;
 
 /* Check a configuration without touching the GPU. */

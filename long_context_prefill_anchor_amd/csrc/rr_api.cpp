@@ -72,6 +72,13 @@ rr_status check_cfg(const rr_config* c) {
     if (c->d != 64) return fail(RR_EUNSUPPORTED, "only d = 64 is implemented (got %d)", c->d);
     if (c->k + c->m > 32) return fail(RR_EUNSUPPORTED, "k + m must be <= 32 (got %d)", c->k + c->m);
     if (c->r > 32) return fail(RR_EUNSUPPORTED, "r must be <= 32 (got %d)", c->r);
+    if (c->sink < 0 || c->recent < 0)
+        return fail(RR_EINVAL, "need sink >= 0, recent >= 0 (got %d, %d)", c->sink, c->recent);
+    if (c->sink + c->recent > 32)
+        return fail(RR_EUNSUPPORTED, "sink + recent must be <= 32 (got %d)", c->sink + c->recent);
+    if (c->k + c->m + c->sink + c->recent + c->r > 64)
+        return fail(RR_EUNSUPPORTED, "k + m + sink + recent + r must be <= 64 (got %d)",
+                    c->k + c->m + c->sink + c->recent + c->r);
     if (c->nk > 4096) return fail(RR_EUNSUPPORTED, "nk must be <= 4096 (got %d)", c->nk);
     if (c->nq > 65536) return fail(RR_EUNSUPPORTED, "nq must be <= 65536 (got %d)", c->nq);
     return RR_OK;
@@ -151,6 +158,8 @@ rr::RouteArgs route_args(const rr_ledger* L, const void* q, const void* k, int l
     a.k = L->cfg.k;
     a.m = L->cfg.m;
     a.r = L->cfg.r;
+    a.sink = L->cfg.sink;
+    a.recent = L->cfg.recent;
     a.c = L->c;
     a.sel = L->sel;
     a.layer = layer;
@@ -180,7 +189,7 @@ rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
     rr_ledger* L = new (std::nothrow) rr_ledger;
     if (!L) return fail(RR_ENOMEM, "host allocation failed");
     L->cfg = *cfg;
-    L->c = cfg->k + cfg->m + cfg->r;
+    L->c = cfg->k + cfg->m + cfg->sink + cfg->recent + cfg->r;
     L->sel = cfg->k + cfg->m;
     L->G = (cfg->nq + rr::ROUTE_ROWS - 1) / rr::ROUTE_ROWS;
     hipError_t e = hipGetDevice(&L->device);
@@ -346,9 +355,9 @@ rr_status rr_ledger_get(const rr_ledger* L, int32_t* route, int32_t* sent, int32
     hipError_t e = hipSuccess;
     if (route)
         e = hipMemcpy2DAsync(route, L->cfg.k * sizeof(int32_t), L->ids, pitch, L->cfg.k * sizeof(int32_t), rows, kind, st);
-    if (e == hipSuccess && sent && L->cfg.m + L->cfg.r > 0)
-        e = hipMemcpy2DAsync(sent, (L->cfg.m + L->cfg.r) * sizeof(int32_t), L->ids + L->cfg.k, pitch,
-                             (L->cfg.m + L->cfg.r) * sizeof(int32_t), rows, kind, st);
+    if (e == hipSuccess && sent && (L->c - L->cfg.k) > 0)
+        e = hipMemcpy2DAsync(sent, (L->c - L->cfg.k) * sizeof(int32_t), L->ids + L->cfg.k, pitch,
+                             (L->c - L->cfg.k) * sizeof(int32_t), rows, kind, st);
     if (e == hipSuccess && anchor_layer)
         e = hipMemcpyAsync(anchor_layer, L->anchor, rows * sizeof(int32_t), kind, st);
     if (e == hipSuccess && dst_is_host) e = hipStreamSynchronize(st);
@@ -359,7 +368,7 @@ rr_status rr_ledger_get(const rr_ledger* L, int32_t* route, int32_t* sent, int32
 rr_status rr_ledger_set(rr_ledger* L, const int32_t* route, const int32_t* sent, const int32_t* anchor_layer,
                         int32_t last_layer, int32_t src_is_host, void* stream) {
     if (!L) return fail(RR_EINVAL, "ledger is NULL");
-    if (!route || !anchor_layer || (!sent && L->cfg.m + L->cfg.r > 0))
+    if (!route || !anchor_layer || (!sent && (L->c - L->cfg.k) > 0))
         return fail(RR_EINVAL, "route, sent and anchor_layer are required");
     if (last_layer < 0) return fail(RR_EINVAL, "last_layer must be >= 0 (got %d)", last_layer);
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -368,9 +377,9 @@ rr_status rr_ledger_set(rr_ledger* L, const int32_t* route, const int32_t* sent,
     const size_t pitch = (size_t)L->c * sizeof(int32_t);
     hipError_t e = hipMemcpy2DAsync(L->ids, pitch, route, L->cfg.k * sizeof(int32_t), L->cfg.k * sizeof(int32_t),
                                     rows, kind, st);
-    if (e == hipSuccess && L->cfg.m + L->cfg.r > 0)
-        e = hipMemcpy2DAsync(L->ids + L->cfg.k, pitch, sent, (L->cfg.m + L->cfg.r) * sizeof(int32_t),
-                             (L->cfg.m + L->cfg.r) * sizeof(int32_t), rows, kind, st);
+    if (e == hipSuccess && (L->c - L->cfg.k) > 0)
+        e = hipMemcpy2DAsync(L->ids + L->cfg.k, pitch, sent, (L->c - L->cfg.k) * sizeof(int32_t),
+                             (L->c - L->cfg.k) * sizeof(int32_t), rows, kind, st);
     if (e == hipSuccess) e = hipMemcpyAsync(L->anchor, anchor_layer, rows * sizeof(int32_t), kind, st);
     if (e == hipSuccess && src_is_host) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(L, e, "ledger copy in");

@@ -9,7 +9,7 @@ namespace rr {
 struct RouteArgs {
     const void* qp;             // [H, nq, 64] f32 or bf16
     const void* kp;             // [H, nk, 64]
-    int32_t* ids;               // ledger IDs [H, nq, c]: route k | near-miss m | random r
+    int32_t* ids;               // ledger IDs [H, nq, c]: route k | near-miss m | mandatory sink+recent | random r
     int32_t* anchor;            // [H, nq]
     const uint8_t* flags;       // reroute: refresh flags [H, nq] from the rescore kernel
     const float* hint;          // reroute: first selection threshold per row [H, nq]
@@ -19,6 +19,7 @@ struct RouteArgs {
     int32_t* out_head_counts;   // reroute, optional: [H]
     int32_t* out_n_rows;        // reroute, optional: [1]
     int H, nq, nk, k, m, r, c, sel;
+    int sink, recent;           // mandatory sentinels: chunks [0, sink) and the row's last `recent`
     int layer;
     uint32_t seed_lo, seed_hi;
 };

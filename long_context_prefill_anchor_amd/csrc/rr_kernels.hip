@@ -355,12 +355,12 @@ __device__ __forceinline__ void sort16_asc_u32(uint32_t (&v)[16]) {
 
 constexpr int RLIST = 32;          // per-row list of drawn random sentinels (r <= 32)
 
-// Random sentinels (Section 3.1, item 2) and the ledger write of one row, split over the row's
-// quad of lanes (sub = lane & 3).  hv: this lane's half of the row's final list (see
-// quad_merge_split: lanes 0 and 3 hold positions [0, 16), lanes 1 and 2 [16, 32)).  LDS per row
-// slot: a bitmap of W = (nk + 31) / 32 + 1 words holding route, near-miss and drawn chunks (what
-// a draw must avoid), the list of drawn chunks in draw order, then a staging row of c IDs plus a
-// spare slot.
+// Mandatory and random sentinels (Section 3.1, items 3 and 2) and the ledger write of one row,
+// split over the row's quad of lanes (sub = lane & 3).  hv: this lane's half of the row's final
+// list (see quad_merge_split: lanes 0 and 3 hold positions [0, 16), lanes 1 and 2 [16, 32)).
+// LDS per row slot: a bitmap of W = (nk + 31) / 32 + 1 words holding route, near-miss,
+// mandatory and drawn chunks (what a draw must avoid), the list of drawn chunks in draw order,
+// then a staging row of c IDs plus a spare slot.
 // The first 16 draws (Philox blocks 0..3, one block per lane) are decided in parallel: draw t
 // is taken iff its chunk is not in the bitmap, no earlier draw hit the same chunk, and fewer
 // than r draws before it were taken.  Rows that need more draws continue one draw at a time.
@@ -386,7 +386,32 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
         }
     }
 
-    const int pool = my_n - ki - mi;
+    // Mandatory sentinels (Section 3.1, item 3): the sink chunks [0, sink) and the row's last
+    // `recent` allowed chunks, ascending, skipping those already in the route or near-miss
+    // set; marked so that the draws avoid them.  One lane walks them (sink + recent <= 32).
+    const int mw = p.sink + p.recent;
+    int mand = 0;
+    if (mw > 0) {
+        if (sub == 0) {
+            int32_t* mseg = stage + p.k + p.m;
+            const int s_end = min(p.sink, my_n);
+            const int r_beg = max(s_end, my_n - p.recent);
+            for (int pass = 0; pass < 2; ++pass) {
+                const int j0 = pass ? r_beg : 0, j1 = pass ? my_n : s_end;
+                for (int j = j0; j < j1; ++j) {
+                    const uint32_t bit = 1u << (j & 31);
+                    const uint32_t word = bm[j >> 5];
+                    if ((word & bit) == 0u) {
+                        bm[j >> 5] = word | bit;
+                        mseg[mand++] = j;
+                    }
+                }
+            }
+            for (int s2 = mand; s2 < mw; ++s2) mseg[s2] = -1;
+        }
+        mand = dpp_i<DPP_BCAST0>(mand);
+    }
+    const int pool = my_n - ki - mi - mand;
     const int rwant = min(p.r, pool);
     int taken = 0;                                    // random sentinels taken so far
     if (p.r > 0 && pool > p.r) {
@@ -515,12 +540,12 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
     for (int i = 0; i < 16; ++i) {
         const int q = 16 * half + i;
         const int d_sel = (q < tr) ? q : (q < tr + tn) ? p.k + (q - tr) : p.c;
-        const int d_rnd = (q < taken) ? p.k + p.m + q : p.c;
+        const int d_rnd = (q < taken) ? p.k + p.m + mw + q : p.c;
         stage[(sub < 2) ? d_sel : d_rnd] = (int32_t)((sub < 2) ? (key[i] & 0xFFFFu) : key[i]);
     }
     for (int s2 = tr + sub; s2 < p.k; s2 += 4) stage[s2] = -1;
     for (int s2 = tn + sub; s2 < p.m; s2 += 4) stage[p.k + s2] = -1;
-    for (int s2 = taken + sub; s2 < p.r; s2 += 4) stage[p.k + p.m + s2] = -1;
+    for (int s2 = taken + sub; s2 < p.r; s2 += 4) stage[p.k + p.m + mw + s2] = -1;
     // The quad copies the staged row out: four consecutive IDs per instruction and row.
     int32_t* dst = p.ids + ((size_t)h * p.nq + my_row) * p.c;
     for (int e2 = sub; e2 < p.c; e2 += 4) dst[e2] = stage[e2];

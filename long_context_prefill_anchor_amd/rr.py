@@ -31,7 +31,8 @@ class rr_config(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("nq", ctypes.c_int32), ("nk", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("k", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("r", ctypes.c_int32), ("gamma", ctypes.c_float), ("causal", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("dtype", ctypes.c_int32), ("seed", ctypes.c_uint64), ("sink", ctypes.c_int32),
+                ("recent", ctypes.c_int32)]
 
 
 class rr_relay_out(ctypes.Structure):
@@ -106,9 +107,10 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_config(heads, nq, nk, d=64, k=12, m=12, r=8, gamma=0.0, causal=False,
-                dtype="bf16", seed=0) -> rr_config:
+                dtype="bf16", seed=0, sink=0, recent=0) -> rr_config:
     return rr_config(heads, nq, nk, d, k, m, r, float(gamma), int(bool(causal)),
-                     RR_BF16 if dtype == "bf16" else RR_F32, int(seed) & (2**64 - 1))
+                     RR_BF16 if dtype == "bf16" else RR_F32, int(seed) & (2**64 - 1),
+                     int(sink), int(recent))
 
 
 # ------------------------------------------------------------------------- raw entry points
@@ -189,10 +191,11 @@ class Ledger:
     """Owns one rr_ledger handle; torch tensors in, torch tensors out (device memory only)."""
 
     def __init__(self, heads, nq, nk, d=64, k=12, m=12, r=8, gamma=0.0, causal=False,
-                 dtype="bf16", seed=0):
-        self.cfg = make_config(heads, nq, nk, d, k, m, r, gamma, causal, dtype, seed)
+                 dtype="bf16", seed=0, sink=0, recent=0):
+        self.cfg = make_config(heads, nq, nk, d, k, m, r, gamma, causal, dtype, seed, sink, recent)
         self.heads, self.nq, self.nk, self.k, self.m, self.r = heads, nq, nk, k, m, r
-        self.c = k + m + r
+        self.sink, self.recent = sink, recent
+        self.c = k + m + sink + recent + r
         self.handle = rr_ledger_create(self.cfg)
 
     def close(self):
@@ -230,13 +233,13 @@ class Ledger:
                            out.n_rows, out.alpha, out.beta, out.cand_scores)
 
     def get(self, stream=None):
-        """(route [H,nq,k], sent [H,nq,m+r], anchor [H,nq]) as device int32 tensors."""
+        """(route [H,nq,k], sent [H,nq,c-k], anchor [H,nq]) as device int32 tensors."""
         import torch
         H, nq = self.heads, self.nq
         route = torch.empty((H, nq, self.k), dtype=torch.int32, device="cuda")
-        sent = torch.empty((H, nq, self.m + self.r), dtype=torch.int32, device="cuda")
+        sent = torch.empty((H, nq, self.c - self.k), dtype=torch.int32, device="cuda")
         anchor = torch.empty((H, nq), dtype=torch.int32, device="cuda")
-        rr_ledger_get(self.handle, route, sent if self.m + self.r else None, anchor, False, stream)
+        rr_ledger_get(self.handle, route, sent if self.c > self.k else None, anchor, False, stream)
         return route, sent, anchor
 
     def profile(self, enable=True):
@@ -246,5 +249,5 @@ class Ledger:
         return rr_ledger_kernel_times(self.handle)
 
     def set(self, route, sent, anchor, last_layer, stream=None):
-        rr_ledger_set(self.handle, route, sent if self.m + self.r else None, anchor, last_layer,
+        rr_ledger_set(self.handle, route, sent if self.c > self.k else None, anchor, last_layer,
                       False, stream)

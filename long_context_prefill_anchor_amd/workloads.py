@@ -29,10 +29,12 @@ class Workload:
     causal: bool = False        # key chunk j allowed for query chunk i only if j <= i
     gamma: float = 0.0          # guard margin of Eq. 8
     seed: int = 0
+    sink: int = 0               # mandatory sink sentinels (Section 3.1, item 3)
+    recent: int = 0             # mandatory recent sentinels (Section 3.1, item 3)
 
     @property
     def c(self) -> int:
-        return self.k + self.m + self.r
+        return self.k + self.m + self.sink + self.recent + self.r
 
     def is_anchor(self, layer: int) -> bool:
         return layer == 0 or layer in self.anchors

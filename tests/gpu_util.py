@@ -33,7 +33,8 @@ def upload(x: np.ndarray):
 
 def oracle_cfg(led: rr.Ledger, dtype: str, gamma=0.0, causal=False, seed=0):
     return O.RouteConfig(heads=led.heads, nq=led.nq, nk=led.nk, d=64, k=led.k, m=led.m, r=led.r,
-                         gamma=gamma, causal=causal, seed=seed, dtype=dtype)
+                         gamma=gamma, causal=causal, seed=seed, dtype=dtype, sink=led.sink,
+                         recent=led.recent)
 
 
 def ledger_np(led: rr.Ledger):

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     L = rr.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert rr.rr_abi_version() == 1
+    assert rr.rr_abi_version() == 2
 
 
 def cfg(**kw):
@@ -45,6 +45,31 @@ def test_config_check_accepts_every_named_workload():
         assert rr.rr_config_check(c) == rr.RR_OK, (w.name, rr.rr_last_error())
     # the full-routing comparator: m = r = 0
     assert rr.rr_config_check(cfg(m=0, r=0)) == rr.RR_OK
+    # mandatory sentinels up to c = 64
+    assert rr.rr_config_check(cfg(k=12, m=12, r=24, sink=8, recent=8)) == rr.RR_OK
+
+
+def test_config_struct_layout_matches_the_header(tmp_path):
+    """The binding's rr_config and relay-output structs have the size and field offsets a C
+    compiler gives the header's declarations."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"rr.h\"\n"
+                   "int main(void) { printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(rr_config), "
+                   "offsetof(rr_config, seed), offsetof(rr_config, sink), offsetof(rr_config, recent), "
+                   "sizeof(rr_relay_out), offsetof(rr_relay_out, cand_scores)); return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert got == [ctypes.sizeof(rr.rr_config), rr.rr_config.seed.offset, rr.rr_config.sink.offset,
+                   rr.rr_config.recent.offset, ctypes.sizeof(rr.rr_relay_out),
+                   rr.rr_relay_out.cand_scores.offset]
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -62,6 +87,10 @@ def test_config_check_accepts_every_named_workload():
     (dict(k=20, m=13), rr.RR_EUNSUPPORTED, "k + m"),
     (dict(r=33), rr.RR_EUNSUPPORTED, "r must"),
     (dict(nk=8192), rr.RR_EUNSUPPORTED, "nk"),
+    (dict(sink=-1), rr.RR_EINVAL, "sink >= 0"),
+    (dict(recent=-2), rr.RR_EINVAL, "recent >= 0"),
+    (dict(sink=20, recent=13), rr.RR_EUNSUPPORTED, "sink + recent"),
+    (dict(k=16, m=16, r=32, sink=1), rr.RR_EUNSUPPORTED, "<= 64"),
 ])
 def test_config_check_rejects(kw, status, needle):
     assert rr.rr_config_check(cfg(**kw)) == status

@@ -21,8 +21,9 @@ def _gpu():
     yield
 
 
-def make(heads, nq, nk, k=12, m=12, r=8, dtype="bf16", causal=False, seed=0, gamma=0.0):
-    led = rr.Ledger(heads, nq, nk, 64, k, m, r, gamma, causal, dtype, seed)
+def make(heads, nq, nk, k=12, m=12, r=8, dtype="bf16", causal=False, seed=0, gamma=0.0,
+         sink=0, recent=0):
+    led = rr.Ledger(heads, nq, nk, 64, k, m, r, gamma, causal, dtype, seed, sink=sink, recent=recent)
     return led, U.oracle_cfg(led, dtype, gamma, causal, seed)
 
 
@@ -61,11 +62,26 @@ def inputs(kind, heads, nq, nk, dtype, seed):
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("case", ANCHOR_CASES, ids=[c[0] for c in ANCHOR_CASES])
+# Mandatory sink / recent sentinels (Section 3.1, item 3): name, heads, nq, nk, k, m, r, sink,
+# recent, dtype, causal, seed, input kind
+MAND_ANCHOR_CASES = [
+    ("mand_f32", 2, 100, 77, 8, 8, 8, 2, 2, "f32", False, 20, "gauss"),
+    ("mand_bf16_causal", 2, 200, 200, 12, 12, 4, 2, 2, "bf16", True, 21, "gauss"),
+    ("mand_int_ties", 1, 128, 128, 12, 12, 4, 1, 3, "f32", False, 22, "int"),
+    ("mand_c64", 1, 96, 512, 12, 12, 24, 8, 8, "bf16", False, 23, "gauss"),
+    ("mand_only", 1, 64, 100, 12, 0, 0, 4, 4, "f32", False, 24, "gauss"),
+    ("mand_tiny_pool", 1, 40, 10, 4, 2, 2, 3, 3, "f32", False, 25, "gauss"),
+    ("mand_equal_keys", 1, 64, 100, 12, 12, 8, 2, 2, "f32", False, 26, "equal"),
+]
+ANCHOR_CASES_ALL = ([c[:7] + (0, 0) + c[7:] for c in ANCHOR_CASES] + MAND_ANCHOR_CASES)
+
+
+@pytest.mark.parametrize("case", ANCHOR_CASES_ALL, ids=[c[0] for c in ANCHOR_CASES_ALL])
 def test_anchor_parity(case):
-    name, H, nq, nk, k, m, r, dtype, causal, seed, kind = case
-    U.log(f"[anchor] {name} H={H} nq={nq} nk={nk} k={k} m={m} r={r} {dtype} causal={causal}")
-    led, cfg = make(H, nq, nk, k, m, r, dtype, causal, seed)
+    name, H, nq, nk, k, m, r, sink, recent, dtype, causal, seed, kind = case
+    U.log(f"[anchor] {name} H={H} nq={nq} nk={nk} k={k} m={m} r={r} sink={sink} recent={recent} "
+          f"{dtype} causal={causal}")
+    led, cfg = make(H, nq, nk, k, m, r, dtype, causal, seed, sink=sink, recent=recent)
     q, kk = inputs(kind, H, nq, nk, dtype, seed)
     tol = 0.0 if kind != "gauss" else U.GAP_TOL
     rep = U.Report()
@@ -98,13 +114,25 @@ RELAY_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", RELAY_CASES, ids=[c[0] for c in RELAY_CASES])
+# with mandatory sentinels: name, heads, nq, nk, k, m, r, sink, recent, dtype, causal, drift, kind
+MAND_RELAY_CASES = [
+    ("relay_mand_bf16", 2, 256, 256, 12, 12, 4, 2, 2, "bf16", False, 0.03, "gauss"),
+    ("relay_mand_causal", 2, 180, 180, 12, 12, 4, 2, 2, "bf16", True, 0.04, "gauss"),
+    ("relay_mand_int", 2, 128, 160, 12, 12, 4, 1, 3, "f32", False, 0.0, "int"),
+    ("relay_mand_c64", 1, 96, 512, 12, 12, 24, 8, 8, "bf16", False, 0.05, "gauss"),
+    ("relay_mand_only", 1, 70, 50, 4, 0, 0, 2, 2, "f32", False, 0.1, "gauss"),
+]
+RELAY_CASES_ALL = ([c[:7] + (0, 0) + c[7:] for c in RELAY_CASES] + MAND_RELAY_CASES)
+
+
+@pytest.mark.parametrize("case", RELAY_CASES_ALL, ids=[c[0] for c in RELAY_CASES_ALL])
 def test_relay_lockstep(case):
     """Same ledger in (oracle anchor at layer 4, injected with rr_ledger_set), relay at layer 5."""
-    name, H, nq, nk, k, m, r, dtype, causal, drift, kind = case
+    name, H, nq, nk, k, m, r, sink, recent, dtype, causal, drift, kind = case
     gamma = 0.01 if name == "relay_guard" else 0.0
-    U.log(f"[relay] {name} H={H} nq={nq} nk={nk} {dtype} causal={causal} drift={drift} gamma={gamma}")
-    led, cfg = make(H, nq, nk, k, m, r, dtype, causal, 21, gamma)
+    U.log(f"[relay] {name} H={H} nq={nq} nk={nk} sink={sink} recent={recent} {dtype} causal={causal} "
+          f"drift={drift} gamma={gamma}")
+    led, cfg = make(H, nq, nk, k, m, r, dtype, causal, 21, gamma, sink=sink, recent=recent)
     q0, k0 = inputs(kind, H, nq, nk, dtype, 31)
     if kind == "int":
         qn, kn = inputs(kind, H, nq, nk, dtype, 32)
@@ -135,7 +163,8 @@ def run_chain_gpu_vs_oracle(w: W.Workload, heads=None, tol=U.GAP_TOL):
     ``rep.notes`` holds the number of rows under exclusion at each layer."""
     import torch
     H = w.heads if heads is None else heads
-    led = rr.Ledger(H, w.n, w.n, 64, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
+    led = rr.Ledger(H, w.n, w.n, 64, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed,
+                    sink=w.sink, recent=w.recent)
     cfg = U.oracle_cfg(led, w.dtype, w.gamma, w.causal, w.seed)
     rel = 1e-5 if w.dtype == "f32" else 1e-3
     rep = U.Report()
@@ -188,6 +217,14 @@ def chain_report(rep):
 def test_chain_tiny():
     U.log("[chain] tiny_chain")
     rep = run_chain_gpu_vs_oracle(W.tiny_chain())
+    chain_report(rep)
+
+
+def test_chain_mandatory_sentinels():
+    """The drift-sweep chain (256 chunks, 16 fp32 layers) with one sink and two recent
+    sentinels in place of three random ones."""
+    U.log("[chain] drift_sweep sigma=0.03 with sink=1 recent=2 r=5")
+    rep = run_chain_gpu_vs_oracle(W.drift_sweep(0.03, 0).with_(sink=1, recent=2, r=5))
     chain_report(rep)
 
 

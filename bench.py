@@ -226,25 +226,32 @@ def sentinel_ablation(seeds=5):
     """Sentinel mixes on the pages' ablation setting (1 x 256 chunks, fp32, 24 layers, drift
     0.003, k = 12; anchors every 8 layers, as in the other chains): mean recall against full
     routing, rerouted fraction and score-pair fraction over the seeds.  Widths beyond
-    k + m = 32 (24 or 48 near-miss) are outside this library's limits and are not run."""
+    k + m = 32 (24 or 48 near-miss) are outside this library's limits and are not run.  The
+    last mix trades three random sentinels for the mandatory kind (Section 3.1, item 3: one
+    sink chunk, two recent chunks); the synthetic walk gives those chunks no special role,
+    and a pair count of c per row is an upper bound when one of them is already routed."""
     import torch
-    mixes = [("random only", 0, 12), ("near-miss only", 12, 0), ("12 near-miss + 12 random", 12, 12),
-             ("12 near-miss + 8 random", 12, 8)]
+    mixes = [("random only", 0, 12, 0, 0), ("near-miss only", 12, 0, 0, 0),
+             ("12 near-miss + 12 random", 12, 12, 0, 0), ("12 near-miss + 8 random", 12, 8, 0, 0),
+             ("12 near-miss + 1 sink + 2 recent + 5 random", 12, 5, 1, 2)]
     out = []
-    for name, m, r in mixes:
+    for name, m, r, sink, recent in mixes:
         acc = np.zeros(3)
         for seed in range(seeds):
-            w = W.drift_sweep(0.003, seed).with_(name=f"ablation_{m}nm_{r}rnd_seed{seed}", layers=24,
-                                                 anchors=W.stride_anchors(24, 8), m=m, r=r)
+            w = W.drift_sweep(0.003, seed).with_(name=f"ablation_{m}nm_{r}rnd_{sink}s{recent}r_seed{seed}",
+                                                 layers=24, anchors=W.stride_anchors(24, 8), m=m, r=r,
+                                                 sink=sink, recent=recent)
             qs, ks = upload_layers(w)
-            led = rr.Ledger(w.heads, w.n, w.n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
+            led = rr.Ledger(w.heads, w.n, w.n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed,
+                            sink=w.sink, recent=w.recent)
             full = rr.Ledger(w.heads, w.n, w.n, w.d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
             q = quality_pass(w, led, full, qs, ks)
             acc += [q["recall"], q["reroute_fraction"], q["pair_fraction"]]
             led.close()
             full.close()
         acc /= seeds
-        out.append({"sentinels": name, "m": m, "r": r, "recall": round(float(acc[0]), 6),
+        out.append({"sentinels": name, "m": m, "r": r, "sink": sink, "recent": recent,
+                    "recall": round(float(acc[0]), 6),
                     "reroute_fraction": round(float(acc[1]), 4), "pair_fraction": round(float(acc[2]), 4)})
     torch.cuda.empty_cache()
     return out
@@ -254,7 +261,8 @@ def relay_vs_full(w, steps, warmup):
     import torch
     H, n = w.heads, w.n
     qs, ks = upload_layers(w)
-    led = rr.Ledger(H, n, n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
+    led = rr.Ledger(H, n, n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed,
+                    sink=w.sink, recent=w.recent)
     full = rr.Ledger(H, n, n, w.d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
     q = quality_pass(w, led, full, qs, ks)
     relay_ms, full_ms, _ = time_chains(w, led, full, qs, ks, steps, warmup)
@@ -262,6 +270,7 @@ def relay_vs_full(w, steps, warmup):
     t_relay = relay_ms[:, relay_layers].sum()
     t_full = full_ms.sum()
     out = {"workload": w.name, "heads": H, "nq": n, "nk": n, "causal": w.causal, "layers": w.layers,
+           "k": w.k, "m": w.m, "r": w.r, "sink": w.sink, "recent": w.recent,
            "relay_routes_per_s": round(H * n * len(relay_layers) * steps / (t_relay / 1e3), 1),
            "full_routing_routes_per_s": round(H * n * w.layers * steps / (t_full / 1e3), 1),
            "speedup_vs_full": round(float((t_full / (w.layers * steps)) / (t_relay / (len(relay_layers) * steps))), 4),
@@ -468,6 +477,13 @@ def main():
     secondary = None if args.no_secondary else secondary_causal()
     drift_sweep = None if args.no_secondary else drift_sweep_batched()
     ablation = None if args.no_secondary else sentinel_ablation()
+    # The headline workload with mandatory sentinels (one sink, two recent) in place of three
+    # random ones: same c = 32, same kernels.
+    mandatory = None
+    if not args.no_secondary:
+        log("[bench] batched heads with mandatory sentinels (sink 1, recent 2, r 5)")
+        mandatory = relay_vs_full(W.batched_heads().with_(name="batched_heads_mandatory", sink=1,
+                                                          recent=2, r=5), steps=3, warmup=1)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -509,6 +525,7 @@ def main():
         "secondary": secondary,
         "drift_sweep": drift_sweep,
         "sentinel_ablation": ablation,
+        "mandatory_sentinels": mandatory,
     }
     print(json.dumps(out), flush=True)
 

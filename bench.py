@@ -99,8 +99,8 @@ def quality_pass(w, led, full, qs, ks):
     recall of the pages' fixed-stride baseline (every row refreshed each 4th layer, the route
     reused unchecked in between), which needs no kernel of its own."""
     import torch
-    H, n = w.heads, w.n
-    n_i = (np.arange(n) + 1) if w.causal else np.full(n, n)          # allowed keys per row
+    H, n = w.heads, w.nq
+    n_i = (np.arange(n) + 1) if w.causal else np.full(n, w.nk)       # allowed keys per row
     c_i = np.minimum(w.c, n_i)                                          # candidates per row
     out = led.alloc_outputs(with_scores=False)
     recall_sum, rows_rerouted, flagged, pairs, relay_pairs = 0.0, 0, {}, 0, 0
@@ -253,6 +253,33 @@ def sentinel_ablation(seeds=5):
         out.append({"sentinels": name, "m": m, "r": r, "sink": sink, "recent": recent,
                     "recall": round(float(acc[0]), 6),
                     "reroute_fraction": round(float(acc[1]), 4), "pair_fraction": round(float(acc[2]), 4)})
+    torch.cuda.empty_cache()
+    return out
+
+
+def preferred_chunks_sweep(sigmas=(0.01, 0.03, 0.06, 0.1), seeds=10):
+    """The cross-layer stability setting (Section 5.1, Table 2, Figure 2): 1 head, 384 query
+    rows, 192 key chunks, 32 fp32 layers, persistent preferred chunks with layer-local drift
+    (generator in synth.py; its preference strength and the anchor schedule are this build's
+    choices), 12 + 20 near-miss + 12 random.  Means over the seeds of relay recall, rerouted
+    fraction and the fixed-stride-4 baseline's recall."""
+    import torch
+    out = []
+    for sigma in sigmas:
+        acc = np.zeros(3)
+        for seed in range(seeds):
+            w = W.preferred_chunks(sigma, seed)
+            qs, ks = upload_layers(w)
+            led = rr.Ledger(w.heads, w.nq, w.nk, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
+            full = rr.Ledger(w.heads, w.nq, w.nk, w.d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
+            q = quality_pass(w, led, full, qs, ks)
+            acc += [q["recall"], q["reroute_fraction"], q["stride4_recall"]]
+            led.close()
+            full.close()
+        acc /= seeds
+        out.append({"drift": sigma, "recall": round(float(acc[0]), 6),
+                    "reroute_fraction": round(float(acc[1]), 4),
+                    "fixed_stride4_recall": round(float(acc[2]), 6)})
     torch.cuda.empty_cache()
     return out
 
@@ -477,6 +504,7 @@ def main():
     secondary = None if args.no_secondary else secondary_causal()
     drift_sweep = None if args.no_secondary else drift_sweep_batched()
     ablation = None if args.no_secondary else sentinel_ablation()
+    preferred = None if args.no_secondary else preferred_chunks_sweep()
     # The headline workload with mandatory sentinels (one sink, two recent) in place of three
     # random ones: same c = 32, same kernels.
     mandatory = None
@@ -526,6 +554,7 @@ def main():
         "drift_sweep": drift_sweep,
         "sentinel_ablation": ablation,
         "mandatory_sentinels": mandatory,
+        "preferred_chunks": preferred,
     }
     print(json.dumps(out), flush=True)
 

@@ -13,9 +13,17 @@ Recipe (one ``numpy.random.default_rng(seed)`` stream, PCG64, draws in this orde
 The walk stays in float32; bf16 workloads hand out round-to-nearest-even bf16
 copies of each layer (the walk itself is never re-rounded).
 
-The drift model follows the pages' "layer-local Gaussian drift" (RouteRelay,
-Section 5.1 Setup); their persistent-preferred-chunk component is not specified
-and is not modelled.
+Workloads with ``drift_model == "local"`` (the persistent-preferred-chunk setting,
+RouteRelay Section 5.1) use instead, from the same kind of stream:
+  1. sigma_l as above;
+  2. base Q then base K, [H, nq, d] and [H, nk, d], N(0,1)/sqrt(d);
+  3. per head, each query row's preferred chunks: the first ``preferred`` entries of
+     ``rng.permutation(nk)`` drawn row by row; the row's base query gains
+     pref_gain * (sum of the base keys of its preferred chunks) / sqrt(preferred);
+  4. for l = 0..L-1: dQ then dK as above and Q^l = base Q + step_l * dQ,
+     K^l = base K + step_l * dK (the drift is local to each layer; it does not accumulate).
+Where the pages leave that generator open (preference strength, how preferences enter the
+vectors) these are this module's choices.
 """
 from __future__ import annotations
 
@@ -65,6 +73,9 @@ def generate(w: Workload, heads: slice | None = None) -> Iterator[LayerInput]:
     random stream is always drawn for all heads so a slice sees the same values
     as the full run.
     """
+    if w.drift_model == "local":
+        yield from _generate_local(w, heads)
+        return
     rng = np.random.default_rng(w.seed)
     sig = layer_sigmas(w, rng)
     shape = (w.heads, w.n, w.d)
@@ -86,6 +97,32 @@ def generate(w: Workload, heads: slice | None = None) -> Iterator[LayerInput]:
         q = q + step32 * rng.standard_normal(shape, dtype=np.float32)
         k = k + step32 * rng.standard_normal(shape, dtype=np.float32)
         yield emit(layer)
+
+
+def _generate_local(w: Workload, heads: slice | None) -> Iterator[LayerInput]:
+    """Persistent preferred chunks plus layer-local drift (recipe in the module docstring)."""
+    rng = np.random.default_rng(w.seed)
+    sig = layer_sigmas(w, rng)
+    inv = np.float32(1.0 / np.sqrt(w.d))
+    qb = rng.standard_normal((w.heads, w.nq, w.d), dtype=np.float32) * inv
+    kb = rng.standard_normal((w.heads, w.nk, w.d), dtype=np.float32) * inv
+    if w.preferred > 0:
+        gain = np.float32(w.pref_gain / np.sqrt(w.preferred))
+        for h in range(w.heads):
+            for i in range(w.nq):
+                pref = rng.permutation(w.nk)[: w.preferred]
+                qb[h, i] += gain * kb[h, pref].sum(axis=0, dtype=np.float32)
+    sel = heads if heads is not None else slice(None)
+    for layer in range(w.layers):
+        step = sig[layer] if w.drift_scale == "absolute" else sig[layer] / np.sqrt(w.d)
+        step32 = np.float32(step)
+        q = qb + step32 * rng.standard_normal(qb.shape, dtype=np.float32)
+        k = kb + step32 * rng.standard_normal(kb.shape, dtype=np.float32)
+        qs, ks = q[sel], k[sel]
+        if w.dtype == "bf16":
+            yield LayerInput(layer, float(sig[layer]), fp32_to_bf16_bits(qs), fp32_to_bf16_bits(ks))
+        else:
+            yield LayerInput(layer, float(sig[layer]), np.ascontiguousarray(qs), np.ascontiguousarray(ks))
 
 
 def integer_inputs(heads: int, n: int, d: int, seed: int, lo: int = -2, hi: int = 2,

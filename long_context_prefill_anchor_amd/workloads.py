@@ -17,7 +17,7 @@ class Workload:
     name: str
     heads: int
     layers: int
-    n: int                      # nq = nk chunk rows per head
+    n: int                      # query chunk rows per head (and key chunks unless nk_ is set)
     d: int                      # routing representation width
     dtype: str                  # "f32" or "bf16": what the routing kernels read
     drift: Tuple[float, float]  # (lo, hi): lo == hi -> fixed sigma, else sigma_l ~ U[lo, hi)
@@ -31,6 +31,18 @@ class Workload:
     seed: int = 0
     sink: int = 0               # mandatory sink sentinels (Section 3.1, item 3)
     recent: int = 0             # mandatory recent sentinels (Section 3.1, item 3)
+    nk_: int = 0                # key chunks per head when it differs from n (0: nk = n)
+    drift_model: str = "walk"   # "walk": Q^l = Q^{l-1} + step*N; "local": Q^l = base + step*N
+    preferred: int = 0          # "local": preferred key chunks per query row
+    pref_gain: float = 0.0      # "local": weight of the preferred chunks in the row's base query
+
+    @property
+    def nq(self) -> int:
+        return self.n
+
+    @property
+    def nk(self) -> int:
+        return self.nk_ or self.n
 
     @property
     def c(self) -> int:
@@ -84,9 +96,24 @@ def causal_large() -> Workload:
                     anchors=stride_anchors(32, 8), causal=True)
 
 
+def preferred_chunks(sigma: float, seed: int = 0) -> Workload:
+    """The cross-layer stability setting (Section 5.1): 1 head, 384 query rows, 192 key chunks,
+    32 fp32 layers; each query row leans towards 12 preferred chunks of its own that persist
+    through depth, and every layer adds its own Gaussian drift around those persistent
+    representations (not a random walk).  The page gives neither the preference strength nor
+    the anchor schedule: gain 1.0 (a preferred chunk's score is raised by about two standard
+    deviations of the scores) and anchors every 8 layers are this module's choices.  The page's
+    24 near-miss sentinels exceed k + m <= 32, so m = 20 with its 12 random sentinels."""
+    return Workload(f"preferred_s{sigma:g}_seed{seed}", heads=1, layers=32, n=384, d=64,
+                    dtype="f32", drift=(sigma, sigma), drift_scale="relative",
+                    anchors=stride_anchors(32, 8), k=12, m=20, r=12, seed=seed, nk_=192,
+                    drift_model="local", preferred=12, pref_gain=1.0)
+
+
 def all_named():
     out = [tiny_chain()]
     out += [drift_sweep(s, seed) for s in (0.01, 0.03, 0.06) for seed in range(10)]
     out += [scale_sweep(n) for n in (128, 256, 512, 1024)]
     out += [batched_heads(), causal_large()]
+    out += [preferred_chunks(s, seed) for s in (0.01, 0.03, 0.06, 0.1) for seed in range(10)]
     return out

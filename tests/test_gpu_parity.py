@@ -163,13 +163,14 @@ def run_chain_gpu_vs_oracle(w: W.Workload, heads=None, tol=U.GAP_TOL):
     ``rep.notes`` holds the number of rows under exclusion at each layer."""
     import torch
     H = w.heads if heads is None else heads
-    led = rr.Ledger(H, w.n, w.n, 64, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed,
+    nq = w.nq
+    led = rr.Ledger(H, w.nq, w.nk, 64, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed,
                     sink=w.sink, recent=w.recent)
     cfg = U.oracle_cfg(led, w.dtype, w.gamma, w.causal, w.seed)
     rel = 1e-5 if w.dtype == "f32" else 1e-3
     rep = U.Report()
     ora_led = None
-    ex = np.zeros((H, w.n), bool)
+    ex = np.zeros((H, nq), bool)
     hs = slice(0, H) if heads is not None else None
     for li in synth.generate(w, hs):
         if ora_led is None or w.is_anchor(li.layer):
@@ -184,10 +185,10 @@ def run_chain_gpu_vs_oracle(w: W.Workload, heads=None, tol=U.GAP_TOL):
             torch.cuda.synchronize()
             gpu = U.ledger_np(led)
             res = O.relay_layer(cfg, li.q, li.k, li.layer, ora_led)
-            g_flags = out.flags.cpu().numpy().reshape(H, w.n)
+            g_flags = out.flags.cpu().numpy().reshape(H, nq)
             if tol > 0:
                 for h in range(H):
-                    for i in range(w.n):
+                    for i in range(nq):
                         if O.relay_gap(res.alpha[h, i], res.beta[h, i], cfg.gamma) < tol:
                             ex[h, i] = True
                 S = U.oracle_scores(cfg, li.q, li.k)
@@ -195,7 +196,7 @@ def run_chain_gpu_vs_oracle(w: W.Workload, heads=None, tol=U.GAP_TOL):
                     if O.selection_gap(S[h, i], O.n_allowed(i, cfg), cfg.k, cfg.m) < tol:
                         ex[h, i] = True
             mask = ~ex
-            rep.rows += H * w.n
+            rep.rows += H * nq
             rep.excluded += int(ex.sum()) - prev_ex
             rep.notes.append(int(ex.sum()))
             assert np.array_equal(g_flags[mask], res.flags[mask]), f"{w.name} layer {li.layer}: flags"
@@ -217,6 +218,14 @@ def chain_report(rep):
 def test_chain_tiny():
     U.log("[chain] tiny_chain")
     rep = run_chain_gpu_vs_oracle(W.tiny_chain())
+    chain_report(rep)
+
+
+def test_chain_preferred_chunks():
+    """The persistent-preferred-chunk chain (384 query rows, 192 key chunks: nq != nk,
+    layer-local drift, 12 + 20 near-miss + 12 random sentinels)."""
+    U.log("[chain] preferred_chunks sigma=0.03 seed=0")
+    rep = run_chain_gpu_vs_oracle(W.preferred_chunks(0.03, 0))
     chain_report(rep)
 
 

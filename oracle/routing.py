@@ -39,6 +39,8 @@ class RouteConfig:
     dtype: str = "f32"          # "f32" or "bf16": encoding of the Q/K arrays handed in
     sink: int = 0               # mandatory sink sentinels: chunks 0 .. sink-1
     recent: int = 0             # mandatory recent sentinels: the row's last `recent` allowed chunks
+    min_reuse: int = 0          # hysteresis: layers a refreshed row is reused untested
+    gamma_extra: float = 0.0    # hysteresis: extra guard of a refreshed row until it passes once
 
     @property
     def mand(self) -> int:
@@ -171,6 +173,13 @@ class Ledger:
     route: np.ndarray    # int32 [H, nq, k]
     sent: np.ndarray     # int32 [H, nq, c - k]
     anchor: np.ndarray   # int32 [H, nq]
+    # uint8 [H, nq]: 1 = the row was last routed by a relay-layer refresh and has not yet
+    # passed a test under the post-refresh guard (hysteresis state; 0 after an anchor)
+    refreshed: np.ndarray = None
+
+    def __post_init__(self):
+        if self.refreshed is None:
+            self.refreshed = np.zeros(self.anchor.shape, np.uint8)
 
     @staticmethod
     def empty(cfg: RouteConfig) -> "Ledger":
@@ -179,7 +188,7 @@ class Ledger:
                       np.full((cfg.heads, cfg.nq), -1, np.int32))
 
     def copy(self) -> "Ledger":
-        return Ledger(self.route.copy(), self.sent.copy(), self.anchor.copy())
+        return Ledger(self.route.copy(), self.sent.copy(), self.anchor.copy(), self.refreshed.copy())
 
     def candidates(self, h: int, i: int) -> np.ndarray:
         """Candidate set A_i = route U sentinels (Section 3.2, Eq. 5), padding dropped."""
@@ -201,6 +210,7 @@ def rebuild_row(cfg: RouteConfig, ledger: Ledger, h: int, layer: int, i: int,
     ledger.sent[h, i, cfg.m: cfg.m + cfg.mand] = _pad(mand, cfg.mand)
     ledger.sent[h, i, cfg.m + cfg.mand:] = _pad(rnd, cfg.r)
     ledger.anchor[h, i] = layer
+    ledger.refreshed[h, i] = 0
 
 
 # ----------------------------------------------------------------------------- anchor layer
@@ -230,14 +240,33 @@ class RelayResult:
     head_counts: np.ndarray   # int32 [H]
 
 
+def relay_decision(cfg: RouteConfig, layer: int, anchor: int, refreshed: int,
+                   alpha: np.float32, beta: np.float32) -> tuple[bool, int]:
+    """Eq. 8 with the hysteresis of Section 3.2 (after Eq. 8).  Returns (refresh the row?,
+    the row's hysteresis state if it is reused).
+
+    Reading: a row refreshed at a relay layer a is reused without a test at layers
+    a+1 .. a+min_reuse (its "minimum reuse horizon"); after that it is tested with the
+    larger guard gamma + gamma_extra until the first layer at which it passes (its margin
+    has "recovered"), and from then on with gamma.  Rows routed at an anchor layer use gamma
+    throughout.  min_reuse = 0 and gamma_extra = 0 give plain Eq. 8.  beta + guard is
+    rounded to fp32 before the strict comparison."""
+    if refreshed and layer - anchor <= cfg.min_reuse:
+        return False, 1
+    guard = np.float32(np.float32(cfg.gamma) + np.float32(cfg.gamma_extra)) if refreshed \
+        else np.float32(cfg.gamma)
+    reuse = alpha > np.float32(beta + guard)
+    return (not reuse), 0
+
+
 def relay_layer(cfg: RouteConfig, q: np.ndarray, k: np.ndarray, layer: int,
                 ledger: Ledger) -> RelayResult:
     """Intermediate layer (Sections 3.2, 4.1, 4.2).  For each row: score the
     candidate set A = R U C (Eq. 5) at this layer; alpha = min over R (Eq. 6),
-    beta = max over C (Eq. 7); the route is reused iff alpha > beta + gamma (Eq. 8),
-    with beta + gamma rounded to fp32.  Otherwise the row is routed in full at this
-    layer and its ledger entry replaced.  Flagged rows are listed in ascending
-    flattened order h * nq + i (the compaction of Section 4.1/4.2)."""
+    beta = max over C (Eq. 7); the route is reused iff alpha > beta + gamma (Eq. 8,
+    with the hysteresis of ``relay_decision``).  Otherwise the row is routed in full at
+    this layer, its ledger entry replaced and marked refreshed.  Flagged rows are listed
+    in ascending flattened order h * nq + i (the compaction of Section 4.1/4.2)."""
     Q, K = decode(q, cfg.dtype), decode(k, cfg.dtype)
     out = ledger.copy()
     H, nq, c = cfg.heads, cfg.nq, cfg.c
@@ -245,7 +274,6 @@ def relay_layer(cfg: RouteConfig, q: np.ndarray, k: np.ndarray, layer: int,
     alpha = np.zeros((H, nq), np.float32)
     beta = np.zeros((H, nq), np.float32)
     cand = np.full((H, nq, c), np.nan, np.float32)
-    gamma32 = np.float32(cfg.gamma)
     for h in range(H):
         for i in range(nq):
             ids = np.concatenate([ledger.route[h, i], ledger.sent[h, i]])
@@ -258,10 +286,14 @@ def relay_layer(cfg: RouteConfig, q: np.ndarray, k: np.ndarray, layer: int,
             a = np.float32(s_route.min())
             b = np.float32(s_sent.max()) if s_sent.size else np.float32(-np.inf)
             alpha[h, i], beta[h, i] = a, b
-            reuse = a > np.float32(b + gamma32)
-            if not reuse:
+            refresh, state = relay_decision(cfg, layer, int(ledger.anchor[h, i]),
+                                            int(ledger.refreshed[h, i]), a, b)
+            if refresh:
                 flags[h, i] = 1
                 rebuild_row(cfg, out, h, layer, i, score_rows(Q[h, i][None, :], K[h])[0])
+                out.refreshed[h, i] = 1
+            else:
+                out.refreshed[h, i] = state
     rows = np.flatnonzero(flags.reshape(-1)).astype(np.int32)
     return RelayResult(out, flags, alpha, beta, cand, rows,
                        flags.sum(axis=1).astype(np.int32))

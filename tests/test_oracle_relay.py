@@ -156,3 +156,79 @@ def test_guard_margin_only_adds_refreshes(drift_chain):
     f1 = O.relay_layer(cfg_of(w).__class__(**{**cfg_of(w).__dict__, "gamma": 0.05}),
                        li.q, li.k, rec.layer, rec.ledger_in).flags
     assert np.all(f1 >= f0) and f1.sum() > f0.sum()
+
+
+# ----------------------------------------------------------------------------- hysteresis
+# Section 3.2 (after Eq. 8): a refreshed row gets a minimum reuse horizon and may use a larger
+# guard until its margin recovers.  Scores below are chosen by hand; the expected flags follow
+# from the reading stated in ``oracle.relay_decision``.
+
+def _unit_inputs(rows_scores, d=16):
+    """Q, K with K = unit vectors: s_ij = rows_scores[i][j] exactly as fp32."""
+    s = np.asarray(rows_scores, np.float32)
+    nq, n = s.shape
+    q = np.zeros((1, nq, d), np.float32)
+    q[0, :, :n] = s
+    return q, np.eye(d, dtype=np.float32)[:n][None]
+
+
+def _hyst_cfg(**kw):
+    base = dict(heads=1, nq=1, nk=6, d=16, k=2, m=2, r=0)
+    base.update(kw)
+    return O.RouteConfig(**base)
+
+
+# layer 0 (anchor): route {0, 1}, near-miss {2, 3}
+L0 = [[0.9, 0.8, 0.5, 0.4, 0.1, 0.0]]
+# layer 1: chunk 2 overtakes chunk 1 -> refresh: route {0, 2}, near-miss {1, 3}
+L1 = [[0.9, 0.6, 0.7, 0.4, 0.1, 0.0]]
+# layer 2: chunk 1 back above chunk 2 (a flip-flop near the tie)
+L2 = [[0.9, 0.7, 0.6, 0.4, 0.1, 0.0]]
+# layer 3: chunk 2 at 0.65 against chunk 1 at 0.6: margin alpha - beta = 0.05
+L3 = [[0.9, 0.6, 0.65, 0.4, 0.1, 0.0]]
+
+
+def _run(cfg, layers):
+    led = O.anchor_layer(cfg, *_unit_inputs(layers[0]), 0)
+    flags = []
+    for li, sc in enumerate(layers[1:], start=1):
+        res = O.relay_layer(cfg, *_unit_inputs(sc), li, led)
+        flags.append(int(res.flags[0, 0]))
+        led = res.ledger
+    return flags, led
+
+
+def test_without_hysteresis_the_row_flip_flops():
+    flags, led = _run(_hyst_cfg(), [L0, L1, L2])
+    assert flags == [1, 1]                 # refreshed at 1, and again at 2
+    assert led.route[0, 0].tolist() == [0, 1] and led.anchor[0, 0] == 2
+    assert led.refreshed[0, 0] == 1
+
+
+def test_minimum_reuse_horizon_skips_the_next_test():
+    """min_reuse = 1: refreshed at layer 1, reused untested at layer 2 (although chunk 1 now
+    beats the route's minimum), tested again at layer 3 (margin 0.05 > 0: reused)."""
+    flags, led = _run(_hyst_cfg(min_reuse=1), [L0, L1, L2, L3])
+    assert flags == [1, 0, 0]
+    assert led.route[0, 0].tolist() == [0, 2] and led.anchor[0, 0] == 1
+    assert led.refreshed[0, 0] == 0        # passed at layer 3: back to the plain guard
+
+
+def test_post_refresh_guard_until_the_margin_recovers():
+    """gamma_extra = 0.1: at layer 3 the refreshed row's margin 0.05 is below the larger
+    guard, so it refreshes again (with gamma_extra = 0 it would be reused)."""
+    flags, _ = _run(_hyst_cfg(min_reuse=1, gamma_extra=0.1), [L0, L1, L2, L3])
+    assert flags == [1, 0, 1]
+    # a row routed at the anchor uses the plain guard: layer 1 with scores L3 passes
+    flags, led = _run(_hyst_cfg(gamma_extra=0.1), [L0, [[0.9, 0.8, 0.75, 0.4, 0.1, 0.0]]])
+    assert flags == [0] and led.refreshed[0, 0] == 0
+
+
+def test_recovered_row_uses_the_plain_guard():
+    """After passing once under the larger guard the row is tested with gamma again: margin
+    0.15 passes gamma + 0.1 (recovers), then margin 0.05 passes plain gamma = 0."""
+    L3b = [[0.9, 0.55, 0.7, 0.4, 0.1, 0.0]]     # route {0, 2}: alpha 0.7, beta 0.55
+    L4 = [[0.9, 0.6, 0.65, 0.4, 0.1, 0.0]]      # alpha 0.65, beta 0.6
+    flags, led = _run(_hyst_cfg(min_reuse=1, gamma_extra=0.1), [L0, L1, L2, L3b, L4])
+    assert flags == [1, 0, 0, 0]
+    assert led.refreshed[0, 0] == 0 and led.anchor[0, 0] == 1

@@ -13,6 +13,9 @@
  *       rescore each row's ledger candidates, alpha = min over R, beta = max over sentinels,
  *       reuse iff alpha > beta + gamma; flagged rows are compacted (ascending h*nq+i) and only
  *       they are routed in full and get new ledger entries (anchor layer := this layer).
+ *   hysteresis    (Section 3.2, after Eq. 8), off by default: a row refreshed at relay layer a
+ *       is reused untested at layers a+1 .. a+min_reuse, then tested with gamma + gamma_extra
+ *       until the first layer at which it passes; rows routed at an anchor layer use gamma.
  *
  * Conventions shared by every entry point
  *   - Q is [heads, nq, d], K is [heads, nk, d], row-major and contiguous, fp32 or bf16
@@ -76,6 +79,9 @@ typedef struct {
     uint64_t seed;    /* random-sentinel key                                           */
     int32_t sink;     /* mandatory sink sentinels (chunks 0 .. sink-1), >= 0           */
     int32_t recent;   /* mandatory recent sentinels (last `recent` allowed chunks), >= 0 */
+    int32_t min_reuse;  /* hysteresis: layers a relay-refreshed row is reused untested, >= 0 */
+    float gamma_extra;  /* hysteresis: added to gamma for a relay-refreshed row until it     *
+                         * passes once; finite and >= 0 (0 and min_reuse 0: plain Eq. 8)      */
 } rr_config;
 /* c = k + m + sink + recent + r ledger IDs per row.  Limits (RR_EUNSUPPORTED beyond them):
  * d == 64, k + m <= 32, r <= 32, sink + recent <= 32, c <= 64, nk <= 4096, nq <= 65536;
@@ -124,10 +130,21 @@ rr_status rr_ledger_get(const rr_ledger* ledger, int32_t* route, int32_t* sent,
 /* Replace the whole ledger (snapshot restore / replay): route, sent and anchor_layer are
  * required, same layout as rr_ledger_get; `last_layer` becomes the last layer seen, so the
  * next relay call must use a greater layer.  The IDs are trusted to be valid for this
- * configuration (in range, allowed, distinct per row).  src_is_host as in rr_ledger_get. */
+ * configuration (in range, allowed, distinct per row).  The hysteresis state is cleared (see
+ * rr_ledger_set_refreshed).  src_is_host as in rr_ledger_get. */
 rr_status rr_ledger_set(rr_ledger* ledger, const int32_t* route, const int32_t* sent,
                         const int32_t* anchor_layer, int32_t last_layer, int32_t src_is_host,
                         void* stream);
+
+/* Hysteresis state, one byte per row [heads, nq]: 1 when the row was last routed by a
+ * relay-layer refresh, 0 when by an anchor layer; with hysteresis on (min_reuse > 0 or
+ * gamma_extra > 0) a relay test that a refreshed row passes under gamma + gamma_extra also
+ * resets it to 0.  rr_ledger_set clears it; rr_ledger_set_refreshed restores a saved copy
+ * (values 0 or 1).  Host or device memory as in rr_ledger_get / rr_ledger_set. */
+rr_status rr_ledger_get_refreshed(const rr_ledger* ledger, uint8_t* refreshed, int32_t dst_is_host,
+                                  void* stream);
+rr_status rr_ledger_set_refreshed(rr_ledger* ledger, const uint8_t* refreshed, int32_t src_is_host,
+                                  void* stream);
 
 /* Per-kernel timing, for measurement.  While profiling is on, every kernel the ledger
  * launches is bracketed by HIP events recorded on its stream (no synchronisation, no device

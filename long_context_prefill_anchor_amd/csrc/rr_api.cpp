@@ -16,12 +16,13 @@
 
 struct rr_ledger {
     rr_config cfg;
-    int c;        // k + m + r
+    int c;        // k + m + sink + recent + r
     int sel;      // k + m
     int G;        // blocks of 64 rows per head
     int device;
     int32_t* ids = nullptr;      // [H, nq, c]
     int32_t* anchor = nullptr;   // [H, nq]
+    uint8_t* refreshed = nullptr; // [H, nq] hysteresis state (1 = refreshed at a relay layer)
     uint8_t* flags_ws = nullptr; // [H, nq]
     float* hint_ws = nullptr;    // [H, nq]
     int32_t* bcount = nullptr;   // [H, G]
@@ -76,6 +77,9 @@ rr_status check_cfg(const rr_config* c) {
         return fail(RR_EINVAL, "need sink >= 0, recent >= 0 (got %d, %d)", c->sink, c->recent);
     if (c->sink + c->recent > 32)
         return fail(RR_EUNSUPPORTED, "sink + recent must be <= 32 (got %d)", c->sink + c->recent);
+    if (c->min_reuse < 0) return fail(RR_EINVAL, "min_reuse must be >= 0 (got %d)", c->min_reuse);
+    if (!(std::isfinite(c->gamma_extra) && c->gamma_extra >= 0.f))
+        return fail(RR_EINVAL, "gamma_extra must be finite and >= 0");
     if (c->k + c->m + c->sink + c->recent + c->r > 64)
         return fail(RR_EUNSUPPORTED, "k + m + sink + recent + r must be <= 64 (got %d)",
                     c->k + c->m + c->sink + c->recent + c->r);
@@ -92,6 +96,7 @@ rr_status hip_fail(rr_ledger* L, hipError_t e, const char* what) {
 void free_all(rr_ledger* L) {
     (void)hipFree(L->ids);
     (void)hipFree(L->anchor);
+    (void)hipFree(L->refreshed);
     (void)hipFree(L->flags_ws);
     (void)hipFree(L->hint_ws);
     (void)hipFree(L->bcount);
@@ -148,6 +153,7 @@ rr::RouteArgs route_args(const rr_ledger* L, const void* q, const void* k, int l
     a.kp = k;
     a.ids = L->ids;
     a.anchor = L->anchor;
+    a.refreshed = L->refreshed;
     a.flags = L->flags_ws;
     a.hint = L->hint_ws;
     a.bcount = L->bcount;
@@ -203,6 +209,7 @@ rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
         {(void**)&L->anchor, rows * sizeof(int32_t)},
         {(void**)&L->flags_ws, rows},
         {(void**)&L->hint_ws, rows * sizeof(float)},
+        {(void**)&L->refreshed, rows},
         {(void**)&L->bcount, (size_t)cfg->heads * L->G * sizeof(int32_t)},
         {(void**)&L->blist, (size_t)cfg->heads * L->G * rr::ROUTE_ROWS * sizeof(int32_t)},
     };
@@ -216,6 +223,7 @@ rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
     }
     e = hipMemset(L->anchor, 0xFF, rows * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(L->ids, 0xFF, rows * L->c * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMemset(L->refreshed, 0, rows);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         free_all(L);
@@ -285,7 +293,8 @@ rr_status rr_anchor_route(rr_ledger* L, const void* q, const void* k, int32_t la
     if (!q || !k) return fail(RR_EINVAL, "q and k must be device pointers");
     if (layer < 0) return fail(RR_EINVAL, "layer must be >= 0 (got %d)", layer);
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const rr::RouteArgs a = route_args(L, q, k, layer);
+    rr::RouteArgs a = route_args(L, q, k, layer);
+    a.refresh_mark = 0;
     const int tix = time_begin(L, RR_KERNEL_ROUTE, st);
     const hipError_t e = rr::launch_route(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, false, st);
     time_end(L, tix, st);
@@ -327,12 +336,18 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
     s.c = L->c;
     s.sel = L->sel;
     s.gamma = L->cfg.gamma;
+    s.anchor = L->anchor;
+    s.refreshed = L->refreshed;
+    s.layer = layer;
+    s.min_reuse = L->cfg.min_reuse;
+    s.gamma_extra = L->cfg.gamma_extra;
     int tix = time_begin(L, RR_KERNEL_RESCORE, st);
     hipError_t e = rr::launch_rescore(s, L->cfg.dtype == RR_BF16, st);
     time_end(L, tix, st);
     if (e != hipSuccess) return hip_fail(L, e, "rescore launch");
 
     rr::RouteArgs a = route_args(L, q, k, layer);
+    a.refresh_mark = 1;
     a.out_rows = out ? out->rows : nullptr;
     a.out_head_counts = out ? out->head_counts : nullptr;
     a.out_n_rows = out ? out->n_rows : nullptr;
@@ -381,11 +396,36 @@ rr_status rr_ledger_set(rr_ledger* L, const int32_t* route, const int32_t* sent,
         e = hipMemcpy2DAsync(L->ids + L->cfg.k, pitch, sent, (L->c - L->cfg.k) * sizeof(int32_t),
                              (L->c - L->cfg.k) * sizeof(int32_t), rows, kind, st);
     if (e == hipSuccess) e = hipMemcpyAsync(L->anchor, anchor_layer, rows * sizeof(int32_t), kind, st);
+    if (e == hipSuccess) e = hipMemsetAsync(L->refreshed, 0, rows, st);
     if (e == hipSuccess && src_is_host) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(L, e, "ledger copy in");
     L->anchored = true;
     L->poisoned = false;
     L->last_layer = last_layer;
+    return ok();
+}
+
+rr_status rr_ledger_get_refreshed(const rr_ledger* L, uint8_t* refreshed, int32_t dst_is_host, void* stream) {
+    if (!L || !refreshed) return fail(RR_EINVAL, "ledger or refreshed is NULL");
+    if (L->poisoned) return fail(RR_ESTATE, "ledger is poisoned by an earlier device error");
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const size_t rows = (size_t)L->cfg.heads * L->cfg.nq;
+    hipError_t e = hipMemcpyAsync(refreshed, L->refreshed, rows,
+                                  dst_is_host ? hipMemcpyDeviceToHost : hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && dst_is_host) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(RR_EDEVICE, "hysteresis state copy out: %s", hipGetErrorString(e));
+    return ok();
+}
+
+rr_status rr_ledger_set_refreshed(rr_ledger* L, const uint8_t* refreshed, int32_t src_is_host, void* stream) {
+    if (!L || !refreshed) return fail(RR_EINVAL, "ledger or refreshed is NULL");
+    if (L->poisoned) return fail(RR_ESTATE, "ledger is poisoned by an earlier device error");
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const size_t rows = (size_t)L->cfg.heads * L->cfg.nq;
+    hipError_t e = hipMemcpyAsync(L->refreshed, refreshed, rows,
+                                  src_is_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && src_is_host) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(L, e, "hysteresis state copy in");
     return ok();
 }
 

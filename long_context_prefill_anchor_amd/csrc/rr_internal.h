@@ -11,6 +11,7 @@ struct RouteArgs {
     const void* kp;             // [H, nk, 64]
     int32_t* ids;               // ledger IDs [H, nq, c]: route k | near-miss m | mandatory sink+recent | random r
     int32_t* anchor;            // [H, nq]
+    uint8_t* refreshed;         // [H, nq] hysteresis state: each emitted row gets refresh_mark
     const uint8_t* flags;       // reroute: refresh flags [H, nq] from the rescore kernel
     const float* hint;          // reroute: first selection threshold per row [H, nq]
     const int32_t* bcount;      // reroute: flagged rows per rescore block [H, G]
@@ -21,6 +22,7 @@ struct RouteArgs {
     int H, nq, nk, k, m, r, c, sel;
     int sink, recent;           // mandatory sentinels: chunks [0, sink) and the row's last `recent`
     int layer;
+    int refresh_mark;           // 0 for an anchor launch, 1 for a reroute
     uint32_t seed_lo, seed_hi;
 };
 
@@ -28,6 +30,8 @@ struct RescoreArgs {
     const void* qp;
     const void* kp;
     const int32_t* ids;         // [H, nq, c]
+    const int32_t* anchor;      // [H, nq] layer of each row's last full routing (hysteresis)
+    uint8_t* refreshed;         // [H, nq] hysteresis state, cleared when a refreshed row passes
     uint8_t* flags_ws;          // [H, nq]
     float* hint_ws;             // [H, nq]
     int32_t* bcount;            // [H, G] flagged rows per block of 64 rows
@@ -38,6 +42,8 @@ struct RescoreArgs {
     float* cand_scores;         // optional [H, nq, c]
     int H, nq, nk, k, m, r, c, sel;
     float gamma;
+    int layer, min_reuse;       // hysteresis (on when min_reuse > 0 or gamma_extra > 0)
+    float gamma_extra;
 };
 
 constexpr int ROUTE_ROWS = 64;   // rows per route block and per rescore block

@@ -493,7 +493,10 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
         }
     }
     taken = dpp_i<DPP_BCAST0>(taken);                 // lane 0 holds the final count
-    if (sub == 0) p.anchor[(size_t)h * p.nq + my_row] = p.layer;
+    if (sub == 0) {
+        p.anchor[(size_t)h * p.nq + my_row] = p.layer;
+        p.refreshed[(size_t)h * p.nq + my_row] = (uint8_t)p.refresh_mark;
+    }
 
     // Sort keys: lanes 0 / 1 take list positions [0,16) / [16,32) as (segment << 16) | index
     // (segment 0 route, 1 near-miss, 2 none), lanes 2 / 3 the drawn chunks [0,16) / [16,32)
@@ -1171,9 +1174,22 @@ void k_rescore(RescoreArgs p) {
         }
     }
     // Eq. 8: reuse iff alpha > beta + gamma (a row without any route ID is refreshed).
+    // Hysteresis (Section 3.2, after Eq. 8): a row refreshed at a relay layer a is reused
+    // untested up to layer a + min_reuse, then tested with gamma + gamma_extra until it passes
+    // once, which clears its state.
     if (lane < RS_ROWS) {
         const int i = i0 + lane;
-        const bool reuse = res_alpha < INFINITY && res_alpha > res_beta + p.gamma;
+        bool reuse;
+        if (p.min_reuse > 0 || p.gamma_extra > 0.f) {                   // uniform
+            const size_t fl = (size_t)h * p.nq + min(i, p.nq - 1);
+            const bool ref = p.refreshed[fl] != 0;
+            const bool skip = ref && p.layer - p.anchor[fl] <= p.min_reuse;
+            const float guard = ref ? p.gamma + p.gamma_extra : p.gamma;
+            reuse = skip || (res_alpha < INFINITY && res_alpha > res_beta + guard);
+            if (i < p.nq && ref && reuse && !skip) p.refreshed[fl] = 0;
+        } else {
+            reuse = res_alpha < INFINITY && res_alpha > res_beta + p.gamma;
+        }
         if (i < p.nq) {
             const size_t flat = (size_t)h * p.nq + i;
             p.flags_ws[flat] = reuse ? 0 : 1;

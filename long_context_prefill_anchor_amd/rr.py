@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "RR_OK", -1: "RR_EINVAL", -2: "RR_EUNSUPPORTED", -3: "RR_ENOM
 # Entry points declared in include/rr.h, in declaration order.
 ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_destroy", "rr_anchor_route",
                 "rr_relay_layer", "rr_ledger_get", "rr_ledger_set", "rr_ledger_config",
-                "rr_ledger_profile", "rr_ledger_kernel_times", "rr_last_error", "rr_abi_version")
+                "rr_ledger_get_refreshed", "rr_ledger_set_refreshed", "rr_ledger_profile",
+                "rr_ledger_kernel_times", "rr_last_error", "rr_abi_version")
 RR_KERNEL_ROUTE, RR_KERNEL_RESCORE, RR_KERNEL_REROUTE, RR_KERNEL_KINDS = 0, 1, 2, 3
 
 
@@ -32,7 +33,7 @@ class rr_config(ctypes.Structure):
                 ("d", ctypes.c_int32), ("k", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("r", ctypes.c_int32), ("gamma", ctypes.c_float), ("causal", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("seed", ctypes.c_uint64), ("sink", ctypes.c_int32),
-                ("recent", ctypes.c_int32)]
+                ("recent", ctypes.c_int32), ("min_reuse", ctypes.c_int32), ("gamma_extra", ctypes.c_float)]
 
 
 class rr_relay_out(ctypes.Structure):
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.rr_ledger_get.argtypes = [vp, vp, vp, vp, i32, vp]
         L.rr_ledger_set.argtypes = [vp, vp, vp, vp, i32, i32, vp]
         L.rr_ledger_config.argtypes = [vp, P(rr_config)]
+        L.rr_ledger_get_refreshed.argtypes = [vp, vp, i32, vp]
+        L.rr_ledger_set_refreshed.argtypes = [vp, vp, i32, vp]
         L.rr_ledger_profile.argtypes = [vp, i32]
         L.rr_ledger_kernel_times.argtypes = [vp, P(i32), P(ctypes.c_double)]
         L.rr_last_error.restype = ctypes.c_char_p
@@ -107,10 +110,10 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_config(heads, nq, nk, d=64, k=12, m=12, r=8, gamma=0.0, causal=False,
-                dtype="bf16", seed=0, sink=0, recent=0) -> rr_config:
+                dtype="bf16", seed=0, sink=0, recent=0, min_reuse=0, gamma_extra=0.0) -> rr_config:
     return rr_config(heads, nq, nk, d, k, m, r, float(gamma), int(bool(causal)),
                      RR_BF16 if dtype == "bf16" else RR_F32, int(seed) & (2**64 - 1),
-                     int(sink), int(recent))
+                     int(sink), int(recent), int(min_reuse), float(gamma_extra))
 
 
 # ------------------------------------------------------------------------- raw entry points
@@ -154,6 +157,16 @@ def rr_ledger_set(handle, route, sent, anchor_layer, last_layer: int, src_is_hos
            "rr_ledger_set")
 
 
+def rr_ledger_get_refreshed(handle, refreshed, dst_is_host: bool, stream=None) -> None:
+    _check(lib().rr_ledger_get_refreshed(handle, _ptr(refreshed), int(bool(dst_is_host)), _stream(stream)),
+           "rr_ledger_get_refreshed")
+
+
+def rr_ledger_set_refreshed(handle, refreshed, src_is_host: bool, stream=None) -> None:
+    _check(lib().rr_ledger_set_refreshed(handle, _ptr(refreshed), int(bool(src_is_host)), _stream(stream)),
+           "rr_ledger_set_refreshed")
+
+
 def rr_ledger_profile(handle, enable: bool) -> None:
     _check(lib().rr_ledger_profile(handle, int(bool(enable))), "rr_ledger_profile")
 
@@ -191,8 +204,10 @@ class Ledger:
     """Owns one rr_ledger handle; torch tensors in, torch tensors out (device memory only)."""
 
     def __init__(self, heads, nq, nk, d=64, k=12, m=12, r=8, gamma=0.0, causal=False,
-                 dtype="bf16", seed=0, sink=0, recent=0):
-        self.cfg = make_config(heads, nq, nk, d, k, m, r, gamma, causal, dtype, seed, sink, recent)
+                 dtype="bf16", seed=0, sink=0, recent=0, min_reuse=0, gamma_extra=0.0):
+        self.cfg = make_config(heads, nq, nk, d, k, m, r, gamma, causal, dtype, seed, sink, recent,
+                               min_reuse, gamma_extra)
+        self.min_reuse, self.gamma_extra = min_reuse, gamma_extra
         self.heads, self.nq, self.nk, self.k, self.m, self.r = heads, nq, nk, k, m, r
         self.sink, self.recent = sink, recent
         self.c = k + m + sink + recent + r
@@ -241,6 +256,16 @@ class Ledger:
         anchor = torch.empty((H, nq), dtype=torch.int32, device="cuda")
         rr_ledger_get(self.handle, route, sent if self.c > self.k else None, anchor, False, stream)
         return route, sent, anchor
+
+    def get_refreshed(self, stream=None):
+        """Hysteresis state [H, nq] as a device uint8 tensor."""
+        import torch
+        out = torch.empty((self.heads, self.nq), dtype=torch.uint8, device="cuda")
+        rr_ledger_get_refreshed(self.handle, out, False, stream)
+        return out
+
+    def set_refreshed(self, refreshed, stream=None):
+        rr_ledger_set_refreshed(self.handle, refreshed, False, stream)
 
     def profile(self, enable=True):
         rr_ledger_profile(self.handle, enable)

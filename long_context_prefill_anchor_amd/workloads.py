@@ -31,6 +31,8 @@ class Workload:
     seed: int = 0
     sink: int = 0               # mandatory sink sentinels (Section 3.1, item 3)
     recent: int = 0             # mandatory recent sentinels (Section 3.1, item 3)
+    min_reuse: int = 0          # hysteresis (Section 3.2): untested reuse after a refresh
+    gamma_extra: float = 0.0    # hysteresis: extra guard after a refresh until a test passes
     nk_: int = 0                # key chunks per head when it differs from n (0: nk = n)
     drift_model: str = "walk"   # "walk": Q^l = Q^{l-1} + step*N; "local": Q^l = base + step*N
     preferred: int = 0          # "local": preferred key chunks per query row

@@ -173,8 +173,9 @@ class Ledger:
     route: np.ndarray    # int32 [H, nq, k]
     sent: np.ndarray     # int32 [H, nq, c - k]
     anchor: np.ndarray   # int32 [H, nq]
-    # uint8 [H, nq]: 1 = the row was last routed by a relay-layer refresh and has not yet
-    # passed a test under the post-refresh guard (hysteresis state; 0 after an anchor)
+    # uint8 [H, nq] hysteresis state: 1 when the row was last routed by a relay-layer
+    # refresh, 0 when by an anchor layer; with hysteresis on, also 0 once the refreshed row
+    # has passed a test under the post-refresh guard
     refreshed: np.ndarray = None
 
     def __post_init__(self):
@@ -249,8 +250,11 @@ def relay_decision(cfg: RouteConfig, layer: int, anchor: int, refreshed: int,
     a+1 .. a+min_reuse (its "minimum reuse horizon"); after that it is tested with the
     larger guard gamma + gamma_extra until the first layer at which it passes (its margin
     has "recovered"), and from then on with gamma.  Rows routed at an anchor layer use gamma
-    throughout.  min_reuse = 0 and gamma_extra = 0 give plain Eq. 8.  beta + guard is
-    rounded to fp32 before the strict comparison."""
+    throughout.  min_reuse = 0 and gamma_extra = 0 give plain Eq. 8; the state is then never
+    consulted and a reused row keeps it (it only records how the row was last routed).
+    beta + guard is rounded to fp32 before the strict comparison."""
+    if cfg.min_reuse == 0 and cfg.gamma_extra == 0:
+        return not (alpha > np.float32(beta + np.float32(cfg.gamma))), refreshed
     if refreshed and layer - anchor <= cfg.min_reuse:
         return False, 1
     guard = np.float32(np.float32(cfg.gamma) + np.float32(cfg.gamma_extra)) if refreshed \

@@ -34,20 +34,22 @@ def upload(x: np.ndarray):
 def oracle_cfg(led: rr.Ledger, dtype: str, gamma=0.0, causal=False, seed=0):
     return O.RouteConfig(heads=led.heads, nq=led.nq, nk=led.nk, d=64, k=led.k, m=led.m, r=led.r,
                          gamma=gamma, causal=causal, seed=seed, dtype=dtype, sink=led.sink,
-                         recent=led.recent)
+                         recent=led.recent, min_reuse=led.min_reuse, gamma_extra=led.gamma_extra)
 
 
 def ledger_np(led: rr.Ledger):
     route, sent, anchor = led.get()
+    refreshed = led.get_refreshed()
     import torch
     torch.cuda.synchronize()
-    return route.cpu().numpy(), sent.cpu().numpy(), anchor.cpu().numpy()
+    return route.cpu().numpy(), sent.cpu().numpy(), anchor.cpu().numpy(), refreshed.cpu().numpy()
 
 
 def set_ledger(led: rr.Ledger, ol: O.Ledger, last_layer: int):
     import torch
     led.set(torch.from_numpy(ol.route).cuda(), torch.from_numpy(ol.sent).cuda(),
             torch.from_numpy(ol.anchor).cuda(), last_layer)
+    led.set_refreshed(torch.from_numpy(np.ascontiguousarray(ol.refreshed)).cuda())
 
 
 def oracle_scores(cfg: O.RouteConfig, q, k) -> np.ndarray:
@@ -75,10 +77,10 @@ class Report:
 
 
 def compare_ledgers(gpu, ora: O.Ledger, mask: np.ndarray, what: str):
-    """Bit-equality of route / sent / anchor on rows where mask is True."""
-    g_route, g_sent, g_anchor = gpu
+    """Bit-equality of route / sent / anchor / hysteresis state on rows where mask is True."""
+    g_route, g_sent, g_anchor, g_ref = gpu
     for name, g, o in (("route", g_route, ora.route), ("sent", g_sent, ora.sent),
-                       ("anchor", g_anchor, ora.anchor)):
+                       ("anchor", g_anchor, ora.anchor), ("refreshed", g_ref, ora.refreshed)):
         gm, om = g[mask], o[mask]
         if not np.array_equal(gm, om):
             bad = np.argwhere(mask)[np.flatnonzero((gm != om).reshape(len(gm), -1).any(axis=1))]
@@ -133,6 +135,16 @@ def anchor_parity(led, cfg, q, k, layer, tol, rep: Report, rows=None):
     return gpu, ora
 
 
+def relay_excluded(cfg, layer, ledger_in, h, i, alpha, beta, tol) -> bool:
+    """Relay decision gap below tol, with the row's own guard (a relay-refreshed row past its
+    reuse horizon is tested with gamma + gamma_extra; inside the horizon there is no test)."""
+    ref = bool(ledger_in.refreshed[h, i])
+    if ref and layer - int(ledger_in.anchor[h, i]) <= cfg.min_reuse:
+        return False
+    guard = float(np.float32(np.float32(cfg.gamma) + np.float32(cfg.gamma_extra))) if ref else cfg.gamma
+    return O.relay_gap(alpha, beta, guard) < tol
+
+
 def relay_parity(led, cfg, q, k, layer, ledger_in: O.Ledger, tol, rel, rep: Report, excluded_in=None):
     """GPU relay layer (started from ``ledger_in``) vs oracle.  Returns the GPU ledger, the
     oracle result and the rows excluded from here on."""
@@ -168,7 +180,7 @@ def relay_parity(led, cfg, q, k, layer, ledger_in: O.Ledger, tol, rel, rep: Repo
     if tol > 0:
         for h in range(H):
             for i in range(nq):
-                if O.relay_gap(res.alpha[h, i], res.beta[h, i], cfg.gamma) < tol:
+                if relay_excluded(cfg, layer, ledger_in, h, i, res.alpha[h, i], res.beta[h, i], tol):
                     ex[h, i] = True
         S = None
         for h, i in np.argwhere(res.flags == 1):

@@ -60,15 +60,17 @@ def test_config_struct_layout_matches_the_header(tmp_path):
     inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
     src = tmp_path / "layout.c"
     src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"rr.h\"\n"
-                   "int main(void) { printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(rr_config), "
+                   "int main(void) { printf(\"%zu %zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(rr_config), "
                    "offsetof(rr_config, seed), offsetof(rr_config, sink), offsetof(rr_config, recent), "
+                   "offsetof(rr_config, min_reuse), offsetof(rr_config, gamma_extra), "
                    "sizeof(rr_relay_out), offsetof(rr_relay_out, cand_scores)); return 0; }\n")
     exe = tmp_path / "layout"
     subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
                                           text=True).stdout.split()]
     assert got == [ctypes.sizeof(rr.rr_config), rr.rr_config.seed.offset, rr.rr_config.sink.offset,
-                   rr.rr_config.recent.offset, ctypes.sizeof(rr.rr_relay_out),
+                   rr.rr_config.recent.offset, rr.rr_config.min_reuse.offset,
+                   rr.rr_config.gamma_extra.offset, ctypes.sizeof(rr.rr_relay_out),
                    rr.rr_relay_out.cand_scores.offset]
 
 
@@ -91,6 +93,9 @@ def test_config_struct_layout_matches_the_header(tmp_path):
     (dict(recent=-2), rr.RR_EINVAL, "recent >= 0"),
     (dict(sink=20, recent=13), rr.RR_EUNSUPPORTED, "sink + recent"),
     (dict(k=16, m=16, r=32, sink=1), rr.RR_EUNSUPPORTED, "<= 64"),
+    (dict(min_reuse=-1), rr.RR_EINVAL, "min_reuse"),
+    (dict(gamma_extra=-0.1), rr.RR_EINVAL, "gamma_extra"),
+    (dict(gamma_extra=float("inf")), rr.RR_EINVAL, "gamma_extra"),
 ])
 def test_config_check_rejects(kw, status, needle):
     assert rr.rr_config_check(cfg(**kw)) == status
@@ -121,6 +126,8 @@ def test_null_ledger_is_rejected_by_every_call():
     assert L.rr_ledger_get(None, None, None, None, 1, None) == rr.RR_EINVAL
     assert L.rr_ledger_set(None, 1, 1, 1, 0, 1, None) == rr.RR_EINVAL
     assert L.rr_ledger_config(None, None) == rr.RR_EINVAL
+    assert L.rr_ledger_get_refreshed(None, 1, 1, None) == rr.RR_EINVAL
+    assert L.rr_ledger_set_refreshed(None, 1, 1, None) == rr.RR_EINVAL
     assert L.rr_ledger_profile(None, 1) == rr.RR_EINVAL
     assert L.rr_ledger_kernel_times(None, None, None) == rr.RR_EINVAL
     assert "NULL" in rr.rr_last_error() or "required" in rr.rr_last_error()

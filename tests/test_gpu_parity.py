@@ -165,7 +165,7 @@ def run_chain_gpu_vs_oracle(w: W.Workload, heads=None, tol=U.GAP_TOL):
     H = w.heads if heads is None else heads
     nq = w.nq
     led = rr.Ledger(H, w.nq, w.nk, 64, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed,
-                    sink=w.sink, recent=w.recent)
+                    sink=w.sink, recent=w.recent, min_reuse=w.min_reuse, gamma_extra=w.gamma_extra)
     cfg = U.oracle_cfg(led, w.dtype, w.gamma, w.causal, w.seed)
     rel = 1e-5 if w.dtype == "f32" else 1e-3
     rep = U.Report()
@@ -189,7 +189,8 @@ def run_chain_gpu_vs_oracle(w: W.Workload, heads=None, tol=U.GAP_TOL):
             if tol > 0:
                 for h in range(H):
                     for i in range(nq):
-                        if O.relay_gap(res.alpha[h, i], res.beta[h, i], cfg.gamma) < tol:
+                        if U.relay_excluded(cfg, li.layer, ora_led, h, i, res.alpha[h, i],
+                                            res.beta[h, i], tol):
                             ex[h, i] = True
                 S = U.oracle_scores(cfg, li.q, li.k)
                 for h, i in np.argwhere(res.flags == 1):
@@ -226,6 +227,49 @@ def test_chain_preferred_chunks():
     layer-local drift, 12 + 20 near-miss + 12 random sentinels)."""
     U.log("[chain] preferred_chunks sigma=0.03 seed=0")
     rep = run_chain_gpu_vs_oracle(W.preferred_chunks(0.03, 0))
+    chain_report(rep)
+
+
+# Hysteresis (Section 3.2, after Eq. 8): min_reuse, gamma_extra
+HYST_CASES = [
+    ("hyst_horizon", 1, 0.0),
+    ("hyst_guard", 0, 0.02),
+    ("hyst_both", 2, 0.01),
+]
+
+
+@pytest.mark.parametrize("case", HYST_CASES, ids=[c[0] for c in HYST_CASES])
+def test_relay_lockstep_hysteresis(case):
+    """Oracle anchor at layer 4 and relay at 5 (which refreshes some rows and marks them),
+    injected with rr_ledger_set + rr_ledger_set_refreshed; then relay layer 6 on both sides."""
+    name, min_reuse, gamma_extra = case
+    H, nq, nk, dtype = 2, 256, 256, "bf16"
+    U.log(f"[relay] {name} min_reuse={min_reuse} gamma_extra={gamma_extra}")
+    led = rr.Ledger(H, nq, nk, 64, 12, 12, 8, 0.0, False, dtype, 21, min_reuse=min_reuse,
+                    gamma_extra=gamma_extra)
+    cfg = U.oracle_cfg(led, dtype, 0.0, False, 21)
+    q0, k0 = inputs("gauss", H, nq, nk, dtype, 31)
+    q1 = synth.perturb(q0, 0.03 / 8, seed=41, dtype=dtype)
+    k1 = synth.perturb(k0, 0.03 / 8, seed=42, dtype=dtype)
+    q2 = synth.perturb(q1, 0.03 / 8, seed=43, dtype=dtype)
+    k2 = synth.perturb(k1, 0.03 / 8, seed=44, dtype=dtype)
+    ora5 = O.relay_layer(cfg, q1, k1, 5, O.anchor_layer(cfg, q0, k0, 4)).ledger
+    assert ora5.refreshed.sum() > 0
+    rep = U.Report()
+    gpu, res, ex = U.relay_parity(led, cfg, q2, k2, 6, ora5, U.GAP_TOL, 1e-3, rep)
+    skipped = int(((ora5.refreshed == 1) & (6 - ora5.anchor <= min_reuse)).sum())
+    U.log(f"   rows={rep.rows} flagged={int(res.flags.sum())} untested={skipped} "
+          f"still marked={int(res.ledger.refreshed.sum())} excluded={rep.excluded}")
+    if min_reuse >= 1:
+        assert skipped == int(ora5.refreshed.sum())
+    led.close()
+
+
+def test_chain_hysteresis():
+    """The drift-sweep chain with a one-layer reuse horizon and a 0.01 post-refresh guard;
+    both sides carry their own hysteresis state through the chain."""
+    U.log("[chain] drift_sweep sigma=0.03 with min_reuse=1 gamma_extra=0.01")
+    rep = run_chain_gpu_vs_oracle(W.drift_sweep(0.03, 0).with_(min_reuse=1, gamma_extra=0.01))
     chain_report(rep)
 
 

@@ -289,7 +289,7 @@ def relay_vs_full(w, steps, warmup):
     H, n = w.heads, w.n
     qs, ks = upload_layers(w)
     led = rr.Ledger(H, n, n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed,
-                    sink=w.sink, recent=w.recent)
+                    sink=w.sink, recent=w.recent, min_reuse=w.min_reuse, gamma_extra=w.gamma_extra)
     full = rr.Ledger(H, n, n, w.d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
     q = quality_pass(w, led, full, qs, ks)
     relay_ms, full_ms, _ = time_chains(w, led, full, qs, ks, steps, warmup)
@@ -298,6 +298,7 @@ def relay_vs_full(w, steps, warmup):
     t_full = full_ms.sum()
     out = {"workload": w.name, "heads": H, "nq": n, "nk": n, "causal": w.causal, "layers": w.layers,
            "k": w.k, "m": w.m, "r": w.r, "sink": w.sink, "recent": w.recent,
+           "min_reuse": w.min_reuse, "gamma_extra": w.gamma_extra,
            "relay_routes_per_s": round(H * n * len(relay_layers) * steps / (t_relay / 1e3), 1),
            "full_routing_routes_per_s": round(H * n * w.layers * steps / (t_full / 1e3), 1),
            "speedup_vs_full": round(float((t_full / (w.layers * steps)) / (t_relay / (len(relay_layers) * steps))), 4),
@@ -505,6 +506,16 @@ def main():
     drift_sweep = None if args.no_secondary else drift_sweep_batched()
     ablation = None if args.no_secondary else sentinel_ablation()
     preferred = None if args.no_secondary else preferred_chunks_sweep()
+    # Hysteresis (Section 3.2): a one-layer reuse horizon after each relay refresh, alone and
+    # with a post-refresh guard of 0.005, on the headline chain.
+    hysteresis = None
+    if not args.no_secondary:
+        hysteresis = []
+        for mr, ge in ((1, 0.0), (1, 0.005)):
+            log(f"[bench] batched heads with hysteresis (min_reuse {mr}, gamma_extra {ge})")
+            hysteresis.append(relay_vs_full(W.batched_heads().with_(name="batched_heads_hysteresis",
+                                                                    min_reuse=mr, gamma_extra=ge),
+                                            steps=3, warmup=1))
     # The headline workload with mandatory sentinels (one sink, two recent) in place of three
     # random ones: same c = 32, same kernels.
     mandatory = None
@@ -555,6 +566,7 @@ def main():
         "sentinel_ablation": ablation,
         "mandatory_sentinels": mandatory,
         "preferred_chunks": preferred,
+        "hysteresis": hysteresis,
     }
     print(json.dumps(out), flush=True)
 

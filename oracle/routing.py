@@ -41,6 +41,13 @@ class RouteConfig:
     recent: int = 0             # mandatory recent sentinels: the row's last `recent` allowed chunks
     min_reuse: int = 0          # hysteresis: layers a refreshed row is reused untested
     gamma_extra: float = 0.0    # hysteresis: extra guard of a refreshed row until it passes once
+    # width bucket (Section 4.4): ledger row r holds query row q_rows[r] of a Q with nq_q rows
+    # per head; None = every query row, in order
+    q_rows: Optional[tuple] = None
+    nq_q: int = 0
+
+    def query_row(self, r: int) -> int:
+        return r if self.q_rows is None else int(self.q_rows[r])
 
     @property
     def mand(self) -> int:
@@ -72,9 +79,17 @@ def score_rows(q_rows: np.ndarray, keys: np.ndarray) -> np.ndarray:
 
 
 def n_allowed(i: int, cfg: RouteConfig) -> int:
-    """Key chunks query chunk i may route to: all nk, or 0..i under the causal chunk
-    mask (the router's own masking, Section 4.3)."""
-    return i + 1 if cfg.causal else cfg.nk
+    """Key chunks the query chunk of ledger row i may route to: all nk, or 0..q under the
+    causal chunk mask, q being the row's query chunk (the router's own masking,
+    Section 4.3)."""
+    return cfg.query_row(i) + 1 if cfg.causal else cfg.nk
+
+
+def query_rows(cfg: RouteConfig, Qh: np.ndarray) -> np.ndarray:
+    """One head's query representations of the ledger's rows, in ledger order: a width
+    bucket (Section 4.4, "ledgers are bucketed by route width") holds a subset of the
+    query rows; its ledger row r is query row q_rows[r]."""
+    return Qh if cfg.q_rows is None else Qh[np.asarray(cfg.q_rows, dtype=np.int64)]
 
 
 def preference_order(s_row: np.ndarray, n: int) -> np.ndarray:
@@ -205,7 +220,9 @@ def rebuild_row(cfg: RouteConfig, ledger: Ledger, h: int, layer: int, i: int,
     n = n_allowed(i, cfg)
     route, near = select(s_row, n, cfg.k, cfg.m)
     mand = mandatory_sentinels(n, cfg.sink, cfg.recent, np.concatenate([route, near]))
-    rnd = random_sentinels(cfg.seed, h, layer, i, n, np.concatenate([route, near, mand]), cfg.r)
+    # the sampler's counter names the query row, so a row draws the same sentinels in any bucket
+    rnd = random_sentinels(cfg.seed, h, layer, cfg.query_row(i), n,
+                           np.concatenate([route, near, mand]), cfg.r)
     ledger.route[h, i] = _pad(route, cfg.k)
     ledger.sent[h, i, : cfg.m] = _pad(near, cfg.m)
     ledger.sent[h, i, cfg.m: cfg.m + cfg.mand] = _pad(mand, cfg.mand)
@@ -222,7 +239,7 @@ def anchor_layer(cfg: RouteConfig, q: np.ndarray, k: np.ndarray, layer: int) -> 
     Q, K = decode(q, cfg.dtype), decode(k, cfg.dtype)
     led = Ledger.empty(cfg)
     for h in range(cfg.heads):
-        S = score_rows(Q[h], K[h])
+        S = score_rows(query_rows(cfg, Q[h]), K[h])
         for i in range(cfg.nq):
             rebuild_row(cfg, led, h, layer, i, S[i])
     return led
@@ -279,10 +296,12 @@ def relay_layer(cfg: RouteConfig, q: np.ndarray, k: np.ndarray, layer: int,
     beta = np.zeros((H, nq), np.float32)
     cand = np.full((H, nq, c), np.nan, np.float32)
     for h in range(H):
+        Qr = query_rows(cfg, Q[h])
         for i in range(nq):
             ids = np.concatenate([ledger.route[h, i], ledger.sent[h, i]])
             valid = ids >= 0
-            s = score_rows(Q[h, i][None, :], K[h][ids[valid]])[0]
+            qi = Qr[i]
+            s = score_rows(qi[None, :], K[h][ids[valid]])[0]
             cand[h, i, valid] = s
             rmask = valid[: cfg.k]
             s_route = s[: int(rmask.sum())]
@@ -294,7 +313,7 @@ def relay_layer(cfg: RouteConfig, q: np.ndarray, k: np.ndarray, layer: int,
                                             int(ledger.refreshed[h, i]), a, b)
             if refresh:
                 flags[h, i] = 1
-                rebuild_row(cfg, out, h, layer, i, score_rows(Q[h, i][None, :], K[h])[0])
+                rebuild_row(cfg, out, h, layer, i, score_rows(qi[None, :], K[h])[0])
                 out.refreshed[h, i] = 1
             else:
                 out.refreshed[h, i] = state
@@ -311,7 +330,7 @@ def exact_routes(cfg: RouteConfig, q: np.ndarray, k: np.ndarray) -> np.ndarray:
     Q, K = decode(q, cfg.dtype), decode(k, cfg.dtype)
     out = np.full((cfg.heads, cfg.nq, cfg.k), -1, np.int32)
     for h in range(cfg.heads):
-        S = score_rows(Q[h], K[h])
+        S = score_rows(query_rows(cfg, Q[h]), K[h])
         for i in range(cfg.nq):
             route, _ = select(S[i], n_allowed(i, cfg), cfg.k, 0)
             out[h, i] = _pad(route, cfg.k)

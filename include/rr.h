@@ -109,6 +109,19 @@ rr_status rr_config_check(const rr_config* cfg);
  * call).  The ledger starts empty: the first compute call on it must be rr_anchor_route. */
 rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out);
 
+/* Width bucket (Section 4.4: ledgers are bucketed by route width; Section 4.3: the ledger
+ * stores whichever width the routing policy asks for): a ledger over cfg->nq of the query
+ * rows only, with the bucket's own k, m, r.  q_rows (host memory, copied; cfg->nq entries,
+ * strictly ascending, each in [0, nq_q)) names the query row of each ledger row; the Q handed
+ * to rr_anchor_route / rr_relay_layer is then [heads, nq_q, d] (all query rows), K as usual.
+ * Each ledger row is routed exactly as that query row would be in a ledger over all rows
+ * with the same configuration (causal limit and sentinel draws follow the query row).
+ * Ledger contents, flags, alpha, beta and the compacted list are indexed by ledger row
+ * (h * cfg->nq + r).  Causal buckets need nq_q == nk.  Errors as rr_ledger_create, plus
+ * RR_EINVAL for a NULL or malformed q_rows. */
+rr_status rr_ledger_create_rows(const rr_config* cfg, const int32_t* q_rows, int32_t nq_q,
+                                rr_ledger** out);
+
 /* Free the ledger (synchronises the device first).  NULL is ignored. */
 void rr_ledger_destroy(rr_ledger* ledger);
 

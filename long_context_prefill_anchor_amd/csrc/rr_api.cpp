@@ -23,6 +23,8 @@ struct rr_ledger {
     int32_t* ids = nullptr;      // [H, nq, c]
     int32_t* anchor = nullptr;   // [H, nq]
     uint8_t* refreshed = nullptr; // [H, nq] hysteresis state (1 = refreshed at a relay layer)
+    int32_t* qmap = nullptr;     // width bucket: [nq] query row of each ledger row (else null)
+    int nq_q = 0;                // query rows per head of the Q handed to compute calls
     uint8_t* flags_ws = nullptr; // [H, nq]
     float* hint_ws = nullptr;    // [H, nq]
     int32_t* bcount = nullptr;   // [H, G]
@@ -58,7 +60,7 @@ rr_status ok() {
     return RR_OK;
 }
 
-rr_status check_cfg(const rr_config* c) {
+rr_status check_cfg(const rr_config* c, bool bucket) {
     if (!c) return fail(RR_EINVAL, "config is NULL");
     if (c->heads < 1 || c->nq < 1 || c->nk < 1)
         return fail(RR_EINVAL, "heads, nq and nk must be >= 1 (got %d, %d, %d)", c->heads, c->nq, c->nk);
@@ -67,7 +69,7 @@ rr_status check_cfg(const rr_config* c) {
     if (!(std::isfinite(c->gamma) && c->gamma >= 0.f)) return fail(RR_EINVAL, "gamma must be finite and >= 0");
     if (c->causal != 0 && c->causal != 1) return fail(RR_EINVAL, "causal must be 0 or 1");
     if (c->dtype != RR_F32 && c->dtype != RR_BF16) return fail(RR_EINVAL, "dtype must be RR_F32 or RR_BF16");
-    if (c->causal && c->nq != c->nk) return fail(RR_EINVAL, "causal routing needs nq == nk");
+    if (c->causal && !bucket && c->nq != c->nk) return fail(RR_EINVAL, "causal routing needs nq == nk");
     if ((int64_t)c->heads * c->nq >= (int64_t)1 << 31 || (int64_t)c->heads * c->nk * 64 >= (int64_t)1 << 40)
         return fail(RR_EINVAL, "problem too large");
     if (c->d != 64) return fail(RR_EUNSUPPORTED, "only d = 64 is implemented (got %d)", c->d);
@@ -97,6 +99,7 @@ void free_all(rr_ledger* L) {
     (void)hipFree(L->ids);
     (void)hipFree(L->anchor);
     (void)hipFree(L->refreshed);
+    (void)hipFree(L->qmap);
     (void)hipFree(L->flags_ws);
     (void)hipFree(L->hint_ws);
     (void)hipFree(L->bcount);
@@ -154,6 +157,8 @@ rr::RouteArgs route_args(const rr_ledger* L, const void* q, const void* k, int l
     a.ids = L->ids;
     a.anchor = L->anchor;
     a.refreshed = L->refreshed;
+    a.qmap = L->qmap;
+    a.nq_q = L->nq_q;
     a.flags = L->flags_ws;
     a.hint = L->hint_ws;
     a.bcount = L->bcount;
@@ -183,21 +188,23 @@ int32_t rr_abi_version(void) { return RR_ABI_VERSION; }
 const char* rr_last_error(void) { return g_err.c_str(); }
 
 rr_status rr_config_check(const rr_config* cfg) {
-    const rr_status st = check_cfg(cfg);
+    const rr_status st = check_cfg(cfg, false);
     return st == RR_OK ? ok() : st;
 }
 
-rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
-    if (!out) return fail(RR_EINVAL, "out is NULL");
-    *out = nullptr;
-    const rr_status st = check_cfg(cfg);
-    if (st != RR_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Shared by rr_ledger_create and rr_ledger_create_rows (q_rows: validated host array or null).
+rr_status create_ledger(const rr_config* cfg, const int32_t* q_rows, int32_t nq_q, rr_ledger** out) {
     rr_ledger* L = new (std::nothrow) rr_ledger;
     if (!L) return fail(RR_ENOMEM, "host allocation failed");
     L->cfg = *cfg;
     L->c = cfg->k + cfg->m + cfg->sink + cfg->recent + cfg->r;
     L->sel = cfg->k + cfg->m;
     L->G = (cfg->nq + rr::ROUTE_ROWS - 1) / rr::ROUTE_ROWS;
+    L->nq_q = q_rows ? nq_q : cfg->nq;
     hipError_t e = hipGetDevice(&L->device);
     if (e != hipSuccess) {
         delete L;
@@ -212,8 +219,10 @@ rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
         {(void**)&L->refreshed, rows},
         {(void**)&L->bcount, (size_t)cfg->heads * L->G * sizeof(int32_t)},
         {(void**)&L->blist, (size_t)cfg->heads * L->G * rr::ROUTE_ROWS * sizeof(int32_t)},
+        {(void**)&L->qmap, q_rows ? (size_t)cfg->nq * sizeof(int32_t) : 0},
     };
     for (auto& a : allocs) {
+        if (a.p == (void**)&L->qmap && !q_rows) continue;
         e = hipMalloc(a.p, a.bytes ? a.bytes : 4);
         if (e != hipSuccess) {
             free_all(L);
@@ -224,6 +233,8 @@ rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
     e = hipMemset(L->anchor, 0xFF, rows * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(L->ids, 0xFF, rows * L->c * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(L->refreshed, 0, rows);
+    if (e == hipSuccess && q_rows)
+        e = hipMemcpy(L->qmap, q_rows, (size_t)cfg->nq * sizeof(int32_t), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         free_all(L);
@@ -232,6 +243,34 @@ rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
     }
     *out = L;
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out) {
+    if (!out) return fail(RR_EINVAL, "out is NULL");
+    *out = nullptr;
+    const rr_status st = check_cfg(cfg, false);
+    if (st != RR_OK) return st;
+    return create_ledger(cfg, nullptr, 0, out);
+}
+
+rr_status rr_ledger_create_rows(const rr_config* cfg, const int32_t* q_rows, int32_t nq_q, rr_ledger** out) {
+    if (!out) return fail(RR_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!q_rows) return fail(RR_EINVAL, "q_rows is NULL");
+    const rr_status st = check_cfg(cfg, true);
+    if (st != RR_OK) return st;
+    if (nq_q < cfg->nq || nq_q > 65536)
+        return fail(RR_EINVAL, "nq_q must be in [nq, 65536] (got %d for nq = %d)", nq_q, cfg->nq);
+    if (cfg->causal && nq_q != cfg->nk) return fail(RR_EINVAL, "causal routing needs nq_q == nk");
+    for (int r = 0; r < cfg->nq; ++r) {
+        if (q_rows[r] < 0 || q_rows[r] >= nq_q || (r > 0 && q_rows[r] <= q_rows[r - 1]))
+            return fail(RR_EINVAL, "q_rows must ascend strictly within [0, nq_q) (entry %d = %d)", r, q_rows[r]);
+    }
+    return create_ledger(cfg, q_rows, nq_q, out);
 }
 
 void rr_ledger_destroy(rr_ledger* L) {
@@ -338,6 +377,8 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
     s.gamma = L->cfg.gamma;
     s.anchor = L->anchor;
     s.refreshed = L->refreshed;
+    s.qmap = L->qmap;
+    s.nq_q = L->nq_q;
     s.layer = layer;
     s.min_reuse = L->cfg.min_reuse;
     s.gamma_extra = L->cfg.gamma_extra;

@@ -7,7 +7,8 @@
 namespace rr {
 
 struct RouteArgs {
-    const void* qp;             // [H, nq, 64] f32 or bf16
+    const void* qp;             // [H, nq_q, 64] f32 or bf16
+    const int32_t* qmap;        // width bucket: ledger row r is query row qmap[r]; null = identity
     const void* kp;             // [H, nk, 64]
     int32_t* ids;               // ledger IDs [H, nq, c]: route k | near-miss m | mandatory sink+recent | random r
     int32_t* anchor;            // [H, nq]
@@ -23,11 +24,14 @@ struct RouteArgs {
     int sink, recent;           // mandatory sentinels: chunks [0, sink) and the row's last `recent`
     int layer;
     int refresh_mark;           // 0 for an anchor launch, 1 for a reroute
+    int nq_q;                   // query rows per head in qp (nq when qmap is null)
     uint32_t seed_lo, seed_hi;
 };
 
 struct RescoreArgs {
-    const void* qp;
+    const void* qp;             // [H, nq_q, 64]
+    const int32_t* qmap;        // as in RouteArgs
+    int nq_q;
     const void* kp;
     const int32_t* ids;         // [H, nq, c]
     const int32_t* anchor;      // [H, nq] layer of each row's last full routing (hysteresis)

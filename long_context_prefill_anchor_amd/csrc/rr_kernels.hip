@@ -265,7 +265,8 @@ __host__ __forceinline__ int xcd_grid(int nlogical) { return (nlogical + XCDS - 
 
 struct RouteShared {
     uint64_t thr[ROWS];      // shared threshold key per row (max over the waves' lower bounds)
-    int32_t rows[ROWS];
+    int32_t rows[ROWS];      // ledger row of each slot (-1: none)
+    int32_t qrows[ROWS];     // its query row (differs in a width bucket)
     int32_t redo;
 };
 
@@ -368,7 +369,7 @@ constexpr int RLIST = 32;          // per-row list of drawn random sentinels (r 
 // lanes 2 and 3 the drawn chunks by index, each pair with a 16-key network per lane and one
 // bitonic exchange between the two lanes, which leaves every segment in ascending index order.
 __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&hv)[16], int slot, int sub,
-                                           int my_row, int my_n, int h, unsigned char* lds) {
+                                           int my_row, int my_qrow, int my_n, int h, unsigned char* lds) {
     const int ki = min(p.k, my_n);
     const int mi = min(p.m, my_n - ki);
     const int words = (p.nk + 31) >> 5;
@@ -416,7 +417,7 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
     int taken = 0;                                    // random sentinels taken so far
     if (p.r > 0 && pool > p.r) {
         // Draws 4 sub .. 4 sub + 3 from Philox block `sub`.
-        const P4 w4 = philox4x32_10(P4{(uint32_t)sub, (uint32_t)my_row, (uint32_t)p.layer, (uint32_t)h},
+        const P4 w4 = philox4x32_10(P4{(uint32_t)sub, (uint32_t)my_qrow, (uint32_t)p.layer, (uint32_t)h},
                                     p.seed_lo, p.seed_hi);
         uint32_t jj[4];
         jj[0] = __umulhi(w4.x, (uint32_t)my_n);
@@ -461,7 +462,7 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
             P4 v4 = {0u, 0u, 0u, 0u};
             for (int t = 16; t < 65536 && __ballot(drawing); ++t) {
                 if ((t & 3) == 0) {
-                    P4 c = {(uint32_t)(t >> 2), (uint32_t)my_row, (uint32_t)p.layer, (uint32_t)h};
+                    P4 c = {(uint32_t)(t >> 2), (uint32_t)my_qrow, (uint32_t)p.layer, (uint32_t)h};
                     v4 = philox4x32_10(c, p.seed_lo, p.seed_hi);
                 }
                 const uint32_t uu = ((t & 3) == 0) ? v4.x : ((t & 3) == 1) ? v4.y : ((t & 3) == 2) ? v4.z : v4.w;
@@ -564,7 +565,7 @@ struct RowCtx {
     const E* Qh;
     const E* Kh;
     uint32_t* my_buf;
-    int qslot, qsub, q_row, q_n;
+    int qslot, qsub, q_row, q_n, q_qrow;
     bool q_redo;
 };
 
@@ -584,9 +585,9 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
     const auto* Qh = cx.Qh;
     const auto* Kh = cx.Kh;
     uint32_t* my_buf = cx.my_buf;
-    const int qslot = cx.qslot, qsub = cx.qsub, q_row = cx.q_row, q_n = cx.q_n;
+    const int qslot = cx.qslot, qsub = cx.qsub, q_row = cx.q_row, q_n = cx.q_n, q_qrow = cx.q_qrow;
     if constexpr (REROUTE) {
-        if (!primed) tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
+        if (!primed) tile.load_q(Qh, sh.qrows[lane & 31], sh.qrows[32 + (lane & 31)], lane);
     } else {
         (void)Qh;
     }
@@ -683,7 +684,7 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
                 emit_now = emit_now && cx.q_redo;
             }
         }
-        if (emit_now) emit_split(p, hv, qslot, qsub, q_row, q_n, h, dyn_lds);
+        if (emit_now) emit_split(p, hv, qslot, qsub, q_row, q_qrow, q_n, h, dyn_lds);
         __syncthreads();                                                // LDS free, sh.redo final
     }
 }
@@ -698,7 +699,7 @@ __device__ __forceinline__ void redo_rows(const RouteArgs& p, RouteShared& sh, u
     if (threadIdx.x == 0) sh.redo = 0;
     asm volatile("" : "+v"(cx.my_n), "+v"(cx.nmin), "+v"(cx.my_row), "+v"(cx.ntiles));
     asm volatile("" : "+v"(cx.Kh), "+v"(cx.Qh), "+v"(cx.my_buf));
-    asm volatile("" : "+v"(cx.q_row), "+v"(cx.q_n), "+v"(cx.qslot), "+v"(cx.qsub));
+    asm volatile("" : "+v"(cx.q_row), "+v"(cx.q_n), "+v"(cx.qslot), "+v"(cx.qsub), "+v"(cx.q_qrow));
     Tile<DT> tile;
     typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
     select_and_emit<DT, CAUSAL, true>(p, sh, dyn_lds, tile, kbuf, false, cx, 1);
@@ -815,28 +816,34 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
             sh.rows[lane] = (i < p.nq) ? i : -1;
         }
     }
+    if (wave == 0) {
+        // Query row of each slot: a width bucket's ledger rows are a subset of the query rows.
+        const int r = sh.rows[lane];
+        sh.qrows[lane] = (r < 0) ? -1 : (p.qmap ? p.qmap[r] : r);
+    }
     if (threadIdx.x == 0) sh.redo = 0;
     __syncthreads();
 
     // ------------------------------------------------------------------ per-row setup
     const int my_row = sh.rows[lane];
-    const int my_n = (my_row < 0) ? 0 : (CAUSAL ? my_row + 1 : p.nk);
+    const int my_n = (my_row < 0) ? 0 : (CAUSAL ? sh.qrows[lane] + 1 : p.nk);
     // Wave-uniform after the reductions; readfirstlane lets the compiler see it.
     const int kmax = __builtin_amdgcn_readfirstlane(wave_max_i(my_n));
     const int nmin = __builtin_amdgcn_readfirstlane(wave_min_i((my_row < 0) ? (1 << 30) : my_n));
     const int ntiles = (kmax + TK - 1) / TK;
-    const E* Qh = reinterpret_cast<const E*>(p.qp) + (size_t)h * p.nq * 64;
+    const E* Qh = reinterpret_cast<const E*>(p.qp) + (size_t)h * p.nq_q * 64;
     const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
     Tile<DT> tile;
     typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
-    if constexpr (!REROUTE) tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
+    if constexpr (!REROUTE) tile.load_q(Qh, sh.qrows[lane & 31], sh.qrows[32 + (lane & 31)], lane);
 
     uint32_t* my_buf = reinterpret_cast<uint32_t*>(dyn_lds) + (size_t)wave * 2 * CAP * ROWS + lane;
     // Final merge and ledger write run one row per quad of lanes over all four waves.
     const int qslot = 16 * wave + (lane >> 2);
     const int qsub = lane & 3;
     const int q_row = sh.rows[qslot];
-    const int q_n = (q_row < 0) ? 0 : (CAUSAL ? q_row + 1 : p.nk);
+    const int q_qrow = sh.qrows[qslot];
+    const int q_n = (q_row < 0) ? 0 : (CAUSAL ? q_qrow + 1 : p.nk);
 
     // ------------------------------------------------------------------ first threshold
     uint64_t base_thr;
@@ -844,7 +851,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
         // The threshold load first, then the query rows and the first key tiles: the three
         // round trips overlap, and waiting for the threshold does not wait for the others.
         const float hraw = p.hint[(size_t)h * p.nq + max(my_row, 0)];
-        tile.load_q(Qh, sh.rows[lane & 31], sh.rows[32 + (lane & 31)], lane);
+        tile.load_q(Qh, sh.qrows[lane & 31], sh.qrows[32 + (lane & 31)], lane);
         fill_ring<DT>(tile, kbuf, Kh, wave, p.nk, lane);
         const float hv = (my_row >= 0) ? hraw : -INFINITY;
         const float t = (hv == -INFINITY) ? -INFINITY : hv - (fabsf(hv) * 1e-4f + 1e-6f);
@@ -911,7 +918,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     __syncthreads();
 
     // ------------------------------------------------------------------ streaming pass
-    RowCtx<DT> cx{lane, wave, h, my_row, my_n, nmin, ntiles, Qh, Kh, my_buf, qslot, qsub, q_row, q_n, false};
+    RowCtx<DT> cx{lane, wave, h, my_row, my_n, nmin, ntiles, Qh, Kh, my_buf, qslot, qsub, q_row, q_n, q_qrow, false};
     select_and_emit<DT, CAUSAL, REROUTE>(p, sh, dyn_lds, tile, kbuf, REROUTE, cx, 0);
     if constexpr (REROUTE) {
         if (sh.redo) redo_rows<DT, CAUSAL>(p, sh, dyn_lds, cx);         // uniform; rare
@@ -1064,8 +1071,8 @@ void k_rescore(RescoreArgs p) {
     const int lane = threadIdx.x & 63;
     const int i0 = b * ROWS + wave * RS_ROWS;
     const int nrow = max(0, min(RS_ROWS, p.nq - i0));   // rows of this wave inside the head
-    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(reinterpret_cast<const char*>(p.qp) + (size_t)h * p.nq * ROW_BYTES,
-                                                (uint32_t)p.nq * ROW_BYTES);
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(reinterpret_cast<const char*>(p.qp) + (size_t)h * p.nq_q * ROW_BYTES,
+                                                (uint32_t)p.nq_q * ROW_BYTES);
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(reinterpret_cast<const char*>(p.kp) + (size_t)h * p.nk * ROW_BYTES,
                                                 (uint32_t)p.nk * ROW_BYTES);
     const __amdgpu_buffer_rsrc_t rI = make_rsrc(p.ids + (size_t)h * p.nq * p.c, (uint32_t)(p.nq * p.c * 4));
@@ -1075,7 +1082,9 @@ void k_rescore(RescoreArgs p) {
         constexpr int PIECES = RS_ROWS * ROW_BYTES / 16;
         for (int x = lane; x < PIECES; x += 64) {
             const int rr = x / (ROW_BYTES / 16), piece = x % (ROW_BYTES / 16);
-            const uint4 v = buf_load16(rQ, rr < nrow ? (uint32_t)(i0 + rr) * ROW_BYTES + 16u * piece : OOB);
+            // a width bucket's ledger row names its query row through qmap
+            const int qr = p.qmap ? (rr < nrow ? p.qmap[i0 + rr] : 0) : i0 + rr;
+            const uint4 v = buf_load16(rQ, rr < nrow ? (uint32_t)qr * ROW_BYTES + 16u * piece : OOB);
             *reinterpret_cast<uint4*>(&sq[wave][rr][16 * piece]) = v;
         }
         const int nid = nrow * p.c;

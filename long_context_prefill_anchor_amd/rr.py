@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "RR_OK", -1: "RR_EINVAL", -2: "RR_EUNSUPPORTED", -3: "RR_ENOM
                 -4: "RR_EDEVICE", -5: "RR_ESTATE"}
 
 # Entry points declared in include/rr.h, in declaration order.
-ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_destroy", "rr_anchor_route",
+ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_create_rows", "rr_ledger_destroy",
+                "rr_anchor_route",
                 "rr_relay_layer", "rr_ledger_get", "rr_ledger_set", "rr_ledger_config",
                 "rr_ledger_get_refreshed", "rr_ledger_set_refreshed", "rr_ledger_profile",
                 "rr_ledger_kernel_times", "rr_last_error", "rr_abi_version")
@@ -56,6 +57,7 @@ def lib() -> ctypes.CDLL:
         vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER
         L.rr_config_check.argtypes = [P(rr_config)]
         L.rr_ledger_create.argtypes = [P(rr_config), P(vp)]
+        L.rr_ledger_create_rows.argtypes = [P(rr_config), P(i32), i32, P(vp)]
         L.rr_ledger_destroy.argtypes = [vp]
         L.rr_ledger_destroy.restype = None
         L.rr_anchor_route.argtypes = [vp, vp, vp, i32, vp]
@@ -125,6 +127,14 @@ def rr_config_check(cfg: rr_config) -> int:
 def rr_ledger_create(cfg: rr_config) -> int:
     h = ctypes.c_void_p()
     _check(lib().rr_ledger_create(ctypes.byref(cfg), ctypes.byref(h)), "rr_ledger_create")
+    return h.value
+
+
+def rr_ledger_create_rows(cfg: rr_config, q_rows, nq_q: int) -> int:
+    rows = (ctypes.c_int32 * len(q_rows))(*[int(x) for x in q_rows])
+    h = ctypes.c_void_p()
+    _check(lib().rr_ledger_create_rows(ctypes.byref(cfg), rows, int(nq_q), ctypes.byref(h)),
+           "rr_ledger_create_rows")
     return h.value
 
 
@@ -204,14 +214,24 @@ class Ledger:
     """Owns one rr_ledger handle; torch tensors in, torch tensors out (device memory only)."""
 
     def __init__(self, heads, nq, nk, d=64, k=12, m=12, r=8, gamma=0.0, causal=False,
-                 dtype="bf16", seed=0, sink=0, recent=0, min_reuse=0, gamma_extra=0.0):
+                 dtype="bf16", seed=0, sink=0, recent=0, min_reuse=0, gamma_extra=0.0,
+                 q_rows=None):
+        """``q_rows``: a width bucket over these query rows (ascending) of a Q with ``nq``
+        rows per head; the ledger then has len(q_rows) rows."""
+        self.q_rows = None if q_rows is None else tuple(int(x) for x in q_rows)
+        self.nq_q = nq
+        if self.q_rows is not None:
+            nq = len(self.q_rows)
         self.cfg = make_config(heads, nq, nk, d, k, m, r, gamma, causal, dtype, seed, sink, recent,
                                min_reuse, gamma_extra)
         self.min_reuse, self.gamma_extra = min_reuse, gamma_extra
         self.heads, self.nq, self.nk, self.k, self.m, self.r = heads, nq, nk, k, m, r
         self.sink, self.recent = sink, recent
         self.c = k + m + sink + recent + r
-        self.handle = rr_ledger_create(self.cfg)
+        if self.q_rows is None:
+            self.handle = rr_ledger_create(self.cfg)
+        else:
+            self.handle = rr_ledger_create_rows(self.cfg, self.q_rows, self.nq_q)
 
     def close(self):
         if getattr(self, "handle", None):

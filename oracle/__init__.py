@@ -14,7 +14,7 @@ the page's printed tables; see each test's docstring for the pin it provides.
 from .philox import philox4x32_10, philox4x64_10  # noqa: F401
 from .routing import (  # noqa: F401
     Ledger, LayerRecord, RelayResult, RouteConfig, anchor_layer, decode, exact_routes,
-    ledger_bytes, n_allowed, pair_counts, preference_order, random_sentinels, rebuild_row,
-    relay_gap, relay_layer, reroute_fraction, route_recall, run_chain, score_rows, select,
-    selection_gap, SAMPLER_DRAW_CAP,
+    ledger_bytes, mandatory_sentinels, n_allowed, pair_counts, preference_order, query_rows,
+    random_sentinels, rebuild_row, relay_decision, relay_gap, relay_layer, reroute_fraction,
+    route_recall, run_chain, score_rows, select, selection_gap, SAMPLER_DRAW_CAP,
 )

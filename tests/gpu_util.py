@@ -34,7 +34,8 @@ def upload(x: np.ndarray):
 def oracle_cfg(led: rr.Ledger, dtype: str, gamma=0.0, causal=False, seed=0):
     return O.RouteConfig(heads=led.heads, nq=led.nq, nk=led.nk, d=64, k=led.k, m=led.m, r=led.r,
                          gamma=gamma, causal=causal, seed=seed, dtype=dtype, sink=led.sink,
-                         recent=led.recent, min_reuse=led.min_reuse, gamma_extra=led.gamma_extra)
+                         recent=led.recent, min_reuse=led.min_reuse, gamma_extra=led.gamma_extra,
+                         q_rows=led.q_rows, nq_q=led.nq_q)
 
 
 def ledger_np(led: rr.Ledger):
@@ -54,7 +55,7 @@ def set_ledger(led: rr.Ledger, ol: O.Ledger, last_layer: int):
 
 def oracle_scores(cfg: O.RouteConfig, q, k) -> np.ndarray:
     Q, K = O.decode(q, cfg.dtype), O.decode(k, cfg.dtype)
-    return np.stack([O.score_rows(Q[h], K[h]) for h in range(cfg.heads)])
+    return np.stack([O.score_rows(O.query_rows(cfg, Q[h]), K[h]) for h in range(cfg.heads)])
 
 
 def selection_excluded(cfg: O.RouteConfig, S: np.ndarray, tol: float, rows=None) -> np.ndarray:

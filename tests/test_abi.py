@@ -102,6 +102,24 @@ def test_config_check_rejects(kw, status, needle):
     assert needle in rr.rr_last_error()
 
 
+def test_width_bucket_rejects_bad_row_lists():
+    """rr_ledger_create_rows validates its row list on the host before touching the device."""
+    L = rr.lib()
+    h = ctypes.c_void_p(77)
+
+    def create(rows, nq_q, **kw):
+        arr = (ctypes.c_int32 * max(1, len(rows)))(*rows)
+        return L.rr_ledger_create_rows(ctypes.byref(cfg(nq=len(rows), **kw)), arr if rows else None,
+                                       nq_q, ctypes.byref(h))
+    assert create([], 64) == rr.RR_EINVAL                      # NULL list
+    assert create([3, 2, 9], 64) == rr.RR_EINVAL and "ascend" in rr.rr_last_error()
+    assert create([1, 1], 64) == rr.RR_EINVAL                  # not strictly ascending
+    assert create([0, 64], 64) == rr.RR_EINVAL                 # outside [0, nq_q)
+    assert create([0, 5], 1) == rr.RR_EINVAL and "nq_q" in rr.rr_last_error()
+    assert create([0, 5], 64, causal=True, nk=32) == rr.RR_EINVAL and "causal" in rr.rr_last_error()
+    assert h.value is None
+
+
 def test_bad_dtype_and_causal_flag():
     c = cfg()
     c.dtype = 7

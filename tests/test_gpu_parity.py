@@ -230,6 +230,38 @@ def test_chain_preferred_chunks():
     chain_report(rep)
 
 
+# Width buckets (Section 4.4): name, heads, query rows, nk, dtype, causal, narrow and wide (k, m, r)
+BUCKET_CASES = [
+    ("buckets_bf16", 2, 300, 256, "bf16", False, (8, 8, 8), (16, 12, 8)),
+    ("buckets_f32_causal", 2, 200, 200, "f32", True, (4, 4, 6), (12, 12, 8)),
+    ("buckets_ragged", 1, 130, 1100, "bf16", False, (12, 0, 0), (20, 12, 16)),
+]
+
+
+@pytest.mark.parametrize("case", BUCKET_CASES, ids=[c[0] for c in BUCKET_CASES])
+def test_width_buckets(case):
+    """Two width buckets over complementary query-row sets, each with its own k, m, r: both
+    anchor at layer 3 and relay at layer 4 on the full Q, against the oracle bucket (pinned on
+    the CPU to the same rows of a ledger over every row)."""
+    name, H, nq, nk, dtype, causal, narrow, wide = case
+    rng = np.random.default_rng(7)
+    pick = rng.random(nq) < 0.35
+    q0, k0 = inputs("gauss", H, nq, nk, dtype, 51)
+    q1 = synth.perturb(q0, 0.04 / 8, seed=52, dtype=dtype)
+    k1 = synth.perturb(k0, 0.04 / 8, seed=53, dtype=dtype)
+    rel = 1e-5 if dtype == "f32" else 1e-3
+    for rows, (k, m, r) in ((np.flatnonzero(pick), narrow), (np.flatnonzero(~pick), wide)):
+        U.log(f"[bucket] {name} rows={len(rows)} of {nq} k={k} m={m} r={r} {dtype} causal={causal}")
+        led = rr.Ledger(H, nq, nk, 64, k, m, r, 0.0, causal, dtype, 61, q_rows=rows)
+        cfg = U.oracle_cfg(led, dtype, 0.0, causal, 61)
+        rep = U.Report()
+        _, ora = U.anchor_parity(led, cfg, q0, k0, 3, U.GAP_TOL, rep)
+        _, res, _ = U.relay_parity(led, cfg, q1, k1, 4, ora, U.GAP_TOL, rel, rep)
+        U.log(f"   rows={rep.rows} flagged={int(res.flags.sum())} excluded={rep.excluded}")
+        assert rep.excluded <= max(2, rep.rows // 100)
+        led.close()
+
+
 # Hysteresis (Section 3.2, after Eq. 8): min_reuse, gamma_extra
 HYST_CASES = [
     ("hyst_horizon", 1, 0.0),

@@ -11,6 +11,7 @@ Attention", Sections 2.1, 3.1-3.5, 4.1-4.2, 5).  Every function is pinned by
 ``tests/test_oracle_*.py`` against brute force, closed forms, invariants and
 the page's printed tables; see each test's docstring for the pin it provides.
 """
+from .attention import sparse_attention  # noqa: F401
 from .philox import philox4x32_10, philox4x64_10  # noqa: F401
 from .routing import (  # noqa: F401
     Ledger, LayerRecord, RelayResult, RouteConfig, anchor_layer, decode, exact_routes,

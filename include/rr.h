@@ -159,6 +159,25 @@ rr_status rr_ledger_get_refreshed(const rr_ledger* ledger, uint8_t* refreshed, i
 rr_status rr_ledger_set_refreshed(rr_ledger* ledger, const uint8_t* refreshed, int32_t src_is_host,
                                   void* stream);
 
+/* Sparse attention over routed chunks, the routes' consumer (Section 2.1: the selected chunks
+ * are expanded into token indices for a sparse online-softmax kernel; Section 2.2, Eq. 3):
+ * for every query token t of query chunk i, out[t] = softmax(q_t K_R^T / sqrt(64)) V_R, where
+ * R is the set of tokens of the chunks listed in routes[h][i] (chunk j = tokens j*64 ..
+ * j*64+63; entries outside [0, nk) are padding; in causal mode only key tokens s <= t, and
+ * chunks j > i contribute nothing).  A token with no routed key gets 0.
+ *   q      [heads, nq*64, 64] bf16 (raw bits), row-major
+ *   k      [heads, nk*64, 64] bf16
+ *   vt     [heads, nk, 64 (d), 64 (token)] bf16: V of each chunk transposed
+ *   routes [heads, nq, kr] int32, e.g. the route tensor of rr_ledger_get (kr = k)
+ *   out    [heads, nq*64, 64] fp32, written completely
+ * All device memory owned by the caller; asynchronous on `stream`.  Scores and the softmax
+ * are fp32; the probabilities enter the value product rounded to bf16.  Stateless (no
+ * ledger).  Errors: RR_EINVAL for NULL pointers, sizes < 1, causal with nq != nk;
+ * RR_EUNSUPPORTED for chunk_tokens != 64 or kr > 64; RR_EDEVICE if the launch fails. */
+rr_status rr_sparse_attention(const void* q, const void* k, const void* vt, const int32_t* routes,
+                              int32_t heads, int32_t nq, int32_t nk, int32_t kr, int32_t chunk_tokens,
+                              int32_t causal, float* out, void* stream);
+
 /* Per-kernel timing, for measurement.  While profiling is on, every kernel the ledger
  * launches is bracketed by HIP events recorded on its stream (no synchronisation, no device
  * allocation; the events are created on the host as needed, without the system-scope fence

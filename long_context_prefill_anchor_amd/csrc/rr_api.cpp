@@ -470,4 +470,32 @@ rr_status rr_ledger_set_refreshed(rr_ledger* L, const uint8_t* refreshed, int32_
     return ok();
 }
 
+rr_status rr_sparse_attention(const void* q, const void* k, const void* vt, const int32_t* routes,
+                              int32_t heads, int32_t nq, int32_t nk, int32_t kr, int32_t chunk_tokens,
+                              int32_t causal, float* out, void* stream) {
+    if (!q || !k || !vt || !routes || !out) return fail(RR_EINVAL, "q, k, vt, routes and out are required");
+    if (heads < 1 || nq < 1 || nk < 1 || kr < 1)
+        return fail(RR_EINVAL, "heads, nq, nk and kr must be >= 1 (got %d, %d, %d, %d)", heads, nq, nk, kr);
+    if (causal != 0 && causal != 1) return fail(RR_EINVAL, "causal must be 0 or 1");
+    if (causal && nq != nk) return fail(RR_EINVAL, "causal attention needs nq == nk");
+    if (chunk_tokens != 64) return fail(RR_EUNSUPPORTED, "only 64-token chunks are implemented (got %d)", chunk_tokens);
+    if (kr > 64) return fail(RR_EUNSUPPORTED, "kr must be <= 64 (got %d)", kr);
+    if ((int64_t)heads * nq >= (int64_t)1 << 31 || (int64_t)heads * nk * 64 * 64 >= (int64_t)1 << 40)
+        return fail(RR_EINVAL, "problem too large");
+    rr::AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.vt = vt;
+    a.routes = routes;
+    a.out = out;
+    a.H = heads;
+    a.nq = nq;
+    a.nk = nk;
+    a.kr = kr;
+    a.causal = causal;
+    const hipError_t e = rr::launch_sparse_attn(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(RR_EDEVICE, "sparse attention launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

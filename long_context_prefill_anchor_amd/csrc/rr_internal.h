@@ -50,10 +50,21 @@ struct RescoreArgs {
     float gamma_extra;
 };
 
+// Sparse attention over routed chunks (rr_attention.hip).
+struct AttnArgs {
+    const void* q;              // [H, nq*64, 64] bf16
+    const void* k;              // [H, nk*64, 64] bf16
+    const void* vt;             // [H, nk, 64 (d), 64 (token)] bf16
+    const int32_t* routes;      // [H, nq, kr], -1 padded
+    float* out;                 // [H, nq*64, 64]
+    int H, nq, nk, kr, causal;
+};
+
 constexpr int ROUTE_ROWS = 64;   // rows per route block and per rescore block
 
 hipError_t launch_route(const RouteArgs& a, bool bf16, bool causal, bool reroute, hipStream_t st);
 hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st);
 size_t route_lds_bytes(int nk, int c);
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
 
 }  // namespace rr

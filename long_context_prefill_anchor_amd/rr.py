@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "RR_OK", -1: "RR_EINVAL", -2: "RR_EUNSUPPORTED", -3: "RR_ENOM
 ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_create_rows", "rr_ledger_destroy",
                 "rr_anchor_route",
                 "rr_relay_layer", "rr_ledger_get", "rr_ledger_set", "rr_ledger_config",
-                "rr_ledger_get_refreshed", "rr_ledger_set_refreshed", "rr_ledger_profile",
+                "rr_ledger_get_refreshed", "rr_ledger_set_refreshed", "rr_sparse_attention",
+                "rr_ledger_profile",
                 "rr_ledger_kernel_times", "rr_last_error", "rr_abi_version")
 RR_KERNEL_ROUTE, RR_KERNEL_RESCORE, RR_KERNEL_REROUTE, RR_KERNEL_KINDS = 0, 1, 2, 3
 
@@ -66,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.rr_ledger_set.argtypes = [vp, vp, vp, vp, i32, i32, vp]
         L.rr_ledger_config.argtypes = [vp, P(rr_config)]
         L.rr_ledger_get_refreshed.argtypes = [vp, vp, i32, vp]
+        L.rr_sparse_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
         L.rr_ledger_set_refreshed.argtypes = [vp, vp, i32, vp]
         L.rr_ledger_profile.argtypes = [vp, i32]
         L.rr_ledger_kernel_times.argtypes = [vp, P(i32), P(ctypes.c_double)]
@@ -175,6 +177,13 @@ def rr_ledger_get_refreshed(handle, refreshed, dst_is_host: bool, stream=None) -
 def rr_ledger_set_refreshed(handle, refreshed, src_is_host: bool, stream=None) -> None:
     _check(lib().rr_ledger_set_refreshed(handle, _ptr(refreshed), int(bool(src_is_host)), _stream(stream)),
            "rr_ledger_set_refreshed")
+
+
+def rr_sparse_attention(q, k, vt, routes, heads: int, nq: int, nk: int, kr: int, out,
+                        causal: bool = False, chunk_tokens: int = 64, stream=None) -> None:
+    _check(lib().rr_sparse_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(routes), int(heads), int(nq),
+                                     int(nk), int(kr), int(chunk_tokens), int(bool(causal)), _ptr(out),
+                                     _stream(stream)), "rr_sparse_attention")
 
 
 def rr_ledger_profile(handle, enable: bool) -> None:

@@ -284,6 +284,56 @@ def preferred_chunks_sweep(sigmas=(0.01, 0.03, 0.06, 0.1), seeds=10):
     return out
 
 
+def sparse_attention_measure(reps=20):
+    """The routes' consumer (Section 2.1 token expansion, Eq. 3): sparse online-softmax
+    attention of every query token over the tokens of its chunk's route, at the headline
+    shape (32 heads x 1024 chunks of 64 tokens = 65,536 tokens per head, d = 64, bf16), with
+    the routes of an anchor ledger on the workload's first layer and seeded synthetic token
+    Q, K, V drawn on the device.  Reported against both bounds: MFMA flops of the two
+    products, and the bytes a gather moves when nothing is reused (Q, each routed chunk's K and
+    V per query chunk, O)."""
+    import torch
+    w = W.batched_heads().with_(layers=1)
+    H, n, T, d = w.heads, w.n, 64, w.d
+    qs, ks = upload_layers(w)
+    led = rr.Ledger(H, n, n, d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
+    led.anchor(qs[0], ks[0], 0)
+    routes = led.get()[0]
+    torch.cuda.synchronize()
+    g = torch.Generator(device="cuda").manual_seed(2024)
+    qt = (torch.randn((H, n * T, d), generator=g, device="cuda") / 8).to(torch.bfloat16)
+    kt = (torch.randn((H, n * T, d), generator=g, device="cuda") / 8).to(torch.bfloat16)
+    vt = (torch.randn((H, n * T, d), generator=g, device="cuda") / 8).to(torch.bfloat16)
+    vt = vt.view(H, n, T, d).transpose(2, 3).contiguous()
+    out = torch.empty((H, n * T, d), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        rr.rr_sparse_attention(qt, kt, vt, routes, H, n, n, w.k, out)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        rr.rr_sparse_attention(qt, kt, vt, routes, H, n, n, w.k, out)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / reps
+    valid = int((routes >= 0).sum().item())
+    flops = float(valid) * T * T * d * 2 * 2
+    gathered = float(H * n * T * d * 2 + valid * T * d * 2 * 2 + H * n * T * d * 4)
+    unique = float(H * n * T * d * (2 * 3 + 4))
+    ach_f = flops / (us * 1e-6) / 1e12
+    ach_b = gathered / (us * 1e-6) / 1e9
+    led.close()
+    del qs, ks, qt, kt, vt, out
+    torch.cuda.empty_cache()
+    return {"kernel": "k_sparse_attn<false>", "workload": "batched_heads tokens (32 heads x 1024 chunks x 64 tokens)",
+            "chunk_tokens": T, "route_k": w.k, "routed_chunks": valid, "avg_us": round(us, 2), "reps": reps,
+            "mfma": {"flops": flops, "achieved": round(ach_f, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach_f / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "hbm_gathered": {"bytes": gathered, "achieved": round(ach_b, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(ach_b / HBM_PEAK_GBS, 4)},
+            "unique_bytes": unique}
+
+
 class LedgerGroup:
     """Width-bucket ledgers driven as one: each call goes to every bucket in turn."""
 
@@ -456,6 +506,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the side measurements (64-head 4096-chunk causal; fixed-drift sweep; sentinel ablation)")
+    ap.add_argument("--only-attention", action="store_true",
+                    help="measure only the sparse attention over routed chunks and print its JSON")
     ap.add_argument("--calib-copy", action="store_true",
                     help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (counter calibration)")
     args = ap.parse_args()
@@ -471,6 +523,9 @@ def main():
     rr.lib()
     if args.calib_copy:
         calib_copy()
+    if args.only_attention:
+        print(json.dumps({"sparse_attention": sparse_attention_measure()}), flush=True)
+        return
     w = W.batched_heads()
     H, n, d = w.heads, w.n, w.d
     log(f"[bench] generating + uploading {w.layers} layers of {H}x{n}x{d} bf16 Q and K")
@@ -569,6 +624,12 @@ def main():
     ablation = None if args.no_secondary else sentinel_ablation()
     preferred = None if args.no_secondary else preferred_chunks_sweep()
     buckets = None if args.no_secondary else width_buckets()
+    attention = None
+    if not args.no_secondary:
+        log("[bench] sparse attention over the routes (token expansion, Eq. 3)")
+        attention = sparse_attention_measure()
+        attention["routing_relay_layer_us"] = round(relay_layer_us, 2)
+        attention["routing_share_of_layer"] = round(relay_layer_us / (relay_layer_us + attention["avg_us"]), 4)
     # Hysteresis (Section 3.2): a one-layer reuse horizon after each relay refresh, alone and
     # with a post-refresh guard of 0.005, on the headline chain.
     hysteresis = None
@@ -631,6 +692,7 @@ def main():
         "preferred_chunks": preferred,
         "hysteresis": hysteresis,
         "width_buckets": buckets,
+        "sparse_attention": attention,
     }
     print(json.dumps(out), flush=True)
 

@@ -30,7 +30,6 @@ namespace rr {
 namespace {
 
 typedef float f32x16a __attribute__((ext_vector_type(16)));
-typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int AT = 64;                 // tokens per chunk
 constexpr int AW = 2;                  // waves per block (32 query tokens each)
@@ -40,12 +39,8 @@ struct Half {                          // one 32-key half of a routed chunk, in 
     bf16x8 v[2][2];                    // A operand of O^T: [d tile][k-step]
 };
 
-__device__ __forceinline__ bf16x8 pack8(u16x4 a, u16x4 b) {
-    u32x4 w;
-    w[0] = (uint32_t)a[0] | ((uint32_t)a[1] << 16);
-    w[1] = (uint32_t)a[2] | ((uint32_t)a[3] << 16);
-    w[2] = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
-    w[3] = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
+__device__ __forceinline__ bf16x8 pack8(uint2 a, uint2 b) {     // four bf16 from each run
+    u32x4 w = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(bf16x8, w);
 }
 
@@ -64,8 +59,8 @@ __device__ __forceinline__ void load_half(Half& hf, const uint16_t* Kh, const ui
         const uint16_t* vrow = vbase + (size_t)(32 * g + (lane & 31)) * AT + 32 * half + 4 * sub;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const u16x4 a = *reinterpret_cast<const u16x4*>(vrow + 16 * u);
-            const u16x4 b = *reinterpret_cast<const u16x4*>(vrow + 16 * u + 8);
+            const uint2 a = *reinterpret_cast<const uint2*>(vrow + 16 * u);
+            const uint2 b = *reinterpret_cast<const uint2*>(vrow + 16 * u + 8);
             hf.v[g][u] = pack8(a, b);
         }
     }
@@ -88,7 +83,7 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {   // round to nearest e
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(64 * AW) void k_sparse_attn(AttnArgs p) {
+__global__ __launch_bounds__(64 * AW) __attribute__((amdgpu_waves_per_eu(3))) void k_sparse_attn(AttnArgs p) {
     const int blk = blockIdx.x;
     const int h = blk / p.nq;
     const int i = blk % p.nq;
@@ -109,77 +104,72 @@ __global__ __launch_bounds__(64 * AW) void k_sparse_attn(AttnArgs p) {
         for (int s = 0; s < 4; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * sub);
     }
 
-    // Work list: the valid routed chunks (uniform over the block), two halves each.
+    // The routed chunks are walked in route order (uniform over the block), two 32-key halves
+    // each; half buffers A (first half) and B (second half) alternate so that each load is
+    // issued one half ahead of its use and nothing is copied between registers.
     const float scale = 0.125f * 1.4426950408889634f;    // 1/sqrt(64) * log2(e): exp2 below
     f32x16a o0 = f32x16a{}, o1 = f32x16a{};              // O^T, d 0-31 and 32-63
     float mrun = -INFINITY, lrun = 0.f;
-    int nj = 0;
-    int next = -1;
-    // Find the first valid chunk.
-    for (; nj < p.kr; ++nj) {
-        const int c = route[nj];
-        if (c >= 0 && c < p.nk && (!CAUSAL || c <= i)) { next = c; break; }
-    }
-    Half cur, nxt;
-    if (next >= 0) load_half(cur, Kh, Vth, next, 0, lane);
-    while (next >= 0) {
-        const int chunk = next;
-        for (int half = 0; half < 2; ++half) {
-            // Prefetch the next half (this chunk's second half, else the next valid chunk's first).
-            int pchunk = chunk, phalf = 1;
-            if (half == 1) {
-                pchunk = -1;
-                phalf = 0;
-                for (++nj; nj < p.kr; ++nj) {
-                    const int c = route[nj];
-                    if (c >= 0 && c < p.nk && (!CAUSAL || c <= i)) { pchunk = c; break; }
-                }
-            }
-            if (pchunk >= 0) load_half(nxt, Kh, Vth, pchunk, phalf, lane);
-
-            f32x16a s = f32x16a{};
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.k[k4], qb[k4], s, 0, 0, 0);
-            // lane L, register v: key 32*half + 8(v/4) + 4 sub + v%4 of this chunk, query qloc
-            float mt = -INFINITY;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float x = s[v] * scale;
-                if constexpr (CAUSAL) {
-                    const int key = 32 * half + 8 * (v >> 2) + 4 * sub + (v & 3);
-                    if (chunk == i && key > qloc) x = -INFINITY;
-                }
-                s[v] = x;
-                mt = fmaxf(mt, x);
-            }
-            mt = pair_max(mt);
-            const float mnew = fmaxf(mrun, mt);
-            const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-            const float corr = exp2f(mrun - muse);
-            float ls = 0.f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                s[v] = exp2f(s[v] - muse);
-                ls += s[v];
-            }
-            lrun = lrun * corr + pair_sum(ls);
-            mrun = mnew;
-            o0 *= corr;
-            o1 *= corr;
-            // B operand of O^T, k-step u: slots t = 0..7 are registers 8u + t.
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                u32x4 w;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    w[t] = bf16_bits(s[8 * u + 2 * t]) | (bf16_bits(s[8 * u + 2 * t + 1]) << 16);
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
-                o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[0][u], pb, o0, 0, 0, 0);
-                o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[1][u], pb, o1, 0, 0, 0);
-            }
-            if (pchunk >= 0) cur = nxt;
-            if (half == 1) next = pchunk;
+    auto next_valid = [&](int from) {
+        for (int j = from; j < p.kr; ++j) {
+            const int c = route[j];
+            if (c >= 0 && c < p.nk && (!CAUSAL || c <= i)) return j;
         }
+        return -1;
+    };
+    // One half: S^T = K_half Q^T, online-softmax update, O^T += V_half^T P^T.
+    auto process = [&](const Half& hf, int chunk, int half) {
+        f32x16a s = f32x16a{};
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf.k[k4], qb[k4], s, 0, 0, 0);
+        // lane L, register v: key 32*half + 8(v/4) + 4 sub + v%4 of this chunk, query qloc
+        float mt = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            float x = s[v] * scale;
+            if constexpr (CAUSAL) {
+                const int key = 32 * half + 8 * (v >> 2) + 4 * sub + (v & 3);
+                if (chunk == i && key > qloc) x = -INFINITY;
+            }
+            s[v] = x;
+            mt = fmaxf(mt, x);
+        }
+        mt = pair_max(mt);
+        const float mnew = fmaxf(mrun, mt);
+        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+        const float corr = exp2f(mrun - muse);
+        float ls = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            s[v] = exp2f(s[v] - muse);
+            ls += s[v];
+        }
+        lrun = lrun * corr + pair_sum(ls);
+        mrun = mnew;
+        o0 *= corr;
+        o1 *= corr;
+        // B operand of O^T, k-step u: slots t = 0..7 are registers 8u + t.
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            u32x4 w;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                w[t] = bf16_bits(s[8 * u + 2 * t]) | (bf16_bits(s[8 * u + 2 * t + 1]) << 16);
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf.v[0][u], pb, o0, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf.v[1][u], pb, o1, 0, 0, 0);
+        }
+    };
+    Half A, B;
+    int j = next_valid(0);
+    if (j >= 0) load_half(A, Kh, Vth, route[j], 0, lane);
+    while (j >= 0) {
+        const int chunk = route[j];
+        load_half(B, Kh, Vth, chunk, 1, lane);
+        process(A, chunk, 0);
+        j = next_valid(j + 1);
+        if (j >= 0) load_half(A, Kh, Vth, route[j], 0, lane);
+        process(B, chunk, 1);
     }
     // O[query][d] = O^T[d][query] / l; lane L holds d = 8(v/4) + 4 sub + v%4 (+32): runs of four.
     const float inv = (lrun > 0.f) ? 1.f / lrun : 0.f;

@@ -120,6 +120,27 @@ def test_width_bucket_rejects_bad_row_lists():
     assert h.value is None
 
 
+def test_sparse_attention_rejects_bad_arguments():
+    """rr_sparse_attention validates on the host: nothing is launched for these."""
+    L = rr.lib()
+    f = L.rr_sparse_attention
+    ok = dict(q=1, k=1, vt=1, routes=1, heads=2, nq=4, nk=4, kr=3, T=64, causal=0, out=1)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["k"], a["vt"], a["routes"], a["heads"], a["nq"], a["nk"], a["kr"], a["T"],
+                 a["causal"], a["out"], None)
+    assert call(q=None) == rr.RR_EINVAL and "required" in rr.rr_last_error()
+    assert call(out=None) == rr.RR_EINVAL
+    assert call(heads=0) == rr.RR_EINVAL
+    assert call(kr=0) == rr.RR_EINVAL
+    assert call(causal=2) == rr.RR_EINVAL
+    assert call(causal=1, nk=5) == rr.RR_EINVAL and "nq == nk" in rr.rr_last_error()
+    assert call(T=128) == rr.RR_EUNSUPPORTED and "64-token" in rr.rr_last_error()
+    assert call(kr=65) == rr.RR_EUNSUPPORTED
+
+
 def test_bad_dtype_and_causal_flag():
     c = cfg()
     c.dtype = 7

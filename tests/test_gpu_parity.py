@@ -235,7 +235,10 @@ BUCKET_CASES = [
     ("buckets_bf16", 2, 300, 256, "bf16", False, (8, 8, 8), (16, 12, 8)),
     ("buckets_f32_causal", 2, 200, 200, "f32", True, (4, 4, 6), (12, 12, 8)),
     ("buckets_ragged", 1, 130, 1100, "bf16", False, (12, 0, 0), (20, 12, 16)),
+    # every option at once: mandatory sentinels and hysteresis inside causal buckets
+    ("buckets_all_options", 2, 180, 180, "bf16", True, (6, 6, 4), (12, 8, 6)),
 ]
+BUCKET_EXTRA = {"buckets_all_options": dict(sink=1, recent=2, min_reuse=1, gamma_extra=0.005)}
 
 
 @pytest.mark.parametrize("case", BUCKET_CASES, ids=[c[0] for c in BUCKET_CASES])
@@ -252,7 +255,8 @@ def test_width_buckets(case):
     rel = 1e-5 if dtype == "f32" else 1e-3
     for rows, (k, m, r) in ((np.flatnonzero(pick), narrow), (np.flatnonzero(~pick), wide)):
         U.log(f"[bucket] {name} rows={len(rows)} of {nq} k={k} m={m} r={r} {dtype} causal={causal}")
-        led = rr.Ledger(H, nq, nk, 64, k, m, r, 0.0, causal, dtype, 61, q_rows=rows)
+        led = rr.Ledger(H, nq, nk, 64, k, m, r, 0.0, causal, dtype, 61, q_rows=rows,
+                        **BUCKET_EXTRA.get(name, {}))
         cfg = U.oracle_cfg(led, dtype, 0.0, causal, 61)
         rep = U.Report()
         _, ora = U.anchor_parity(led, cfg, q0, k0, 3, U.GAP_TOL, rep)
@@ -302,6 +306,14 @@ def test_chain_hysteresis():
     both sides carry their own hysteresis state through the chain."""
     U.log("[chain] drift_sweep sigma=0.03 with min_reuse=1 gamma_extra=0.01")
     rep = run_chain_gpu_vs_oracle(W.drift_sweep(0.03, 0).with_(min_reuse=1, gamma_extra=0.01))
+    chain_report(rep)
+
+
+def test_chain_all_options_causal():
+    """The causal drift-sweep chain with mandatory sentinels and hysteresis together."""
+    U.log("[chain] drift_sweep sigma=0.03 causal, sink=1 recent=1 r=6 min_reuse=1 gamma_extra=0.005")
+    rep = run_chain_gpu_vs_oracle(W.drift_sweep(0.03, 1).with_(causal=True, sink=1, recent=1, r=6,
+                                                               min_reuse=1, gamma_extra=0.005))
     chain_report(rep)
 
 

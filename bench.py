@@ -284,16 +284,17 @@ def preferred_chunks_sweep(sigmas=(0.01, 0.03, 0.06, 0.1), seeds=10):
     return out
 
 
-def sparse_attention_measure(reps=20):
+def sparse_attention_measure(reps=20, causal=False):
     """The routes' consumer (Section 2.1 token expansion, Eq. 3): sparse online-softmax
     attention of every query token over the tokens of its chunk's route, at the headline
-    shape (32 heads x 1024 chunks of 64 tokens = 65,536 tokens per head, d = 64, bf16), with
-    the routes of an anchor ledger on the workload's first layer and seeded synthetic token
-    Q, K, V drawn on the device.  Reported against both bounds: MFMA flops of the two
-    products, and the bytes a gather moves when nothing is reused (Q, each routed chunk's K and
-    V per query chunk, O)."""
+    shape (32 heads x 1024 chunks of 64 tokens = 65,536 tokens per head, d = 64, bf16), or
+    with ``causal`` at the causal workload's shape (64 heads x 4096 chunks = 262,144 tokens
+    per head), with the routes of an anchor ledger on the workload's first layer and seeded
+    synthetic token Q, K, V drawn on the device.  Reported against both bounds: MFMA flops of
+    the two products (causal: of the unmasked pairs), and the bytes a gather moves when
+    nothing is reused (Q, each routed chunk's K and V per query chunk, O)."""
     import torch
-    w = W.batched_heads().with_(layers=1)
+    w = (W.causal_large() if causal else W.batched_heads()).with_(layers=1)
     H, n, T, d = w.heads, w.n, 64, w.d
     qs, ks = upload_layers(w)
     led = rr.Ledger(H, n, n, d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
@@ -307,17 +308,21 @@ def sparse_attention_measure(reps=20):
     vt = vt.view(H, n, T, d).transpose(2, 3).contiguous()
     out = torch.empty((H, n * T, d), dtype=torch.float32, device="cuda")
     for _ in range(3):
-        rr.rr_sparse_attention(qt, kt, vt, routes, H, n, n, w.k, out)
+        rr.rr_sparse_attention(qt, kt, vt, routes, H, n, n, w.k, out, causal=causal)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
     for _ in range(reps):
-        rr.rr_sparse_attention(qt, kt, vt, routes, H, n, n, w.k, out)
+        rr.rr_sparse_attention(qt, kt, vt, routes, H, n, n, w.k, out, causal=causal)
     ev1.record()
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / reps
     valid = int((routes >= 0).sum().item())
-    flops = float(valid) * T * T * d * 2 * 2
+    pairs = float(valid) * T * T
+    if causal:                                   # the diagonal chunk keeps T (T + 1) / 2 pairs
+        own = (routes == torch.arange(n, device=routes.device).view(1, n, 1)).sum().item()
+        pairs -= float(own) * T * (T - 1) / 2
+    flops = pairs * d * 2 * 2
     gathered = float(H * n * T * d * 2 + valid * T * d * 2 * 2 + H * n * T * d * 4)
     unique = float(H * n * T * d * (2 * 3 + 4))
     ach_f = flops / (us * 1e-6) / 1e12
@@ -325,7 +330,8 @@ def sparse_attention_measure(reps=20):
     led.close()
     del qs, ks, qt, kt, vt, out
     torch.cuda.empty_cache()
-    return {"kernel": "k_sparse_attn<false>", "workload": "batched_heads tokens (32 heads x 1024 chunks x 64 tokens)",
+    return {"kernel": f"k_sparse_attn<{str(causal).lower()}>",
+            "workload": f"{w.name} tokens ({H} heads x {n} chunks x {T} tokens)",
             "chunk_tokens": T, "route_k": w.k, "routed_chunks": valid, "avg_us": round(us, 2), "reps": reps,
             "mfma": {"flops": flops, "achieved": round(ach_f, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach_f / MFMA_BF16_PEAK_TFLOPS, 4)},
@@ -624,12 +630,18 @@ def main():
     ablation = None if args.no_secondary else sentinel_ablation()
     preferred = None if args.no_secondary else preferred_chunks_sweep()
     buckets = None if args.no_secondary else width_buckets()
-    attention = None
+    attention, attention_causal = None, None
     if not args.no_secondary:
         log("[bench] sparse attention over the routes (token expansion, Eq. 3)")
         attention = sparse_attention_measure()
         attention["routing_relay_layer_us"] = round(relay_layer_us, 2)
         attention["routing_share_of_layer"] = round(relay_layer_us / (relay_layer_us + attention["avg_us"]), 4)
+        log("[bench] causal sparse attention at the 64 x 4096 shape")
+        attention_causal = sparse_attention_measure(reps=5, causal=True)
+        if secondary is not None:
+            attention_causal["routing_relay_layer_us"] = secondary["relay_layer_us_median"]
+            attention_causal["routing_share_of_layer"] = round(
+                secondary["relay_layer_us_median"] / (secondary["relay_layer_us_median"] + attention_causal["avg_us"]), 4)
     # Hysteresis (Section 3.2): a one-layer reuse horizon after each relay refresh, alone and
     # with a post-refresh guard of 0.005, on the headline chain.
     hysteresis = None
@@ -693,6 +705,7 @@ def main():
         "hysteresis": hysteresis,
         "width_buckets": buckets,
         "sparse_attention": attention,
+        "sparse_attention_causal": attention_causal,
     }
     print(json.dumps(out), flush=True)
 

@@ -209,8 +209,46 @@ __device__ __forceinline__ void merge16_into_top(uint64_t (&top)[TOPW], const ui
 // Sort the lane's buffered (score bits, index) pairs and merge them into its top list.
 // `fresh`: every lane's list is still empty, so the first sorted chunk is copied in.
 // buf: slot-major, scores at buf[j * ROWS], their key indices BUF_IDX words further on.
+// A last chunk of at most 8 (common once the threshold is tight) takes an 8-key network and
+// merges through the same 32-key cascade: the slots past 8 would only add empty keys.
+__device__ __forceinline__ void drain8(uint64_t (&top)[TOPW], const uint32_t* buf, int c0, int cnt, bool& fresh) {
+    uint64_t x[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        if (c0 + s < cnt) {
+            const uint32_t* e = buf + (c0 + s) * ROWS;
+            x[s] = make_key(__uint_as_float(e[0]), e[BUF_IDX]);
+        } else {
+            x[s] = EMPTY_KEY;
+        }
+    }
+    sort_desc<8>(x);
+    if (fresh) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) top[s] = x[s];
+        fresh = false;
+        return;
+    }
+    // max(top[i], x'[31 - i]) with x' = x followed by empty keys: only the last 8 change.
+#pragma unroll
+    for (int i = 24; i < 32; ++i) {
+        const uint64_t c = x[31 - i];
+        top[i] = c > top[i] ? c : top[i];
+    }
+#pragma unroll
+    for (int s = 16; s >= 1; s >>= 1) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            if ((i & s) == 0) ce_desc(top[i], top[i + s]);
+    }
+}
+
 __device__ __forceinline__ void drain(uint64_t (&top)[TOPW], const uint32_t* buf, int cnt, bool& fresh) {
     const int maxc = wave_max_i(cnt);
+    if (maxc <= 8) {                                                  // uniform
+        if (maxc > 0) drain8(top, buf, 0, cnt, fresh);
+        return;
+    }
     for (int c0 = 0; c0 < maxc; c0 += 16) {
         uint64_t x[16];
 #pragma unroll

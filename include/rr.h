@@ -84,7 +84,8 @@ typedef struct {
                          * passes once; finite and >= 0 (0 and min_reuse 0: plain Eq. 8)      */
 } rr_config;
 /* c = k + m + sink + recent + r ledger IDs per row.  Limits (RR_EUNSUPPORTED beyond them):
- * d == 64, k + m <= 32, r <= 32, sink + recent <= 32, c <= 64, nk <= 4096, nq <= 65536;
+ * d == 64, k + m <= 64 (k + m > 32 only with nk <= 1024), r <= 32, sink + recent <= 32,
+ * c <= 64, nk <= 4096, nq <= 65536;
  * heads * nq < 2^31 (RR_EINVAL).  A row with fewer allowed chunks than c gets shorter
  * segments, padded with -1. */
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librr.so")
-SOURCES = ["rr_api.cpp", "rr_kernels.hip", "rr_attention.hip"]
+SOURCES = ["rr_api.cpp", "rr_kernels.hip", "rr_attention.hip", "rr_wide.hip"]
 ARCH = os.environ.get("RR_OFFLOAD_ARCH", "gfx950")
 
 

@@ -73,7 +73,9 @@ rr_status check_cfg(const rr_config* c, bool bucket) {
     if ((int64_t)c->heads * c->nq >= (int64_t)1 << 31 || (int64_t)c->heads * c->nk * 64 >= (int64_t)1 << 40)
         return fail(RR_EINVAL, "problem too large");
     if (c->d != 64) return fail(RR_EUNSUPPORTED, "only d = 64 is implemented (got %d)", c->d);
-    if (c->k + c->m > 32) return fail(RR_EUNSUPPORTED, "k + m must be <= 32 (got %d)", c->k + c->m);
+    if (c->k + c->m > 64) return fail(RR_EUNSUPPORTED, "k + m must be <= 64 (got %d)", c->k + c->m);
+    if (c->k + c->m > 32 && c->nk > 1024)
+        return fail(RR_EUNSUPPORTED, "k + m > 32 needs nk <= 1024 (got k + m = %d, nk = %d)", c->k + c->m, c->nk);
     if (c->r > 32) return fail(RR_EUNSUPPORTED, "r must be <= 32 (got %d)", c->r);
     if (c->sink < 0 || c->recent < 0)
         return fail(RR_EINVAL, "need sink >= 0, recent >= 0 (got %d, %d)", c->sink, c->recent);
@@ -335,7 +337,9 @@ rr_status rr_anchor_route(rr_ledger* L, const void* q, const void* k, int32_t la
     rr::RouteArgs a = route_args(L, q, k, layer);
     a.refresh_mark = 0;
     const int tix = time_begin(L, RR_KERNEL_ROUTE, st);
-    const hipError_t e = rr::launch_route(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, false, st);
+    // Near-miss sets past the main kernel's 32-entry lists go to the one-wave-per-row kernel.
+    const hipError_t e = L->sel > 32 ? rr::launch_route_wide(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, false, st)
+                                     : rr::launch_route(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, false, st);
     time_end(L, tix, st);
     if (e != hipSuccess) return hip_fail(L, e, "anchor route launch");
     L->anchored = true;
@@ -393,7 +397,8 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
     a.out_head_counts = out ? out->head_counts : nullptr;
     a.out_n_rows = out ? out->n_rows : nullptr;
     tix = time_begin(L, RR_KERNEL_REROUTE, st);
-    e = rr::launch_route(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, true, st);
+    e = L->sel > 32 ? rr::launch_route_wide(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, true, st)
+                    : rr::launch_route(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, true, st);
     time_end(L, tix, st);
     if (e != hipSuccess) return hip_fail(L, e, "reroute launch");
     L->last_layer = layer;

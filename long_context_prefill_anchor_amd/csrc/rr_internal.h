@@ -66,5 +66,7 @@ hipError_t launch_route(const RouteArgs& a, bool bf16, bool causal, bool reroute
 hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st);
 size_t route_lds_bytes(int nk, int c);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
+// k + m > 32 (rr_wide.hip): one wave per row, same ledger rules; nk <= 1024.
+hipError_t launch_route_wide(const RouteArgs& a, bool bf16, bool causal, bool reroute, hipStream_t st);
 
 }  // namespace rr

@@ -86,7 +86,8 @@ def test_config_struct_layout_matches_the_header(tmp_path):
     (dict(gamma=float("nan")), rr.RR_EINVAL, "gamma"),
     (dict(causal=True, nk=32), rr.RR_EINVAL, "causal"),
     (dict(d=128), rr.RR_EUNSUPPORTED, "d = 64"),
-    (dict(k=20, m=13), rr.RR_EUNSUPPORTED, "k + m"),
+    (dict(k=20, m=45), rr.RR_EUNSUPPORTED, "k + m"),
+    (dict(k=20, m=13, r=4, nk=2048), rr.RR_EUNSUPPORTED, "nk <= 1024"),
     (dict(r=33), rr.RR_EUNSUPPORTED, "r must"),
     (dict(nk=8192), rr.RR_EUNSUPPORTED, "nk"),
     (dict(sink=-1), rr.RR_EINVAL, "sink >= 0"),

@@ -266,6 +266,78 @@ def test_width_buckets(case):
         led.close()
 
 
+# Near-miss sets past 32 entries (Table 3's 24-wide row and beyond): the one-wave-per-row kernel.
+# name, heads, nq, nk, k, m, r, sink, recent, dtype, causal, seed, input kind
+WIDE_ANCHOR_CASES = [
+    ("wide_nm24_f32", 1, 64, 256, 12, 24, 12, 0, 0, "f32", False, 30, "gauss"),
+    ("wide_nm40_bf16", 2, 100, 300, 16, 40, 8, 0, 0, "bf16", False, 31, "gauss"),
+    ("wide_causal_bf16", 2, 150, 150, 12, 24, 12, 0, 0, "bf16", True, 32, "gauss"),
+    ("wide_mandatory", 1, 70, 200, 12, 30, 10, 2, 2, "f32", False, 33, "gauss"),
+    ("wide_int_ties", 1, 96, 128, 12, 24, 12, 0, 0, "f32", False, 34, "int"),
+    ("wide_short_rows", 1, 40, 30, 12, 24, 12, 1, 1, "f32", False, 35, "gauss"),
+    ("wide_nk1024", 1, 64, 1024, 12, 48, 4, 0, 0, "bf16", False, 36, "gauss"),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_ANCHOR_CASES, ids=[c[0] for c in WIDE_ANCHOR_CASES])
+def test_anchor_parity_wide(case):
+    name, H, nq, nk, k, m, r, sink, recent, dtype, causal, seed, kind = case
+    U.log(f"[anchor wide] {name} H={H} nq={nq} nk={nk} k={k} m={m} r={r} sink={sink} recent={recent} "
+          f"{dtype} causal={causal}")
+    led, cfg = make(H, nq, nk, k, m, r, dtype, causal, seed, sink=sink, recent=recent)
+    q, kk = inputs(kind, H, nq, nk, dtype, seed)
+    tol = 0.0 if kind != "gauss" else U.GAP_TOL
+    rep = U.Report()
+    U.anchor_parity(led, cfg, q, kk, 3, tol, rep)
+    U.log(f"   rows={rep.rows} excluded={rep.excluded}")
+    if kind != "gauss":
+        assert rep.excluded == 0
+    # Gaps between neighbouring ranks shrink deeper in the order (rank k + m = 56 of 300 keys
+    # sits ~1e-3 from its neighbour): a few rows more fall under the 1e-5 exclusion rule.
+    assert rep.excluded <= max(2, rep.rows // 20)
+    led.close()
+
+
+WIDE_RELAY_CASES = [
+    ("wide_relay_f32", 2, 128, 256, 12, 24, 12, 0, 0, "f32", False, 0.05, "gauss"),
+    ("wide_relay_causal", 1, 160, 160, 12, 36, 8, 1, 2, "bf16", True, 0.04, "gauss"),
+    ("wide_relay_int", 1, 128, 200, 12, 24, 12, 0, 0, "f32", False, 0.0, "int"),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_RELAY_CASES, ids=[c[0] for c in WIDE_RELAY_CASES])
+def test_relay_lockstep_wide(case):
+    name, H, nq, nk, k, m, r, sink, recent, dtype, causal, drift, kind = case
+    U.log(f"[relay wide] {name} H={H} nq={nq} nk={nk} k={k} m={m} r={r} {dtype} causal={causal}")
+    led, cfg = make(H, nq, nk, k, m, r, dtype, causal, 21, 0.0, sink=sink, recent=recent)
+    q0, k0 = inputs(kind, H, nq, nk, dtype, 31)
+    if kind == "int":
+        qn, kn = inputs(kind, H, nq, nk, dtype, 32)
+        q1, k1 = q0.copy(), k0.copy()
+        q1[:, 1::4] = qn[:, 1::4]
+        k1[:, ::9] = kn[:, ::9]
+    else:
+        q1 = synth.perturb(q0, drift / 8, seed=41, dtype=dtype)
+        k1 = synth.perturb(k0, drift / 8, seed=42, dtype=dtype)
+    ora0 = O.anchor_layer(cfg, q0, k0, 4)
+    tol = 0.0 if kind != "gauss" else U.GAP_TOL
+    rel = 1e-5 if dtype == "f32" else 1e-3
+    rep = U.Report()
+    gpu, res, ex = U.relay_parity(led, cfg, q1, k1, 5, ora0, tol, rel, rep)
+    nflag = int(res.flags.sum())
+    U.log(f"   rows={rep.rows} flagged={nflag} excluded={rep.excluded}")
+    assert 0 < nflag < H * nq
+    led.close()
+
+
+def test_chain_wide_near_miss():
+    """Table 3's 24-wide near-miss mix on its setting (256 chunks, fp32, drift 0.003, 24 layers)."""
+    U.log("[chain] sentinel ablation setting with 24 near-miss + 12 random")
+    rep = run_chain_gpu_vs_oracle(W.drift_sweep(0.003, 0).with_(layers=24, anchors=W.stride_anchors(24, 8),
+                                                                m=24, r=12))
+    chain_report(rep)
+
+
 # Hysteresis (Section 3.2, after Eq. 8): min_reuse, gamma_extra
 HYST_CASES = [
     ("hyst_horizon", 1, 0.0),

@@ -225,15 +225,17 @@ def drift_sweep_batched(sigmas=(0.01, 0.03, 0.06), steps=2, warmup=1):
 def sentinel_ablation(seeds=5):
     """Sentinel mixes on the pages' ablation setting (1 x 256 chunks, fp32, 24 layers, drift
     0.003, k = 12; anchors every 8 layers, as in the other chains): mean recall against full
-    routing, rerouted fraction and score-pair fraction over the seeds.  Widths beyond
-    k + m = 32 (24 or 48 near-miss) are outside this library's limits and are not run.  The
+    routing, rerouted fraction and score-pair fraction over the seeds.  The 24-wide near-miss
+    row runs on the one-wave-per-row kernel (k + m = 36); the 48-wide row needs c = 72 ledger
+    entries, past this library's 64, so 40 near-miss + 12 random (c = 64) stands nearest.  The
     last mix trades three random sentinels for the mandatory kind (Section 3.1, item 3: one
     sink chunk, two recent chunks); the synthetic walk gives those chunks no special role,
     and a pair count of c per row is an upper bound when one of them is already routed."""
     import torch
     mixes = [("random only", 0, 12, 0, 0), ("near-miss only", 12, 0, 0, 0),
              ("12 near-miss + 12 random", 12, 12, 0, 0), ("12 near-miss + 8 random", 12, 8, 0, 0),
-             ("12 near-miss + 1 sink + 2 recent + 5 random", 12, 5, 1, 2)]
+             ("12 near-miss + 1 sink + 2 recent + 5 random", 12, 5, 1, 2),
+             ("24 near-miss + 12 random", 24, 12, 0, 0), ("40 near-miss + 12 random", 40, 12, 0, 0)]
     out = []
     for name, m, r, sink, recent in mixes:
         acc = np.zeros(3)
@@ -630,6 +632,10 @@ def main():
     ablation = None if args.no_secondary else sentinel_ablation()
     preferred = None if args.no_secondary else preferred_chunks_sweep()
     buckets = None if args.no_secondary else width_buckets()
+    wide = None
+    if not args.no_secondary:
+        log("[bench] batched heads with a 24-wide near-miss set (k + m = 36: one-wave-per-row kernel)")
+        wide = relay_vs_full(W.batched_heads().with_(name="batched_heads_nm24", m=24, r=8), steps=2, warmup=1)
     attention, attention_causal = None, None
     if not args.no_secondary:
         log("[bench] sparse attention over the routes (token expansion, Eq. 3)")
@@ -704,6 +710,7 @@ def main():
         "preferred_chunks": preferred,
         "hysteresis": hysteresis,
         "width_buckets": buckets,
+        "wide_near_miss": wide,
         "sparse_attention": attention,
         "sparse_attention_causal": attention_causal,
     }

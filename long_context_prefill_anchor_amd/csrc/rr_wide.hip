@@ -31,11 +31,14 @@ constexpr int WW = 4;                  // waves (rows) per block
 constexpr int WKT = 16;                // keys per lane: nk <= 1024
 constexpr int WBM = 1024 / 32 + 1;     // bitmap words per row
 
-__device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }   // bf16 bits
-__device__ __forceinline__ float widen(float f) { return f; }
+// Element e of a 16-byte load: eight bf16 (raw bits) or four fp32 values.
+__device__ __forceinline__ float elem_of(const u32x4& w, int e, const uint16_t*) {
+    const uint32_t word = w[e >> 1];
+    return __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
+}
+__device__ __forceinline__ float elem_of(const u32x4& w, int e, const float*) { return __uint_as_float(w[e]); }
 
 struct WideShared {
-    float q[WW][64];
     uint64_t list[WW][64];
     uint32_t bm[WW][WBM];
     int32_t stage[WW][65];
@@ -85,8 +88,13 @@ __global__ __launch_bounds__(64 * WW) void k_route_wide(RouteArgs p) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int per_head = (p.nq + WW - 1) / WW;
-    const int h = blockIdx.x / per_head;
-    const int row = (blockIdx.x % per_head) * WW + wave;
+    // Workgroups go to the 8 XCDs round-robin; renumber so that each XCD runs a contiguous
+    // range of blocks, i.e. whole heads, whose key rows then stay in that XCD's L2.
+    const int per_xcd = (int)gridDim.x / 8;
+    const int lb = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+    if (lb >= p.H * per_head) return;                     // grid padding
+    const int h = lb / per_head;
+    const int row = (lb % per_head) * WW + wave;
     if (row >= p.nq) return;                              // whole wave; no block barriers below
     const size_t flat = (size_t)h * p.nq + row;
     if constexpr (REROUTE) {
@@ -96,8 +104,16 @@ __global__ __launch_bounds__(64 * WW) void k_route_wide(RouteArgs p) {
     const int n = CAUSAL ? qrow + 1 : p.nk;
 
     // ---------------------------------------------------------------- scores and keys
+    // The query row in registers; each key row read with 16-byte loads.
     const E* qv = reinterpret_cast<const E*>(p.qp) + ((size_t)h * p.nq_q + qrow) * 64;
-    sh.q[wave][lane] = widen(qv[lane]);
+    constexpr int PER = 16 / sizeof(E);                   // elements per 16-byte load
+    float qf[64];
+#pragma unroll
+    for (int c = 0; c < 64 / PER; ++c) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(qv + PER * c);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) qf[PER * c + e] = elem_of(w, e, (const E*)nullptr);
+    }
     const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
     uint64_t key[WKT];
 #pragma unroll
@@ -107,8 +123,12 @@ __global__ __launch_bounds__(64 * WW) void k_route_wide(RouteArgs p) {
         if (j < n) {
             const E* kr = Kh + (size_t)j * 64;
             float acc = 0.f;
-#pragma unroll 16
-            for (int d = 0; d < 64; ++d) acc = fmaf(sh.q[wave][d], widen(kr[d]), acc);
+#pragma unroll
+            for (int c = 0; c < 64 / PER; ++c) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(kr + PER * c);
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc = fmaf(qf[PER * c + e], elem_of(w, e, (const E*)nullptr), acc);
+            }
             key[t] = make_key(acc, (uint32_t)j);
         }
     }
@@ -251,7 +271,8 @@ __global__ __launch_bounds__(64) void k_wide_outputs(RouteArgs p) {
 template <typename E, bool CAUSAL, bool REROUTE>
 hipError_t launch_wide_t(const RouteArgs& a, hipStream_t st) {
     const int per_head = (a.nq + WW - 1) / WW;
-    hipLaunchKernelGGL((k_route_wide<E, CAUSAL, REROUTE>), dim3((unsigned)(a.H * per_head)), dim3(64 * WW), 0, st, a);
+    const unsigned blocks = (unsigned)((a.H * per_head + 7) / 8 * 8);      // a multiple of the 8 XCDs
+    hipLaunchKernelGGL((k_route_wide<E, CAUSAL, REROUTE>), dim3(blocks), dim3(64 * WW), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && REROUTE && (a.out_rows || a.out_head_counts || a.out_n_rows)) {
         hipLaunchKernelGGL(k_wide_outputs, dim3((unsigned)a.H), dim3(64), 0, st, a);

@@ -1,22 +1,30 @@
 // Routing with near-miss sets wider than the main route kernel's 32-entry lists
-// (32 < k + m <= 64): one wave per query row.
+// (32 < k + m <= 64): MFMA scores into LDS, then one wave per query row for the selection.
 //
 // "RouteRelay: Event-Triggered Cross-Layer Route Reuse for Efficient Dynamic Sparse
 // Attention", Section 2.1 Eq. 1-2 (scores, top-k route), Section 3.1 items 1-3 (near-miss,
 // random and mandatory sentinels, Eq. 4 ledger), Sections 4.1-4.2 (reroute of flagged rows);
 // Table 3 evaluates 24- and 48-wide near-miss sets.
 //
-// Per row, in one wave: each lane scores the keys lane, lane + 64, ... (fp32 dot products of
-// the row's query, held in LDS, with the key rows); an exact radix select over the 64-bit keys
-// (orderable score, then lower index first) finds the (k+m)-th largest; the keys at or above
-// it are compacted and sorted across lanes with a bitonic network, so lane r holds rank r.
-// Route = ranks below k, near-miss = the next m.  The ledger row is then written with the same
+// A block takes 16 consecutive query rows of one head.  Its eight waves first score the rows
+// against every key with v_mfma_f32_16x16x32_bf16 (fp32 inputs: v_mfma_f32_16x16x4f32), 16
+// keys per tile and tiles dealt round-robin to the waves, into an LDS table of orderable fp32
+// scores (0 = no key).  Each row then goes to one wave, which finds its exact top-(k+m) over
+// the 64-bit keys (orderable score, then lower index first): lane l holds keys l, l + 64, ...;
+// the (k+m)-th largest of the 64 lane maxima is a lower bound of the (k+m)-th largest key, so
+// the keys at or above it (at least k+m of them, at most 64 in the common case) are compacted
+// and sorted across lanes with a bitonic network, leaving rank r in lane r; when more than 64
+// keys pass the bound, an exact radix select over the 64-bit keys finds the threshold instead.
+// Route and near-miss are put in index order by a second lane sort.  Lane exchanges are DPP
+// moves and the 16- and 32-lane swaps, so the sorts stay in the VALU.
+// Route = the k largest, near-miss = the next m.  The ledger row is then written with the same
 // rules as the main kernel: segments ascending by index, mandatory sink / recent chunks not
 // already routed, random draws from Philox4x32-10 (counter = (t div 4, query row, layer,
 // head)) accepted in draw order when the chunk is still in the pool, a fill with the
 // lowest-index free chunks when the pool is not larger than r or the draw cap is reached.
-// The kernel keeps no threshold state, so anchor and reroute use it alike; a reroute wave
-// returns at once for a row the rescore kernel did not flag.
+// The kernel keeps no threshold state, so anchor and reroute use it alike; in a reroute a
+// block scores its rows only if the rescore kernel flagged one of them and writes only the
+// flagged ones.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,143 +35,140 @@ namespace rr {
 
 namespace {
 
-constexpr int WW = 4;                  // waves (rows) per block
-constexpr int WKT = 16;                // keys per lane: nk <= 1024
+constexpr int WR = 16;                 // query rows per block (the MFMA's row count)
+constexpr int WWAVES = 8;              // waves per block
+constexpr int WKT = 16;                // keys per lane in the selection: nk <= 1024
 constexpr int WBM = 1024 / 32 + 1;     // bitmap words per row
-
-// Element e of a 16-byte load: eight bf16 (raw bits) or four fp32 values.
-__device__ __forceinline__ float elem_of(const u32x4& w, int e, const uint16_t*) {
-    const uint32_t word = w[e >> 1];
-    return __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
-}
-__device__ __forceinline__ float elem_of(const u32x4& w, int e, const float*) { return __uint_as_float(w[e]); }
+constexpr int SST = 1024 + 4;          // u32 row stride of the score table (the pad spreads the
+                                       // four 4-row groups of an MFMA result over the banks)
 
 struct WideShared {
-    uint64_t list[WW][64];
-    uint32_t bm[WW][WBM];
-    int32_t stage[WW][65];
+    uint32_t s[WR][SST];               // orderable scores of the block's rows; 0 = no key
+    uint64_t list[WWAVES][64];         // candidate keys, then the row's random draws (u32)
+    uint32_t bm[WWAVES][WBM];          // chunks already in the row's ledger
+    int32_t stage[WWAVES][65];         // the row's ledger entries before the copy out
 };
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    const int lo = __shfl_xor((int)(uint32_t)v, m);
-    const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+// The value of lane (lane ^ J), all in the VALU: quad permutes for J = 1, 2; a row shift each
+// way for J = 4; a row rotation for J = 8; the 16- and 32-lane swaps for J = 16, 32 (the swap of
+// a register with itself returns the own value in one result and the partner's in the other).
+template <int J> __device__ __forceinline__ uint32_t xor_lane(uint32_t v, int lane) {
+    if constexpr (J == 1) return (uint32_t)dpp_i<0xB1>((int)v);               // quad_perm [1,0,3,2]
+    else if constexpr (J == 2) return (uint32_t)dpp_i<0x4E>((int)v);          // quad_perm [2,3,0,1]
+    else if constexpr (J == 4) {
+        const uint32_t up = (uint32_t)dpp_i<0x104>((int)v);                    // row_shl:4, lane i <- i + 4
+        const uint32_t dn = (uint32_t)dpp_i<0x114>((int)v);                    // row_shr:4, lane i <- i - 4
+        return (lane & 4) ? dn : up;
+    } else if constexpr (J == 8) return (uint32_t)dpp_i<0x128>((int)v);       // row_ror:8
+    else if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (r[0] == v) ? r[1] : r[0];
+    } else {
+        static_assert(J == 32, "lane distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (r[0] == v) ? r[1] : r[0];
+    }
+}
+template <int J> __device__ __forceinline__ uint64_t xor_lane(uint64_t v, int lane) {
+    const uint32_t lo = xor_lane<J>((uint32_t)v, lane);
+    const uint32_t hi = xor_lane<J>((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
 }
 
-// Bitonic sort across the 64 lanes, one value per lane: descending (u64) or ascending (u32).
-__device__ __forceinline__ uint64_t lane_sort_desc_u64(uint64_t v, int lane) {
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t o = shfl_xor_u64(v, j);
-            const bool keep_max = (((lane & k) == 0) == ((lane & j) == 0));
-            v = keep_max ? (v > o ? v : o) : (v > o ? o : v);
-        }
-    }
+// Bitonic sort across the 64 lanes, one value per lane, ascending or descending.
+template <int K, int J, bool DESC, typename T> __device__ __forceinline__ T bitonic_merge(T v, int lane) {
+    const T o = xor_lane<J>(v, lane);
+    const bool low = ((lane & K) == 0) == ((lane & J) == 0);   // keeps the smaller one (ascending)
+    v = (low != DESC) ? (v < o ? v : o) : (v < o ? o : v);
+    if constexpr (J > 1) v = bitonic_merge<K, J / 2, DESC>(v, lane);
     return v;
 }
-
-__device__ __forceinline__ uint32_t lane_sort_asc_u32(uint32_t v, int lane) {
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint32_t o = (uint32_t)__shfl_xor((int)v, j);
-            const bool keep_min = (((lane & k) == 0) == ((lane & j) == 0));
-            v = keep_min ? min(v, o) : max(v, o);
-        }
-    }
-    return v;
+template <int K, bool DESC, typename T> __device__ __forceinline__ T bitonic_sort(T v, int lane) {
+    if constexpr (K > 2) v = bitonic_sort<K / 2, DESC>(v, lane);
+    return bitonic_merge<K, K / 2, DESC>(v, lane);
 }
+__device__ __forceinline__ uint64_t lane_sort_desc_u64(uint64_t v, int lane) { return bitonic_sort<64, true>(v, lane); }
+__device__ __forceinline__ uint32_t lane_sort_asc_u32(uint32_t v, int lane) { return bitonic_sort<64, false>(v, lane); }
 
 __device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {
     return __popcll(mask & ((1ull << lane) - 1ull));
 }
 
-// E: uint16_t (bf16 bits) or float.
-template <typename E, bool CAUSAL, bool REROUTE>
-__global__ __launch_bounds__(64 * WW) void k_route_wide(RouteArgs p) {
-    __shared__ WideShared sh;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int per_head = (p.nq + WW - 1) / WW;
-    // Workgroups go to the 8 XCDs round-robin; renumber so that each XCD runs a contiguous
-    // range of blocks, i.e. whole heads, whose key rows then stay in that XCD's L2.
-    const int per_xcd = (int)gridDim.x / 8;
-    const int lb = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
-    if (lb >= p.H * per_head) return;                     // grid padding
-    const int h = lb / per_head;
-    const int row = (lb % per_head) * WW + wave;
-    if (row >= p.nq) return;                              // whole wave; no block barriers below
+__device__ __forceinline__ uint64_t wkey(uint32_t o, int j) {
+    return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+
+// The ledger row of block row bi (query row `row` of head h), from the score table.
+template <bool CAUSAL>
+__device__ __forceinline__ void emit_row(const RouteArgs& p, WideShared& sh, int wave, int lane, int h, int row,
+                                         int bi) {
+    // Opaque per row: otherwise the sorts' per-lane stage conditions are hoisted out of the
+    // row loop as 64-bit masks and spill.
+    asm volatile("" : "+v"(lane));
     const size_t flat = (size_t)h * p.nq + row;
-    if constexpr (REROUTE) {
-        if (p.flags[flat] == 0) return;
-    }
     const int qrow = p.qmap ? p.qmap[row] : row;
     const int n = CAUSAL ? qrow + 1 : p.nk;
-
-    // ---------------------------------------------------------------- scores and keys
-    // The query row in registers; each key row read with 16-byte loads.
-    const E* qv = reinterpret_cast<const E*>(p.qp) + ((size_t)h * p.nq_q + qrow) * 64;
-    constexpr int PER = 16 / sizeof(E);                   // elements per 16-byte load
-    float qf[64];
-#pragma unroll
-    for (int c = 0; c < 64 / PER; ++c) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(qv + PER * c);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) qf[PER * c + e] = elem_of(w, e, (const E*)nullptr);
-    }
-    const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
-    uint64_t key[WKT];
+    uint32_t o[WKT];
 #pragma unroll
     for (int t = 0; t < WKT; ++t) {
         const int j = lane + 64 * t;
-        key[t] = EMPTY_KEY;
-        if (j < n) {
-            const E* kr = Kh + (size_t)j * 64;
-            float acc = 0.f;
-#pragma unroll
-            for (int c = 0; c < 64 / PER; ++c) {
-                const u32x4 w = *reinterpret_cast<const u32x4*>(kr + PER * c);
-#pragma unroll
-                for (int e = 0; e < PER; ++e) acc = fmaf(qf[PER * c + e], elem_of(w, e, (const E*)nullptr), acc);
-            }
-            key[t] = make_key(acc, (uint32_t)j);
-        }
+        o[t] = (j < n) ? sh.s[bi][j] : 0u;
     }
+    uint64_t* list = sh.list[wave];
 
     // ---------------------------------------------------------------- exact top-(k+m)
     const int sel = min(p.sel, n);
-    uint64_t thr = 0ull;                                  // the sel-th largest key
-    for (int b = 63; b >= 0; --b) {
-        const uint64_t cand = thr | (1ull << b);
-        int c = 0;
+    // Lanes 0 .. min(n, 64) - 1 hold at least one key and sel <= min(n, 64), so the sel-th
+    // largest lane maximum is a key's score: at least sel keys reach it.
+    uint32_t lm = 0u;
 #pragma unroll
-        for (int t = 0; t < WKT; ++t) c += (key[t] >= cand) ? 1 : 0;
-        if (wave_sum_i(c) >= sel) thr = cand;
+    for (int t = 0; t < WKT; ++t) lm = max(lm, o[t]);
+    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)lane_sort_asc_u32(lm, lane), 64 - sel);
+    int cnt = 0;
+#pragma unroll
+    for (int t = 0; t < WKT; ++t) cnt += (o[t] >= tau) ? 1 : 0;
+    const int C = wave_sum_i(cnt);
+    int held;                                             // keys in the list, the top sel among them
+    if (tau != 0u && C <= 64) {
+        int pos = wave_incl_scan_i(cnt) - cnt;
+#pragma unroll
+        for (int t = 0; t < WKT; ++t)
+            if (o[t] >= tau) list[pos++] = wkey(o[t], lane + 64 * t);
+        held = C;
+    } else {
+        // More than 64 keys reach tau: an exact radix select over the 64-bit keys finds the
+        // sel-th largest, and exactly the sel keys at or above it are kept.
+        uint64_t thr = 0ull;
+        for (int b = 63; b >= 0; --b) {
+            const uint64_t cand = thr | (1ull << b);
+            int c = 0;
+#pragma unroll
+            for (int t = 0; t < WKT; ++t) c += (o[t] != 0u && wkey(o[t], lane + 64 * t) >= cand) ? 1 : 0;
+            if (wave_sum_i(c) >= sel) thr = cand;
+        }
+        int mine = 0;
+#pragma unroll
+        for (int t = 0; t < WKT; ++t) mine += (o[t] != 0u && wkey(o[t], lane + 64 * t) >= thr) ? 1 : 0;
+        int pos = wave_incl_scan_i(mine) - mine;
+#pragma unroll
+        for (int t = 0; t < WKT; ++t)
+            if (o[t] != 0u && wkey(o[t], lane + 64 * t) >= thr && pos < 64) list[pos++] = wkey(o[t], lane + 64 * t);
+        held = sel;
     }
-    int mine = 0;
-#pragma unroll
-    for (int t = 0; t < WKT; ++t) mine += (key[t] >= thr && key[t] != EMPTY_KEY) ? 1 : 0;
-    int pos = wave_incl_scan_i(mine) - mine;
-#pragma unroll
-    for (int t = 0; t < WKT; ++t)
-        if (key[t] >= thr && key[t] != EMPTY_KEY && pos < 64) sh.list[wave][pos++] = key[t];
-    const uint64_t ranked = lane_sort_desc_u64(lane < sel ? sh.list[wave][lane] : EMPTY_KEY, lane);
+    const uint64_t ranked = lane_sort_desc_u64(lane < held ? list[lane] : 0ull, lane);   // lane r: rank r
 
     // ---------------------------------------------------------------- route and near-miss
     const int ki = min(p.k, n);
     const int mi = min(p.m, n - ki);
     const bool used = lane < ki + mi;
-    const uint32_t idx = key_index(ranked);
+    const uint32_t idx = 0xFFFFFFFFu - (uint32_t)ranked;
     const uint32_t skey = used ? (((lane < ki) ? 0u : 0x10000u) | idx) : 0xFFFFFFFFu;
     const uint32_t sorted = lane_sort_asc_u32(skey, lane);   // route ascending, then near-miss ascending
     uint32_t* bm = sh.bm[wave];
     int32_t* stage = sh.stage[wave];
     const int words = (n + 31) >> 5;
     if (lane < WBM) bm[lane] = 0u;
-    if (used) atomicOr(&bm[idx >> 5], 1u << (idx & 31));
+    if (used && idx < (uint32_t)n) atomicOr(&bm[idx >> 5], 1u << (idx & 31));
     for (int e = lane; e < p.c; e += 64) stage[e] = -1;
     if (lane < ki) stage[lane] = (int32_t)(sorted & 0xFFFFu);
     else if (lane < ki + mi) stage[p.k + (lane - ki)] = (int32_t)(sorted & 0xFFFFu);
@@ -190,23 +195,30 @@ __global__ __launch_bounds__(64 * WW) void k_route_wide(RouteArgs p) {
     // Accepted chunks go to the row's list (its key list is free again) in draw order.
     const int pool = n - ki - mi - mand;
     const int rwant = min(p.r, pool);
-    uint32_t* rlist = reinterpret_cast<uint32_t*>(sh.list[wave]);
+    uint32_t* rlist = reinterpret_cast<uint32_t*>(list);
     int taken = 0;
     if (p.r > 0 && pool > p.r) {
-        for (int t0 = 0; t0 < 65536 && taken < p.r; t0 += 64) {
+        // A round covers draws t0 .. t0 + L - 1, L ending at the draw that would fill the row if
+        // none of them repeated an earlier one, so only those draws are checked against each other.
+        for (int t0 = 0; t0 < 65536 && taken < p.r;) {
             const int t = t0 + lane;
             const P4 w4 = philox4x32_10(P4{(uint32_t)(t >> 2), (uint32_t)qrow, (uint32_t)p.layer, (uint32_t)h},
                                         p.seed_lo, p.seed_hi);
             const uint32_t u = ((t & 3) == 0) ? w4.x : ((t & 3) == 1) ? w4.y : ((t & 3) == 2) ? w4.z : w4.w;
             const uint32_t j = __umulhi(u, (uint32_t)n);
-            const bool inpool = (bm[j >> 5] & (1u << (j & 31))) == 0u;
+            const bool inpool = t < 65536 && (bm[j >> 5] & (1u << (j & 31))) == 0u;
+            const uint64_t m_in = __ballot(inpool);
+            const int need = p.r - taken;
+            // in-pool draws up to and including this lane (for lane 63, 2 << 63 wraps to 0: all bits)
+            const int upto = __popcll(m_in & ((2ull << lane) - 1ull));
+            const uint64_t at_need = __ballot(inpool && upto == need);
+            const int L = at_need ? (int)__builtin_ctzll(at_need) + 1 : 64;
             bool dup = false;                             // an earlier draw of this round hit j
-            for (int l2 = 0; l2 < 63; ++l2) {
+            for (int l2 = 0; l2 < L - 1; ++l2) {
                 const uint32_t jj = (uint32_t)__builtin_amdgcn_readlane((int)j, l2);
-                const int ok2 = __builtin_amdgcn_readlane((int)inpool, l2);
-                dup = dup || (l2 < lane && ok2 != 0 && jj == j);
+                dup = dup || (l2 < lane && ((m_in >> l2) & 1ull) != 0ull && jj == j);
             }
-            const bool acc = inpool && !dup;
+            const bool acc = inpool && !dup && lane < L;
             const uint64_t m = __ballot(acc);
             const int rank = lanes_below(m, lane);
             if (acc && taken + rank < p.r) {
@@ -214,6 +226,7 @@ __global__ __launch_bounds__(64 * WW) void k_route_wide(RouteArgs p) {
                 rlist[taken + rank] = j;
             }
             taken = min(p.r, taken + __popcll(m));
+            t0 += L;
         }
     }
     if (taken < rwant && lane == 0) {
@@ -228,8 +241,12 @@ __global__ __launch_bounds__(64 * WW) void k_route_wide(RouteArgs p) {
             }
         }
     }
-    const uint32_t rsorted = lane_sort_asc_u32(lane < rwant ? rlist[lane] : 0xFFFFFFFFu, lane);
-    if (lane < rwant) stage[p.k + p.m + mw + lane] = (int32_t)rsorted;
+    if (rwant > 0) {
+        const uint32_t rv = lane < rwant ? rlist[lane] : 0xFFFFFFFFu;
+        // up to 16 draws sit in lanes 0-15: a sort within each 16-lane row is enough
+        const uint32_t rsorted = (rwant <= 16) ? bitonic_sort<16, false>(rv, lane) : lane_sort_asc_u32(rv, lane);
+        if (lane < rwant) stage[p.k + p.m + mw + lane] = (int32_t)rsorted;
+    }
 
     // ---------------------------------------------------------------- ledger row
     int32_t* dst = p.ids + flat * p.c;
@@ -238,6 +255,125 @@ __global__ __launch_bounds__(64 * WW) void k_route_wide(RouteArgs p) {
         p.anchor[flat] = p.layer;
         p.refreshed[flat] = (uint8_t)p.refresh_mark;
     }
+}
+
+// One 16-row group: score table, then the ledger rows.  Called by every wave of the block.
+template <typename E, bool CAUSAL, bool REROUTE>
+__device__ __forceinline__ void route_group(const RouteArgs& p, WideShared& sh, int wave, int lane, int h, int r0) {
+    const int nrows = min(WR, p.nq - r0);
+    bool want = lane < nrows;
+    if constexpr (REROUTE) want = want && p.flags[(size_t)h * p.nq + r0 + (want ? lane : 0)] != 0;
+    const uint64_t todo = __ballot(want);                 // the same in every wave
+    if (todo == 0ull) return;                             // whole block: nothing to write
+
+    // ---------------------------------------------------------------- score table
+    // Keys up to the last written row's limit (query rows ascend with the block's rows).
+    const int last = r0 + 63 - __builtin_clzll(todo);
+    const int nmax = CAUSAL ? (p.qmap ? p.qmap[last] : last) + 1 : p.nk;
+    const int ntile = (nmax + 15) >> 4;
+    const int g = lane >> 4, c = lane & 15;
+    // A operand: block row c (rows past the ledger read its last row; their scores are unused).
+    const int arow = min(r0 + c, p.nq - 1);
+    const E* qv = reinterpret_cast<const E*>(p.qp) + ((size_t)h * p.nq_q + (p.qmap ? p.qmap[arow] : arow)) * 64;
+    const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
+    int nlim[4];                                          // key limit of result rows 4g .. 4g+3
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int r = r0 + 4 * g + v;
+        nlim[v] = (r < p.nq) ? (CAUSAL ? (p.qmap ? p.qmap[r] : r) + 1 : p.nk) : 0;
+    }
+    auto put = [&](int tile, const f32x4& acc) {
+        // result lane layout: key 16 tile + c, rows 4g + v
+        const int key = 16 * tile + c;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sh.s[4 * g + v][key] = (key < nlim[v]) ? orderable(acc[v]) : 0u;
+    };
+    if constexpr (sizeof(E) == 2) {
+        // k-step s of a tile contracts d = 32 s + 8 g .. 32 s + 8 g + 7 in lane group g.
+        const bf16x8 qa0 = *reinterpret_cast<const bf16x8*>(qv + 8 * g);
+        const bf16x8 qa1 = *reinterpret_cast<const bf16x8*>(qv + 32 + 8 * g);
+        constexpr int TG = 1024 / 16 / WWAVES;            // tiles per wave at nk = 1024
+        bf16x8 kb[TG][2];
+#pragma unroll
+        for (int u = 0; u < TG; ++u) {
+            const int tile = wave + WWAVES * u;
+            if (tile < ntile) {
+                const E* kr = Kh + (size_t)min(16 * tile + c, p.nk - 1) * 64 + 8 * g;
+                kb[u][0] = *reinterpret_cast<const bf16x8*>(kr);
+                kb[u][1] = *reinterpret_cast<const bf16x8*>(kr + 32);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < TG; ++u) {
+            const int tile = wave + WWAVES * u;
+            if (tile < ntile) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0, kb[u][0], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1, kb[u][1], acc, 0, 0, 0);
+                put(tile, acc);
+            }
+        }
+    } else {
+        // k-step s contracts d = 16 g + s in lane group g (s = 0 .. 15).
+        float qa[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(qv + 16 * g + 4 * u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qa[4 * u + e] = __uint_as_float(w[e]);
+        }
+        for (int t0 = wave; t0 < ntile; t0 += 4 * WWAVES) {
+            float kb[4][16];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int tile = t0 + WWAVES * u;
+                if (tile < ntile) {
+                    const E* kr = Kh + (size_t)min(16 * tile + c, p.nk - 1) * 64 + 16 * g;
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const u32x4 w = *reinterpret_cast<const u32x4*>(kr + 4 * q4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) kb[u][4 * q4 + e] = __uint_as_float(w[e]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int tile = t0 + WWAVES * u;
+                if (tile < ntile) {
+                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s], kb[u][s], acc, 0, 0, 0);
+                    put(tile, acc);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---------------------------------------------------------------- ledger rows
+    // The block's written rows in order, dealt round-robin to the waves.
+    uint64_t rest = todo;
+    for (int x = 0; rest != 0ull; ++x) {
+        const int bi = __builtin_ctzll(rest);
+        rest &= rest - 1ull;
+        if ((x % WWAVES) == wave) emit_row<CAUSAL>(p, sh, wave, lane, h, r0 + bi, bi);
+    }
+}
+
+// E: uint16_t (bf16 bits) or float.
+template <typename E, bool CAUSAL, bool REROUTE>
+__global__ __launch_bounds__(64 * WWAVES) __attribute__((amdgpu_waves_per_eu(4))) void k_route_wide(RouteArgs p) {
+    __shared__ WideShared sh;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int per_head = (p.nq + WR - 1) / WR;
+    // Workgroups go to the 8 XCDs round-robin; renumber so that each XCD runs a contiguous
+    // range of blocks, i.e. whole heads, whose key rows then stay in that XCD's L2.
+    const int per_xcd = (int)gridDim.x / 8;
+    const int lb = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+    if (lb >= p.H * per_head) return;                     // grid padding (whole block)
+    route_group<E, CAUSAL, REROUTE>(p, sh, wave, lane, lb / per_head, (lb % per_head) * WR);
 }
 
 // Compacted list of flagged rows (ascending h*nq + i), per-head counts and total, for the
@@ -270,9 +406,9 @@ __global__ __launch_bounds__(64) void k_wide_outputs(RouteArgs p) {
 
 template <typename E, bool CAUSAL, bool REROUTE>
 hipError_t launch_wide_t(const RouteArgs& a, hipStream_t st) {
-    const int per_head = (a.nq + WW - 1) / WW;
+    const int per_head = (a.nq + WR - 1) / WR;
     const unsigned blocks = (unsigned)((a.H * per_head + 7) / 8 * 8);      // a multiple of the 8 XCDs
-    hipLaunchKernelGGL((k_route_wide<E, CAUSAL, REROUTE>), dim3(blocks), dim3(64 * WW), 0, st, a);
+    hipLaunchKernelGGL((k_route_wide<E, CAUSAL, REROUTE>), dim3(blocks), dim3(64 * WWAVES), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && REROUTE && (a.out_rows || a.out_head_counts || a.out_n_rows)) {
         hipLaunchKernelGGL(k_wide_outputs, dim3((unsigned)a.H), dim3(64), 0, st, a);

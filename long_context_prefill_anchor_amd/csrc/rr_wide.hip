@@ -44,7 +44,7 @@ constexpr int SST = 1024 + 4;          // u32 row stride of the score table (the
 
 struct WideShared {
     uint32_t s[WR][SST];               // orderable scores of the block's rows; 0 = no key
-    uint64_t list[WWAVES][64];         // candidate keys, then the row's random draws (u32)
+    uint64_t list[WWAVES][2][64];      // candidate keys of a wave's two rows; then random draws (u32)
     uint32_t bm[WWAVES][WBM];          // chunks already in the row's ledger
     int32_t stage[WWAVES][65];         // the row's ledger entries before the copy out
 };
@@ -87,7 +87,23 @@ template <int K, bool DESC, typename T> __device__ __forceinline__ T bitonic_sor
     if constexpr (K > 2) v = bitonic_sort<K / 2, DESC>(v, lane);
     return bitonic_merge<K, K / 2, DESC>(v, lane);
 }
-__device__ __forceinline__ uint64_t lane_sort_desc_u64(uint64_t v, int lane) { return bitonic_sort<64, true>(v, lane); }
+// The same over NR independent values per lane (one per row), stage by stage, so that the
+// rows' exchange chains interleave.
+template <int K, int J, bool DESC, int NR, typename T>
+__device__ __forceinline__ void bitonic_merge_n(T (&v)[NR], int lane) {
+    T o[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) o[r] = xor_lane<J>(v[r], lane);
+    const bool low = ((lane & K) == 0) == ((lane & J) == 0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) v[r] = (low != DESC) ? (v[r] < o[r] ? v[r] : o[r]) : (v[r] < o[r] ? o[r] : v[r]);
+    if constexpr (J > 1) bitonic_merge_n<K, J / 2, DESC>(v, lane);
+}
+template <int K, bool DESC, int NR, typename T>
+__device__ __forceinline__ void bitonic_sort_n(T (&v)[NR], int lane) {
+    if constexpr (K > 2) bitonic_sort_n<K / 2, DESC>(v, lane);
+    bitonic_merge_n<K, K / 2, DESC>(v, lane);
+}
 __device__ __forceinline__ uint32_t lane_sort_asc_u32(uint32_t v, int lane) { return bitonic_sort<64, false>(v, lane); }
 
 __device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {
@@ -98,72 +114,14 @@ __device__ __forceinline__ uint64_t wkey(uint32_t o, int j) {
     return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
 
-// The ledger row of block row bi (query row `row` of head h), from the score table.
-template <bool CAUSAL>
-__device__ __forceinline__ void emit_row(const RouteArgs& p, WideShared& sh, int wave, int lane, int h, int row,
-                                         int bi) {
-    // Opaque per row: otherwise the sorts' per-lane stage conditions are hoisted out of the
-    // row loop as 64-bit masks and spill.
-    asm volatile("" : "+v"(lane));
+// The ledger row of query row `row` of head h, given its route and near-miss: `used` / `idx`
+// (lanes below ki + mi hold the chosen chunks, in any order) and `sorted` (lane e < ki: the e-th
+// route chunk ascending; lane ki + e < ki + mi: the e-th near-miss chunk ascending).
+__device__ __forceinline__ void write_row(const RouteArgs& p, WideShared& sh, int wave, int lane, int h, int row,
+                                          int qrow, int n, int ki, int mi, bool used, uint32_t idx,
+                                          uint32_t sorted) {
     const size_t flat = (size_t)h * p.nq + row;
-    const int qrow = p.qmap ? p.qmap[row] : row;
-    const int n = CAUSAL ? qrow + 1 : p.nk;
-    uint32_t o[WKT];
-#pragma unroll
-    for (int t = 0; t < WKT; ++t) {
-        const int j = lane + 64 * t;
-        o[t] = (j < n) ? sh.s[bi][j] : 0u;
-    }
-    uint64_t* list = sh.list[wave];
-
-    // ---------------------------------------------------------------- exact top-(k+m)
-    const int sel = min(p.sel, n);
-    // Lanes 0 .. min(n, 64) - 1 hold at least one key and sel <= min(n, 64), so the sel-th
-    // largest lane maximum is a key's score: at least sel keys reach it.
-    uint32_t lm = 0u;
-#pragma unroll
-    for (int t = 0; t < WKT; ++t) lm = max(lm, o[t]);
-    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)lane_sort_asc_u32(lm, lane), 64 - sel);
-    int cnt = 0;
-#pragma unroll
-    for (int t = 0; t < WKT; ++t) cnt += (o[t] >= tau) ? 1 : 0;
-    const int C = wave_sum_i(cnt);
-    int held;                                             // keys in the list, the top sel among them
-    if (tau != 0u && C <= 64) {
-        int pos = wave_incl_scan_i(cnt) - cnt;
-#pragma unroll
-        for (int t = 0; t < WKT; ++t)
-            if (o[t] >= tau) list[pos++] = wkey(o[t], lane + 64 * t);
-        held = C;
-    } else {
-        // More than 64 keys reach tau: an exact radix select over the 64-bit keys finds the
-        // sel-th largest, and exactly the sel keys at or above it are kept.
-        uint64_t thr = 0ull;
-        for (int b = 63; b >= 0; --b) {
-            const uint64_t cand = thr | (1ull << b);
-            int c = 0;
-#pragma unroll
-            for (int t = 0; t < WKT; ++t) c += (o[t] != 0u && wkey(o[t], lane + 64 * t) >= cand) ? 1 : 0;
-            if (wave_sum_i(c) >= sel) thr = cand;
-        }
-        int mine = 0;
-#pragma unroll
-        for (int t = 0; t < WKT; ++t) mine += (o[t] != 0u && wkey(o[t], lane + 64 * t) >= thr) ? 1 : 0;
-        int pos = wave_incl_scan_i(mine) - mine;
-#pragma unroll
-        for (int t = 0; t < WKT; ++t)
-            if (o[t] != 0u && wkey(o[t], lane + 64 * t) >= thr && pos < 64) list[pos++] = wkey(o[t], lane + 64 * t);
-        held = sel;
-    }
-    const uint64_t ranked = lane_sort_desc_u64(lane < held ? list[lane] : 0ull, lane);   // lane r: rank r
-
-    // ---------------------------------------------------------------- route and near-miss
-    const int ki = min(p.k, n);
-    const int mi = min(p.m, n - ki);
-    const bool used = lane < ki + mi;
-    const uint32_t idx = 0xFFFFFFFFu - (uint32_t)ranked;
-    const uint32_t skey = used ? (((lane < ki) ? 0u : 0x10000u) | idx) : 0xFFFFFFFFu;
-    const uint32_t sorted = lane_sort_asc_u32(skey, lane);   // route ascending, then near-miss ascending
+    uint64_t* list = sh.list[wave][0];
     uint32_t* bm = sh.bm[wave];
     int32_t* stage = sh.stage[wave];
     const int words = (n + 31) >> 5;
@@ -258,6 +216,90 @@ __device__ __forceinline__ void emit_row(const RouteArgs& p, WideShared& sh, int
 }
 
 // One 16-row group: score table, then the ledger rows.  Called by every wave of the block.
+// Exact top-(k+m) of NR rows (block rows bi[r], query rows row[r]) from the score table, the
+// rows side by side, then each row's ledger write.
+template <bool CAUSAL, int NR>
+__device__ __forceinline__ void emit_rows(const RouteArgs& p, WideShared& sh, int wave, int lane, int h,
+                                          const int (&row)[NR], const int (&bi)[NR]) {
+    // Opaque per call: otherwise the sorts' per-lane stage conditions are hoisted out of the
+    // row loop as 64-bit masks and spill.
+    asm volatile("" : "+v"(lane));
+    int qrow[NR], n[NR], sel[NR];
+    uint32_t o[NR][WKT];
+    uint32_t lm[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        qrow[r] = p.qmap ? p.qmap[row[r]] : row[r];
+        n[r] = CAUSAL ? qrow[r] + 1 : p.nk;
+        sel[r] = min(p.sel, n[r]);
+        lm[r] = 0u;
+#pragma unroll
+        for (int t = 0; t < WKT; ++t) {
+            const int j = lane + 64 * t;
+            o[r][t] = (j < n[r]) ? sh.s[bi[r]][j] : 0u;
+            lm[r] = max(lm[r], o[r][t]);
+        }
+    }
+    // Lanes 0 .. min(n, 64) - 1 hold at least one key and sel <= min(n, 64), so the sel-th
+    // largest lane maximum tau is a key's score: at least sel keys reach it.
+    bitonic_sort_n<64, false>(lm, lane);
+    uint64_t cand[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)lm[r], 64 - sel[r]);
+        int cnt = 0;
+#pragma unroll
+        for (int t = 0; t < WKT; ++t) cnt += (o[r][t] >= tau) ? 1 : 0;
+        const int C = wave_sum_i(cnt);
+        uint64_t* list = sh.list[wave][r];
+        int held;                                         // keys in the list, the top sel among them
+        if (tau != 0u && C <= 64) {
+            int pos = wave_incl_scan_i(cnt) - cnt;
+#pragma unroll
+            for (int t = 0; t < WKT; ++t)
+                if (o[r][t] >= tau) list[pos++] = wkey(o[r][t], lane + 64 * t);
+            held = C;
+        } else {
+            // More than 64 keys reach tau: an exact radix select over the 64-bit keys finds the
+            // sel-th largest, and exactly the sel keys at or above it are kept.
+            uint64_t thr = 0ull;
+            for (int b = 63; b >= 0; --b) {
+                const uint64_t c64 = thr | (1ull << b);
+                int c = 0;
+#pragma unroll
+                for (int t = 0; t < WKT; ++t) c += (o[r][t] != 0u && wkey(o[r][t], lane + 64 * t) >= c64) ? 1 : 0;
+                if (wave_sum_i(c) >= sel[r]) thr = c64;
+            }
+            int mine = 0;
+#pragma unroll
+            for (int t = 0; t < WKT; ++t) mine += (o[r][t] != 0u && wkey(o[r][t], lane + 64 * t) >= thr) ? 1 : 0;
+            int pos = wave_incl_scan_i(mine) - mine;
+#pragma unroll
+            for (int t = 0; t < WKT; ++t)
+                if (o[r][t] != 0u && wkey(o[r][t], lane + 64 * t) >= thr && pos < 64)
+                    list[pos++] = wkey(o[r][t], lane + 64 * t);
+            held = sel[r];
+        }
+        cand[r] = lane < held ? list[lane] : 0ull;
+    }
+    bitonic_sort_n<64, true>(cand, lane);                 // lane e: rank e
+    int ki[NR], mi[NR];
+    bool used[NR];
+    uint32_t idx[NR], skey[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        ki[r] = min(p.k, n[r]);
+        mi[r] = min(p.m, n[r] - ki[r]);
+        used[r] = lane < ki[r] + mi[r];
+        idx[r] = 0xFFFFFFFFu - (uint32_t)cand[r];
+        skey[r] = used[r] ? (((lane < ki[r]) ? 0u : 0x10000u) | idx[r]) : 0xFFFFFFFFu;
+    }
+    bitonic_sort_n<64, false>(skey, lane);                // route ascending, then near-miss ascending
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+        write_row(p, sh, wave, lane, h, row[r], qrow[r], n[r], ki[r], mi[r], used[r], idx[r], skey[r]);
+}
+
 template <typename E, bool CAUSAL, bool REROUTE>
 __device__ __forceinline__ void route_group(const RouteArgs& p, WideShared& sh, int wave, int lane, int h, int r0) {
     const int nrows = min(WR, p.nq - r0);
@@ -352,12 +394,20 @@ __device__ __forceinline__ void route_group(const RouteArgs& p, WideShared& sh, 
     __syncthreads();
 
     // ---------------------------------------------------------------- ledger rows
-    // The block's written rows in order, dealt round-robin to the waves.
+    // The block's written rows in order, dealt round-robin to the waves: at most 16 rows, so a
+    // wave takes the wave-th and, if present, the (wave + 8)-th.
     uint64_t rest = todo;
-    for (int x = 0; rest != 0ull; ++x) {
-        const int bi = __builtin_ctzll(rest);
-        rest &= rest - 1ull;
-        if ((x % WWAVES) == wave) emit_row<CAUSAL>(p, sh, wave, lane, h, r0 + bi, bi);
+    for (int x = 0; x < wave && rest != 0ull; ++x) rest &= rest - 1ull;
+    if (rest == 0ull) return;
+    const int b0 = __builtin_ctzll(rest);
+    for (int x = 0; x < WWAVES && rest != 0ull; ++x) rest &= rest - 1ull;
+    if (rest != 0ull) {
+        const int b1 = __builtin_ctzll(rest);
+        const int rows[2] = {r0 + b0, r0 + b1}, bis[2] = {b0, b1};
+        emit_rows<CAUSAL, 2>(p, sh, wave, lane, h, rows, bis);
+    } else {
+        const int rows[1] = {r0 + b0}, bis[1] = {b0};
+        emit_rows<CAUSAL, 1>(p, sh, wave, lane, h, rows, bis);
     }
 }
 

@@ -237,8 +237,12 @@ BUCKET_CASES = [
     ("buckets_ragged", 1, 130, 1100, "bf16", False, (12, 0, 0), (20, 12, 16)),
     # every option at once: mandatory sentinels and hysteresis inside causal buckets
     ("buckets_all_options", 2, 180, 180, "bf16", True, (6, 6, 4), (12, 8, 6)),
+    # a bucket past 32 near-miss + route entries: the wide kernel through the query-row map
+    ("buckets_wide_bf16", 2, 200, 300, "bf16", False, (8, 8, 8), (12, 24, 8)),
+    ("buckets_wide_all_options", 1, 180, 180, "bf16", True, (6, 6, 4), (12, 30, 6)),
 ]
-BUCKET_EXTRA = {"buckets_all_options": dict(sink=1, recent=2, min_reuse=1, gamma_extra=0.005)}
+_ALL = dict(sink=1, recent=2, min_reuse=1, gamma_extra=0.005)
+BUCKET_EXTRA = {"buckets_all_options": _ALL, "buckets_wide_all_options": _ALL}
 
 
 @pytest.mark.parametrize("case", BUCKET_CASES, ids=[c[0] for c in BUCKET_CASES])
@@ -266,7 +270,7 @@ def test_width_buckets(case):
         led.close()
 
 
-# Near-miss sets past 32 entries (Table 3's 24-wide row and beyond): the one-wave-per-row kernel.
+# Near-miss sets past 32 entries (Table 3's 24-wide row and beyond): the wide kernel.
 # name, heads, nq, nk, k, m, r, sink, recent, dtype, causal, seed, input kind
 WIDE_ANCHOR_CASES = [
     ("wide_nm24_f32", 1, 64, 256, 12, 24, 12, 0, 0, "f32", False, 30, "gauss"),

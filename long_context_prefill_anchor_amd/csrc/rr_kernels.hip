@@ -1088,7 +1088,7 @@ __device__ __forceinline__ int cand_of_lane(int lane) {
 // flight while a row is reduced.  The block ends by listing its flagged rows (ascending) for
 // the reroute kernel.
 template <typename DT, int NP>
-__global__ __launch_bounds__(RESCORE_THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(typename Elem<DT>::type) == 2 ? 8 : 4)))
+__global__ __launch_bounds__(RESCORE_THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(typename Elem<DT>::type) == 2 && NP == 1 ? 8 : 4)))
 void k_rescore(RescoreArgs p) {
     typedef typename Elem<DT>::type E;
     constexpr uint32_t ROW_BYTES = 64 * sizeof(E);

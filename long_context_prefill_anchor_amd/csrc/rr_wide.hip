@@ -427,29 +427,28 @@ __global__ __launch_bounds__(64 * WWAVES) __attribute__((amdgpu_waves_per_eu(4))
 }
 
 // Compacted list of flagged rows (ascending h*nq + i), per-head counts and total, for the
-// wide reroute (the main reroute kernel writes these from its prologue).  One wave per head.
+// wide reroute (the main reroute kernel writes these from its prologue).  One wave per 64-row
+// rescore block, in head-major order: its rows go after those of every earlier block, whose
+// flagged counts the rescore kernel left in bcount.
 __global__ __launch_bounds__(64) void k_wide_outputs(RouteArgs p) {
-    const int h = blockIdx.x;
+    const int G = (p.nq + ROUTE_ROWS - 1) / ROUTE_ROWS;
+    const int gl = blockIdx.x;                            // h * G + g
+    const int h = gl / G, g = gl % G;
     const int lane = threadIdx.x;
-    const int G = (p.nq + 63) / 64;
     int acc = 0;
-    for (int x = lane; x < h * G; x += 64) acc += p.bcount[x];
+    for (int x = lane; x < gl; x += 64) acc += p.bcount[x];
     const int offset = wave_sum_i(acc);
-    int cnt = 0;
-    for (int x = lane; x < G; x += 64) cnt += p.bcount[(size_t)h * G + x];
-    const int count_h = wave_sum_i(cnt);
-    if (lane == 0) {
-        if (p.out_head_counts) p.out_head_counts[h] = count_h;
-        if (p.out_n_rows && h == p.H - 1) p.out_n_rows[0] = offset + count_h;
-    }
-    if (p.out_rows) {
-        int run = 0;
-        for (int b = 0; b < G; ++b) {
-            const int i = b * 64 + lane;
-            const bool f = i < p.nq && p.flags[(size_t)h * p.nq + i];
-            const uint64_t m = __ballot(f);
-            if (f) p.out_rows[offset + run + lanes_below(m, lane)] = h * p.nq + i;
-            run += __popcll(m);
+    const int i = g * ROUTE_ROWS + lane;
+    const bool f = i < p.nq && p.flags[(size_t)h * p.nq + i] != 0;
+    const uint64_t m = __ballot(f);
+    if (p.out_rows && f) p.out_rows[offset + lanes_below(m, lane)] = h * p.nq + i;
+    if (g == G - 1) {                                     // the head's last block: its count and the total
+        int hc = 0;
+        for (int x = lane; x < G; x += 64) hc += p.bcount[(size_t)h * G + x];
+        const int count_h = wave_sum_i(hc);
+        if (lane == 0) {
+            if (p.out_head_counts) p.out_head_counts[h] = count_h;
+            if (p.out_n_rows && h == p.H - 1) p.out_n_rows[0] = offset + __popcll(m);
         }
     }
 }
@@ -461,7 +460,8 @@ hipError_t launch_wide_t(const RouteArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((k_route_wide<E, CAUSAL, REROUTE>), dim3(blocks), dim3(64 * WWAVES), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && REROUTE && (a.out_rows || a.out_head_counts || a.out_n_rows)) {
-        hipLaunchKernelGGL(k_wide_outputs, dim3((unsigned)a.H), dim3(64), 0, st, a);
+        const int G = (a.nq + ROUTE_ROWS - 1) / ROUTE_ROWS;
+        hipLaunchKernelGGL(k_wide_outputs, dim3((unsigned)(a.H * G)), dim3(64), 0, st, a);
         e = hipGetLastError();
     }
     return e;

@@ -263,7 +263,7 @@ def preferred_chunks_sweep(sigmas=(0.01, 0.03, 0.06, 0.1), seeds=10):
     """The cross-layer stability setting (Section 5.1, Table 2, Figure 2): 1 head, 384 query
     rows, 192 key chunks, 32 fp32 layers, persistent preferred chunks with layer-local drift
     (generator in synth.py; its preference strength and the anchor schedule are this build's
-    choices), 12 + 20 near-miss + 12 random.  Means over the seeds of relay recall, rerouted
+    choices), 12 + 24 near-miss + 12 random.  Means over the seeds of relay recall, rerouted
     fraction and the fixed-stride-4 baseline's recall."""
     import torch
     out = []

@@ -104,11 +104,11 @@ def preferred_chunks(sigma: float, seed: int = 0) -> Workload:
     through depth, and every layer adds its own Gaussian drift around those persistent
     representations (not a random walk).  The page gives neither the preference strength nor
     the anchor schedule: gain 1.0 (a preferred chunk's score is raised by about two standard
-    deviations of the scores) and anchors every 8 layers are this module's choices.  The page's
-    24 near-miss sentinels exceed k + m <= 32, so m = 20 with its 12 random sentinels."""
+    deviations of the scores) and anchors every 8 layers are this module's choices.  Sentinels
+    as on the page: 24 near-miss and 12 random."""
     return Workload(f"preferred_s{sigma:g}_seed{seed}", heads=1, layers=32, n=384, d=64,
                     dtype="f32", drift=(sigma, sigma), drift_scale="relative",
-                    anchors=stride_anchors(32, 8), k=12, m=20, r=12, seed=seed, nk_=192,
+                    anchors=stride_anchors(32, 8), k=12, m=24, r=12, seed=seed, nk_=192,
                     drift_model="local", preferred=12, pref_gain=1.0)
 
 

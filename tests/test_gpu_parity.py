@@ -224,7 +224,7 @@ def test_chain_tiny():
 
 def test_chain_preferred_chunks():
     """The persistent-preferred-chunk chain (384 query rows, 192 key chunks: nq != nk,
-    layer-local drift, 12 + 20 near-miss + 12 random sentinels)."""
+    layer-local drift, 12 + 24 near-miss + 12 random sentinels, on the wide kernel)."""
     U.log("[chain] preferred_chunks sigma=0.03 seed=0")
     rep = run_chain_gpu_vs_oracle(W.preferred_chunks(0.03, 0))
     chain_report(rep)

@@ -9,15 +9,16 @@
 // A block takes 16 consecutive query rows of one head.  Its eight waves first score the rows
 // against every key with v_mfma_f32_16x16x32_bf16 (fp32 inputs: v_mfma_f32_16x16x4f32), 16
 // keys per tile and tiles dealt round-robin to the waves, into an LDS table of orderable fp32
-// scores (0 = no key).  Each row then goes to one wave, which finds its exact top-(k+m) over
+// scores (0 = no key).  Each row then goes to one wave (two rows per wave, side by side, so
+// that their exchange chains interleave), which finds its exact top-(k+m) over
 // the 64-bit keys (orderable score, then lower index first): lane l holds keys l, l + 64, ...;
 // the (k+m)-th largest of the 64 lane maxima is a lower bound of the (k+m)-th largest key, so
 // the keys at or above it (at least k+m of them, at most 64 in the common case) are compacted
 // and sorted across lanes with a bitonic network, leaving rank r in lane r; when more than 64
 // keys pass the bound, an exact radix select over the 64-bit keys finds the threshold instead.
 // Route and near-miss are put in index order by a second lane sort.  Lane exchanges are DPP
-// moves and the 16- and 32-lane swaps, so the sorts stay in the VALU.
-// Route = the k largest, near-miss = the next m.  The ledger row is then written with the same
+// moves and the 16- and 32-lane swaps, so the sorts stay in the VALU.  Route = the k largest,
+// near-miss = the next m.  The ledger row is then written with the same
 // rules as the main kernel: segments ascending by index, mandatory sink / recent chunks not
 // already routed, random draws from Philox4x32-10 (counter = (t div 4, query row, layer,
 // head)) accepted in draw order when the chunk is still in the pool, a fill with the

@@ -280,6 +280,9 @@ WIDE_ANCHOR_CASES = [
     ("wide_int_ties", 1, 96, 128, 12, 24, 12, 0, 0, "f32", False, 34, "int"),
     ("wide_short_rows", 1, 40, 30, 12, 24, 12, 1, 1, "f32", False, 35, "gauss"),
     ("wide_nk1024", 1, 64, 1024, 12, 48, 4, 0, 0, "bf16", False, 36, "gauss"),
+    ("wide_km64", 1, 80, 200, 16, 48, 0, 0, 0, "bf16", False, 37, "gauss"),     # c = k + m = 64
+    ("wide_route40", 1, 72, 160, 40, 0, 8, 0, 0, "f32", False, 38, "gauss"),    # wide route, no near-miss
+    ("wide_km64_ties", 1, 64, 96, 16, 48, 0, 0, 0, "f32", False, 39, "int"),
 ]
 
 
@@ -306,6 +309,7 @@ WIDE_RELAY_CASES = [
     ("wide_relay_f32", 2, 128, 256, 12, 24, 12, 0, 0, "f32", False, 0.05, "gauss"),
     ("wide_relay_causal", 1, 160, 160, 12, 36, 8, 1, 2, "bf16", True, 0.04, "gauss"),
     ("wide_relay_int", 1, 128, 200, 12, 24, 12, 0, 0, "f32", False, 0.0, "int"),
+    ("wide_relay_route40", 1, 96, 300, 40, 8, 8, 0, 0, "bf16", False, 0.05, "gauss"),
 ]
 
 

@@ -25,7 +25,7 @@
 // lowest-index free chunks when the pool is not larger than r or the draw cap is reached.
 // The kernel keeps no threshold state, so anchor and reroute use it alike; in a reroute a
 // block scores its rows only if the rescore kernel flagged one of them and writes only the
-// flagged ones.
+// flagged ones, and its first wave also writes those rows' entries of the compacted list.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -213,6 +213,32 @@ __device__ __forceinline__ void write_row(const RouteArgs& p, WideShared& sh, in
     if (lane == 0) {
         p.anchor[flat] = p.layer;
         p.refreshed[flat] = (uint8_t)p.refresh_mark;
+    }
+}
+
+// Reroute outputs for the block's 16 rows (wave 0): their places in the compacted list of
+// flagged rows (ascending h*nq + i) come after the flagged rows of every earlier 64-row rescore
+// block, whose counts the rescore kernel left in bcount, and after this block's earlier rows
+// of its own 64-row block.  The head's last block writes its count, the last head's the total.
+__device__ __forceinline__ void wide_outputs(const RouteArgs& p, int lane, int h, int r0) {
+    const int G = (p.nq + ROUTE_ROWS - 1) / ROUTE_ROWS;
+    const int g64 = r0 / ROUTE_ROWS;
+    int acc = 0;
+    for (int x = lane; x < h * G + g64; x += 64) acc += p.bcount[x];
+    const int before = g64 * ROUTE_ROWS + lane;           // rows of the 64-row block before r0
+    const bool fb = before < r0 && p.flags[(size_t)h * p.nq + before] != 0;
+    const int offset = wave_sum_i(acc) + __popcll(__ballot(fb));
+    const bool f = lane < WR && r0 + lane < p.nq && p.flags[(size_t)h * p.nq + r0 + lane] != 0;
+    const uint64_t m = __ballot(f);
+    if (p.out_rows && f) p.out_rows[offset + lanes_below(m, lane)] = h * p.nq + r0 + lane;
+    if (r0 + WR >= p.nq) {
+        int hc = 0;
+        for (int x = lane; x < G; x += 64) hc += p.bcount[(size_t)h * G + x];
+        const int count_h = wave_sum_i(hc);
+        if (lane == 0) {
+            if (p.out_head_counts) p.out_head_counts[h] = count_h;
+            if (p.out_n_rows && h == p.H - 1) p.out_n_rows[0] = offset + __popcll(m);
+        }
     }
 }
 
@@ -424,34 +450,11 @@ __global__ __launch_bounds__(64 * WWAVES) __attribute__((amdgpu_waves_per_eu(4))
     const int per_xcd = (int)gridDim.x / 8;
     const int lb = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
     if (lb >= p.H * per_head) return;                     // grid padding (whole block)
-    route_group<E, CAUSAL, REROUTE>(p, sh, wave, lane, lb / per_head, (lb % per_head) * WR);
-}
-
-// Compacted list of flagged rows (ascending h*nq + i), per-head counts and total, for the
-// wide reroute (the main reroute kernel writes these from its prologue).  One wave per 64-row
-// rescore block, in head-major order: its rows go after those of every earlier block, whose
-// flagged counts the rescore kernel left in bcount.
-__global__ __launch_bounds__(64) void k_wide_outputs(RouteArgs p) {
-    const int G = (p.nq + ROUTE_ROWS - 1) / ROUTE_ROWS;
-    const int gl = blockIdx.x;                            // h * G + g
-    const int h = gl / G, g = gl % G;
-    const int lane = threadIdx.x;
-    int acc = 0;
-    for (int x = lane; x < gl; x += 64) acc += p.bcount[x];
-    const int offset = wave_sum_i(acc);
-    const int i = g * ROUTE_ROWS + lane;
-    const bool f = i < p.nq && p.flags[(size_t)h * p.nq + i] != 0;
-    const uint64_t m = __ballot(f);
-    if (p.out_rows && f) p.out_rows[offset + lanes_below(m, lane)] = h * p.nq + i;
-    if (g == G - 1) {                                     // the head's last block: its count and the total
-        int hc = 0;
-        for (int x = lane; x < G; x += 64) hc += p.bcount[(size_t)h * G + x];
-        const int count_h = wave_sum_i(hc);
-        if (lane == 0) {
-            if (p.out_head_counts) p.out_head_counts[h] = count_h;
-            if (p.out_n_rows && h == p.H - 1) p.out_n_rows[0] = offset + __popcll(m);
-        }
+    const int h = lb / per_head, r0 = (lb % per_head) * WR;
+    if constexpr (REROUTE) {
+        if (wave == 0 && (p.out_rows || p.out_head_counts || p.out_n_rows)) wide_outputs(p, lane, h, r0);
     }
+    route_group<E, CAUSAL, REROUTE>(p, sh, wave, lane, h, r0);
 }
 
 template <typename E, bool CAUSAL, bool REROUTE>
@@ -459,13 +462,7 @@ hipError_t launch_wide_t(const RouteArgs& a, hipStream_t st) {
     const int per_head = (a.nq + WR - 1) / WR;
     const unsigned blocks = (unsigned)((a.H * per_head + 7) / 8 * 8);      // a multiple of the 8 XCDs
     hipLaunchKernelGGL((k_route_wide<E, CAUSAL, REROUTE>), dim3(blocks), dim3(64 * WWAVES), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e == hipSuccess && REROUTE && (a.out_rows || a.out_head_counts || a.out_n_rows)) {
-        const int G = (a.nq + ROUTE_ROWS - 1) / ROUTE_ROWS;
-        hipLaunchKernelGGL(k_wide_outputs, dim3((unsigned)(a.H * G)), dim3(64), 0, st, a);
-        e = hipGetLastError();
-    }
-    return e;
+    return hipGetLastError();
 }
 
 }  // namespace

@@ -255,19 +255,4 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
     return r;
 }
 
-__device__ __forceinline__ float wave_min_in(float v, int width) {
-    for (int o = width >> 1; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-__device__ __forceinline__ float wave_max_in(float v, int width) {
-    for (int o = width >> 1; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-__device__ __forceinline__ int wave_sum_in(int v, int width) {
-    for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
 }  // namespace rr

@@ -33,7 +33,9 @@ from long_context_prefill_anchor_amd import rr, synth, workloads as W  # noqa: E
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
-KERNEL_SRC = os.path.join(ROOT, "long_context_prefill_anchor_amd", "csrc", "rr_kernels.hip")
+# the routing kernels' source and the headers it includes
+KERNEL_SRCS = tuple(os.path.join(ROOT, "long_context_prefill_anchor_amd", "csrc", f)
+                    for f in ("rr_kernels.hip", "rr_device.h", "rr_internal.h"))
 BUILD_SCRIPT = os.path.join(ROOT, "long_context_prefill_anchor_amd", "build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_route_reroute_batched_heads.txt")
 CALIB_BYTES = 256 << 20         # plain copy used to calibrate the HBM byte counters
@@ -470,9 +472,10 @@ def cpu_baseline(w, max_seconds=20.0):
 
 
 def kernel_build_hash():
-    """sha256 of the kernel source followed by the build script (its compiler flags)."""
+    """sha256 of the kernel source and its headers, followed by the build script (its compiler
+    flags)."""
     h = hashlib.sha256()
-    for path in (KERNEL_SRC, BUILD_SCRIPT):
+    for path in (*KERNEL_SRCS, BUILD_SCRIPT):
         h.update(open(path, "rb").read())
     return h.hexdigest()
 

@@ -245,7 +245,7 @@ __device__ __forceinline__ void wide_outputs(const RouteArgs& p, int lane, int h
 // One 16-row group: score table, then the ledger rows.  Called by every wave of the block.
 // Exact top-(k+m) of NR rows (block rows bi[r], query rows row[r]) from the score table, the
 // rows side by side, then each row's ledger write.
-template <bool CAUSAL, int NR>
+template <bool CAUSAL, bool REROUTE, int NR>
 __device__ __forceinline__ void emit_rows(const RouteArgs& p, WideShared& sh, int wave, int lane, int h,
                                           const int (&row)[NR], const int (&bi)[NR]) {
     // Opaque per call: otherwise the sorts' per-lane stage conditions are hoisted out of the
@@ -267,24 +267,49 @@ __device__ __forceinline__ void emit_rows(const RouteArgs& p, WideShared& sh, in
             lm[r] = max(lm[r], o[r][t]);
         }
     }
-    // Lanes 0 .. min(n, 64) - 1 hold at least one key and sel <= min(n, 64), so the sel-th
-    // largest lane maximum tau is a key's score: at least sel keys reach it.
-    bitonic_sort_n<64, false>(lm, lane);
+    // The prefilter bound tau: at least sel keys must reach it.  In a reroute, the rescore
+    // kernel's hint (the row's lowest current score over its old route and near-miss, -inf if a
+    // slot was empty) serves when between sel and 64 keys reach it (it comes from other
+    // arithmetic, so a key it names may score a rounding lower here).  Otherwise: lanes
+    // 0 .. min(n, 64) - 1 hold at least one key and sel <= min(n, 64), so the sel-th largest
+    // lane maximum is a key's score that at least sel keys reach.
+    uint32_t tau[NR];
+    bool need_sort = !REROUTE;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        tau[r] = 0u;
+        if constexpr (REROUTE) {
+            const float hv = p.hint[(size_t)h * p.nq + row[r]];
+            const uint32_t th = (hv > -INFINITY) ? orderable(hv) : 0u;
+            int ch = 0;
+#pragma unroll
+            for (int t = 0; t < WKT; ++t) ch += (o[r][t] >= th) ? 1 : 0;
+            const int C = wave_sum_i(ch);
+            if (th != 0u && C >= sel[r] && C <= 64) tau[r] = th;
+            else need_sort = true;
+        }
+    }
+    if (need_sort) {
+        bitonic_sort_n<64, false>(lm, lane);
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            if (tau[r] == 0u) tau[r] = (uint32_t)__builtin_amdgcn_readlane((int)lm[r], 64 - sel[r]);
+    }
     uint64_t cand[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)lm[r], 64 - sel[r]);
+        const uint32_t tau_r = tau[r];
         int cnt = 0;
 #pragma unroll
-        for (int t = 0; t < WKT; ++t) cnt += (o[r][t] >= tau) ? 1 : 0;
+        for (int t = 0; t < WKT; ++t) cnt += (o[r][t] >= tau_r) ? 1 : 0;
         const int C = wave_sum_i(cnt);
         uint64_t* list = sh.list[wave][r];
         int held;                                         // keys in the list, the top sel among them
-        if (tau != 0u && C <= 64) {
+        if (tau_r != 0u && C <= 64) {
             int pos = wave_incl_scan_i(cnt) - cnt;
 #pragma unroll
             for (int t = 0; t < WKT; ++t)
-                if (o[r][t] >= tau) list[pos++] = wkey(o[r][t], lane + 64 * t);
+                if (o[r][t] >= tau_r) list[pos++] = wkey(o[r][t], lane + 64 * t);
             held = C;
         } else {
             // More than 64 keys reach tau: an exact radix select over the 64-bit keys finds the
@@ -431,10 +456,10 @@ __device__ __forceinline__ void route_group(const RouteArgs& p, WideShared& sh, 
     if (rest != 0ull) {
         const int b1 = __builtin_ctzll(rest);
         const int rows[2] = {r0 + b0, r0 + b1}, bis[2] = {b0, b1};
-        emit_rows<CAUSAL, 2>(p, sh, wave, lane, h, rows, bis);
+        emit_rows<CAUSAL, REROUTE, 2>(p, sh, wave, lane, h, rows, bis);
     } else {
         const int rows[1] = {r0 + b0}, bis[1] = {b0};
-        emit_rows<CAUSAL, 1>(p, sh, wave, lane, h, rows, bis);
+        emit_rows<CAUSAL, REROUTE, 1>(p, sh, wave, lane, h, rows, bis);
     }
 }
 

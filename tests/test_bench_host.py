@@ -1,5 +1,5 @@
-"""Host-side pieces of bench.py: the recall metric, the fixed-stride baseline and the
-one-GPU rule (no GPU needed)."""
+"""Host-side pieces of bench.py: the recall metric, the fixed-stride baseline, the one-GPU
+rule and the traffic record's source check (no GPU needed)."""
 import os
 import subprocess
 import sys
@@ -36,3 +36,16 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_traffic_record_needs_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    """The committed counter summary is used only while the hash of the routing kernel source,
+    its headers and the build script matches the one written in it; any change to those files
+    (here: one more byte in a copy of the source) turns the traffic figure into None."""
+    good = bench.kernel_build_hash()
+    src = tmp_path / "rr_kernels.hip"
+    src.write_bytes(open(bench.KERNEL_SRCS[0], "rb").read() + b"\n")
+    monkeypatch.setattr(bench, "KERNEL_SRCS", (str(src),) + tuple(bench.KERNEL_SRCS[1:]))
+    assert bench.kernel_build_hash() != good
+    assert bench.recorded_traffic("reroute") is None
+    assert any(p.endswith("rr_device.h") for p in bench.KERNEL_SRCS)

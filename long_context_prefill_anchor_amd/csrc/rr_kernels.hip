@@ -1088,7 +1088,7 @@ __device__ __forceinline__ int cand_of_lane(int lane) {
 // flight while a row is reduced.  The block ends by listing its flagged rows (ascending) for
 // the reroute kernel.
 template <typename DT, int NP>
-__global__ __launch_bounds__(RESCORE_THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(typename Elem<DT>::type) == 2 && NP == 1 ? 8 : 4)))
+__global__ __launch_bounds__(RESCORE_THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(typename Elem<DT>::type) == 2 ? 8 : 4)))
 void k_rescore(RescoreArgs p) {
     typedef typename Elem<DT>::type E;
     constexpr uint32_t ROW_BYTES = 64 * sizeof(E);
@@ -1168,8 +1168,12 @@ void k_rescore(RescoreArgs p) {
             float part[NI];
 #pragma unroll
             for (int j = 0; j < NI; ++j) part[j] = Dot<DT>::acc(qv, kv[slot][j], 0.f);
-            if (rr + DEPTH < RS_ROWS) issue(slot, rr + DEPTH);
+            // fp32 rows with 64 candidates: the next row's 16 loads would stay live through the
+            // reduce-scatter and spill, so they go out after it.
+            constexpr bool LATE = NP == 2;
+            if (!LATE && rr + DEPTH < RS_ROWS) issue(slot, rr + DEPTH);
             const float sc = reduce_scatter<LPR, NP>(part, lane);
+            if (LATE && rr + DEPTH < RS_ROWS) issue(slot, rr + DEPTH);
             const bool valid = (cown < p.c) && sid[wave][rr * p.c + min(cown, p.c - 1)] >= 0;
             const float vr = (ownR && valid) ? sc : INFINITY;
             const float vsel = (ownSel && valid) ? sc : INFINITY;

@@ -224,6 +224,71 @@ def drift_sweep_batched(sigmas=(0.01, 0.03, 0.06), steps=2, warmup=1):
     return out
 
 
+def quality_only(w):
+    """Untimed quality pass of one workload (relay chain and full-routing comparator)."""
+    led = rr.Ledger(w.heads, w.nq, w.nk, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed,
+                    sink=w.sink, recent=w.recent, min_reuse=w.min_reuse, gamma_extra=w.gamma_extra)
+    full = rr.Ledger(w.heads, w.nq, w.nk, w.d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
+    qs, ks = upload_layers(w)
+    q = quality_pass(w, led, full, qs, ks)
+    led.close()
+    full.close()
+    return q
+
+
+def drift_sweep_table2(sigmas=(0.01, 0.03, 0.06), seeds=10):
+    """The drift-sweep workload as stated (1 head x 256 chunks, fp32, 16 layers, anchor stride 8,
+    k = 12, m = 12, r = 8, ten seeds): per drift, the means over the seeds of the rerouted
+    fraction and the recall against full routing (all layers and relay layers' rho), the
+    analogue of the page's Table 2; relay and full-routing layer times at seed 0 (one head
+    of 256 rows: launch-bound)."""
+    import torch
+    out = []
+    for sigma in sigmas:
+        acc = np.zeros(5)
+        for seed in range(seeds):
+            q = quality_only(W.drift_sweep(sigma, seed))
+            acc += [q["recall"], q["reroute_fraction"], q["relay_rho_mean"], q["pair_fraction"],
+                    q["stride4_recall"]]
+        acc /= seeds
+        t = relay_vs_full(W.drift_sweep(sigma, 0), steps=5, warmup=2)
+        out.append({"sigma": sigma, "seeds": seeds, "recall": round(float(acc[0]), 6),
+                    "reroute_fraction": round(float(acc[1]), 4), "relay_rho_mean": round(float(acc[2]), 4),
+                    "pair_fraction": round(float(acc[3]), 4), "fixed_stride4_recall": round(float(acc[4]), 6),
+                    "relay_layer_us_median_seed0": t["relay_layer_us_median"],
+                    "full_layer_us_median_seed0": t["full_layer_us_median"],
+                    "speedup_vs_full_seed0": t["speedup_vs_full"]})
+    torch.cuda.empty_cache()
+    return out
+
+
+def scale_sweep_table4(ns=(128, 256, 512, 1024), seeds=3):
+    """The scale-sweep workload as stated (1 head, n in {128, 256, 512, 1024} chunks, bf16,
+    32 layers, drift 0.03, anchor stride 8, k = 12, m = 12, r = 8), seeds 0-2 like the page's
+    three seeds: per n, the means of the fraction of full-routing score pairs evaluated, the
+    recall, the rerouted fraction and relay rho (the analogue of the page's Table 4); relay
+    routes/s, layer times and speedup against the same GPU's full routing at seed 0."""
+    import torch
+    out = []
+    for n in ns:
+        acc = np.zeros(4)
+        for seed in range(seeds):
+            q = quality_only(W.scale_sweep(n, seed))
+            acc += [q["pair_fraction"], q["recall"], q["reroute_fraction"], q["relay_rho_mean"]]
+        acc /= seeds
+        t = relay_vs_full(W.scale_sweep(n, 0), steps=5, warmup=2)
+        out.append({"n": n, "seeds": seeds, "pair_fraction": round(float(acc[0]), 4),
+                    "recall": round(float(acc[1]), 6), "reroute_fraction": round(float(acc[2]), 4),
+                    "relay_rho_mean": round(float(acc[3]), 4),
+                    "relay_routes_per_s_seed0": t["relay_routes_per_s"],
+                    "full_routing_routes_per_s_seed0": t["full_routing_routes_per_s"],
+                    "relay_layer_us_median_seed0": t["relay_layer_us_median"],
+                    "full_layer_us_median_seed0": t["full_layer_us_median"],
+                    "speedup_vs_full_seed0": t["speedup_vs_full"]})
+    torch.cuda.empty_cache()
+    return out
+
+
 def sentinel_ablation(seeds=5):
     """Sentinel mixes on the pages' ablation setting (1 x 256 chunks, fp32, 24 layers, drift
     0.003, k = 12; anchors every 8 layers, as in the other chains): mean recall against full
@@ -437,20 +502,25 @@ def relay_vs_full(w, steps, warmup):
     return out
 
 
-def cpu_baseline(w, max_seconds=20.0):
-    """The oracle, unmodified, on a bounded sample: the first heads of the same workload, as
-    many chain layers as fit in ~max_seconds; single-threaded BLAS."""
+CPU_WORKERS_MAX = 16             # the GPU machine's CPU share for one GPU
+
+
+def _cpu_head_chain(args):
+    """One worker of cpu_baseline: the oracle, unmodified, on one head of the workload (its own
+    seeded layers), for as many chain layers as fit in `budget` seconds (at least two relay
+    layers), with single-threaded BLAS.  Returns (anchor layers, their seconds, relay layers,
+    their seconds)."""
+    w, h, budget = args
     import oracle as O
     from threadpoolctl import threadpool_limits
-    heads = 4
-    cfg = O.RouteConfig(heads=heads, nq=w.n, nk=w.n, d=w.d, k=w.k, m=w.m, r=w.r, gamma=w.gamma,
+    cfg = O.RouteConfig(heads=1, nq=w.n, nk=w.n, d=w.d, k=w.k, m=w.m, r=w.r, gamma=w.gamma,
                         causal=w.causal, seed=w.seed, dtype=w.dtype)
     t_relay = t_anchor = 0.0
     n_relay = n_anchor = 0
     led = None
     t_start = time.perf_counter()
     with threadpool_limits(limits=1):
-        for li in synth.generate(w, slice(0, heads)):
+        for li in synth.generate(w, slice(h, h + 1)):
             t0 = time.perf_counter()
             if led is None or w.is_anchor(li.layer):
                 led = O.anchor_layer(cfg, li.q, li.k, li.layer)
@@ -460,15 +530,35 @@ def cpu_baseline(w, max_seconds=20.0):
                 led = O.relay_layer(cfg, li.q, li.k, li.layer, led).ledger
                 t_relay += time.perf_counter() - t0
                 n_relay += 1
-            if time.perf_counter() - t_start > max_seconds and n_relay >= 2:
+            if time.perf_counter() - t_start > budget and n_relay >= 2:
                 break
-    rows = heads * w.n
-    return {"value": rows * n_relay / t_relay, "unit": "relay-layer query-row routes/s",
-            "cores": 1, "kind": "oracle",
-            "sample": f"{heads} of {w.heads} heads, layers 0-{n_anchor + n_relay - 1} "
-                      f"({n_anchor} anchor, {n_relay} relay), single-threaded NumPy",
-            "full_routing_value": rows * n_anchor / t_anchor if n_anchor else None,
-            "relay_over_full_time": (t_relay / n_relay) / (t_anchor / n_anchor) if n_anchor else None}
+    return n_anchor, t_anchor, n_relay, t_relay
+
+
+def cpu_baseline(w, max_seconds=20.0):
+    """The oracle, unmodified, on a bounded sample of the same workload, on the host's cores:
+    one worker process per core (at most CPU_WORKERS_MAX), each running one head's chain with
+    single-threaded BLAS for ~max_seconds; heads are independent, so the workers' rates add up.
+    Call it before the GPU is initialised: the workers are started as fresh interpreters."""
+    import multiprocessing as mp
+    cores = max(1, min(len(os.sched_getaffinity(0)), CPU_WORKERS_MAX, w.heads))
+    with mp.get_context("spawn").Pool(cores) as pool:
+        res = pool.map(_cpu_head_chain, [(w, h, max_seconds) for h in range(cores)])
+    rows = w.n
+    relay_rate = sum(rows * nr / tr for _, _, nr, tr in res)
+    full_rate = sum(rows * na / ta for na, ta, _, _ in res)
+    per_relay = float(np.mean([tr / nr for _, _, nr, tr in res]))
+    per_anchor = float(np.mean([ta / na for na, ta, _, _ in res]))
+    n_rel = [nr for _, _, nr, _ in res]
+    n_anc = [na for na, _, _, _ in res]
+    return {"value": relay_rate, "unit": "relay-layer query-row routes/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"heads 0-{cores - 1} of {w.heads}, one head per worker process (single-threaded "
+                      f"NumPy each), {min(n_anc)}-{max(n_anc)} anchor and {min(n_rel)}-{max(n_rel)} relay "
+                      f"layers per head from layer 0 (~{max_seconds:g} s per worker); value = sum of the "
+                      f"workers' relay-layer rates",
+            "full_routing_value": full_rate,
+            "relay_over_full_time": per_relay / per_anchor}
 
 
 def kernel_build_hash():
@@ -526,6 +616,13 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); heads shard across GPUs "
               "with no exchange, so run one process per GPU on its own heads.", file=sys.stderr)
         sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.only_attention:
+        # before the GPU is initialised: the oracle's worker processes start from a clean parent
+        log("[bench] cpu_baseline: oracle on a bounded sample, on the host cores")
+        cpu = cpu_baseline(W.batched_heads(), args.cpu_seconds)
+        log(f"[bench] cpu_baseline: {cpu['value']:.1f} routes/s on {cpu['cores']} cores")
 
     import torch
     if not torch.cuda.is_available():
@@ -632,6 +729,12 @@ def main():
     torch.cuda.empty_cache()
     secondary = None if args.no_secondary else secondary_causal()
     drift_sweep = None if args.no_secondary else drift_sweep_batched()
+    drift_t2 = scale_t4 = None
+    if not args.no_secondary:
+        log("[bench] drift sweep workload (1 x 256 fp32, ten seeds per drift)")
+        drift_t2 = drift_sweep_table2()
+        log("[bench] scale sweep workload (1 x {128 .. 1024} bf16, three seeds per size)")
+        scale_t4 = scale_sweep_table4()
     ablation = None if args.no_secondary else sentinel_ablation()
     preferred = None if args.no_secondary else preferred_chunks_sweep()
     buckets = None if args.no_secondary else width_buckets()
@@ -669,11 +772,6 @@ def main():
         mandatory = relay_vs_full(W.batched_heads().with_(name="batched_heads_mandatory", sink=1,
                                                           recent=2, r=5), steps=3, warmup=1)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] cpu_baseline: oracle on a bounded sample")
-        cpu = cpu_baseline(w, args.cpu_seconds)
-
     out = {
         "metric": "relay-layer query-row routes/sec at Nk=1024 + speedup vs full routing; top-k recall",
         "value": round(value, 1),
@@ -708,6 +806,8 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
         "drift_sweep": drift_sweep,
+        "drift_sweep_1x256": drift_t2,
+        "scale_sweep": scale_t4,
         "sentinel_ablation": ablation,
         "mandatory_sentinels": mandatory,
         "preferred_chunks": preferred,

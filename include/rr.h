@@ -107,7 +107,12 @@ typedef struct {
 rr_status rr_config_check(const rr_config* cfg);
 
 /* Allocate a ledger and its scratch memory on the current HIP device (the only allocating
- * call).  The ledger starts empty: the first compute call on it must be rr_anchor_route. */
+ * call).  The ledger is the routing state of Section 4.1 (three row-major tensors: the route
+ * IDs, the sentinel IDs and the anchor layer of each query row, Eq. 4), held in device memory
+ * owned by the library until rr_ledger_destroy.  It starts empty: the first compute call on it
+ * must be rr_anchor_route.  Errors: RR_EINVAL / RR_EUNSUPPORTED for a bad or unsupported
+ * configuration (see rr_config_check), RR_ENOMEM if an allocation fails, RR_EDEVICE if
+ * initialising it fails; *out is then NULL. */
 rr_status rr_ledger_create(const rr_config* cfg, rr_ledger** out);
 
 /* Width bucket (Section 4.4: ledgers are bucketed by route width; Section 4.3: the ledger
@@ -136,16 +141,23 @@ rr_status rr_anchor_route(rr_ledger* ledger, const void* q, const void* k, int32
 rr_status rr_relay_layer(rr_ledger* ledger, const void* q, const void* k, int32_t layer,
                          void* stream, const rr_relay_out* out);
 
-/* Copy the ledger out (layout above).  Any pointer may be NULL to skip that tensor.
- * dst_is_host = 1: host memory, the call waits for `stream`; 0: device memory, asynchronous. */
+/* Copy the ledger out as the three tensors of Section 4.1 (layout above: route
+ * [heads, nq, k], sentinels [heads, nq, m + sink + recent + r], anchor layer [heads, nq], all
+ * int32, row-major; the caller owns the destination buffers, sized exactly so).  Any pointer may
+ * be NULL to skip that tensor.  dst_is_host = 1: host memory, the call waits for `stream`;
+ * 0: device memory, asynchronous.  Errors: RR_EINVAL for a NULL ledger, RR_ESTATE if the ledger
+ * is poisoned, RR_EDEVICE if a copy fails. */
 rr_status rr_ledger_get(const rr_ledger* ledger, int32_t* route, int32_t* sent,
                         int32_t* anchor_layer, int32_t dst_is_host, void* stream);
 
-/* Replace the whole ledger (snapshot restore / replay): route, sent and anchor_layer are
- * required, same layout as rr_ledger_get; `last_layer` becomes the last layer seen, so the
- * next relay call must use a greater layer.  The IDs are trusted to be valid for this
- * configuration (in range, allowed, distinct per row).  The hysteresis state is cleared (see
- * rr_ledger_set_refreshed).  src_is_host as in rr_ledger_get. */
+/* Replace the whole ledger (snapshot restore / replay) with the three tensors of Section 4.1:
+ * route, sent and anchor_layer are required, same layout as rr_ledger_get, caller-owned and
+ * only read; `last_layer` becomes the last layer seen, so the next relay call must use a
+ * greater layer.  The IDs are trusted to be valid for this configuration (in range, allowed,
+ * distinct per row; IDs outside [0, nk) are treated as padding by the relay rescoring, a
+ * causal-violating or repeated ID is not detected).  The hysteresis state is cleared (see
+ * rr_ledger_set_refreshed).  src_is_host as in rr_ledger_get.  Errors: RR_EINVAL for NULL
+ * arguments or last_layer < 0; RR_EDEVICE if a copy fails (the ledger is then poisoned). */
 rr_status rr_ledger_set(rr_ledger* ledger, const int32_t* route, const int32_t* sent,
                         const int32_t* anchor_layer, int32_t last_layer, int32_t src_is_host,
                         void* stream);

@@ -1168,8 +1168,10 @@ void k_rescore(RescoreArgs p) {
             float part[NI];
 #pragma unroll
             for (int j = 0; j < NI; ++j) part[j] = Dot<DT>::acc(qv, kv[slot][j], 0.f);
-            // fp32 rows with 64 candidates: the next row's 16 loads would stay live through the
-            // reduce-scatter and spill, so they go out after it.
+            // Two candidate passes (c > 32), bf16 and fp32 alike: the next row's loads (8 or 16
+            // of them) would stay live through the reduce-scatter and push the kernel past its
+            // register budget (64 VGPRs for bf16 at eight waves per SIMD), so they go out after
+            // it.  The build's resource report and its test check that no k_rescore spills.
             constexpr bool LATE = NP == 2;
             if (!LATE && rr + DEPTH < RS_ROWS) issue(slot, rr + DEPTH);
             const float sc = reduce_scatter<LPR, NP>(part, lane);

@@ -280,14 +280,47 @@ def relay_decision(cfg: RouteConfig, layer: int, anchor: int, refreshed: int,
     return (not reuse), 0
 
 
+def _relay_row(cfg: RouteConfig, qi: np.ndarray, Kh: np.ndarray, layer: int,
+               ledger: Ledger, out: Ledger, h: int, i: int):
+    """One row of an intermediate layer: score its candidate set A = R U C at this layer
+    (Eq. 5); alpha = min over R (Eq. 6), beta = max over C (Eq. 7), -inf when C is empty;
+    reuse iff alpha > beta + gamma (Eq. 8, with the hysteresis of ``relay_decision``).
+    A failing row is routed in full at this layer into ``out`` and marked refreshed.
+    Returns (flag, alpha, beta, candidate scores in ledger order with NaN for padding)."""
+    ids = np.concatenate([ledger.route[h, i], ledger.sent[h, i]])
+    valid = ids >= 0
+    s = score_rows(qi[None, :], Kh[ids[valid]])[0]
+    cand = np.full(cfg.c, np.nan, np.float32)
+    cand[valid] = s
+    n_route = int(valid[: cfg.k].sum())
+    s_route, s_sent = s[:n_route], s[n_route:]
+    a = np.float32(s_route.min())
+    b = np.float32(s_sent.max()) if s_sent.size else np.float32(-np.inf)
+    refresh, state = relay_decision(cfg, layer, int(ledger.anchor[h, i]), int(ledger.refreshed[h, i]), a, b)
+    if refresh:
+        rebuild_row(cfg, out, h, layer, i, score_rows(qi[None, :], Kh)[0])
+        out.refreshed[h, i] = 1
+    else:
+        out.refreshed[h, i] = state
+    return (1 if refresh else 0), a, b, cand
+
+
 def relay_layer(cfg: RouteConfig, q: np.ndarray, k: np.ndarray, layer: int,
                 ledger: Ledger) -> RelayResult:
-    """Intermediate layer (Sections 3.2, 4.1, 4.2).  For each row: score the
-    candidate set A = R U C (Eq. 5) at this layer; alpha = min over R (Eq. 6),
-    beta = max over C (Eq. 7); the route is reused iff alpha > beta + gamma (Eq. 8,
-    with the hysteresis of ``relay_decision``).  Otherwise the row is routed in full at
-    this layer, its ledger entry replaced and marked refreshed.  Flagged rows are listed
-    in ascending flattened order h * nq + i (the compaction of Section 4.1/4.2)."""
+    """Intermediate layer (Sections 3.2, 4.1, 4.2): every row goes through ``_relay_row``.
+    Flagged rows are listed in ascending flattened order h * nq + i (the compaction of
+    Section 4.1/4.2)."""
+    return relay_layer_rows(cfg, q, k, layer, ledger,
+                            [(h, i) for h in range(cfg.heads) for i in range(cfg.nq)])
+
+
+def relay_layer_rows(cfg: RouteConfig, q: np.ndarray, k: np.ndarray, layer: int,
+                     ledger: Ledger, rows) -> RelayResult:
+    """The intermediate layer of ``relay_layer`` restricted to the (h, i) pairs in ``rows``
+    (rows are independent, Section 3.2): flags, alpha, beta, candidate scores and ledger
+    entries are those of ``relay_layer`` at those rows; every other row keeps its input
+    ledger entry, flag 0, alpha = beta = 0 and NaN scores.  ``rows`` lists and head counts
+    cover the given rows only."""
     Q, K = decode(q, cfg.dtype), decode(k, cfg.dtype)
     out = ledger.copy()
     H, nq, c = cfg.heads, cfg.nq, cfg.c
@@ -295,31 +328,14 @@ def relay_layer(cfg: RouteConfig, q: np.ndarray, k: np.ndarray, layer: int,
     alpha = np.zeros((H, nq), np.float32)
     beta = np.zeros((H, nq), np.float32)
     cand = np.full((H, nq, c), np.nan, np.float32)
-    for h in range(H):
-        Qr = query_rows(cfg, Q[h])
-        for i in range(nq):
-            ids = np.concatenate([ledger.route[h, i], ledger.sent[h, i]])
-            valid = ids >= 0
-            qi = Qr[i]
-            s = score_rows(qi[None, :], K[h][ids[valid]])[0]
-            cand[h, i, valid] = s
-            rmask = valid[: cfg.k]
-            s_route = s[: int(rmask.sum())]
-            s_sent = s[int(rmask.sum()):]
-            a = np.float32(s_route.min())
-            b = np.float32(s_sent.max()) if s_sent.size else np.float32(-np.inf)
-            alpha[h, i], beta[h, i] = a, b
-            refresh, state = relay_decision(cfg, layer, int(ledger.anchor[h, i]),
-                                            int(ledger.refreshed[h, i]), a, b)
-            if refresh:
-                flags[h, i] = 1
-                rebuild_row(cfg, out, h, layer, i, score_rows(qi[None, :], K[h])[0])
-                out.refreshed[h, i] = 1
-            else:
-                out.refreshed[h, i] = state
-    rows = np.flatnonzero(flags.reshape(-1)).astype(np.int32)
-    return RelayResult(out, flags, alpha, beta, cand, rows,
-                       flags.sum(axis=1).astype(np.int32))
+    Qrows = {}
+    for h, i in rows:
+        if h not in Qrows:
+            Qrows[h] = query_rows(cfg, Q[h])
+        flags[h, i], alpha[h, i], beta[h, i], cand[h, i] = _relay_row(cfg, Qrows[h][i], K[h], layer,
+                                                                      ledger, out, h, i)
+    flat = np.flatnonzero(flags.reshape(-1)).astype(np.int32)
+    return RelayResult(out, flags, alpha, beta, cand, flat, flags.sum(axis=1).astype(np.int32))
 
 
 # ----------------------------------------------------------------------------- full routing every layer

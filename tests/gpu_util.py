@@ -91,20 +91,54 @@ def compare_ledgers(gpu, ora: O.Ledger, mask: np.ndarray, what: str):
 
 
 def check_scores(got, ref, rel, rms, what):
+    """|got - ref| <= rel * (|ref| + rms) where the oracle value is finite; where it is NaN
+    (no ID) or +-inf (beta of a row without sentinels) the GPU value must be the same
+    NaN / infinity.  Returns the largest error over the finite oracle values."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
-    both_nan = np.isnan(got) & np.isnan(ref)
-    both_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
-    ok = both_nan | both_inf
-    err = np.where(ok, 0.0, np.abs(got - ref))
-    lim = rel * (np.abs(np.where(ok, 0, ref)) + rms)
-    bad = ~(ok | (err <= lim))
-    if bad.any():
-        idx = np.argwhere(bad)[0]
-        raise AssertionError(f"{what}: {bad.sum()} values out of tolerance, first {tuple(idx)}: "
-                             f"gpu={got[tuple(idx)]} oracle={ref[tuple(idx)]}")
-    finite = np.isfinite(err)
-    return float(err[finite].max()) if finite.any() else 0.0
+    rms = np.broadcast_to(np.asarray(rms, np.float64), np.broadcast_shapes(got.shape, ref.shape))
+    got, ref = np.broadcast_arrays(got, ref)
+    fin = np.isfinite(ref)
+    special_ok = (np.isnan(ref) & np.isnan(got)) | (np.isinf(ref) & (got == ref))
+    err = np.zeros(got.shape)
+    err[fin] = np.abs(got[fin] - ref[fin])
+    lim = np.zeros(got.shape)
+    lim[fin] = rel * (np.abs(ref[fin]) + rms[fin])
+    ok = np.where(fin, np.isfinite(got) & (err <= lim), special_ok)
+    if not ok.all():
+        idx = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{what}: {int((~ok).sum())} values out of tolerance, first {idx}: "
+                             f"gpu={got[idx]} oracle={ref[idx]}")
+    return float(err[fin].max()) if fin.any() else 0.0
+
+
+def check_compaction(g_rows, g_counts, g_flags, res, mask, what):
+    """The GPU's compacted list (Sections 4.1-4.2: ascending h*nq+i of flagged rows) and its
+    per-head counts against the oracle's, on rows outside the exclusion mask: the list must be
+    strictly ascending, name exactly the rows the oracle flags among the compared rows, and
+    each head count must equal the oracle's plus the GPU-minus-oracle flag difference on that
+    head's excluded rows."""
+    H, nq = res.flags.shape
+    g_rows = np.asarray(g_rows, np.int64)
+    assert np.all(np.diff(g_rows) > 0), f"{what}: compacted list not strictly ascending"
+    assert g_rows.size == 0 or (g_rows[0] >= 0 and g_rows[-1] < H * nq), f"{what}: list entry out of range"
+    listed = np.zeros(H * nq, np.uint8)
+    listed[g_rows] = 1
+    listed = listed.reshape(H, nq)
+    if not np.array_equal(listed[mask], res.flags[mask]):
+        h, i = np.argwhere(mask & (listed != res.flags))[0]
+        raise AssertionError(f"{what}: compacted list differs from the oracle's at row (h={h}, i={i}): "
+                             f"gpu lists it {bool(listed[h, i])}, oracle flags it {bool(res.flags[h, i])}")
+    ora_rows = set(int(x) for x in res.rows)
+    cmp_rows = set(int(x) for x in np.flatnonzero(mask.reshape(-1)))
+    assert (set(int(x) for x in g_rows) & cmp_rows) == (ora_rows & cmp_rows), f"{what}: compacted list"
+    diff = ((np.asarray(g_flags, np.int64) - res.flags.astype(np.int64)) * (~mask)).sum(axis=1)
+    expect = res.head_counts.astype(np.int64) + diff
+    if not np.array_equal(np.asarray(g_counts, np.int64), expect):
+        h = int(np.flatnonzero(np.asarray(g_counts) != expect)[0])
+        raise AssertionError(f"{what}: head count of head {h}: gpu={g_counts[h]} oracle={res.head_counts[h]} "
+                             f"(+{diff[h]} from excluded rows)")
+    assert np.array_equal(np.asarray(g_counts), listed.sum(axis=1)), f"{what}: head counts vs the list"
 
 
 def run_anchor(led: rr.Ledger, q, k, layer: int):
@@ -117,11 +151,12 @@ def run_anchor(led: rr.Ledger, q, k, layer: int):
 def anchor_parity(led, cfg, q, k, layer, tol, rep: Report, rows=None):
     """GPU anchor layer vs oracle on all rows (or the given (h, i) sample)."""
     gpu = run_anchor(led, q, k, layer)
-    S = oracle_scores(cfg, q, k)
     if rows is None:
+        S = oracle_scores(cfg, q, k)
         ora = O.anchor_layer(cfg, q, k, layer)
         mask = ~selection_excluded(cfg, S, tol)
     else:
+        S = sampled_score_rows(cfg, q, k, rows)         # {(h, i): row}: no full score matrix
         ora = O.Ledger.empty(cfg)
         for h, i in rows:
             O.rebuild_row(cfg, ora, h, layer, i, S[h, i])
@@ -166,6 +201,7 @@ def relay_parity(led, cfg, q, k, layer, ledger_in: O.Ledger, tol, rel, rep: Repo
     g_counts = out.head_counts.cpu().numpy()
 
     # the compacted list is exactly the GPU's own flagged rows, ascending, with matching counts
+    # (and below, on the compared rows, the oracle's list and counts)
     assert np.array_equal(g_rows, np.flatnonzero(g_flags.reshape(-1))), "compacted list"
     assert np.array_equal(g_counts, g_flags.sum(axis=1)), "head counts"
 
@@ -196,5 +232,84 @@ def relay_parity(led, cfg, q, k, layer, ledger_in: O.Ledger, tol, rel, rep: Repo
         bad = np.argwhere(mask & (g_flags != res.flags))[0]
         raise AssertionError(f"layer {layer}: flags differ, first {tuple(bad)}: gpu={g_flags[tuple(bad)]} "
                              f"oracle={res.flags[tuple(bad)]} alpha={res.alpha[tuple(bad)]} beta={res.beta[tuple(bad)]}")
+    check_compaction(g_rows, g_counts, g_flags, res, mask, f"relay layer {layer}")
     compare_ledgers(gpu, res.ledger, mask, f"relay layer {layer}")
     return gpu, res, ex
+
+
+def sampled_score_rows(cfg: O.RouteConfig, q, k, rows):
+    """Oracle score rows (fp32, Eq. 1) of the given (h, i) pairs only: {(h, i): [nk]}."""
+    Q, K = O.decode(q, cfg.dtype), O.decode(k, cfg.dtype)
+    out = {}
+    by_head = {}
+    for h, i in rows:
+        by_head.setdefault(h, []).append(i)
+    for h, ii in by_head.items():
+        S = O.score_rows(O.query_rows(cfg, Q[h])[np.asarray(ii)], K[h])
+        for r, i in enumerate(ii):
+            out[(h, i)] = S[r]
+    return out
+
+
+def relay_parity_sampled(led, cfg, q0, k0, q1, k1, rows, tol, rel, rep: Report):
+    """GPU anchor at layer 0 and relay at layer 1 over every row; the oracle on the sampled
+    (h, i) pairs only: its own anchor ledger entries for those rows, then its relay of them
+    (rows are independent, Section 3.2).  Compared on the sampled rows outside the exclusions:
+    the anchor ledger, then flags, alpha, beta, candidate scores, the rerouted ledger rows and
+    the compacted list; on every row: the list equals the GPU's own flags, ascending, and the
+    head counts match it.  Returns (number of compared rows, flagged among them)."""
+    import torch
+    H, nq = cfg.heads, cfg.nq
+    rows = sorted(set((int(h), int(i)) for h, i in rows))
+    gpu0 = run_anchor(led, q0, k0, 0)
+    S0 = sampled_score_rows(cfg, q0, k0, rows)
+    ora0 = O.Ledger.empty(cfg)
+    mask = np.zeros((H, nq), bool)
+    for h, i in rows:
+        O.rebuild_row(cfg, ora0, h, 0, i, S0[(h, i)])
+        mask[h, i] = O.selection_gap(S0[(h, i)], O.n_allowed(i, cfg), cfg.k, cfg.m) >= tol
+    compare_ledgers(gpu0, ora0, mask, "sampled anchor layer 0")
+
+    out = led.alloc_outputs()
+    led.relay(upload(q1), upload(k1), 1, out)
+    torch.cuda.synchronize()
+    gpu1 = ledger_np(led)
+    g_flags = out.flags.cpu().numpy().reshape(H, nq)
+    g_alpha = out.alpha.cpu().numpy().reshape(H, nq)
+    g_beta = out.beta.cpu().numpy().reshape(H, nq)
+    g_cand = out.cand_scores.cpu().numpy().reshape(H, nq, cfg.c)
+    n_rows = int(out.n_rows.cpu().numpy()[0])
+    g_rows = out.rows.cpu().numpy()[:n_rows]
+    g_counts = out.head_counts.cpu().numpy()
+    # every row: the list is the GPU's own flagged rows, ascending; counts per head match it
+    assert np.array_equal(g_rows, np.flatnonzero(g_flags.reshape(-1))), "compacted list vs flags"
+    assert np.array_equal(g_counts, g_flags.sum(axis=1)), "head counts vs flags"
+
+    res = O.relay_layer_rows(cfg, q1, k1, 1, ora0, rows)
+    S1 = None
+    for h, i in rows:
+        if not mask[h, i]:
+            continue
+        if relay_excluded(cfg, 1, ora0, h, i, res.alpha[h, i], res.beta[h, i], tol):
+            mask[h, i] = False
+        elif res.flags[h, i]:
+            if S1 is None:
+                S1 = sampled_score_rows(cfg, q1, k1, [(a, b) for a, b in rows if res.flags[a, b]])
+            if O.selection_gap(S1[(h, i)], O.n_allowed(i, cfg), cfg.k, cfg.m) < tol:
+                mask[h, i] = False
+    rep.rows += len(rows)
+    rep.excluded += len(rows) - int(mask.sum())
+    rms = np.sqrt(np.nanmean(res.cand_scores[mask].astype(np.float64) ** 2, axis=1))
+    e1 = check_scores(g_cand[mask], res.cand_scores[mask], rel, rms[:, None], "sampled candidate scores")
+    e2 = check_scores(g_alpha[mask], res.alpha[mask], rel, rms, "sampled alpha")
+    e3 = check_scores(g_beta[mask], res.beta[mask], rel, rms, "sampled beta")
+    rep.max_score_err = max(rep.max_score_err, e1, e2, e3)
+    if not np.array_equal(g_flags[mask], res.flags[mask]):
+        bad = np.argwhere(mask & (g_flags != res.flags))[0]
+        raise AssertionError(f"sampled relay: flags differ at {tuple(bad)}: gpu={g_flags[tuple(bad)]} "
+                             f"oracle={res.flags[tuple(bad)]}")
+    listed = np.zeros(H * nq, np.uint8)
+    listed[g_rows] = 1
+    assert np.array_equal(listed.reshape(H, nq)[mask], res.flags[mask]), "compacted list vs oracle flags"
+    compare_ledgers(gpu1, res.ledger, mask, "sampled relay layer 1")
+    return int(mask.sum()), int(res.flags[mask].sum())

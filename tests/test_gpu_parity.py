@@ -202,7 +202,10 @@ def run_chain_gpu_vs_oracle(w: W.Workload, heads=None, tol=U.GAP_TOL):
             rep.notes.append(int(ex.sum()))
             assert np.array_equal(g_flags[mask], res.flags[mask]), f"{w.name} layer {li.layer}: flags"
             n_rows = int(out.n_rows.cpu().numpy()[0])
-            assert np.array_equal(out.rows.cpu().numpy()[:n_rows], np.flatnonzero(g_flags.reshape(-1)))
+            g_rows = out.rows.cpu().numpy()[:n_rows]
+            assert np.array_equal(g_rows, np.flatnonzero(g_flags.reshape(-1)))
+            U.check_compaction(g_rows, out.head_counts.cpu().numpy(), g_flags, res, mask,
+                               f"{w.name} relay layer {li.layer}")
             U.compare_ledgers(gpu, res.ledger, mask, f"{w.name} relay layer {li.layer}")
             ora_led = res.ledger
     led.close()
@@ -457,6 +460,30 @@ def test_full_size_causal_large_sampled():
     rep = U.Report()
     U.anchor_parity(led, cfg, l0.q, l0.k, 0, U.GAP_TOL, rep, rows=sorted(rows))
     U.log(f"   rows={rep.rows} excluded={rep.excluded}")
+    assert rep.excluded <= max(2, rep.rows // 50)
+    led.close()
+
+
+def test_full_size_causal_large_relay_sampled():
+    """Full 64 x 4096 causal bf16: GPU anchor at layer 0 and relay at layer 1 on every row (the
+    reroute's flagged-row search then spans 64 rescore blocks per head, the edge of its
+    block-count scan); the oracle relays sampled rows from its own anchor entries: every head's
+    first 64 rows (rows shorter than k + m, sentinel segments still filling), the last 64 rows
+    of every 8th head (rows near 4095) and 2000 random (head, row) pairs."""
+    w = W.causal_large()
+    U.log("[full] causal_large anchor layer 0 + relay layer 1, sampled rows")
+    gen = synth.generate(w)
+    l0, l1 = next(gen), next(gen)
+    led, cfg = make(w.heads, w.n, w.n, w.k, w.m, w.r, w.dtype, True, w.seed)
+    rng = np.random.default_rng(1)
+    rows = {(h, i) for h in range(w.heads) for i in range(64)}
+    rows |= {(h, i) for h in range(0, w.heads, 8) for i in range(w.n - 64, w.n)}
+    rows |= {(int(h), int(i)) for h, i in zip(rng.integers(0, w.heads, 2000), rng.integers(0, w.n, 2000))}
+    rep = U.Report()
+    compared, flagged = U.relay_parity_sampled(led, cfg, l0.q, l0.k, l1.q, l1.k, rows, U.GAP_TOL, 1e-3, rep)
+    U.log(f"   sampled={rep.rows} compared={compared} flagged={flagged} excluded={rep.excluded} "
+          f"max|ds|={rep.max_score_err:.2e}")
+    assert compared >= 6000 and flagged > 1000
     assert rep.excluded <= max(2, rep.rows // 50)
     led.close()
 

@@ -27,20 +27,30 @@ def drift_chain():
     return w, layers, recs
 
 
-def test_anchor_layers_reproduce_full_routing(tiny_chain, drift_chain):
+@pytest.fixture(scope="module")
+def causal_chain():
+    """The drift-sweep chain under the causal chunk mask (j <= i): the same pins as the
+    non-causal chains, so the causal branch of exact_routes is checked too."""
+    w = W.drift_sweep(0.03, seed=2).with_(causal=True, layers=12)
+    layers = list(synth.generate(w))
+    recs = O.run_chain(cfg_of(w), layers, w.anchors, keep_ledgers=True)
+    return w, layers, recs
+
+
+def test_anchor_layers_reproduce_full_routing(tiny_chain, drift_chain, causal_chain):
     """Anchor layers perform full routing (abstract; Section 4.1): their route equals
     the exact per-layer top-k for every row."""
-    for _, _, recs in (tiny_chain, drift_chain):
+    for _, _, recs in (tiny_chain, drift_chain, causal_chain):
         for rec in recs:
             if rec.kind == "anchor":
                 np.testing.assert_array_equal(rec.used_route, rec.exact_route)
 
 
-def test_decision_consistency(tiny_chain, drift_chain):
+def test_decision_consistency(tiny_chain, drift_chain, causal_chain):
     """Unflagged row: the relayed route and the whole ledger entry are unchanged.
     Flagged row: its route is the exact top-k at this layer and its anchor layer is
     this layer (Section 3.2; Section 4.1 update path)."""
-    for _, _, recs in (tiny_chain, drift_chain):
+    for _, _, recs in (tiny_chain, drift_chain, causal_chain):
         for rec in recs:
             if rec.kind != "relay":
                 continue
@@ -232,3 +242,88 @@ def test_recovered_row_uses_the_plain_guard():
     flags, led = _run(_hyst_cfg(min_reuse=1, gamma_extra=0.1), [L0, L1, L2, L3b, L4])
     assert flags == [1, 0, 0, 0]
     assert led.refreshed[0, 0] == 0 and led.anchor[0, 0] == 1
+
+
+def test_lemma1_route_stability_causal(causal_chain):
+    """Lemma 1 (Section 3.3) under the causal mask: omitted = allowed chunks j <= i outside
+    the anchor route; Delta^a > 2 eps implies the exact top-k at l is R^a and no flag."""
+    w, layers, recs = causal_chain
+    cfg = cfg_of(w)
+    scores = [O.score_rows(O.decode(li.q, cfg.dtype)[0], O.decode(li.k, cfg.dtype)[0]).astype(np.float64)
+              for li in layers]
+    checked = 0
+    for rec in recs:
+        if rec.kind != "relay":
+            continue
+        lin = rec.ledger_in
+        for i in range(cfg.nq):
+            n = O.n_allowed(i, cfg)
+            a = int(lin.anchor[0, i])
+            R = lin.route[0, i][lin.route[0, i] >= 0]
+            Sa, Sl = scores[a][i][:n], scores[rec.layer][i][:n]
+            omitted = np.setdiff1d(np.arange(n), R)
+            delta = np.inf if omitted.size == 0 else Sa[R].min() - Sa[omitted].max()
+            eps = np.abs(Sl - Sa).max()
+            if delta > 2 * eps:
+                checked += 1
+                exact = rec.exact_route[0, i]
+                assert set(exact[exact >= 0].tolist()) == set(R.tolist())
+                assert rec.flags[0, i] == 0
+    assert checked > 20
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_exact_routes_causal_brute_force(seed):
+    """exact_routes with the causal mask against Python's sorted() over j <= i on tie-heavy
+    integer inputs: rows i < k keep all of 0..i, padded with -1."""
+    nq = 14
+    cfg = O.RouteConfig(heads=2, nq=nq, nk=nq, d=4, k=5, m=0, r=0, causal=True, seed=seed)
+    q, k = synth.integer_inputs(2, nq, 4, seed=seed, lo=-1, hi=1)
+    got = O.exact_routes(cfg, q, k)
+    for h in range(2):
+        for i in range(nq):
+            s = [sum(int(a) * int(b) for a, b in zip(q[h, i], k[h, j])) for j in range(i + 1)]
+            best = sorted(range(i + 1), key=lambda j: (-s[j], j))[: cfg.k]
+            want = sorted(best) + [-1] * (cfg.k - len(best))
+            assert got[h, i].tolist() == want, (h, i)
+
+
+# ----------------------------------------------------------------------------- exclusion gap
+# relay_gap decides which rows the GPU comparison leaves out: the distance of Eq. 8's test
+# alpha > beta + gamma from its threshold.
+
+
+def test_relay_gap_hand_worked_values():
+    assert O.relay_gap(1.0, 0.5, 0.2) == pytest.approx(0.3)
+    assert O.relay_gap(0.5, 1.0, 0.0) == pytest.approx(0.5)       # beta above alpha
+    assert O.relay_gap(0.25, 0.25, 0.0) == 0.0                     # the strict test's tie
+    assert O.relay_gap(0.7, 0.5, 0.2) == pytest.approx(0.0, abs=1e-12)   # guard sits exactly at the margin
+    assert O.relay_gap(-0.25, -0.75, 0.125) == pytest.approx(0.375)
+    assert O.relay_gap(np.float32(0.5), np.float32(0.5), 0.0) == 0.0
+
+
+def test_relay_gap_no_sentinels_is_never_near_the_threshold():
+    """beta = -inf (a row without sentinels, Eq. 7 over an empty set): the row is always
+    reused, whatever alpha and gamma are, so it can never sit near the decision."""
+    assert O.relay_gap(0.1, -np.inf, 0.0) == np.inf
+    assert O.relay_gap(-5.0, -np.inf, 0.3) == np.inf
+    cfg = O.RouteConfig(heads=1, nq=1, nk=4, d=4, gamma=0.3)
+    refresh, _ = O.relay_decision(cfg, 1, 0, 0, np.float32(-5.0), np.float32(-np.inf))
+    assert not refresh
+
+
+def test_relay_gap_is_the_distance_to_the_decision_flip():
+    """Moving alpha by less than the gap never changes Eq. 8's decision (with the guard);
+    moving it by a little more than the gap towards the threshold always does.  A gap that
+    dropped gamma, or had the sign of beta or gamma flipped, fails this on random triples."""
+    rng = np.random.default_rng(3)
+    for _ in range(2000):
+        a, b = rng.standard_normal(2)
+        g = float(rng.choice([0.0, 0.01, 0.1, 0.5]))
+        gap = O.relay_gap(a, b, g)
+        reuse = a > b + g
+        for frac in (0.25, 0.5, 0.9):
+            assert (a + frac * gap > b + g) == reuse
+            assert (a - frac * gap > b + g) == reuse
+        toward = -1.0 if reuse else 1.0
+        assert (a + toward * 1.1 * gap > b + g) != reuse

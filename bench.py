@@ -471,30 +471,32 @@ def width_buckets(steps=3, warmup=1):
     return out
 
 
-def relay_vs_full(w, steps, warmup):
+def relay_vs_full(w, steps, warmup, mode="auto", with_quality=True):
     import torch
     H, n = w.heads, w.n
     qs, ks = upload_layers(w)
     led = rr.Ledger(H, n, n, w.d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed,
                     sink=w.sink, recent=w.recent, min_reuse=w.min_reuse, gamma_extra=w.gamma_extra)
+    led.set_relay_mode(mode)
     full = rr.Ledger(H, n, n, w.d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
-    q = quality_pass(w, led, full, qs, ks)
+    q = quality_pass(w, led, full, qs, ks) if with_quality else None
     relay_ms, full_ms, _ = time_chains(w, led, full, qs, ks, steps, warmup)
     relay_layers = [l for l in range(w.layers) if not w.is_anchor(l)]
     t_relay = relay_ms[:, relay_layers].sum()
     t_full = full_ms.sum()
     out = {"workload": w.name, "heads": H, "nq": n, "nk": n, "causal": w.causal, "layers": w.layers,
            "k": w.k, "m": w.m, "r": w.r, "sink": w.sink, "recent": w.recent,
-           "min_reuse": w.min_reuse, "gamma_extra": w.gamma_extra,
+           "min_reuse": w.min_reuse, "gamma_extra": w.gamma_extra, "relay_mode": mode,
            "relay_routes_per_s": round(H * n * len(relay_layers) * steps / (t_relay / 1e3), 1),
            "full_routing_routes_per_s": round(H * n * w.layers * steps / (t_full / 1e3), 1),
            "speedup_vs_full": round(float((t_full / (w.layers * steps)) / (t_relay / (len(relay_layers) * steps))), 4),
            "relay_layer_us_median": round(float(np.median(relay_ms[:, relay_layers]) * 1e3), 2),
            "full_layer_us_median": round(float(np.median(full_ms) * 1e3), 2),
-           "recall": round(q["recall"], 6), "reroute_fraction": round(q["reroute_fraction"], 4),
-           "relay_rho_mean": round(q["relay_rho_mean"], 4), "pair_fraction": round(q["pair_fraction"], 4),
-           "fixed_stride4_recall": round(q["stride4_recall"], 6),
            "steps": steps}
+    if q is not None:
+        out.update({"recall": round(q["recall"], 6), "reroute_fraction": round(q["reroute_fraction"], 4),
+                    "relay_rho_mean": round(q["relay_rho_mean"], 4), "pair_fraction": round(q["pair_fraction"], 4),
+                    "fixed_stride4_recall": round(q["stride4_recall"], 6)})
     led.close()
     full.close()
     del qs, ks
@@ -598,6 +600,15 @@ def calib_copy():
     del a, b
 
 
+def side(fn, *a, **kw):
+    """A side measurement: its result, or {"error": ...} if it fails (the headline stands)."""
+    try:
+        return fn(*a, **kw)
+    except Exception as e:                               # noqa: BLE001 - recorded in the line
+        log(f"[bench] side measurement {fn.__name__} failed: {e!r}")
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -690,6 +701,7 @@ def main():
         return (ms * 1e3 / nl) if nl else None, nl
     t_resc, n_resc = avg_us(kt_led, rr.RR_KERNEL_RESCORE)
     t_rer, n_rer = avg_us(kt_led, rr.RR_KERNEL_REROUTE)
+    t_rel, n_rel = avg_us(kt_led, rr.RR_KERNEL_RELAY)
     t_anc, n_anc = avg_us(kt_led, rr.RR_KERNEL_ROUTE)
     t_full, n_full = avg_us(kt_full, rr.RR_KERNEL_ROUTE)
 
@@ -709,48 +721,76 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
                 "per_launch": {"flops": flops, "avg_us": round(us, 2), "launches": nl}}
 
-    rer = mfma_line("k_route<bf16, reroute> (flagged rows)", reroute_flops, t_rer, n_rer)
-    rer["traffic"] = recorded_traffic("reroute")
-    ach_resc = rescore_bytes / (t_resc * 1e-6) / 1e9
+    # rescoring flops: 2*d per candidate of every row (the fused kernel's first phase)
+    rescore_flops = 2.0 * d * H * n * w.c
     kernels = {
-        "rescore": {"kernel": "k_rescore<bf16, 1>", "bound": "hbm", "achieved": round(ach_resc, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_resc / HBM_PEAK_GBS, 4),
-                    "per_launch": {"bytes": rescore_bytes, "avg_us": round(t_resc, 2), "launches": n_resc},
-                    "traffic": recorded_traffic("rescore")},
-        "reroute": rer,
         "full_routing": mfma_line("k_route<bf16, full> (k=12, m=r=0)", full_flops, t_full, n_full),
         "anchor": mfma_line("k_route<bf16, full> (k=12, m=12, r=8)", full_flops, t_anc, n_anc),
     }
-    roofline = dict(rer)
+    roofline = None
+    if n_rel:
+        # fused relay layer: the rescoring of every row plus the full scoring of the flagged rows
+        rel = mfma_line("k_relay<bf16> (rescore + compaction + reroute of flagged rows)",
+                        rescore_flops + reroute_flops, t_rel, n_rel)
+        ach_b = rescore_bytes / (t_rel * 1e-6) / 1e9
+        rel["rescore_bytes"] = {"bytes": rescore_bytes, "achieved": round(ach_b, 1), "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": round(ach_b / HBM_PEAK_GBS, 4)}
+        rel["traffic"] = recorded_traffic("relay")
+        kernels["relay"] = rel
+        roofline = dict(rel)
+    if n_resc:
+        ach_resc = rescore_bytes / (t_resc * 1e-6) / 1e9
+        kernels["rescore"] = {"kernel": "k_rescore<bf16, 1>", "bound": "hbm", "achieved": round(ach_resc, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_resc / HBM_PEAK_GBS, 4),
+                              "per_launch": {"bytes": rescore_bytes, "avg_us": round(t_resc, 2), "launches": n_resc},
+                              "traffic": recorded_traffic("rescore")}
+    if n_rer:
+        rer = mfma_line("k_route<bf16, reroute> (flagged rows)", reroute_flops, t_rer, n_rer)
+        rer["traffic"] = recorded_traffic("reroute")
+        kernels["reroute"] = rer
+        if roofline is None:
+            roofline = dict(rer)
 
     led.close()
     full.close()
     del qs, ks
     torch.cuda.empty_cache()
-    secondary = None if args.no_secondary else secondary_causal()
-    drift_sweep = None if args.no_secondary else drift_sweep_batched()
+    secondary = None if args.no_secondary else side(secondary_causal)
+    relay_modes = None
+    if not args.no_secondary:
+        # the fused schedule needs a head's keys in 128 KB of LDS: the 1024-chunk workload only
+        relay_modes = []
+        for wl, modes in ((W.batched_heads(), ("fused", "compacted")), (W.causal_large(), ("compacted",))):
+            for mode in modes:
+                log(f"[bench] relay schedule {mode}: {wl.name}")
+                r = side(relay_vs_full, wl, steps=3, warmup=1, mode=mode, with_quality=False)
+                relay_modes.append({k: r[k] for k in ("workload", "relay_mode", "relay_layer_us_median",
+                                                      "full_layer_us_median", "speedup_vs_full",
+                                                      "relay_routes_per_s")} if "error" not in r else r)
+    drift_sweep = None if args.no_secondary else side(drift_sweep_batched)
     drift_t2 = scale_t4 = None
     if not args.no_secondary:
         log("[bench] drift sweep workload (1 x 256 fp32, ten seeds per drift)")
-        drift_t2 = drift_sweep_table2()
+        drift_t2 = side(drift_sweep_table2)
         log("[bench] scale sweep workload (1 x {128 .. 1024} bf16, three seeds per size)")
-        scale_t4 = scale_sweep_table4()
-    ablation = None if args.no_secondary else sentinel_ablation()
-    preferred = None if args.no_secondary else preferred_chunks_sweep()
-    buckets = None if args.no_secondary else width_buckets()
+        scale_t4 = side(scale_sweep_table4)
+    ablation = None if args.no_secondary else side(sentinel_ablation)
+    preferred = None if args.no_secondary else side(preferred_chunks_sweep)
+    buckets = None if args.no_secondary else side(width_buckets)
     wide = None
     if not args.no_secondary:
         log("[bench] batched heads with a 24-wide near-miss set (k + m = 36: one-wave-per-row kernel)")
-        wide = relay_vs_full(W.batched_heads().with_(name="batched_heads_nm24", m=24, r=8), steps=2, warmup=1)
+        wide = side(relay_vs_full, W.batched_heads().with_(name="batched_heads_nm24", m=24, r=8), steps=2, warmup=1)
     attention, attention_causal = None, None
     if not args.no_secondary:
         log("[bench] sparse attention over the routes (token expansion, Eq. 3)")
-        attention = sparse_attention_measure()
-        attention["routing_relay_layer_us"] = round(relay_layer_us, 2)
-        attention["routing_share_of_layer"] = round(relay_layer_us / (relay_layer_us + attention["avg_us"]), 4)
+        attention = side(sparse_attention_measure)
+        if "error" not in attention:
+            attention["routing_relay_layer_us"] = round(relay_layer_us, 2)
+            attention["routing_share_of_layer"] = round(relay_layer_us / (relay_layer_us + attention["avg_us"]), 4)
         log("[bench] causal sparse attention at the 64 x 4096 shape")
-        attention_causal = sparse_attention_measure(reps=5, causal=True)
-        if secondary is not None:
+        attention_causal = side(sparse_attention_measure, reps=5, causal=True)
+        if secondary is not None and "error" not in secondary and "error" not in attention_causal:
             attention_causal["routing_relay_layer_us"] = secondary["relay_layer_us_median"]
             attention_causal["routing_share_of_layer"] = round(
                 secondary["relay_layer_us_median"] / (secondary["relay_layer_us_median"] + attention_causal["avg_us"]), 4)
@@ -761,16 +801,16 @@ def main():
         hysteresis = []
         for mr, ge in ((1, 0.0), (1, 0.005)):
             log(f"[bench] batched heads with hysteresis (min_reuse {mr}, gamma_extra {ge})")
-            hysteresis.append(relay_vs_full(W.batched_heads().with_(name="batched_heads_hysteresis",
-                                                                    min_reuse=mr, gamma_extra=ge),
-                                            steps=3, warmup=1))
+            hysteresis.append(side(relay_vs_full, W.batched_heads().with_(name="batched_heads_hysteresis",
+                                                                          min_reuse=mr, gamma_extra=ge),
+                                   steps=3, warmup=1))
     # The headline workload with mandatory sentinels (one sink, two recent) in place of three
     # random ones: same c = 32, same kernels.
     mandatory = None
     if not args.no_secondary:
         log("[bench] batched heads with mandatory sentinels (sink 1, recent 2, r 5)")
-        mandatory = relay_vs_full(W.batched_heads().with_(name="batched_heads_mandatory", sink=1,
-                                                          recent=2, r=5), steps=3, warmup=1)
+        mandatory = side(relay_vs_full, W.batched_heads().with_(name="batched_heads_mandatory", sink=1,
+                                                                recent=2, r=5), steps=3, warmup=1)
 
     out = {
         "metric": "relay-layer query-row routes/sec at Nk=1024 + speedup vs full routing; top-k recall",
@@ -805,6 +845,7 @@ def main():
         "graph": graph,
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "relay_modes": relay_modes,
         "drift_sweep": drift_sweep,
         "drift_sweep_1x256": drift_t2,
         "scale_sweep": scale_t4,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define RR_ABI_VERSION 2
+#define RR_ABI_VERSION 3
 
 typedef enum {
     RR_OK = 0,
@@ -141,6 +141,23 @@ rr_status rr_anchor_route(rr_ledger* ledger, const void* q, const void* k, int32
 rr_status rr_relay_layer(rr_ledger* ledger, const void* q, const void* k, int32_t layer,
                          void* stream, const rr_relay_out* out);
 
+/* How a relay layer is launched (the result is the same; only the schedule differs):
+ *   RR_RELAY_FUSED      one kernel: each block takes 128 ledger rows of one head, stages the
+ *                       head's keys in LDS, rescores its rows (Eq. 5-8) from there, gathers its
+ *                       flagged rows into its first row slots (the compaction of Sections
+ *                       4.1-4.2, within the block) and routes only those in full, as two 64-row
+ *                       slices.  Needs k + m <= 32, c <= 32 and nk * d * (2 for bf16, 4 for fp32)
+ *                       <= 128 KiB (nk <= 1024 in bf16).  Latency-bound layers take this path.
+ *   RR_RELAY_COMPACTED  the two kernels of Section 4.2: rescoring of every row, then a reroute
+ *                       grid over the layer's compacted flagged rows, 64 per block, so that the
+ *                       reroute's work scales with the flagged fraction.  Large layers.
+ *   RR_RELAY_AUTO       (default) fused when it fits and heads * ceil(nq / 128) <= 512, else
+ *                       compacted.
+ * Errors: RR_EINVAL for a NULL ledger or an unknown mode; RR_EUNSUPPORTED for RR_RELAY_FUSED
+ * outside its limits. */
+typedef enum { RR_RELAY_AUTO = 0, RR_RELAY_FUSED = 1, RR_RELAY_COMPACTED = 2 } rr_relay_mode;
+rr_status rr_ledger_set_relay_mode(rr_ledger* ledger, int32_t mode);
+
 /* Copy the ledger out as the three tensors of Section 4.1 (layout above: route
  * [heads, nq, k], sentinels [heads, nq, m + sink + recent + r], anchor layer [heads, nq], all
  * int32, row-major; the caller owns the destination buffers, sized exactly so).  Any pointer may
@@ -199,10 +216,12 @@ rr_status rr_sparse_attention(const void* q, const void* k, const void* vt, cons
  * duration in milliseconds (arrays of RR_KERNEL_KINDS entries, indexed by rr_kernel_kind),
  * and clears the record.  rr_ledger_profile(ledger, 1) also clears it; 0 stops recording. */
 typedef enum {
-    RR_KERNEL_ROUTE = 0,    /* full routing of every row (rr_anchor_route)               */
-    RR_KERNEL_RESCORE = 1,  /* candidate rescoring + flags (first kernel of a relay)      */
-    RR_KERNEL_REROUTE = 2,  /* full routing of the flagged rows (second kernel of a relay) */
-    RR_KERNEL_KINDS = 3
+    RR_KERNEL_ROUTE = 0,    /* full routing of every row (rr_anchor_route)                      */
+    RR_KERNEL_RESCORE = 1,  /* candidate rescoring + flags (first kernel of a compacted relay)   */
+    RR_KERNEL_REROUTE = 2,  /* full routing of the flagged rows (second kernel of a compacted relay) */
+    RR_KERNEL_RELAY = 3,    /* fused relay layer: rescoring, compaction and reroute in one kernel */
+    RR_KERNEL_LIST = 4,     /* compacted-list output of a fused relay (only when asked for)       */
+    RR_KERNEL_KINDS = 5
 } rr_kernel_kind;
 rr_status rr_ledger_profile(rr_ledger* ledger, int32_t enable);
 rr_status rr_ledger_kernel_times(rr_ledger* ledger, int32_t* launches, double* total_ms);

@@ -29,6 +29,7 @@ struct rr_ledger {
     float* hint_ws = nullptr;    // [H, nq]
     int32_t* bcount = nullptr;   // [H, G]
     int32_t* blist = nullptr;    // [H, G, 64]
+    int32_t relay_mode = RR_RELAY_AUTO;
     int32_t last_layer = -1;
     bool anchored = false;
     bool poisoned = false;
@@ -150,6 +151,21 @@ void release_events(rr_ledger* L) {
     for (auto e : L->spare) (void)hipEventDestroy(e);
     L->timed.clear();
     L->spare.clear();
+}
+
+// Fused relay layers serve layers of up to this many 128-row blocks (two per compute unit):
+// there the fixed latency of a reroute block, not its work, sets the time, and one launch per
+// layer that rescores from LDS and skips the threshold pass beats the two-kernel schedule.
+constexpr long long FUSED_MAX_BLOCKS = 512;
+
+bool fused_fits(const rr_ledger* L) {
+    return rr::relay_fits(L->cfg.nk, L->c, L->sel, L->cfg.dtype == RR_BF16);
+}
+
+bool use_fused(const rr_ledger* L) {
+    if (!fused_fits(L)) return false;
+    if (L->relay_mode != RR_RELAY_AUTO) return L->relay_mode == RR_RELAY_FUSED;
+    return (long long)L->cfg.heads * ((L->cfg.nq + 127) / 128) <= FUSED_MAX_BLOCKS;
 }
 
 rr::RouteArgs route_args(const rr_ledger* L, const void* q, const void* k, int layer) {
@@ -386,13 +402,30 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
     s.layer = layer;
     s.min_reuse = L->cfg.min_reuse;
     s.gamma_extra = L->cfg.gamma_extra;
+    rr::RouteArgs a = route_args(L, q, k, layer);
+    a.refresh_mark = 1;
+    const bool bf16 = L->cfg.dtype == RR_BF16;
+    if (use_fused(L)) {
+        int tix = time_begin(L, RR_KERNEL_RELAY, st);
+        hipError_t e = rr::launch_relay(s, a, bf16, L->cfg.causal != 0, st);
+        time_end(L, tix, st);
+        if (e != hipSuccess) return hip_fail(L, e, "relay launch");
+        if (out && (out->rows || out->head_counts || out->n_rows)) {
+            tix = time_begin(L, RR_KERNEL_LIST, st);
+            e = rr::launch_compact_out(L->bcount, L->blist, L->cfg.heads, L->cfg.nq, out->rows, out->head_counts,
+                                       out->n_rows, st);
+            time_end(L, tix, st);
+            if (e != hipSuccess) return hip_fail(L, e, "compacted-list launch");
+        }
+        L->last_layer = layer;
+        return ok();
+    }
+
     int tix = time_begin(L, RR_KERNEL_RESCORE, st);
-    hipError_t e = rr::launch_rescore(s, L->cfg.dtype == RR_BF16, st);
+    hipError_t e = rr::launch_rescore(s, bf16, st);
     time_end(L, tix, st);
     if (e != hipSuccess) return hip_fail(L, e, "rescore launch");
 
-    rr::RouteArgs a = route_args(L, q, k, layer);
-    a.refresh_mark = 1;
     a.out_rows = out ? out->rows : nullptr;
     a.out_head_counts = out ? out->head_counts : nullptr;
     a.out_n_rows = out ? out->n_rows : nullptr;
@@ -402,6 +435,17 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
     time_end(L, tix, st);
     if (e != hipSuccess) return hip_fail(L, e, "reroute launch");
     L->last_layer = layer;
+    return ok();
+}
+
+rr_status rr_ledger_set_relay_mode(rr_ledger* L, int32_t mode) {
+    if (!L) return fail(RR_EINVAL, "ledger is NULL");
+    if (mode != RR_RELAY_AUTO && mode != RR_RELAY_FUSED && mode != RR_RELAY_COMPACTED)
+        return fail(RR_EINVAL, "unknown relay mode %d", mode);
+    if (mode == RR_RELAY_FUSED && !fused_fits(L))
+        return fail(RR_EUNSUPPORTED, "the fused relay needs k + m <= 32, c <= 32 and a head's keys in 128 KB "
+                    "(got k + m = %d, c = %d, nk = %d)", L->sel, L->c, L->cfg.nk);
+    L->relay_mode = mode;
     return ok();
 }
 

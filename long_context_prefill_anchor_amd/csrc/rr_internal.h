@@ -64,6 +64,14 @@ constexpr int ROUTE_ROWS = 64;   // rows per route block and per rescore block
 
 hipError_t launch_route(const RouteArgs& a, bool bf16, bool causal, bool reroute, hipStream_t st);
 hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st);
+// Fused relay layer: rescoring, in-block compaction and reroute of every 128-row block in one
+// launch, with the head's keys staged in LDS; leaves bcount / blist for launch_compact_out.
+// Only where relay_fits (k + m <= 32, c <= 32, the keys of a head in 128 KB).
+bool relay_fits(int nk, int c, int sel, bool bf16);
+hipError_t launch_relay(const RescoreArgs& s, const RouteArgs& a, bool bf16, bool causal, hipStream_t st);
+// Compacted list (ascending h*nq+i), per-head counts and total from bcount / blist.
+hipError_t launch_compact_out(const int32_t* bcount, const int32_t* blist, int H, int nq, int32_t* out_rows,
+                              int32_t* out_head_counts, int32_t* out_n_rows, hipStream_t st);
 size_t route_lds_bytes(int nk, int c);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
 // k + m > 32 (rr_wide.hip): one wave per row, same ledger rules; nk <= 1024.

@@ -301,6 +301,22 @@ __device__ __forceinline__ int slice_major_block(int H, int G) {
 
 __host__ __forceinline__ int xcd_grid(int nlogical) { return (nlogical + XCDS - 1) / XCDS * XCDS; }
 
+// LDS a route block (64 rows, SPLIT waves) needs: the per-wave candidate buffers, the cross-wave
+// exchange lists, the pass-1 group maxima and the ledger-write area, which alias; rounded up to
+// 16 bytes.
+__host__ __device__ __forceinline__ size_t route_lds_bytes_dev(int nk, int c) {
+    const size_t cand = (size_t)SPLIT * CAP * ROWS * sizeof(uint2);
+    const size_t xl = (size_t)SPLIT * XWAVE * sizeof(uint64_t);
+    const size_t gm = (size_t)ROWS * GSTRIDE * sizeof(float);
+    const size_t em = (size_t)ROWS * (((nk + 31) / 32 + 1) + 32 + c + 1) * sizeof(uint32_t);
+    size_t m = cand > xl ? cand : xl;
+    m = m > gm ? m : gm;
+    m = m > em ? m : em;
+    return (m + 15) / 16 * 16;
+}
+
+size_t route_lds_bytes(int nk, int c) { return route_lds_bytes_dev(nk, c); }
+
 struct RouteShared {
     uint64_t thr[ROWS];      // shared threshold key per row (max over the waves' lower bounds)
     int32_t rows[ROWS];      // ledger row of each slot (-1: none)
@@ -734,13 +750,43 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
 template <typename DT, bool CAUSAL>
 __device__ __forceinline__ void redo_rows(const RouteArgs& p, RouteShared& sh, unsigned char* dyn_lds, RowCtx<DT>& cx) {
     __syncthreads();                                                    // everyone has read sh.redo
-    if (threadIdx.x == 0) sh.redo = 0;
+    if (cx.wave == 0 && cx.lane == 0) sh.redo = 0;
     asm volatile("" : "+v"(cx.my_n), "+v"(cx.nmin), "+v"(cx.my_row), "+v"(cx.ntiles));
     asm volatile("" : "+v"(cx.Kh), "+v"(cx.Qh), "+v"(cx.my_buf));
     asm volatile("" : "+v"(cx.q_row), "+v"(cx.q_n), "+v"(cx.qslot), "+v"(cx.qsub), "+v"(cx.q_qrow));
     Tile<DT> tile;
     typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
     select_and_emit<DT, CAUSAL, true>(p, sh, dyn_lds, tile, kbuf, false, cx, 1);
+}
+
+// Per-lane state of a route block once sh.rows / sh.qrows name its rows: one row per lane for
+// the scoring passes (all four waves cover all 64 slots), one row per quad of lanes for the
+// merge and the ledger write.
+template <typename DT, bool CAUSAL>
+__device__ __forceinline__ RowCtx<DT> row_context(const RouteArgs& p, const RouteShared& sh, unsigned char* dyn_lds,
+                                                  int h, int wave, int lane) {
+    typedef typename Elem<DT>::type E;
+    RowCtx<DT> cx;
+    cx.lane = lane;
+    cx.wave = wave;
+    cx.h = h;
+    cx.my_row = sh.rows[lane];
+    cx.my_n = (cx.my_row < 0) ? 0 : (CAUSAL ? sh.qrows[lane] + 1 : p.nk);
+    // Wave-uniform after the reductions; readfirstlane lets the compiler see it.
+    const int kmax = __builtin_amdgcn_readfirstlane(wave_max_i(cx.my_n));
+    cx.nmin = __builtin_amdgcn_readfirstlane(wave_min_i((cx.my_row < 0) ? (1 << 30) : cx.my_n));
+    cx.ntiles = (kmax + TK - 1) / TK;
+    cx.Qh = reinterpret_cast<const E*>(p.qp) + (size_t)h * p.nq_q * 64;
+    cx.Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
+    cx.my_buf = reinterpret_cast<uint32_t*>(dyn_lds) + (size_t)wave * 2 * CAP * ROWS + lane;
+    // Final merge and ledger write run one row per quad of lanes over all four waves.
+    cx.qslot = 16 * wave + (lane >> 2);
+    cx.qsub = lane & 3;
+    cx.q_row = sh.rows[cx.qslot];
+    cx.q_qrow = sh.qrows[cx.qslot];
+    cx.q_n = (cx.q_row < 0) ? 0 : (CAUSAL ? cx.q_qrow + 1 : p.nk);
+    cx.q_redo = false;
+    return cx;
 }
 
 template <typename DT, bool CAUSAL, bool REROUTE>
@@ -863,25 +909,13 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     __syncthreads();
 
     // ------------------------------------------------------------------ per-row setup
-    const int my_row = sh.rows[lane];
-    const int my_n = (my_row < 0) ? 0 : (CAUSAL ? sh.qrows[lane] + 1 : p.nk);
-    // Wave-uniform after the reductions; readfirstlane lets the compiler see it.
-    const int kmax = __builtin_amdgcn_readfirstlane(wave_max_i(my_n));
-    const int nmin = __builtin_amdgcn_readfirstlane(wave_min_i((my_row < 0) ? (1 << 30) : my_n));
-    const int ntiles = (kmax + TK - 1) / TK;
-    const E* Qh = reinterpret_cast<const E*>(p.qp) + (size_t)h * p.nq_q * 64;
-    const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
+    RowCtx<DT> cx = row_context<DT, CAUSAL>(p, sh, dyn_lds, h, wave, lane);
+    const int my_row = cx.my_row, my_n = cx.my_n, nmin = cx.nmin, ntiles = cx.ntiles;
+    const E* Qh = cx.Qh;
+    const E* Kh = cx.Kh;
     Tile<DT> tile;
     typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
     if constexpr (!REROUTE) tile.load_q(Qh, sh.qrows[lane & 31], sh.qrows[32 + (lane & 31)], lane);
-
-    uint32_t* my_buf = reinterpret_cast<uint32_t*>(dyn_lds) + (size_t)wave * 2 * CAP * ROWS + lane;
-    // Final merge and ledger write run one row per quad of lanes over all four waves.
-    const int qslot = 16 * wave + (lane >> 2);
-    const int qsub = lane & 3;
-    const int q_row = sh.rows[qslot];
-    const int q_qrow = sh.qrows[qslot];
-    const int q_n = (q_row < 0) ? 0 : (CAUSAL ? q_qrow + 1 : p.nk);
 
     // ------------------------------------------------------------------ first threshold
     uint64_t base_thr;
@@ -956,7 +990,6 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     __syncthreads();
 
     // ------------------------------------------------------------------ streaming pass
-    RowCtx<DT> cx{lane, wave, h, my_row, my_n, nmin, ntiles, Qh, Kh, my_buf, qslot, qsub, q_row, q_n, q_qrow, false};
     select_and_emit<DT, CAUSAL, REROUTE>(p, sh, dyn_lds, tile, kbuf, REROUTE, cx, 0);
     if constexpr (REROUTE) {
         if (sh.redo) redo_rows<DT, CAUSAL>(p, sh, dyn_lds, cx);         // uniform; rare
@@ -1066,7 +1099,9 @@ __device__ __forceinline__ int cand_of_lane(int lane) {
     return (64 / LPR) * j + lane / LPR;
 }
 
-// Block (h, b): rows 64b..64b+63 of head h; wave w takes rows 4w..4w+3, one at a time.
+// Rescoring of ledger rows i0 .. i0 + nrow - 1 of head h (nrow <= RPW) by one wave, one row at a
+// time; afterwards lane rr (rr < RPW) holds row rr's alpha, its minimum over route + near-miss
+// (the reroute threshold hint), beta, and whether a route or near-miss slot had no ID.
 //
 // Loads.  Each load instruction reads 8 whole key rows: lane L takes 16-byte chunk L % 8 of
 // candidate 8 j + L / 8 in instruction j, so an instruction touches 8 cache lines (the address
@@ -1079,36 +1114,24 @@ __device__ __forceinline__ int cand_of_lane(int lane) {
 //
 // Flags.  Even lanes fold the route scores and odd lanes the route + near-miss scores into one
 // min over their parity, which gives alpha (Eq. 6) and the reroute threshold hint together;
-// the max over sentinel scores is beta (Eq. 7).  Two rows are reduced together, and each wave
-// writes its rows' results with one store per output.  Candidates without an ID count as +inf
-// for the minima and -inf for the max; a route or near-miss slot without one makes the hint -inf.
+// the max over sentinel scores is beta (Eq. 7).  Two rows are reduced together.  Candidates
+// without an ID count as +inf for the minima and -inf for the max; a route or near-miss slot
+// without one makes the hint -inf.
 //
-// The wave's query rows and candidate IDs are staged in LDS (read back by this wave only; LDS
-// operations of one wave complete in order), and the key rows of the next DEPTH rows stay in
-// flight while a row is reduced.  The block ends by listing its flagged rows (ascending) for
-// the reroute kernel.
-template <typename DT, int NP>
-__global__ __launch_bounds__(RESCORE_THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(typename Elem<DT>::type) == 2 ? 8 : 4)))
-void k_rescore(RescoreArgs p) {
+// The wave's query rows (sq: RPW rows) and candidate IDs (sid: RPW rows of 32 * NP entries, -1
+// past c) are staged in LDS, read back by this wave only (LDS operations of one wave complete in order), and the
+// key rows of the next DEPTH rows stay in flight while a row is reduced.
+template <typename DT, int NP, int RPW, int DEPTH>
+__device__ __forceinline__ void rescore_rows(const RescoreArgs& p, int h, int i0, int nrow, int lane,
+                                             unsigned char* sq, int32_t* sid, float& res_alpha, float& res_mu,
+                                             float& res_beta, bool& res_bad) {
     typedef typename Elem<DT>::type E;
     constexpr uint32_t ROW_BYTES = 64 * sizeof(E);
     static_assert(ROW_BYTES == 128 || ROW_BYTES == 256, "bf16 or fp32 rows");
+    static_assert(RPW % 2 == 0 && RPW <= 64, "rows are reduced in pairs, one result lane per row");
     constexpr int LPR = ROW_BYTES / 16;                // lanes per key row in one instruction: 8 or 16
     constexpr int RPI = 64 / LPR;                      // key rows per instruction: 8 or 4
     constexpr int NI = 32 * NP / RPI;                  // instructions per query row
-    constexpr int DEPTH = (NP == 1 && LPR == 8) ? 2 : 1;
-    __shared__ uint32_t row_flag[ROWS];
-    __shared__ __align__(16) unsigned char sq[RS_WAVES][RS_ROWS][ROW_BYTES];
-    __shared__ int32_t sid[RS_WAVES][RS_ROWS * 32 * NP];
-    const int G = (p.nq + ROWS - 1) / ROWS;
-    const int lb = xcd_block(p.H * G);
-    if (lb < 0) return;
-    const int h = lb / G;
-    const int b = lb % G;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int i0 = b * ROWS + wave * RS_ROWS;
-    const int nrow = max(0, min(RS_ROWS, p.nq - i0));   // rows of this wave inside the head
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(reinterpret_cast<const char*>(p.qp) + (size_t)h * p.nq_q * ROW_BYTES,
                                                 (uint32_t)p.nq_q * ROW_BYTES);
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(reinterpret_cast<const char*>(p.kp) + (size_t)h * p.nk * ROW_BYTES,
@@ -1117,19 +1140,21 @@ void k_rescore(RescoreArgs p) {
 
     // Stage the wave's query rows and its rows' candidate IDs (contiguous in the ledger).
     {
-        constexpr int PIECES = RS_ROWS * ROW_BYTES / 16;
+        constexpr int PIECES = RPW * ROW_BYTES / 16;
         for (int x = lane; x < PIECES; x += 64) {
             const int rr = x / (ROW_BYTES / 16), piece = x % (ROW_BYTES / 16);
             // a width bucket's ledger row names its query row through qmap
             const int qr = p.qmap ? (rr < nrow ? p.qmap[i0 + rr] : 0) : i0 + rr;
             const uint4 v = buf_load16(rQ, rr < nrow ? (uint32_t)qr * ROW_BYTES + 16u * piece : OOB);
-            *reinterpret_cast<uint4*>(&sq[wave][rr][16 * piece]) = v;
+            *reinterpret_cast<uint4*>(sq + rr * ROW_BYTES + 16 * piece) = v;
         }
-        const int nid = nrow * p.c;
-        for (int x = lane; x < RS_ROWS * p.c; x += 64) {
-            const int id = buf_load4(rI, x < nid ? (uint32_t)(i0 * p.c + x) * 4u : OOB);
+        // rows padded to 32 NP IDs (-1 past c), so that every later read is unconditional
+        for (int x = lane; x < RPW * 32 * NP; x += 64) {
+            const int rr = x / (32 * NP), c = x % (32 * NP);
+            const bool in = rr < nrow && c < p.c;
+            const int id = buf_load4(rI, in ? (uint32_t)((i0 + rr) * p.c + c) * 4u : OOB);
             // -1 for padding, rows outside the head and any index outside K.
-            sid[wave][x] = (x < nid && (unsigned)id < (unsigned)p.nk) ? id : -1;
+            sid[x] = (in && (unsigned)id < (unsigned)p.nk) ? id : -1;
         }
     }
     const int grp = lane / LPR;                         // key row within an instruction
@@ -1142,8 +1167,7 @@ void k_rescore(RescoreArgs p) {
     auto issue = [&](int slot, int rr) {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int c = RPI * j + grp;
-            const int id = (c < p.c) ? sid[wave][rr * p.c + c] : -1;
+            const int id = sid[rr * 32 * NP + RPI * j + grp];
             kv[slot][j] = buf_load16(rK, id >= 0 ? (uint32_t)id * ROW_BYTES + coff : OOB);
         }
     };
@@ -1151,12 +1175,12 @@ void k_rescore(RescoreArgs p) {
     for (int d = 0; d < DEPTH; ++d) issue(d, d);
 
     const bool ownR = cown < p.k, ownSel = cown < p.sel, ownS = cown >= p.k && cown < p.c;
-    static_assert(RS_ROWS % 2 == 0, "rows are reduced in pairs");
-    // Per-row results, lane rr of the wave holding row rr.
-    float res_alpha = 0.f, res_mu = 0.f, res_beta = 0.f;
-    bool res_bad = false;
+    res_alpha = 0.f;
+    res_mu = 0.f;
+    res_beta = 0.f;
+    res_bad = false;
 #pragma unroll
-    for (int pr = 0; pr < RS_ROWS; pr += 2) {
+    for (int pr = 0; pr < RPW; pr += 2) {
         float A[2], B[2];
         bool bad[2];
 #pragma unroll
@@ -1164,7 +1188,7 @@ void k_rescore(RescoreArgs p) {
             const int rr = pr + t;
             const int slot = rr % DEPTH;
             const int i = i0 + rr;
-            const uint4 qv = *reinterpret_cast<const uint4*>(&sq[wave][rr][coff]);
+            const uint4 qv = *reinterpret_cast<const uint4*>(sq + rr * ROW_BYTES + coff);
             float part[NI];
 #pragma unroll
             for (int j = 0; j < NI; ++j) part[j] = Dot<DT>::acc(qv, kv[slot][j], 0.f);
@@ -1173,10 +1197,12 @@ void k_rescore(RescoreArgs p) {
             // register budget (64 VGPRs for bf16 at eight waves per SIMD), so they go out after
             // it.  The build's resource report and its test check that no k_rescore spills.
             constexpr bool LATE = NP == 2;
-            if (!LATE && rr + DEPTH < RS_ROWS) issue(slot, rr + DEPTH);
+            if (!LATE && rr + DEPTH < RPW) issue(slot, rr + DEPTH);
             const float sc = reduce_scatter<LPR, NP>(part, lane);
-            if (LATE && rr + DEPTH < RS_ROWS) issue(slot, rr + DEPTH);
-            const bool valid = (cown < p.c) && sid[wave][rr * p.c + min(cown, p.c - 1)] >= 0;
+            // (the fence keeps the next row's ID reads from being hoisted above the reduce-scatter)
+            if constexpr (LATE) __builtin_amdgcn_sched_barrier(0);
+            if (LATE && rr + DEPTH < RPW) issue(slot, rr + DEPTH);
+            const bool valid = sid[rr * 32 * NP + cown] >= 0;    // -1 also past c
             const float vr = (ownR && valid) ? sc : INFINITY;
             const float vsel = (ownSel && valid) ? sc : INFINITY;
             B[t] = (ownS && valid) ? sc : -INFINITY;
@@ -1226,32 +1252,67 @@ void k_rescore(RescoreArgs p) {
             res_bad = mine ? bad[t] : res_bad;
         }
     }
-    // Eq. 8: reuse iff alpha > beta + gamma (a row without any route ID is refreshed).
-    // Hysteresis (Section 3.2, after Eq. 8): a row refreshed at a relay layer a is reused
-    // untested up to layer a + min_reuse, then tested with gamma + gamma_extra until it passes
-    // once, which clears its state.
-    if (lane < RS_ROWS) {
-        const int i = i0 + lane;
-        bool reuse;
-        if (p.min_reuse > 0 || p.gamma_extra > 0.f) {                   // uniform
-            const size_t fl = (size_t)h * p.nq + min(i, p.nq - 1);
-            const bool ref = p.refreshed[fl] != 0;
-            const bool skip = ref && p.layer - p.anchor[fl] <= p.min_reuse;
-            const float guard = ref ? p.gamma + p.gamma_extra : p.gamma;
-            reuse = skip || (res_alpha < INFINITY && res_alpha > res_beta + guard);
-            if (i < p.nq && ref && reuse && !skip) p.refreshed[fl] = 0;
-        } else {
-            reuse = res_alpha < INFINITY && res_alpha > res_beta + p.gamma;
-        }
-        if (i < p.nq) {
-            const size_t flat = (size_t)h * p.nq + i;
+}
+
+// Eq. 8 for ledger row i of head h from its rescoring results: reuse iff alpha > beta + gamma
+// (a row without any route ID is refreshed).  Hysteresis (Section 3.2, after Eq. 8): a row
+// refreshed at a relay layer a is reused untested up to layer a + min_reuse, then tested with
+// gamma + gamma_extra until it passes once, which clears its state.  Writes the optional
+// outputs (and, for the reroute kernel, the flag / hint workspaces); returns true when the row
+// is to be rerouted.
+__device__ __forceinline__ bool relay_decide(const RescoreArgs& p, int h, int i, float alpha, float mu, float beta,
+                                             bool bad, bool write_ws) {
+    bool reuse;
+    if (p.min_reuse > 0 || p.gamma_extra > 0.f) {                       // uniform
+        const size_t fl = (size_t)h * p.nq + min(i, p.nq - 1);
+        const bool ref = p.refreshed[fl] != 0;
+        const bool skip = ref && p.layer - p.anchor[fl] <= p.min_reuse;
+        const float guard = ref ? p.gamma + p.gamma_extra : p.gamma;
+        reuse = skip || (alpha < INFINITY && alpha > beta + guard);
+        if (i < p.nq && ref && reuse && !skip) p.refreshed[fl] = 0;
+    } else {
+        reuse = alpha < INFINITY && alpha > beta + p.gamma;
+    }
+    if (i < p.nq) {
+        const size_t flat = (size_t)h * p.nq + i;
+        if (write_ws) {
             p.flags_ws[flat] = reuse ? 0 : 1;
-            p.hint_ws[flat] = res_bad ? -INFINITY : res_mu;
-            if (p.out_flags) p.out_flags[flat] = reuse ? 0 : 1;
-            if (p.out_alpha) p.out_alpha[flat] = res_alpha;
-            if (p.out_beta) p.out_beta[flat] = res_beta;
+            p.hint_ws[flat] = bad ? -INFINITY : mu;
         }
-        row_flag[wave * RS_ROWS + lane] = (i < p.nq && !reuse) ? 1u : 0u;
+        if (p.out_flags) p.out_flags[flat] = reuse ? 0 : 1;
+        if (p.out_alpha) p.out_alpha[flat] = alpha;
+        if (p.out_beta) p.out_beta[flat] = beta;
+    }
+    return i < p.nq && !reuse;
+}
+
+// Block (h, b): rows 64b..64b+63 of head h; wave w takes rows 4w..4w+3, one at a time.  The
+// block ends by listing its flagged rows (ascending) for the reroute kernel.
+template <typename DT, int NP>
+__global__ __launch_bounds__(RESCORE_THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(typename Elem<DT>::type) == 2 ? 8 : 4)))
+void k_rescore(RescoreArgs p) {
+    typedef typename Elem<DT>::type E;
+    constexpr uint32_t ROW_BYTES = 64 * sizeof(E);
+    constexpr int LPR = ROW_BYTES / 16;
+    constexpr int DEPTH = (NP == 1 && LPR == 8) ? 2 : 1;
+    __shared__ uint32_t row_flag[ROWS];
+    __shared__ __align__(16) unsigned char sq[RS_WAVES][RS_ROWS * ROW_BYTES];
+    __shared__ int32_t sid[RS_WAVES][RS_ROWS * 32 * NP];
+    const int G = (p.nq + ROWS - 1) / ROWS;
+    const int lb = xcd_block(p.H * G);
+    if (lb < 0) return;
+    const int h = lb / G;
+    const int b = lb % G;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int i0 = b * ROWS + wave * RS_ROWS;
+    const int nrow = max(0, min(RS_ROWS, p.nq - i0));   // rows of this wave inside the head
+    float alpha, mu, beta;
+    bool bad;
+    rescore_rows<DT, NP, RS_ROWS, DEPTH>(p, h, i0, nrow, lane, sq[wave], sid[wave], alpha, mu, beta, bad);
+    if (lane < RS_ROWS) {
+        const bool f = relay_decide(p, h, i0 + lane, alpha, mu, beta, bad, true);
+        row_flag[wave * RS_ROWS + lane] = f ? 1u : 0u;
     }
     __syncthreads();
     if (wave == 0) {
@@ -1264,17 +1325,276 @@ void k_rescore(RescoreArgs p) {
     }
 }
 
+// ------------------------------------------------------------------------------ fused relay
+
+constexpr int RELAY_ROWS = 2 * ROWS;              // ledger rows per fused relay block
+constexpr int RELAY_WAVES = 2 * SPLIT;            // its waves: two reroute slices of SPLIT waves
+constexpr int RELAY_RPW = RELAY_ROWS / RELAY_WAVES;  // rows rescored per wave
+constexpr uint32_t RELAY_MAX_K_BYTES = 128u << 10;  // a head's keys staged in LDS (1024 bf16 rows)
+
+// Rescoring of ledger rows i0 .. i0 + nrow - 1 (nrow <= RPW) by one wave with the head's key rows
+// resident in LDS (kl: nk rows of 64 elements) and the candidate IDs staged per wave (sid: RPW
+// rows of 32 entries, -1 past c <= 32): the same candidate-to-lane layout, reduce-scatter and min / max folding as
+// rescore_rows, with every key chunk read from LDS (one 16-byte read per lane and 8 candidates).
+// qv[rr]: this lane's 16-byte chunk of row rr's query.  Results as rescore_rows (lane rr).
+template <typename DT, int RPW>
+__device__ __forceinline__ void rescore_rows_lds(const RescoreArgs& p, int h, int i0, int lane, const unsigned char* kl,
+                                                 const int32_t* sid, const uint4 (&qv)[RPW], float& res_alpha,
+                                                 float& res_mu, float& res_beta, bool& res_bad) {
+    typedef typename Elem<DT>::type E;
+    constexpr uint32_t ROW_BYTES = 64 * sizeof(E);
+    constexpr int LPR = ROW_BYTES / 16;
+    constexpr int RPI = 64 / LPR;
+    constexpr int NI = 32 / RPI;                       // one pass of 32 candidates
+    const int grp = lane / LPR;
+    const uint32_t coff = 16u * (lane % LPR);
+    const int b0 = lane & 1;
+    const int cown = cand_of_lane<LPR, 1>(lane);
+    const bool ownR = cown < p.k, ownSel = cown < p.sel, ownS = cown >= p.k && cown < p.c;
+    res_alpha = res_mu = res_beta = 0.f;
+    res_bad = false;
+#pragma unroll
+    for (int pr = 0; pr < RPW; pr += 2) {
+        float A[2], B[2];
+        bool bad[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int rr = pr + t;
+            const int i = i0 + rr;
+            float part[NI];
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                // Unconditional: a missing ID reads row 0, and its score is masked by `valid`
+                // below (a branch here would serialise every read behind its ID read).
+                const int id = sid[rr * 32 + RPI * j + grp];
+                const uint4 kv = *reinterpret_cast<const uint4*>(kl + (size_t)max(id, 0) * ROW_BYTES + coff);
+                part[j] = Dot<DT>::acc(qv[rr], kv, 0.f);
+            }
+            const float sc = reduce_scatter<LPR, 1>(part, lane);
+            const bool valid = sid[rr * 32 + cown] >= 0;        // -1 also past c
+            const float vr = (ownR && valid) ? sc : INFINITY;
+            const float vsel = (ownSel && valid) ? sc : INFINITY;
+            B[t] = (ownS && valid) ? sc : -INFINITY;
+            A[t] = b0 ? vsel : vr;                      // lanes L and L ^ 1 hold the same candidate
+            bad[t] = __ballot(ownSel && !valid) != 0ull;
+            if (p.cand_scores) {                        // uniform
+                if (i < p.nq && cown < p.c && b0 == 0)
+                    p.cand_scores[((size_t)h * p.nq + i) * p.c + cown] = valid ? sc : __builtin_nanf("");
+            }
+        }
+        const bool second = (lane & 2) != 0;
+        float a = vmin2(second ? A[1] : A[0], dpp_f<DPP_XOR2>(second ? A[0] : A[1]));
+        float bb = vmax2(second ? B[1] : B[0], dpp_f<DPP_XOR2>(second ? B[0] : B[1]));
+        a = vmin2(a, dpp_f<DPP_ROR4>(a));
+        bb = vmax2(bb, dpp_f<DPP_ROR4>(bb));
+        a = vmin2(a, dpp_f<DPP_ROR8>(a));
+        bb = vmax2(bb, dpp_f<DPP_ROR8>(bb));
+        {
+            auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+            auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(bb), __float_as_uint(bb), false, false);
+            a = vmin2(__uint_as_float(x[0]), __uint_as_float(x[1]));
+            bb = vmax2(__uint_as_float(y[0]), __uint_as_float(y[1]));
+            auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+            auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(bb), __float_as_uint(bb), false, false);
+            a = vmin2(__uint_as_float(z[0]), __uint_as_float(z[1]));
+            bb = vmax2(__uint_as_float(w[0]), __uint_as_float(w[1]));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float al = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 2 * t));
+            const float mu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 2 * t + 1));
+            const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bb), 2 * t));
+            const bool mine = lane == pr + t;
+            res_alpha = mine ? al : res_alpha;
+            res_mu = mine ? mu : res_mu;
+            res_beta = mine ? be : res_beta;
+            res_bad = mine ? bad[t] : res_bad;
+        }
+    }
+}
+
+// One relay layer (Sections 3.2, 4.1, 4.2) for 128 ledger rows of one head in one block of
+// eight waves (one block per compute unit):
+//   1. the head's keys (nk rows, at most 128 KB) are staged in LDS once, together with each
+//      wave's 16 rows of candidate IDs, and every row is rescored from LDS (rescore_rows_lds)
+//      and decided (Eq. 8);
+//   2. compaction: the block's flagged rows, ascending, go to the row slots 0 .. n-1 (ballot +
+//      prefix count over the two 64-row halves), each with its reroute threshold from its own
+//      rescoring (the smallest current score over its route and near-miss chunks, less a
+//      rounding margin: a lower bound on its (k+m)-th best score); per 64-row half, the flagged
+//      rows and their count also go to blist / bcount for the compacted-list output;
+//   3. reroute: slots 0-63 and 64-127 are two independent 64-row slices, each routed by four
+//      waves with the route kernel's streaming selection and ledger write (select_and_emit);
+//      the keys' LDS area is reused for the slices' buffers.  A slice without rows streams no
+//      key tile.  The block-wide barriers inside select_and_emit are met by both slices in the
+//      same order; a redo (rare) runs in both when either needs it.
+// At the usual flagged fractions (around 0.6) the ~77 flagged rows of a block fill one slice
+// and part of the other, so the reroute runs at the occupancy of full routing (two 64-row
+// slices per compute unit) without its threshold pass, and the rescoring reads keys from LDS
+// instead of gathering them from L2.  A block without a flagged row stops after step 2.
+template <typename DT, bool CAUSAL>
+__global__ __launch_bounds__(ROWS * RELAY_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+void k_relay(RescoreArgs s, RouteArgs p) {
+    typedef typename Elem<DT>::type E;
+    constexpr uint32_t ROW_BYTES = 64 * sizeof(E);
+    constexpr int LPR = ROW_BYTES / 16;
+    constexpr int KPIECES = RELAY_MAX_K_BYTES / 16 / (ROWS * RELAY_WAVES);   // 16-byte pieces per thread
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    __shared__ RouteShared sh[2];
+    __shared__ uint32_t rflag[RELAY_ROWS];
+    __shared__ float rhint[RELAY_ROWS];
+    __shared__ int nflag[2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G2 = (p.nq + RELAY_ROWS - 1) / RELAY_ROWS;
+    const int lb = xcd_block(p.H * G2);
+    if (lb < 0) return;
+    const int h = lb / G2;
+    const int g2 = lb % G2;
+    const uint32_t kbytes = (uint32_t)p.nk * ROW_BYTES;
+    unsigned char* kl = dyn_lds;
+    int32_t* sid = reinterpret_cast<int32_t*>(dyn_lds + RELAY_MAX_K_BYTES) + (size_t)wave * RELAY_RPW * 32;
+    const int i0 = g2 * RELAY_ROWS + wave * RELAY_RPW;
+    const int nrow = max(0, min(RELAY_RPW, p.nq - i0));
+
+    // ------------------------------------------------------------------ 1. staging + rescoring
+    {
+        const __amdgpu_buffer_rsrc_t rK = make_rsrc(reinterpret_cast<const char*>(s.kp) + (size_t)h * p.nk * ROW_BYTES,
+                                                    kbytes);
+        const __amdgpu_buffer_rsrc_t rQ = make_rsrc(reinterpret_cast<const char*>(s.qp) + (size_t)h * s.nq_q * ROW_BYTES,
+                                                    (uint32_t)s.nq_q * ROW_BYTES);
+        const __amdgpu_buffer_rsrc_t rI = make_rsrc(s.ids + (size_t)h * s.nq * s.c, (uint32_t)(s.nq * s.c * 4));
+        // every load goes out before the first LDS write: keys, IDs, query chunks
+        uint4 kreg[KPIECES];
+#pragma unroll
+        for (int x = 0; x < KPIECES; ++x) {
+            const uint32_t off = 16u * (uint32_t)(tid + x * ROWS * RELAY_WAVES);
+            kreg[x] = buf_load16(rK, off < kbytes ? off : OOB);
+        }
+        int idv[RELAY_RPW * 32 / 64];                   // rows padded to 32 IDs
+#pragma unroll
+        for (int u = 0; u < RELAY_RPW * 32 / 64; ++u) {
+            const int x = lane + 64 * u, rr = x / 32, c = x % 32;
+            idv[u] = buf_load4(rI, (rr < nrow && c < s.c) ? (uint32_t)((i0 + rr) * s.c + c) * 4u : OOB);
+        }
+        uint4 qv[RELAY_RPW];
+        const uint32_t coff = 16u * (lane % LPR);
+#pragma unroll
+        for (int rr = 0; rr < RELAY_RPW; ++rr) {
+            const int qr = s.qmap ? (rr < nrow ? s.qmap[i0 + rr] : 0) : i0 + rr;
+            qv[rr] = buf_load16(rQ, rr < nrow ? (uint32_t)qr * ROW_BYTES + coff : OOB);
+        }
+#pragma unroll
+        for (int x = 0; x < KPIECES; ++x) {
+            const uint32_t off = 16u * (uint32_t)(tid + x * ROWS * RELAY_WAVES);
+            if (off < kbytes) *reinterpret_cast<uint4*>(kl + off) = kreg[x];
+        }
+#pragma unroll
+        for (int u = 0; u < RELAY_RPW * 32 / 64; ++u) {
+            const int x = lane + 64 * u, rr = x / 32, c = x % 32;
+            // -1 for padding (also past c), rows outside the head and any index outside K
+            sid[x] = (rr < nrow && c < s.c && (unsigned)idv[u] < (unsigned)s.nk) ? idv[u] : -1;
+        }
+        __syncthreads();                                // the keys are in LDS
+        float alpha, mu, beta;
+        bool bad;
+        rescore_rows_lds<DT, RELAY_RPW>(s, h, i0, lane, kl, sid, qv, alpha, mu, beta, bad);
+        if (lane < RELAY_RPW) {
+            const bool f = relay_decide(s, h, i0 + lane, alpha, mu, beta, bad, false);
+            rflag[wave * RELAY_RPW + lane] = f ? 1u : 0u;
+            rhint[wave * RELAY_RPW + lane] = bad ? -INFINITY : mu;
+        }
+    }
+    __syncthreads();                                    // flags ready; the keys' LDS is free
+
+    // ------------------------------------------------------------------ 2. compaction
+    if (wave < 2) {
+        // wave w takes the rows of half w (64 w .. 64 w + 63 of the block)
+        const int G = (p.nq + ROWS - 1) / ROWS;        // 64-row groups per head (blist / bcount)
+        const int grp = 2 * g2 + wave;
+        const bool f = rflag[64 * wave + lane] != 0u;
+        const uint64_t m = __ballot(f);
+        const int cnt = __popcll(m);
+        const int pos = __popcll(m & ((1ull << lane) - 1ull));
+        const int cnt0 = __popcll(__ballot(rflag[lane] != 0u));
+        const int total = cnt0 + __popcll(__ballot(rflag[64 + lane] != 0u));
+        const int row = 64 * grp + lane;                // ledger row within the head
+        if (f) {                                        // slot: half 0 first, then half 1
+            const int slot = (wave == 0 ? 0 : cnt0) + pos;
+            RouteShared& dst = sh[slot >> 6];
+            const int sl = slot & 63;
+            dst.rows[sl] = row;
+            dst.qrows[sl] = p.qmap ? p.qmap[row] : row;
+            const float hv = rhint[64 * wave + lane];
+            const float t = (hv == -INFINITY) ? -INFINITY : hv - (fabsf(hv) * 1e-4f + 1e-6f);
+            dst.thr[sl] = make_key(t, 0xFFFFFFFFu);
+            s.blist[((size_t)h * G + grp) * ROWS + pos] = row;
+        }
+        if (64 * wave + lane >= total) {                // slots past the flagged rows: no row
+            sh[wave].rows[lane] = -1;
+            sh[wave].qrows[lane] = -1;
+            sh[wave].thr[lane] = NO_PASS_KEY;
+        }
+        if (lane == 0) {
+            if (grp < G) s.bcount[(size_t)h * G + grp] = cnt;
+            nflag[wave] = wave == 0 ? min(total, 64) : max(total - 64, 0);
+            sh[wave].redo = 0;
+        }
+    }
+    __syncthreads();
+    if (nflag[0] == 0) return;                          // uniform: nothing to reroute
+
+    // ------------------------------------------------------------------ 3. reroute, two slices
+    const int slice = wave / SPLIT;
+    const int wv = wave % SPLIT;
+    unsigned char* lds_s = dyn_lds + (size_t)slice * route_lds_bytes_dev(p.nk, p.c);
+    RowCtx<DT> cx = row_context<DT, CAUSAL>(p, sh[slice], lds_s, h, wv, lane);
+    Tile<DT> tile;
+    typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
+    select_and_emit<DT, CAUSAL, true>(p, sh[slice], lds_s, tile, kbuf, false, cx, 0);
+    if (sh[0].redo || sh[1].redo) redo_rows<DT, CAUSAL>(p, sh[slice], lds_s, cx);    // uniform; rare
+}
+
+// The compacted list of a relay layer (Sections 4.1-4.2: ascending h * nq + i of the flagged
+// rows), the flagged rows per head and their total, from the per-block flag counts and
+// ascending row lists (bcount [H, G], blist [H, G, 64]) that the relay leaves: one wave per
+// head.  Launched only when the caller asks for these outputs.
+__global__ __launch_bounds__(64) void k_compact_out(const int32_t* bcount, const int32_t* blist, int H, int nq,
+                                                     int32_t* out_rows, int32_t* out_head_counts,
+                                                     int32_t* out_n_rows) {
+    const int h = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int G = (nq + ROWS - 1) / ROWS;
+    int acc = 0;                                        // flagged rows in the heads before h
+    for (int x = lane; x < h * G; x += 64) acc += bcount[x];
+    const int offset = wave_sum_i(acc);
+    const int32_t* bc = bcount + (size_t)h * G;
+    const int32_t* bl = blist + (size_t)h * G * ROWS;
+    int run = 0;
+    for (int b0 = 0; b0 < G; b0 += 64) {                // uniform
+        const int cnt = (b0 + lane < G) ? bc[b0 + lane] : 0;
+        const int incl = wave_incl_scan_i(cnt);
+        if (out_rows) {
+            const int nb = min(64, G - b0);
+            for (int bb = 0; bb < nb; ++bb) {
+                const int cb = __builtin_amdgcn_readlane(cnt, bb);
+                const int base = run + __builtin_amdgcn_readlane(incl, bb) - cb;
+                if (lane < cb) out_rows[offset + base + lane] = h * nq + bl[(size_t)(b0 + bb) * ROWS + lane];
+            }
+        }
+        run += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) {
+        if (out_head_counts) out_head_counts[h] = run;
+        if (out_n_rows && h == H - 1) out_n_rows[0] = offset + run;
+    }
+}
+
 // ------------------------------------------------------------------------------ launchers
 
-size_t route_lds_bytes(int nk, int c) {
-    const size_t cand = (size_t)SPLIT * CAP * ROWS * sizeof(uint2);
-    const size_t xl = (size_t)SPLIT * XWAVE * sizeof(uint64_t);
-    const size_t gm = (size_t)ROWS * GSTRIDE * sizeof(float);
-    const size_t em = (size_t)ROWS * (((nk + 31) / 32 + 1) + RLIST + c + 1) * sizeof(uint32_t);
-    size_t m = cand > xl ? cand : xl;
-    m = m > gm ? m : gm;
-    return m > em ? m : em;
-}
+
 
 template <typename DT, bool CAUSAL, bool REROUTE>
 static hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
@@ -1291,6 +1611,40 @@ hipError_t launch_route(const RouteArgs& a, bool bf16, bool causal, bool reroute
     }
     if (causal) return reroute ? launch_route_t<float, true, true>(a, st) : launch_route_t<float, true, false>(a, st);
     return reroute ? launch_route_t<float, false, true>(a, st) : launch_route_t<float, false, false>(a, st);
+}
+
+size_t relay_lds_bytes(int nk, int c, bool bf16) {
+    const size_t stage = RELAY_MAX_K_BYTES + (size_t)RELAY_WAVES * RELAY_RPW * 32 * sizeof(int32_t);
+    const size_t slices = 2 * route_lds_bytes_dev(nk, c);
+    (void)bf16;
+    return stage > slices ? stage : slices;
+}
+
+bool relay_fits(int nk, int c, int sel, bool bf16) {
+    const size_t row_bytes = bf16 ? 128 : 256;
+    return sel <= 32 && c <= 32 && (size_t)nk * row_bytes <= RELAY_MAX_K_BYTES &&
+           relay_lds_bytes(nk, c, bf16) + sizeof(RouteShared) * 2 + RELAY_ROWS * 8 + 64 <= (160u << 10);
+}
+
+template <typename DT, bool CAUSAL>
+static hipError_t launch_relay_t(const RescoreArgs& s, const RouteArgs& a, hipStream_t st) {
+    const int G2 = (a.nq + RELAY_ROWS - 1) / RELAY_ROWS;
+    const size_t lds = relay_lds_bytes(a.nk, a.c, sizeof(typename Elem<DT>::type) == 2);
+    hipLaunchKernelGGL((k_relay<DT, CAUSAL>), dim3(xcd_grid(a.H * G2)), dim3(ROWS * RELAY_WAVES), lds, st, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_relay(const RescoreArgs& s, const RouteArgs& a, bool bf16, bool causal, hipStream_t st) {
+    if (!relay_fits(a.nk, a.c, a.sel, bf16)) return hipErrorInvalidValue;
+    if (bf16) return causal ? launch_relay_t<bf16_t, true>(s, a, st) : launch_relay_t<bf16_t, false>(s, a, st);
+    return causal ? launch_relay_t<float, true>(s, a, st) : launch_relay_t<float, false>(s, a, st);
+}
+
+hipError_t launch_compact_out(const int32_t* bcount, const int32_t* blist, int H, int nq, int32_t* out_rows,
+                              int32_t* out_head_counts, int32_t* out_n_rows, hipStream_t st) {
+    hipLaunchKernelGGL(k_compact_out, dim3(H), dim3(64), 0, st, bcount, blist, H, nq, out_rows, out_head_counts,
+                       out_n_rows);
+    return hipGetLastError();
 }
 
 hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st) {

@@ -23,11 +23,14 @@ STATUS_NAMES = {0: "RR_OK", -1: "RR_EINVAL", -2: "RR_EUNSUPPORTED", -3: "RR_ENOM
 # Entry points declared in include/rr.h, in declaration order.
 ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_create_rows", "rr_ledger_destroy",
                 "rr_anchor_route",
-                "rr_relay_layer", "rr_ledger_get", "rr_ledger_set", "rr_ledger_config",
+                "rr_relay_layer", "rr_ledger_set_relay_mode", "rr_ledger_get", "rr_ledger_set", "rr_ledger_config",
                 "rr_ledger_get_refreshed", "rr_ledger_set_refreshed", "rr_sparse_attention",
                 "rr_ledger_profile",
                 "rr_ledger_kernel_times", "rr_last_error", "rr_abi_version")
-RR_KERNEL_ROUTE, RR_KERNEL_RESCORE, RR_KERNEL_REROUTE, RR_KERNEL_KINDS = 0, 1, 2, 3
+RR_KERNEL_ROUTE, RR_KERNEL_RESCORE, RR_KERNEL_REROUTE, RR_KERNEL_RELAY, RR_KERNEL_LIST = 0, 1, 2, 3, 4
+RR_KERNEL_KINDS = 5
+RR_RELAY_AUTO, RR_RELAY_FUSED, RR_RELAY_COMPACTED = 0, 1, 2
+RELAY_MODES = {"auto": RR_RELAY_AUTO, "fused": RR_RELAY_FUSED, "compacted": RR_RELAY_COMPACTED}
 
 
 class rr_config(ctypes.Structure):
@@ -63,6 +66,7 @@ def lib() -> ctypes.CDLL:
         L.rr_ledger_destroy.restype = None
         L.rr_anchor_route.argtypes = [vp, vp, vp, i32, vp]
         L.rr_relay_layer.argtypes = [vp, vp, vp, i32, vp, P(rr_relay_out)]
+        L.rr_ledger_set_relay_mode.argtypes = [vp, i32]
         L.rr_ledger_get.argtypes = [vp, vp, vp, vp, i32, vp]
         L.rr_ledger_set.argtypes = [vp, vp, vp, vp, i32, i32, vp]
         L.rr_ledger_config.argtypes = [vp, P(rr_config)]
@@ -157,6 +161,12 @@ def rr_relay_layer(handle, q, k, layer: int, stream=None, flags=None, rows=None,
                                 ctypes.byref(o) if out else None), "rr_relay_layer")
 
 
+def rr_ledger_set_relay_mode(handle, mode) -> None:
+    """mode: RR_RELAY_AUTO / _FUSED / _COMPACTED, or "auto" / "fused" / "compacted"."""
+    m = RELAY_MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().rr_ledger_set_relay_mode(handle, m), "rr_ledger_set_relay_mode")
+
+
 def rr_ledger_get(handle, route, sent, anchor_layer, dst_is_host: bool, stream=None) -> None:
     _check(lib().rr_ledger_get(handle, _ptr(route), _ptr(sent), _ptr(anchor_layer),
                                int(bool(dst_is_host)), _stream(stream)), "rr_ledger_get")
@@ -191,7 +201,7 @@ def rr_ledger_profile(handle, enable: bool) -> None:
 
 
 def rr_ledger_kernel_times(handle):
-    """[(launches, total_ms)] indexed by RR_KERNEL_ROUTE / _RESCORE / _REROUTE."""
+    """[(launches, total_ms)] indexed by RR_KERNEL_ROUTE / _RESCORE / _REROUTE / _RELAY / _LIST."""
     n = (ctypes.c_int32 * RR_KERNEL_KINDS)()
     ms = (ctypes.c_double * RR_KERNEL_KINDS)()
     _check(lib().rr_ledger_kernel_times(handle, n, ms), "rr_ledger_kernel_times")
@@ -255,6 +265,10 @@ class Ledger:
 
     def anchor(self, q, k, layer, stream=None):
         rr_anchor_route(self.handle, q, k, layer, stream)
+
+    def set_relay_mode(self, mode):
+        """"auto", "fused" or "compacted" (see rr_ledger_set_relay_mode in include/rr.h)."""
+        rr_ledger_set_relay_mode(self.handle, mode)
 
     def alloc_outputs(self, device="cuda", with_scores=True) -> RelayOutputs:
         import torch

@@ -16,6 +16,6 @@ from .philox import philox4x32_10, philox4x64_10  # noqa: F401
 from .routing import (  # noqa: F401
     Ledger, LayerRecord, RelayResult, RouteConfig, anchor_layer, decode, exact_routes,
     ledger_bytes, mandatory_sentinels, n_allowed, pair_counts, preference_order, query_rows,
-    random_sentinels, rebuild_row, relay_decision, relay_gap, relay_layer, reroute_fraction,
+    random_sentinels, rebuild_row, relay_decision, relay_gap, relay_layer, relay_layer_rows, reroute_fraction,
     route_recall, run_chain, score_rows, select, selection_gap, SAMPLER_DRAW_CAP,
 )

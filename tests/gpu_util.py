@@ -181,10 +181,13 @@ def relay_excluded(cfg, layer, ledger_in, h, i, alpha, beta, tol) -> bool:
     return O.relay_gap(alpha, beta, guard) < tol
 
 
-def relay_parity(led, cfg, q, k, layer, ledger_in: O.Ledger, tol, rel, rep: Report, excluded_in=None):
-    """GPU relay layer (started from ``ledger_in``) vs oracle.  Returns the GPU ledger, the
-    oracle result and the rows excluded from here on."""
+def relay_parity(led, cfg, q, k, layer, ledger_in: O.Ledger, tol, rel, rep: Report, excluded_in=None,
+                 mode="auto"):
+    """GPU relay layer (started from ``ledger_in``, launched as ``mode``: auto, fused or
+    compacted) vs oracle.  Returns the GPU ledger, the oracle result and the rows excluded from
+    here on."""
     import torch
+    led.set_relay_mode(mode)
     set_ledger(led, ledger_in, layer - 1)
     out = led.alloc_outputs()
     led.relay(upload(q), upload(k), layer, out)
@@ -251,7 +254,7 @@ def sampled_score_rows(cfg: O.RouteConfig, q, k, rows):
     return out
 
 
-def relay_parity_sampled(led, cfg, q0, k0, q1, k1, rows, tol, rel, rep: Report):
+def relay_parity_sampled(led, cfg, q0, k0, q1, k1, rows, tol, rel, rep: Report, mode="auto"):
     """GPU anchor at layer 0 and relay at layer 1 over every row; the oracle on the sampled
     (h, i) pairs only: its own anchor ledger entries for those rows, then its relay of them
     (rows are independent, Section 3.2).  Compared on the sampled rows outside the exclusions:
@@ -271,6 +274,7 @@ def relay_parity_sampled(led, cfg, q0, k0, q1, k1, rows, tol, rel, rep: Report):
     compare_ledgers(gpu0, ora0, mask, "sampled anchor layer 0")
 
     out = led.alloc_outputs()
+    led.set_relay_mode(mode)
     led.relay(upload(q1), upload(k1), 1, out)
     torch.cuda.synchronize()
     gpu1 = ledger_np(led)

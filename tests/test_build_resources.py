@@ -13,7 +13,8 @@ from long_context_prefill_anchor_amd import build as B
 # instantiations of the main route kernel (fp32 operands need twice the registers of bf16 at
 # two waves per SIMD; the fp32 workloads are the small 128- and 256-chunk ones).
 SCRATCH_ALLOWED = {"k_routeIfLb0ELb0E": 164, "k_routeIfLb1ELb0E": 164,
-                   "k_routeIfLb0ELb1E": 324, "k_routeIfLb1ELb1E": 324}
+                   "k_routeIfLb0ELb1E": 332, "k_routeIfLb1ELb1E": 332,
+                   "k_relayIfLb0": 300, "k_relayIfLb1": 316}
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +29,7 @@ def usage():
 
 def test_report_covers_every_kernel_family(usage):
     names = " ".join(usage)
-    for fam in ("k_route", "k_rescore", "k_route_wide", "k_sparse_attn"):
+    for fam in ("k_route", "k_rescore", "k_relay", "k_compact_out", "k_route_wide", "k_sparse_attn"):
         assert fam in names, fam
 
 

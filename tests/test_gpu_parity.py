@@ -125,14 +125,37 @@ MAND_RELAY_CASES = [
 RELAY_CASES_ALL = ([c[:7] + (0, 0) + c[7:] for c in RELAY_CASES] + MAND_RELAY_CASES)
 
 
+RELAY_MODES = ["fused", "compacted"]
+
+
+def fused_supported(led: rr.Ledger, dtype: str) -> bool:
+    """The fused relay's documented limits (include/rr.h, rr_ledger_set_relay_mode): k + m <= 32,
+    c <= 32, a head's keys in 128 KB."""
+    return led.k + led.m <= 32 and led.c <= 32 and led.nk * (128 if dtype == "bf16" else 256) <= 128 * 1024
+
+
+def require_mode(led: rr.Ledger, dtype: str, mode: str):
+    """Skip a fused-mode case outside the fused relay's limits, after checking that the library
+    refuses it."""
+    if mode == "fused" and not fused_supported(led, dtype):
+        with pytest.raises(rr.RRError) as e:
+            led.set_relay_mode("fused")
+        assert e.value.status == rr.RR_EUNSUPPORTED
+        led.close()
+        pytest.skip("outside the fused relay's limits (refused with RR_EUNSUPPORTED)")
+
+
+@pytest.mark.parametrize("mode", RELAY_MODES)
 @pytest.mark.parametrize("case", RELAY_CASES_ALL, ids=[c[0] for c in RELAY_CASES_ALL])
-def test_relay_lockstep(case):
-    """Same ledger in (oracle anchor at layer 4, injected with rr_ledger_set), relay at layer 5."""
+def test_relay_lockstep(case, mode):
+    """Same ledger in (oracle anchor at layer 4, injected with rr_ledger_set), relay at layer 5,
+    through the fused relay kernel and through the two-kernel compacted schedule."""
     name, H, nq, nk, k, m, r, sink, recent, dtype, causal, drift, kind = case
     gamma = 0.01 if name == "relay_guard" else 0.0
-    U.log(f"[relay] {name} H={H} nq={nq} nk={nk} sink={sink} recent={recent} {dtype} causal={causal} "
+    U.log(f"[relay {mode}] {name} H={H} nq={nq} nk={nk} sink={sink} recent={recent} {dtype} causal={causal} "
           f"drift={drift} gamma={gamma}")
     led, cfg = make(H, nq, nk, k, m, r, dtype, causal, 21, gamma, sink=sink, recent=recent)
+    require_mode(led, dtype, mode)
     q0, k0 = inputs(kind, H, nq, nk, dtype, 31)
     if kind == "int":
         qn, kn = inputs(kind, H, nq, nk, dtype, 32)
@@ -147,7 +170,7 @@ def test_relay_lockstep(case):
     tol = 0.0 if kind != "gauss" else U.GAP_TOL
     rel = 1e-5 if dtype == "f32" else 1e-3
     rep = U.Report()
-    gpu, res, ex = U.relay_parity(led, cfg, q1, k1, 5, ora0, tol, rel, rep)
+    gpu, res, ex = U.relay_parity(led, cfg, q1, k1, 5, ora0, tol, rel, rep, mode=mode)
     nflag = int(res.flags.sum())
     U.log(f"   rows={rep.rows} flagged={nflag} excluded={rep.excluded} max|ds|={rep.max_score_err:.2e}")
     assert 0 < nflag < H * nq
@@ -156,7 +179,7 @@ def test_relay_lockstep(case):
     led.close()
 
 
-def run_chain_gpu_vs_oracle(w: W.Workload, heads=None, tol=U.GAP_TOL):
+def run_chain_gpu_vs_oracle(w: W.Workload, heads=None, tol=U.GAP_TOL, mode="auto"):
     """Both sides run the whole chain on their own state; per-layer comparison with the
     exclusion rule (an excluded row stays excluded until the next anchor layer).
     ``rep.excluded`` counts exclusion events (a row newly excluded at a layer);
@@ -166,6 +189,7 @@ def run_chain_gpu_vs_oracle(w: W.Workload, heads=None, tol=U.GAP_TOL):
     nq = w.nq
     led = rr.Ledger(H, w.nq, w.nk, 64, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed,
                     sink=w.sink, recent=w.recent, min_reuse=w.min_reuse, gamma_extra=w.gamma_extra)
+    led.set_relay_mode(mode)
     cfg = U.oracle_cfg(led, w.dtype, w.gamma, w.causal, w.seed)
     rel = 1e-5 if w.dtype == "f32" else 1e-3
     rep = U.Report()
@@ -219,9 +243,10 @@ def chain_report(rep):
     assert held <= max(4, rep.rows // 20)
 
 
-def test_chain_tiny():
-    U.log("[chain] tiny_chain")
-    rep = run_chain_gpu_vs_oracle(W.tiny_chain())
+@pytest.mark.parametrize("mode", RELAY_MODES)
+def test_chain_tiny(mode):
+    U.log(f"[chain {mode}] tiny_chain")
+    rep = run_chain_gpu_vs_oracle(W.tiny_chain(), mode=mode)
     chain_report(rep)
 
 
@@ -248,8 +273,9 @@ _ALL = dict(sink=1, recent=2, min_reuse=1, gamma_extra=0.005)
 BUCKET_EXTRA = {"buckets_all_options": _ALL, "buckets_wide_all_options": _ALL}
 
 
+@pytest.mark.parametrize("mode", ["auto", "compacted"])
 @pytest.mark.parametrize("case", BUCKET_CASES, ids=[c[0] for c in BUCKET_CASES])
-def test_width_buckets(case):
+def test_width_buckets(case, mode):
     """Two width buckets over complementary query-row sets, each with its own k, m, r: both
     anchor at layer 3 and relay at layer 4 on the full Q, against the oracle bucket (pinned on
     the CPU to the same rows of a ledger over every row)."""
@@ -267,7 +293,7 @@ def test_width_buckets(case):
         cfg = U.oracle_cfg(led, dtype, 0.0, causal, 61)
         rep = U.Report()
         _, ora = U.anchor_parity(led, cfg, q0, k0, 3, U.GAP_TOL, rep)
-        _, res, _ = U.relay_parity(led, cfg, q1, k1, 4, ora, U.GAP_TOL, rel, rep)
+        _, res, _ = U.relay_parity(led, cfg, q1, k1, 4, ora, U.GAP_TOL, rel, rep, mode=mode)
         U.log(f"   rows={rep.rows} flagged={int(res.flags.sum())} excluded={rep.excluded}")
         assert rep.excluded <= max(2, rep.rows // 100)
         led.close()
@@ -357,8 +383,9 @@ HYST_CASES = [
 ]
 
 
+@pytest.mark.parametrize("mode", RELAY_MODES)
 @pytest.mark.parametrize("case", HYST_CASES, ids=[c[0] for c in HYST_CASES])
-def test_relay_lockstep_hysteresis(case):
+def test_relay_lockstep_hysteresis(case, mode):
     """Oracle anchor at layer 4 and relay at 5 (which refreshes some rows and marks them),
     injected with rr_ledger_set + rr_ledger_set_refreshed; then relay layer 6 on both sides."""
     name, min_reuse, gamma_extra = case
@@ -375,7 +402,7 @@ def test_relay_lockstep_hysteresis(case):
     ora5 = O.relay_layer(cfg, q1, k1, 5, O.anchor_layer(cfg, q0, k0, 4)).ledger
     assert ora5.refreshed.sum() > 0
     rep = U.Report()
-    gpu, res, ex = U.relay_parity(led, cfg, q2, k2, 6, ora5, U.GAP_TOL, 1e-3, rep)
+    gpu, res, ex = U.relay_parity(led, cfg, q2, k2, 6, ora5, U.GAP_TOL, 1e-3, rep, mode=mode)
     skipped = int(((ora5.refreshed == 1) & (6 - ora5.anchor <= min_reuse)).sum())
     U.log(f"   rows={rep.rows} flagged={int(res.flags.sum())} untested={skipped} "
           f"still marked={int(res.ledger.refreshed.sum())} excluded={rep.excluded}")
@@ -416,6 +443,13 @@ def test_chain_drift_sweep(sigma, seed):
     chain_report(rep)
 
 
+def test_chain_drift_sweep_compacted():
+    """The drift-sweep chain through the two-kernel compacted relay schedule."""
+    U.log("[chain compacted] drift_sweep sigma=0.03 seed=2")
+    rep = run_chain_gpu_vs_oracle(W.drift_sweep(0.03, 2), mode="compacted")
+    chain_report(rep)
+
+
 @pytest.mark.parametrize("n", [128, 256, 512, 1024])
 def test_chain_scale_sweep(n):
     U.log(f"[chain] scale_sweep n={n}")
@@ -430,16 +464,17 @@ def test_chain_batched_heads_subset():
     chain_report(rep)
 
 
-def test_full_size_batched_heads_layers():
+@pytest.mark.parametrize("mode", RELAY_MODES)
+def test_full_size_batched_heads_layers(mode):
     """Full 32 x 1024 bf16 anchor layer, then one relay layer, every row compared."""
     w = W.batched_heads()
-    U.log("[full] batched_heads anchor layer 0 + relay layer 1, all 32768 rows")
+    U.log(f"[full {mode}] batched_heads anchor layer 0 + relay layer 1, all 32768 rows")
     gen = synth.generate(w)
     l0, l1 = next(gen), next(gen)
     led, cfg = make(w.heads, w.n, w.n, w.k, w.m, w.r, w.dtype, False, w.seed)
     rep = U.Report()
     _, ora0 = U.anchor_parity(led, cfg, l0.q, l0.k, 0, U.GAP_TOL, rep)
-    _, res, _ = U.relay_parity(led, cfg, l1.q, l1.k, 1, ora0, U.GAP_TOL, 1e-3, rep)
+    _, res, _ = U.relay_parity(led, cfg, l1.q, l1.k, 1, ora0, U.GAP_TOL, 1e-3, rep, mode=mode)
     U.log(f"   rows={rep.rows} excluded={rep.excluded} flagged={int(res.flags.sum())} max|ds|={rep.max_score_err:.2e}")
     # the exclusion rate is a property of the data (oracle gaps), ~0.5% at 1024 chunks
     assert rep.excluded <= rep.rows // 50
@@ -464,14 +499,15 @@ def test_full_size_causal_large_sampled():
     led.close()
 
 
-def test_full_size_causal_large_relay_sampled():
+@pytest.mark.parametrize("mode", ["auto", "compacted"])
+def test_full_size_causal_large_relay_sampled(mode):
     """Full 64 x 4096 causal bf16: GPU anchor at layer 0 and relay at layer 1 on every row (the
     reroute's flagged-row search then spans 64 rescore blocks per head, the edge of its
     block-count scan); the oracle relays sampled rows from its own anchor entries: every head's
     first 64 rows (rows shorter than k + m, sentinel segments still filling), the last 64 rows
     of every 8th head (rows near 4095) and 2000 random (head, row) pairs."""
     w = W.causal_large()
-    U.log("[full] causal_large anchor layer 0 + relay layer 1, sampled rows")
+    U.log(f"[full {mode}] causal_large anchor layer 0 + relay layer 1, sampled rows")
     gen = synth.generate(w)
     l0, l1 = next(gen), next(gen)
     led, cfg = make(w.heads, w.n, w.n, w.k, w.m, w.r, w.dtype, True, w.seed)
@@ -480,7 +516,8 @@ def test_full_size_causal_large_relay_sampled():
     rows |= {(h, i) for h in range(0, w.heads, 8) for i in range(w.n - 64, w.n)}
     rows |= {(int(h), int(i)) for h, i in zip(rng.integers(0, w.heads, 2000), rng.integers(0, w.n, 2000))}
     rep = U.Report()
-    compared, flagged = U.relay_parity_sampled(led, cfg, l0.q, l0.k, l1.q, l1.k, rows, U.GAP_TOL, 1e-3, rep)
+    compared, flagged = U.relay_parity_sampled(led, cfg, l0.q, l0.k, l1.q, l1.k, rows, U.GAP_TOL, 1e-3, rep,
+                                               mode=mode)
     U.log(f"   sampled={rep.rows} compared={compared} flagged={flagged} excluded={rep.excluded} "
           f"max|ds|={rep.max_score_err:.2e}")
     assert compared >= 6000 and flagged > 1000
@@ -488,15 +525,17 @@ def test_full_size_causal_large_relay_sampled():
     led.close()
 
 
-def test_repeat_runs_are_bit_identical():
+@pytest.mark.parametrize("mode", RELAY_MODES)
+def test_repeat_runs_are_bit_identical(mode):
     import torch
     w = W.scale_sweep(1024)
-    U.log("[determinism] scale_sweep n=1024, anchor + relay twice")
+    U.log(f"[determinism {mode}] scale_sweep n=1024, anchor + relay twice")
     gen = synth.generate(w)
     l0, l1 = next(gen), next(gen)
     outs = []
     for _ in range(2):
         led = rr.Ledger(1, 1024, 1024, 64, 12, 12, 8, 0.0, False, "bf16", 0)
+        led.set_relay_mode(mode)
         led.anchor(U.upload(l0.q), U.upload(l0.k), 0)
         o = led.alloc_outputs()
         led.relay(U.upload(l1.q), U.upload(l1.k), 1, o)
@@ -533,22 +572,39 @@ def test_state_rules_on_device():
 
 
 @pytest.mark.gpu
-def test_kernel_timing_records_every_launch():
+@pytest.mark.parametrize("mode", RELAY_MODES)
+def test_kernel_timing_records_every_launch(mode):
     import torch
-    U.log("[profile] per-kernel launch events")
+    U.log(f"[profile {mode}] per-kernel launch events")
     led = rr.Ledger(2, 128, 128, 64, 12, 12, 8, 0.0, False, "f32", 0)
+    led.set_relay_mode(mode)
     q, k = synth.gaussian_inputs(2, 128, 128, 64, seed=1)
     qd, kd = U.upload(q), U.upload(k)
     led.profile(True)
     led.anchor(qd, kd, 0)
     led.relay(qd, kd, 1)
-    led.relay(qd, kd, 2)
+    out = led.alloc_outputs(with_scores=False)
+    led.relay(qd, kd, 2, out)                                      # with the compacted-list outputs
     kt = led.kernel_times()
-    assert [n for n, _ in kt] == [1, 2, 2]
-    assert all(ms > 0.0 for _, ms in kt)
-    assert [n for n, _ in led.kernel_times()] == [0, 0, 0]       # reading clears the record
+    want = [1, 0, 0, 2, 1] if mode == "fused" else [1, 2, 2, 0, 0]
+    assert [n for n, _ in kt] == want
+    assert all(ms > 0.0 for n, ms in kt if n)
+    assert [n for n, _ in led.kernel_times()] == [0] * rr.RR_KERNEL_KINDS    # reading clears the record
     led.profile(False)
     led.anchor(qd, kd, 3)
     torch.cuda.synchronize()
-    assert [n for n, _ in led.kernel_times()] == [0, 0, 0]
+    assert [n for n, _ in led.kernel_times()] == [0] * rr.RR_KERNEL_KINDS
+    led.close()
+
+
+def test_relay_mode_rules():
+    U.log("[state] relay modes")
+    led = rr.Ledger(1, 64, 64, 64, 12, 24, 8, 0.0, False, "f32", 0)     # k + m = 36: wide kernel
+    with pytest.raises(rr.RRError) as e:
+        led.set_relay_mode("fused")
+    assert e.value.status == rr.RR_EUNSUPPORTED
+    led.set_relay_mode("compacted")
+    with pytest.raises(rr.RRError) as e:
+        rr.rr_ledger_set_relay_mode(led.handle, 7)
+    assert e.value.status == rr.RR_EINVAL
     led.close()

@@ -327,3 +327,26 @@ def test_relay_gap_is_the_distance_to_the_decision_flip():
             assert (a - frac * gap > b + g) == reuse
         toward = -1.0 if reuse else 1.0
         assert (a + toward * 1.1 * gap > b + g) != reuse
+
+
+def test_relay_layer_rows_equals_relay_layer_on_those_rows(drift_chain):
+    """A sample of rows relayed alone gives the full layer's flags, alpha, beta, candidate
+    scores and ledger entries on those rows (rows are independent, Section 3.2); every other
+    row keeps its input ledger entry."""
+    w, layers, recs = drift_chain
+    rec = next(r for r in recs if r.kind == "relay" and r.flags.sum() > 5)
+    li = layers[rec.layer]
+    cfg = cfg_of(w)
+    full = O.relay_layer(cfg, li.q, li.k, rec.layer, rec.ledger_in)
+    rows = [(0, i) for i in range(0, cfg.nq, 7)]
+    part = O.relay_layer_rows(cfg, li.q, li.k, rec.layer, rec.ledger_in, rows)
+    idx = np.array([i for _, i in rows])
+    np.testing.assert_array_equal(part.flags[0, idx], full.flags[0, idx])
+    np.testing.assert_array_equal(part.alpha[0, idx], full.alpha[0, idx])
+    np.testing.assert_array_equal(part.beta[0, idx], full.beta[0, idx])
+    np.testing.assert_array_equal(part.cand_scores[0, idx], full.cand_scores[0, idx])
+    for name in ("route", "sent", "anchor", "refreshed"):
+        np.testing.assert_array_equal(getattr(part.ledger, name)[0, idx], getattr(full.ledger, name)[0, idx])
+    rest = np.setdiff1d(np.arange(cfg.nq), idx)
+    np.testing.assert_array_equal(part.ledger.route[0, rest], rec.ledger_in.route[0, rest])
+    assert part.flags[0, rest].sum() == 0

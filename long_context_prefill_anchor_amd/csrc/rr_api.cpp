@@ -158,43 +158,144 @@ void release_events(rr_ledger* L) {
 // layer that rescores from LDS and skips the threshold pass beats the two-kernel schedule.
 constexpr long long FUSED_MAX_BLOCKS = 512;
 
-bool fused_fits(const rr_ledger* L) {
-    return rr::relay_fits(L->cfg.nk, L->c, L->sel, L->cfg.dtype == RR_BF16);
+// Non-owning view of a ledger's device state and of the working memory a relay layer's kernels
+// use: taken from an rr_ledger, or from caller memory and the fixed scratch array
+// (rr_relay_layer_noalloc).
+struct LedgerView {
+    rr_config cfg;
+    int c, sel, nq_q;
+    int32_t relay_mode;
+    int32_t* ids;
+    int32_t* anchor;
+    uint8_t* refreshed;
+    const int32_t* qmap;
+    uint8_t* flags_ws;
+    float* hint_ws;
+    int32_t* bcount;
+    int32_t* blist;
+};
+
+LedgerView view_of(const rr_ledger* L) {
+    return LedgerView{L->cfg, L->c, L->sel, L->nq_q, L->relay_mode, L->ids, L->anchor, L->refreshed, L->qmap,
+                      L->flags_ws, L->hint_ws, L->bcount, L->blist};
 }
 
-bool use_fused(const rr_ledger* L) {
-    if (!fused_fits(L)) return false;
-    if (L->relay_mode != RR_RELAY_AUTO) return L->relay_mode == RR_RELAY_FUSED;
-    return (long long)L->cfg.heads * ((L->cfg.nq + 127) / 128) <= FUSED_MAX_BLOCKS;
+bool fused_fits(const LedgerView& v) {
+    return rr::relay_fits(v.cfg.nk, v.c, v.sel, v.cfg.dtype == RR_BF16);
 }
 
-rr::RouteArgs route_args(const rr_ledger* L, const void* q, const void* k, int layer) {
+bool use_fused(const LedgerView& v) {
+    if (!fused_fits(v)) return false;
+    if (v.relay_mode != RR_RELAY_AUTO) return v.relay_mode == RR_RELAY_FUSED;
+    return (long long)v.cfg.heads * ((v.cfg.nq + 127) / 128) <= FUSED_MAX_BLOCKS;
+}
+
+rr::RouteArgs route_args(const LedgerView& v, const void* q, const void* k, int layer) {
     rr::RouteArgs a{};
     a.qp = q;
     a.kp = k;
-    a.ids = L->ids;
-    a.anchor = L->anchor;
-    a.refreshed = L->refreshed;
-    a.qmap = L->qmap;
-    a.nq_q = L->nq_q;
-    a.flags = L->flags_ws;
-    a.hint = L->hint_ws;
-    a.bcount = L->bcount;
-    a.blist = L->blist;
-    a.H = L->cfg.heads;
-    a.nq = L->cfg.nq;
-    a.nk = L->cfg.nk;
-    a.k = L->cfg.k;
-    a.m = L->cfg.m;
-    a.r = L->cfg.r;
-    a.sink = L->cfg.sink;
-    a.recent = L->cfg.recent;
-    a.c = L->c;
-    a.sel = L->sel;
+    a.ids = v.ids;
+    a.anchor = v.anchor;
+    a.refreshed = v.refreshed;
+    a.qmap = v.qmap;
+    a.nq_q = v.nq_q;
+    a.flags = v.flags_ws;
+    a.hint = v.hint_ws;
+    a.bcount = v.bcount;
+    a.blist = v.blist;
+    a.H = v.cfg.heads;
+    a.nq = v.cfg.nq;
+    a.nk = v.cfg.nk;
+    a.k = v.cfg.k;
+    a.m = v.cfg.m;
+    a.r = v.cfg.r;
+    a.sink = v.cfg.sink;
+    a.recent = v.cfg.recent;
+    a.c = v.c;
+    a.sel = v.sel;
     a.layer = layer;
-    a.seed_lo = (uint32_t)(L->cfg.seed & 0xFFFFFFFFull);
-    a.seed_hi = (uint32_t)(L->cfg.seed >> 32);
+    a.seed_lo = (uint32_t)(v.cfg.seed & 0xFFFFFFFFull);
+    a.seed_hi = (uint32_t)(v.cfg.seed >> 32);
     return a;
+}
+
+rr::RouteArgs route_args(const rr_ledger* L, const void* q, const void* k, int layer) {
+    return route_args(view_of(L), q, k, layer);
+}
+
+// The launch sequence of one relay layer (Sections 3.2, 4.1, 4.2) on a view: the fused relay
+// kernel (plus the compacted-list kernel when those outputs are asked for), or the rescoring
+// kernel then the reroute of the compacted rows.  `T`: ledger whose profiling records the
+// launches (null: none).  On failure *what names the launch.
+hipError_t relay_launch(const LedgerView& v, const void* q, const void* k, int32_t layer, hipStream_t st,
+                        const rr_relay_out* out, rr_ledger* T, const char** what) {
+    rr::RescoreArgs s{};
+    s.qp = q;
+    s.kp = k;
+    s.ids = v.ids;
+    s.flags_ws = v.flags_ws;
+    s.hint_ws = v.hint_ws;
+    s.bcount = v.bcount;
+    s.blist = v.blist;
+    s.out_flags = out ? out->flags : nullptr;
+    s.out_alpha = out ? out->alpha : nullptr;
+    s.out_beta = out ? out->beta : nullptr;
+    s.cand_scores = out ? out->cand_scores : nullptr;
+    s.H = v.cfg.heads;
+    s.nq = v.cfg.nq;
+    s.nk = v.cfg.nk;
+    s.k = v.cfg.k;
+    s.m = v.cfg.m;
+    s.r = v.cfg.r;
+    s.c = v.c;
+    s.sel = v.sel;
+    s.gamma = v.cfg.gamma;
+    s.anchor = v.anchor;
+    s.refreshed = v.refreshed;
+    s.qmap = v.qmap;
+    s.nq_q = v.nq_q;
+    s.layer = layer;
+    s.min_reuse = v.cfg.min_reuse;
+    s.gamma_extra = v.cfg.gamma_extra;
+    rr::RouteArgs a = route_args(v, q, k, layer);
+    a.refresh_mark = 1;
+    const bool bf16 = v.cfg.dtype == RR_BF16, causal = v.cfg.causal != 0;
+    const bool timed = T != nullptr;
+    if (use_fused(v)) {
+        int tix = timed ? time_begin(T, RR_KERNEL_RELAY, st) : -1;
+        hipError_t e = rr::launch_relay(s, a, bf16, causal, st);
+        if (timed) time_end(T, tix, st);
+        if (e != hipSuccess) {
+            *what = "relay launch";
+            return e;
+        }
+        if (out && (out->rows || out->head_counts || out->n_rows)) {
+            tix = timed ? time_begin(T, RR_KERNEL_LIST, st) : -1;
+            e = rr::launch_compact_out(v.bcount, v.blist, v.cfg.heads, v.cfg.nq, out->rows, out->head_counts,
+                                       out->n_rows, st);
+            if (timed) time_end(T, tix, st);
+            if (e != hipSuccess) {
+                *what = "compacted-list launch";
+                return e;
+            }
+        }
+        return hipSuccess;
+    }
+    int tix = timed ? time_begin(T, RR_KERNEL_RESCORE, st) : -1;
+    hipError_t e = rr::launch_rescore(s, bf16, st);
+    if (timed) time_end(T, tix, st);
+    if (e != hipSuccess) {
+        *what = "rescore launch";
+        return e;
+    }
+    a.out_rows = out ? out->rows : nullptr;
+    a.out_head_counts = out ? out->head_counts : nullptr;
+    a.out_n_rows = out ? out->n_rows : nullptr;
+    tix = timed ? time_begin(T, RR_KERNEL_REROUTE, st) : -1;
+    e = v.sel > 32 ? rr::launch_route_wide(a, bf16, causal, true, st) : rr::launch_route(a, bf16, causal, true, st);
+    if (timed) time_end(T, tix, st);
+    if (e != hipSuccess) *what = "reroute launch";
+    return e;
 }
 
 }  // namespace
@@ -373,67 +474,9 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
         return fail(RR_ESTATE, "relay layer %d is not after the last layer %d", layer, L->last_layer);
     if (!q || !k) return fail(RR_EINVAL, "q and k must be device pointers");
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-
-    rr::RescoreArgs s{};
-    s.qp = q;
-    s.kp = k;
-    s.ids = L->ids;
-    s.flags_ws = L->flags_ws;
-    s.hint_ws = L->hint_ws;
-    s.bcount = L->bcount;
-    s.blist = L->blist;
-    s.out_flags = out ? out->flags : nullptr;
-    s.out_alpha = out ? out->alpha : nullptr;
-    s.out_beta = out ? out->beta : nullptr;
-    s.cand_scores = out ? out->cand_scores : nullptr;
-    s.H = L->cfg.heads;
-    s.nq = L->cfg.nq;
-    s.nk = L->cfg.nk;
-    s.k = L->cfg.k;
-    s.m = L->cfg.m;
-    s.r = L->cfg.r;
-    s.c = L->c;
-    s.sel = L->sel;
-    s.gamma = L->cfg.gamma;
-    s.anchor = L->anchor;
-    s.refreshed = L->refreshed;
-    s.qmap = L->qmap;
-    s.nq_q = L->nq_q;
-    s.layer = layer;
-    s.min_reuse = L->cfg.min_reuse;
-    s.gamma_extra = L->cfg.gamma_extra;
-    rr::RouteArgs a = route_args(L, q, k, layer);
-    a.refresh_mark = 1;
-    const bool bf16 = L->cfg.dtype == RR_BF16;
-    if (use_fused(L)) {
-        int tix = time_begin(L, RR_KERNEL_RELAY, st);
-        hipError_t e = rr::launch_relay(s, a, bf16, L->cfg.causal != 0, st);
-        time_end(L, tix, st);
-        if (e != hipSuccess) return hip_fail(L, e, "relay launch");
-        if (out && (out->rows || out->head_counts || out->n_rows)) {
-            tix = time_begin(L, RR_KERNEL_LIST, st);
-            e = rr::launch_compact_out(L->bcount, L->blist, L->cfg.heads, L->cfg.nq, out->rows, out->head_counts,
-                                       out->n_rows, st);
-            time_end(L, tix, st);
-            if (e != hipSuccess) return hip_fail(L, e, "compacted-list launch");
-        }
-        L->last_layer = layer;
-        return ok();
-    }
-
-    int tix = time_begin(L, RR_KERNEL_RESCORE, st);
-    hipError_t e = rr::launch_rescore(s, bf16, st);
-    time_end(L, tix, st);
-    if (e != hipSuccess) return hip_fail(L, e, "rescore launch");
-
-    a.out_rows = out ? out->rows : nullptr;
-    a.out_head_counts = out ? out->head_counts : nullptr;
-    a.out_n_rows = out ? out->n_rows : nullptr;
-    tix = time_begin(L, RR_KERNEL_REROUTE, st);
-    e = L->sel > 32 ? rr::launch_route_wide(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, true, st)
-                    : rr::launch_route(a, L->cfg.dtype == RR_BF16, L->cfg.causal != 0, true, st);
-    time_end(L, tix, st);
-    if (e != hipSuccess) return hip_fail(L, e, "reroute launch");
+    const char* what = "";
+    const hipError_t e = relay_launch(view_of(L), q, k, layer, st, out, L, &what);
+    if (e != hipSuccess) return hip_fail(L, e, what);
     L->last_layer = layer;
     return ok();
 }
@@ -442,7 +485,7 @@ rr_status rr_ledger_set_relay_mode(rr_ledger* L, int32_t mode) {
     if (!L) return fail(RR_EINVAL, "ledger is NULL");
     if (mode != RR_RELAY_AUTO && mode != RR_RELAY_FUSED && mode != RR_RELAY_COMPACTED)
         return fail(RR_EINVAL, "unknown relay mode %d", mode);
-    if (mode == RR_RELAY_FUSED && !fused_fits(L))
+    if (mode == RR_RELAY_FUSED && !fused_fits(view_of(L)))
         return fail(RR_EUNSUPPORTED, "the fused relay needs k + m <= 32, c <= 32 and a head's keys in 128 KB "
                     "(got k + m = %d, c = %d, nk = %d)", L->sel, L->c, L->cfg.nk);
     L->relay_mode = mode;

@@ -24,9 +24,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------------- keys
 
 __device__ __forceinline__ uint32_t orderable(float s) {
-    uint32_t u = __float_as_uint(s);
-    u = (u == 0x80000000u) ? 0u : u;                      // -0.0 ties with +0.0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    // -0.0 + 0.0 is +0.0 in round-to-nearest, so both zeros tie; then negative values have all
+    // bits flipped and non-negative ones only the sign bit (no compare, no select).
+    const uint32_t u = __float_as_uint(s + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float from_orderable(uint32_t o) {

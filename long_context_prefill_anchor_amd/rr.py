@@ -57,6 +57,10 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m long_context_prefill_anchor_amd.build`")
+        # torch's HIP runtime must see the devices before this library's first HIP call; bring
+        # it up first, whatever the caller imported or called before.
+        import torch
+        torch.cuda.is_available()
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER
         L.rr_config_check.argtypes = [P(rr_config)]

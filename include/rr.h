@@ -141,6 +141,27 @@ rr_status rr_anchor_route(rr_ledger* ledger, const void* q, const void* k, int32
 rr_status rr_relay_layer(rr_ledger* ledger, const void* q, const void* k, int32_t layer,
                          void* stream, const rr_relay_out* out);
 
+/* Allocation-free relay layer, for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid device allocation): the relay layer of
+ * rr_relay_layer (same kernels and schedule as RR_RELAY_AUTO, same results) on ledger state in
+ * caller-owned device memory, updated in place for the rerouted rows:
+ *   ids          [heads, nq, c]  each row's route (k) then its sentinels laid out as in
+ *                                rr_ledger_get (route and sent concatenated per row)
+ *   anchor_layer [heads, nq]     layer of each row's last full routing
+ *   refreshed    [heads, nq]     hysteresis state (see rr_ledger_get_refreshed)
+ * The layer's working memory (refresh flags, reroute thresholds, per-block flagged-row lists and
+ * counts) is one fixed device array of the library, 2375680 bytes per GPU, held until the
+ * process ends: heads * ceil(nq / 64) * 64 must not exceed 262144 (RR_EUNSUPPORTED otherwise).
+ * Nothing is allocated on the device or the host at call time.  Every call on a GPU uses that
+ * GPU's array, and each call rewrites every entry it reads: calls that overlap on one GPU
+ * (unordered streams) race and must not be issued.  The state is trusted to be an anchored ledger
+ * of this configuration; the layer order is the caller's.  Width buckets are not served.
+ * Errors: RR_EINVAL / RR_EUNSUPPORTED for the configuration (as rr_config_check), NULL pointers,
+ * layer < 0 or the size limit; RR_EDEVICE if a launch fails. */
+rr_status rr_relay_layer_noalloc(const rr_config* cfg, int32_t* ids, int32_t* anchor_layer, uint8_t* refreshed,
+                                 const void* q, const void* k, int32_t layer, void* stream,
+                                 const rr_relay_out* out);
+
 /* How a relay layer is launched (the result is the same; only the schedule differs):
  *   RR_RELAY_FUSED      one kernel: each block takes 128 ledger rows of one head, stages the
  *                       head's keys in LDS, rescores its rows (Eq. 5-8) from there, gathers its

@@ -7,12 +7,21 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
 
 #include "rr.h"
 #include "rr_internal.h"
+
+// Working memory of rr_relay_layer_noalloc: the relay kernels' refresh flags (1 byte per row),
+// reroute thresholds (4), per-block flagged-row lists (4) and per-block counts (4 per 64 rows),
+// for at most NOALLOC_MAX_ROWS rows (heads * ceil(nq / 64) * 64).  One copy per GPU, held until
+// the process ends; host code reaches it only through the address hipGetSymbolAddress returns.
+constexpr size_t NOALLOC_MAX_ROWS = size_t(1) << 18;
+constexpr size_t NOALLOC_SCRATCH_BYTES = NOALLOC_MAX_ROWS * (1 + 4 + 4) + NOALLOC_MAX_ROWS / 64 * 4;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
 
 struct rr_ledger {
     rr_config cfg;
@@ -221,6 +230,30 @@ rr::RouteArgs route_args(const LedgerView& v, const void* q, const void* k, int 
 
 rr::RouteArgs route_args(const rr_ledger* L, const void* q, const void* k, int layer) {
     return route_args(view_of(L), q, k, layer);
+}
+
+// Device address of this GPU's copy of `scratch`, looked up once per device with that device
+// current (each GPU holds its own copy at its own address; in host code the array's name is
+// not a device address).
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+rr_status scratch_for_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RR_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return fail(RR_EUNSUPPORTED, "device %d past the scratch table", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(RR_EDEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return RR_OK;
 }
 
 // The launch sequence of one relay layer (Sections 3.2, 4.1, 4.2) on a view: the fused relay
@@ -478,6 +511,34 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
     const hipError_t e = relay_launch(view_of(L), q, k, layer, st, out, L, &what);
     if (e != hipSuccess) return hip_fail(L, e, what);
     L->last_layer = layer;
+    return ok();
+}
+
+rr_status rr_relay_layer_noalloc(const rr_config* cfg, int32_t* ids, int32_t* anchor_layer, uint8_t* refreshed,
+                                 const void* q, const void* k, int32_t layer, void* stream, const rr_relay_out* out) {
+    const rr_status st0 = check_cfg(cfg, false);
+    if (st0 != RR_OK) return st0;
+    if (!ids || !anchor_layer || !refreshed) return fail(RR_EINVAL, "ids, anchor_layer and refreshed are required");
+    if (!q || !k) return fail(RR_EINVAL, "q and k must be device pointers");
+    if (layer < 0) return fail(RR_EINVAL, "layer must be >= 0 (got %d)", layer);
+    const long long padded = (long long)cfg->heads * ((cfg->nq + 63) / 64) * 64;
+    if (padded > (long long)NOALLOC_MAX_ROWS)
+        return fail(RR_EUNSUPPORTED, "heads * ceil(nq / 64) * 64 = %lld rows exceed the fixed working memory (%zu rows)",
+                    padded, NOALLOC_MAX_ROWS);
+    void* base = nullptr;
+    const rr_status st1 = scratch_for_current_device(&base);
+    if (st1 != RR_OK) return st1;
+    unsigned char* b = static_cast<unsigned char*>(base);
+    constexpr size_t P = NOALLOC_MAX_ROWS;
+    LedgerView v{*cfg, cfg->k + cfg->m + cfg->sink + cfg->recent + cfg->r, cfg->k + cfg->m, cfg->nq, RR_RELAY_AUTO,
+                 ids, anchor_layer, refreshed, nullptr,
+                 b,                                              // refresh flags      [P] u8
+                 reinterpret_cast<float*>(b + P),                // reroute thresholds [P] f32
+                 reinterpret_cast<int32_t*>(b + 5 * P),          // per-block counts   [P / 64] i32
+                 reinterpret_cast<int32_t*>(b + 5 * P + P / 16)};  // per-block lists  [P] i32
+    const char* what = "";
+    const hipError_t e = relay_launch(v, q, k, layer, reinterpret_cast<hipStream_t>(stream), out, nullptr, &what);
+    if (e != hipSuccess) return fail(RR_EDEVICE, "%s: %s", what, hipGetErrorString(e));
     return ok();
 }
 

@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "RR_OK", -1: "RR_EINVAL", -2: "RR_EUNSUPPORTED", -3: "RR_ENOM
 # Entry points declared in include/rr.h, in declaration order.
 ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_create_rows", "rr_ledger_destroy",
                 "rr_anchor_route",
-                "rr_relay_layer", "rr_ledger_set_relay_mode", "rr_ledger_get", "rr_ledger_set", "rr_ledger_config",
+                "rr_relay_layer", "rr_relay_layer_noalloc", "rr_ledger_set_relay_mode", "rr_ledger_get",
+                "rr_ledger_set", "rr_ledger_config",
                 "rr_ledger_get_refreshed", "rr_ledger_set_refreshed", "rr_sparse_attention",
                 "rr_ledger_profile",
                 "rr_ledger_kernel_times", "rr_last_error", "rr_abi_version")
@@ -71,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.rr_anchor_route.argtypes = [vp, vp, vp, i32, vp]
         L.rr_relay_layer.argtypes = [vp, vp, vp, i32, vp, P(rr_relay_out)]
         L.rr_ledger_set_relay_mode.argtypes = [vp, i32]
+        L.rr_relay_layer_noalloc.argtypes = [P(rr_config), vp, vp, vp, vp, vp, i32, vp, P(rr_relay_out)]
         L.rr_ledger_get.argtypes = [vp, vp, vp, vp, i32, vp]
         L.rr_ledger_set.argtypes = [vp, vp, vp, vp, i32, i32, vp]
         L.rr_ledger_config.argtypes = [vp, P(rr_config)]
@@ -163,6 +165,16 @@ def rr_relay_layer(handle, q, k, layer: int, stream=None, flags=None, rows=None,
                      _ptr(beta), _ptr(cand_scores))
     _check(lib().rr_relay_layer(handle, _ptr(q), _ptr(k), int(layer), _stream(stream),
                                 ctypes.byref(o) if out else None), "rr_relay_layer")
+
+
+def rr_relay_layer_noalloc(cfg: rr_config, ids, anchor_layer, refreshed, q, k, layer: int, stream=None,
+                           flags=None, rows=None, head_counts=None, n_rows=None, alpha=None, beta=None,
+                           cand_scores=None, out: bool = True) -> None:
+    o = rr_relay_out(_ptr(flags), _ptr(rows), _ptr(head_counts), _ptr(n_rows), _ptr(alpha),
+                     _ptr(beta), _ptr(cand_scores))
+    _check(lib().rr_relay_layer_noalloc(ctypes.byref(cfg), _ptr(ids), _ptr(anchor_layer), _ptr(refreshed),
+                                        _ptr(q), _ptr(k), int(layer), _stream(stream),
+                                        ctypes.byref(o) if out else None), "rr_relay_layer_noalloc")
 
 
 def rr_ledger_set_relay_mode(handle, mode) -> None:

@@ -92,6 +92,27 @@ __device__ __forceinline__ void ce_asc(T& a, T& b) {        // smaller first
     b = hi;
 }
 
+// 64-bit keys: there is no 64-bit min / max instruction, and the two selects above are each
+// rewritten into a max or a min with a compare of its own.  Selecting the swapped pair as one
+// two-element vector keeps a single compare per exchange (four 32-bit selects on its mask).
+typedef uint64_t u64x2_t __attribute__((ext_vector_type(2)));
+
+template <>
+__device__ __forceinline__ void ce_desc<uint64_t>(uint64_t& a, uint64_t& b) {
+    const bool sw = b > a;
+    const u64x2_t v = sw ? (u64x2_t){b, a} : (u64x2_t){a, b};
+    a = v.x;
+    b = v.y;
+}
+
+template <>
+__device__ __forceinline__ void ce_asc<uint64_t>(uint64_t& a, uint64_t& b) {
+    const bool sw = b < a;
+    const u64x2_t v = sw ? (u64x2_t){b, a} : (u64x2_t){a, b};
+    a = v.x;
+    b = v.y;
+}
+
 // Batcher's odd-even merge sort, descending.
 template <int N, typename T>
 __device__ __forceinline__ void sort_desc(T (&v)[N]) {

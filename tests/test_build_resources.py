@@ -14,7 +14,7 @@ from long_context_prefill_anchor_amd import build as B
 # two waves per SIMD; the fp32 workloads are the small 128- and 256-chunk ones).
 SCRATCH_ALLOWED = {"k_routeIfLb0ELb0E": 164, "k_routeIfLb1ELb0E": 164,
                    "k_routeIfLb0ELb1E": 332, "k_routeIfLb1ELb1E": 332,
-                   "k_relayIfLb0": 300, "k_relayIfLb1": 316}
+                   "k_relayIfLb0": 308, "k_relayIfLb1": 324}
 
 
 @pytest.fixture(scope="module")

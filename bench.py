@@ -292,9 +292,9 @@ def scale_sweep_table4(ns=(128, 256, 512, 1024), seeds=3):
 def sentinel_ablation(seeds=5):
     """Sentinel mixes on the pages' ablation setting (1 x 256 chunks, fp32, 24 layers, drift
     0.003, k = 12; anchors every 8 layers, as in the other chains): mean recall against full
-    routing, rerouted fraction and score-pair fraction over the seeds.  The 24-wide near-miss
-    row runs on the one-wave-per-row kernel (k + m = 36); the 48-wide row needs c = 72 ledger
-    entries, past this library's 64, so 40 near-miss + 12 random (c = 64) stands nearest.  The
+    routing, rerouted fraction and score-pair fraction over the seeds.  The 24- and 48-wide
+    near-miss rows run on the one-wave-per-row kernel (k + m = 36 and 60; the 48-wide row keeps
+    c = 72 ledger entries per row).  The
     last mix trades three random sentinels for the mandatory kind (Section 3.1, item 3: one
     sink chunk, two recent chunks); the synthetic walk gives those chunks no special role,
     and a pair count of c per row is an upper bound when one of them is already routed."""
@@ -302,7 +302,7 @@ def sentinel_ablation(seeds=5):
     mixes = [("random only", 0, 12, 0, 0), ("near-miss only", 12, 0, 0, 0),
              ("12 near-miss + 12 random", 12, 12, 0, 0), ("12 near-miss + 8 random", 12, 8, 0, 0),
              ("12 near-miss + 1 sink + 2 recent + 5 random", 12, 5, 1, 2),
-             ("24 near-miss + 12 random", 24, 12, 0, 0), ("40 near-miss + 12 random", 40, 12, 0, 0)]
+             ("24 near-miss + 12 random", 24, 12, 0, 0), ("48 near-miss + 12 random", 48, 12, 0, 0)]
     out = []
     for name, m, r, sink, recent in mixes:
         acc = np.zeros(3)

@@ -85,7 +85,7 @@ typedef struct {
 } rr_config;
 /* c = k + m + sink + recent + r ledger IDs per row.  Limits (RR_EUNSUPPORTED beyond them):
  * d == 64, k + m <= 64 (k + m > 32 only with nk <= 1024), r <= 32, sink + recent <= 32,
- * c <= 64, nk <= 4096, nq <= 65536;
+ * (hence c <= 128), nk <= 4096, nq <= 65536;
  * heads * nq < 2^31 (RR_EINVAL).  A row with fewer allowed chunks than c gets shorter
  * segments, padded with -1. */
 

@@ -94,8 +94,8 @@ rr_status check_cfg(const rr_config* c, bool bucket) {
     if (c->min_reuse < 0) return fail(RR_EINVAL, "min_reuse must be >= 0 (got %d)", c->min_reuse);
     if (!(std::isfinite(c->gamma_extra) && c->gamma_extra >= 0.f))
         return fail(RR_EINVAL, "gamma_extra must be finite and >= 0");
-    if (c->k + c->m + c->sink + c->recent + c->r > 64)
-        return fail(RR_EUNSUPPORTED, "k + m + sink + recent + r must be <= 64 (got %d)",
+    if (c->k + c->m + c->sink + c->recent + c->r > 128)
+        return fail(RR_EUNSUPPORTED, "k + m + sink + recent + r must be <= 128 (got %d)",
                     c->k + c->m + c->sink + c->recent + c->r);
     if (c->nk > 4096) return fail(RR_EUNSUPPORTED, "nk must be <= 4096 (got %d)", c->nk);
     if (c->nq > 65536) return fail(RR_EUNSUPPORTED, "nq must be <= 65536 (got %d)", c->nq);

@@ -431,20 +431,24 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
     uint32_t* bm = reinterpret_cast<uint32_t*>(lds) + (size_t)slot * (W + RLIST);
     int32_t* rlist = reinterpret_cast<int32_t*>(bm + W);
     int32_t* stage = reinterpret_cast<int32_t*>(lds) + (size_t)ROWS * (W + RLIST) + (size_t)slot * (p.c + 1);
-    for (int w = sub; w < W; w += 4) bm[w] = 0u;
-    if (sub < 2) {                                    // lanes 0 / 1 own positions [0,16) / [16,32)
+    // Bitmap of the chunks a draw must avoid (route, near-miss, mandatory, drawn): only rows
+    // with sentinels need it.
+    const int mw = p.sink + p.recent;
+    if (p.r > 0 || mw > 0) {                          // uniform
+        for (int w = sub; w < W; w += 4) bm[w] = 0u;
+        if (sub < 2) {                                // lanes 0 / 1 own positions [0,16) / [16,32)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int pos = 16 * sub + i;
-            const uint32_t j = key_index(hv[i]);
-            if (pos < ki + mi && hv[i] != EMPTY_KEY) atomicOr(&bm[j >> 5], 1u << (j & 31));
+            for (int i = 0; i < 16; ++i) {
+                const int pos = 16 * sub + i;
+                const uint32_t j = key_index(hv[i]);
+                if (pos < ki + mi && hv[i] != EMPTY_KEY) atomicOr(&bm[j >> 5], 1u << (j & 31));
+            }
         }
     }
 
     // Mandatory sentinels (Section 3.1, item 3): the sink chunks [0, sink) and the row's last
     // `recent` allowed chunks, ascending, skipping those already in the route or near-miss
     // set; marked so that the draws avoid them.  One lane walks them (sink + recent <= 32).
-    const int mw = p.sink + p.recent;
     int mand = 0;
     if (mw > 0) {
         if (sub == 0) {
@@ -1118,13 +1122,18 @@ __device__ __forceinline__ int cand_of_lane(int lane) {
 // without an ID count as +inf for the minima and -inf for the max; a route or near-miss slot
 // without one makes the hint -inf.
 //
-// The wave's query rows (sq: RPW rows) and candidate IDs (sid: RPW rows of 32 * NP entries, -1
-// past c) are staged in LDS, read back by this wave only (LDS operations of one wave complete in order), and the
-// key rows of the next DEPTH rows stay in flight while a row is reduced.
-template <typename DT, int NP, int RPW, int DEPTH>
+// The wave's query rows (sq: RPW rows) and candidate IDs (sid: RPW rows of 32 * NP * NCH entries,
+// -1 past c) are staged in LDS, read back by this wave only (LDS operations of one wave complete
+// in order), and the key rows of the next DEPTH rows stay in flight while a row is reduced.
+// Ledgers wider than 64 entries (NCH = 2, with NP = 2) take each row's candidates as two chunks
+// of 64 in turn and fold the two chunks' route, near-miss and sentinel scores per lane before
+// the cross-lane reduction.
+template <typename DT, int NP, int RPW, int DEPTH, int NCH = 1>
 __device__ __forceinline__ void rescore_rows(const RescoreArgs& p, int h, int i0, int nrow, int lane,
                                              unsigned char* sq, int32_t* sid, float& res_alpha, float& res_mu,
                                              float& res_beta, bool& res_bad) {
+    static_assert(NCH == 1 || (NCH == 2 && NP == 2 && DEPTH == 1), "two chunks of 64 candidates");
+    constexpr int SROW = 32 * NP * NCH;                // staged IDs per row
     typedef typename Elem<DT>::type E;
     constexpr uint32_t ROW_BYTES = 64 * sizeof(E);
     static_assert(ROW_BYTES == 128 || ROW_BYTES == 256, "bf16 or fp32 rows");
@@ -1148,9 +1157,9 @@ __device__ __forceinline__ void rescore_rows(const RescoreArgs& p, int h, int i0
             const uint4 v = buf_load16(rQ, rr < nrow ? (uint32_t)qr * ROW_BYTES + 16u * piece : OOB);
             *reinterpret_cast<uint4*>(sq + rr * ROW_BYTES + 16 * piece) = v;
         }
-        // rows padded to 32 NP IDs (-1 past c), so that every later read is unconditional
-        for (int x = lane; x < RPW * 32 * NP; x += 64) {
-            const int rr = x / (32 * NP), c = x % (32 * NP);
+        // rows padded to SROW IDs (-1 past c), so that every later read is unconditional
+        for (int x = lane; x < RPW * SROW; x += 64) {
+            const int rr = x / SROW, c = x % SROW;
             const bool in = rr < nrow && c < p.c;
             const int id = buf_load4(rI, in ? (uint32_t)((i0 + rr) * p.c + c) * 4u : OOB);
             // -1 for padding, rows outside the head and any index outside K.
@@ -1161,20 +1170,19 @@ __device__ __forceinline__ void rescore_rows(const RescoreArgs& p, int h, int i0
     const uint32_t coff = 16u * (lane % LPR);           // this lane's chunk of it
     // Candidate held after the reduce-scatter (pass ps adds 32 ps).
     const int b0 = lane & 1;
-    const int cown = cand_of_lane<LPR, NP>(lane);       // candidate index 0 .. 32 NP - 1
+    const int cown = cand_of_lane<LPR, NP>(lane);       // candidate index 0 .. 32 NP - 1 (chunk 0)
 
     uint4 kv[DEPTH][NI];
-    auto issue = [&](int slot, int rr) {
+    auto issue = [&](int slot, int rr, int ch) {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int id = sid[rr * 32 * NP + RPI * j + grp];
+            const int id = sid[rr * SROW + 32 * NP * ch + RPI * j + grp];
             kv[slot][j] = buf_load16(rK, id >= 0 ? (uint32_t)id * ROW_BYTES + coff : OOB);
         }
     };
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) issue(d, d);
+    for (int d = 0; d < DEPTH; ++d) issue(d, d, 0);
 
-    const bool ownR = cown < p.k, ownSel = cown < p.sel, ownS = cown >= p.k && cown < p.c;
     res_alpha = 0.f;
     res_mu = 0.f;
     res_beta = 0.f;
@@ -1189,23 +1197,38 @@ __device__ __forceinline__ void rescore_rows(const RescoreArgs& p, int h, int i0
             const int slot = rr % DEPTH;
             const int i = i0 + rr;
             const uint4 qv = *reinterpret_cast<const uint4*>(sq + rr * ROW_BYTES + coff);
-            float part[NI];
+            float vr = INFINITY, vsel = INFINITY;
+            B[t] = -INFINITY;
+            bool badc = false;
 #pragma unroll
-            for (int j = 0; j < NI; ++j) part[j] = Dot<DT>::acc(qv, kv[slot][j], 0.f);
-            // Two candidate passes (c > 32), bf16 and fp32 alike: the next row's loads (8 or 16
-            // of them) would stay live through the reduce-scatter and push the kernel past its
-            // register budget (64 VGPRs for bf16 at eight waves per SIMD), so they go out after
-            // it.  The build's resource report and its test check that no k_rescore spills.
-            constexpr bool LATE = NP == 2;
-            if (!LATE && rr + DEPTH < RPW) issue(slot, rr + DEPTH);
-            const float sc = reduce_scatter<LPR, NP>(part, lane);
-            // (the fence keeps the next row's ID reads from being hoisted above the reduce-scatter)
-            if constexpr (LATE) __builtin_amdgcn_sched_barrier(0);
-            if (LATE && rr + DEPTH < RPW) issue(slot, rr + DEPTH);
-            const bool valid = sid[rr * 32 * NP + cown] >= 0;    // -1 also past c
-            const float vr = (ownR && valid) ? sc : INFINITY;
-            const float vsel = (ownSel && valid) ? sc : INFINITY;
-            B[t] = (ownS && valid) ? sc : -INFINITY;
+            for (int ch = 0; ch < NCH; ++ch) {
+                float part[NI];
+#pragma unroll
+                for (int j = 0; j < NI; ++j) part[j] = Dot<DT>::acc(qv, kv[slot][j], 0.f);
+                // Two candidate passes (c > 32), bf16 and fp32 alike: the next loads (8 or 16 of
+                // them) would stay live through the reduce-scatter and push the kernel past its
+                // register budget (64 VGPRs for bf16 at eight waves per SIMD), so they go out
+                // after it.  The build's resource report and its test check that no k_rescore
+                // spills.
+                constexpr bool LATE = NP == 2;
+                if (!LATE && rr + DEPTH < RPW) issue(slot, rr + DEPTH, 0);
+                const float sc = reduce_scatter<LPR, NP>(part, lane);
+                // (the fence keeps the next ID reads from being hoisted above the reduce-scatter)
+                if constexpr (LATE) __builtin_amdgcn_sched_barrier(0);
+                if (LATE) {
+                    if (ch + 1 < NCH) issue(slot, rr, ch + 1);
+                    else if (rr + DEPTH < RPW) issue(slot, rr + DEPTH, 0);
+                }
+                const int cc = cown + 32 * NP * ch;               // this lane's candidate
+                const bool valid = sid[rr * SROW + cc] >= 0;      // -1 also past c
+                const bool cR = cc < p.k, cSel = cc < p.sel, cS = cc >= p.k && cc < p.c;
+                vr = vmin2(vr, (cR && valid) ? sc : INFINITY);
+                vsel = vmin2(vsel, (cSel && valid) ? sc : INFINITY);
+                B[t] = vmax2(B[t], (cS && valid) ? sc : -INFINITY);
+                badc = badc || (cSel && !valid);
+                if (p.cand_scores && i < p.nq && cc < p.c && (NP == 2 || b0 == 0))
+                    p.cand_scores[((size_t)h * p.nq + i) * p.c + cc] = valid ? sc : __builtin_nanf("");
+            }
             if constexpr (NP == 1) {
                 A[t] = b0 ? vsel : vr;                  // lanes L and L ^ 1 hold the same candidate
             } else {
@@ -1214,9 +1237,7 @@ __device__ __forceinline__ void rescore_rows(const RescoreArgs& p, int h, int i0
                 A[t] = vmin2(b0 ? vsel : vr, dpp_f<DPP_XOR1>(b0 ? vr : vsel));
                 B[t] = vmax2(B[t], dpp_f<DPP_XOR1>(B[t]));
             }
-            bad[t] = __ballot(ownSel && !valid) != 0ull;
-            if (p.cand_scores && i < p.nq && cown < p.c && (NP == 2 || b0 == 0))
-                p.cand_scores[((size_t)h * p.nq + i) * p.c + cown] = valid ? sc : __builtin_nanf("");
+            bad[t] = __ballot(badc) != 0ull;
         }
         // Min / max over each parity of lanes, two rows at once: one exchange with lane ^ 2 leaves
         // the first row in lanes with bit 1 clear and the second in the others, then the common
@@ -1288,7 +1309,7 @@ __device__ __forceinline__ bool relay_decide(const RescoreArgs& p, int h, int i,
 
 // Block (h, b): rows 64b..64b+63 of head h; wave w takes rows 4w..4w+3, one at a time.  The
 // block ends by listing its flagged rows (ascending) for the reroute kernel.
-template <typename DT, int NP>
+template <typename DT, int NP, int NCH>
 __global__ __launch_bounds__(RESCORE_THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(typename Elem<DT>::type) == 2 ? 8 : 4)))
 void k_rescore(RescoreArgs p) {
     typedef typename Elem<DT>::type E;
@@ -1297,7 +1318,7 @@ void k_rescore(RescoreArgs p) {
     constexpr int DEPTH = (NP == 1 && LPR == 8) ? 2 : 1;
     __shared__ uint32_t row_flag[ROWS];
     __shared__ __align__(16) unsigned char sq[RS_WAVES][RS_ROWS * ROW_BYTES];
-    __shared__ int32_t sid[RS_WAVES][RS_ROWS * 32 * NP];
+    __shared__ int32_t sid[RS_WAVES][RS_ROWS * 32 * NP * NCH];
     const int G = (p.nq + ROWS - 1) / ROWS;
     const int lb = xcd_block(p.H * G);
     if (lb < 0) return;
@@ -1309,7 +1330,7 @@ void k_rescore(RescoreArgs p) {
     const int nrow = max(0, min(RS_ROWS, p.nq - i0));   // rows of this wave inside the head
     float alpha, mu, beta;
     bool bad;
-    rescore_rows<DT, NP, RS_ROWS, DEPTH>(p, h, i0, nrow, lane, sq[wave], sid[wave], alpha, mu, beta, bad);
+    rescore_rows<DT, NP, RS_ROWS, DEPTH, NCH>(p, h, i0, nrow, lane, sq[wave], sid[wave], alpha, mu, beta, bad);
     if (lane < RS_ROWS) {
         const bool f = relay_decide(p, h, i0 + lane, alpha, mu, beta, bad, true);
         row_flag[wave * RS_ROWS + lane] = f ? 1u : 0u;
@@ -1466,12 +1487,16 @@ void k_relay(RescoreArgs s, RouteArgs p) {
         const __amdgpu_buffer_rsrc_t rQ = make_rsrc(reinterpret_cast<const char*>(s.qp) + (size_t)h * s.nq_q * ROW_BYTES,
                                                     (uint32_t)s.nq_q * ROW_BYTES);
         const __amdgpu_buffer_rsrc_t rI = make_rsrc(s.ids + (size_t)h * s.nq * s.c, (uint32_t)(s.nq * s.c * 4));
-        // every load goes out before the first LDS write: keys, IDs, query chunks
-        uint4 kreg[KPIECES];
+        // The keys go straight from memory to LDS (buffer loads with an LDS destination, 1 KB per
+        // wave and instruction; bytes past the head's keys read as zeros), beside the IDs and the
+        // query chunks, which go through registers.
 #pragma unroll
         for (int x = 0; x < KPIECES; ++x) {
-            const uint32_t off = 16u * (uint32_t)(tid + x * ROWS * RELAY_WAVES);
-            kreg[x] = buf_load16(rK, off < kbytes ? off : OOB);
+            const uint32_t chunk = (uint32_t)(wave * KPIECES + x) * 1024u;
+            if (chunk < kbytes)                         // uniform
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rK, (__attribute__((address_space(3))) void*)(kl + chunk), 16,
+                    (int)(chunk + 16u * (uint32_t)lane), 0, 0, 0);
         }
         int idv[RELAY_RPW * 32 / 64];                   // rows padded to 32 IDs
 #pragma unroll
@@ -1487,16 +1512,12 @@ void k_relay(RescoreArgs s, RouteArgs p) {
             qv[rr] = buf_load16(rQ, rr < nrow ? (uint32_t)qr * ROW_BYTES + coff : OOB);
         }
 #pragma unroll
-        for (int x = 0; x < KPIECES; ++x) {
-            const uint32_t off = 16u * (uint32_t)(tid + x * ROWS * RELAY_WAVES);
-            if (off < kbytes) *reinterpret_cast<uint4*>(kl + off) = kreg[x];
-        }
-#pragma unroll
         for (int u = 0; u < RELAY_RPW * 32 / 64; ++u) {
             const int x = lane + 64 * u, rr = x / 32, c = x % 32;
             // -1 for padding (also past c), rows outside the head and any index outside K
             sid[x] = (rr < nrow && c < s.c && (unsigned)idv[u] < (unsigned)s.nk) ? idv[u] : -1;
         }
+        __builtin_amdgcn_s_waitcnt(0);                  // this wave's key chunks have landed
         __syncthreads();                                // the keys are in LDS
         float alpha, mu, beta;
         bool bad;
@@ -1649,13 +1670,17 @@ hipError_t launch_compact_out(const int32_t* bcount, const int32_t* blist, int H
 
 hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st) {
     const dim3 grid(xcd_grid(a.H * ((a.nq + ROWS - 1) / ROWS)));
-    const bool two = a.c > 32;                        // candidate passes of 32
+    // candidate passes of 32: one (c <= 32), two (c <= 64), or two chunks of two (c <= 128)
+    const int passes = (a.c + 31) / 32;
+    if (passes > 4) return hipErrorInvalidValue;
     if (bf16) {
-        if (two) hipLaunchKernelGGL((k_rescore<bf16_t, 2>), grid, dim3(RESCORE_THREADS), 0, st, a);
-        else hipLaunchKernelGGL((k_rescore<bf16_t, 1>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        if (passes > 2) hipLaunchKernelGGL((k_rescore<bf16_t, 2, 2>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        else if (passes == 2) hipLaunchKernelGGL((k_rescore<bf16_t, 2, 1>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        else hipLaunchKernelGGL((k_rescore<bf16_t, 1, 1>), grid, dim3(RESCORE_THREADS), 0, st, a);
     } else {
-        if (two) hipLaunchKernelGGL((k_rescore<float, 2>), grid, dim3(RESCORE_THREADS), 0, st, a);
-        else hipLaunchKernelGGL((k_rescore<float, 1>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        if (passes > 2) hipLaunchKernelGGL((k_rescore<float, 2, 2>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        else if (passes == 2) hipLaunchKernelGGL((k_rescore<float, 2, 1>), grid, dim3(RESCORE_THREADS), 0, st, a);
+        else hipLaunchKernelGGL((k_rescore<float, 1, 1>), grid, dim3(RESCORE_THREADS), 0, st, a);
     }
     return hipGetLastError();
 }

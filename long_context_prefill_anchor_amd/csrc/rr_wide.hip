@@ -47,7 +47,7 @@ struct WideShared {
     uint32_t s[WR][SST];               // orderable scores of the block's rows; 0 = no key
     uint64_t list[WWAVES][2][64];      // candidate keys of a wave's two rows; then random draws (u32)
     uint32_t bm[WWAVES][WBM];          // chunks already in the row's ledger
-    int32_t stage[WWAVES][65];         // the row's ledger entries before the copy out
+    int32_t stage[WWAVES][129];        // the row's ledger entries (c <= 128) before the copy out
 };
 
 // The value of lane (lane ^ J), all in the VALU: quad permutes for J = 1, 2; a row shift each

@@ -47,6 +47,9 @@ def test_config_check_accepts_every_named_workload():
     assert rr.rr_config_check(cfg(m=0, r=0)) == rr.RR_OK
     # mandatory sentinels up to c = 64
     assert rr.rr_config_check(cfg(k=12, m=12, r=24, sink=8, recent=8)) == rr.RR_OK
+    # Table 3's widest mix (48 near-miss + 12 random, c = 72) and the widest ledger (c = 128)
+    assert rr.rr_config_check(cfg(k=12, m=48, r=12)) == rr.RR_OK
+    assert rr.rr_config_check(cfg(k=32, m=32, r=32, sink=16, recent=16)) == rr.RR_OK
 
 
 def test_config_struct_layout_matches_the_header(tmp_path):
@@ -93,7 +96,6 @@ def test_config_struct_layout_matches_the_header(tmp_path):
     (dict(sink=-1), rr.RR_EINVAL, "sink >= 0"),
     (dict(recent=-2), rr.RR_EINVAL, "recent >= 0"),
     (dict(sink=20, recent=13), rr.RR_EUNSUPPORTED, "sink + recent"),
-    (dict(k=16, m=16, r=32, sink=1), rr.RR_EUNSUPPORTED, "<= 64"),
     (dict(min_reuse=-1), rr.RR_EINVAL, "min_reuse"),
     (dict(gamma_extra=-0.1), rr.RR_EINVAL, "gamma_extra"),
     (dict(gamma_extra=float("inf")), rr.RR_EINVAL, "gamma_extra"),

@@ -121,6 +121,8 @@ MAND_RELAY_CASES = [
     ("relay_mand_int", 2, 128, 160, 12, 12, 4, 1, 3, "f32", False, 0.0, "int"),
     ("relay_mand_c64", 1, 96, 512, 12, 12, 24, 8, 8, "bf16", False, 0.05, "gauss"),
     ("relay_mand_only", 1, 70, 50, 4, 0, 0, 2, 2, "f32", False, 0.1, "gauss"),
+    # 32-entry lists with a ledger past 64 IDs (c = 80): main kernels, two-chunk rescore
+    ("relay_mand_c80", 1, 96, 300, 12, 20, 32, 8, 8, "bf16", False, 0.05, "gauss"),
 ]
 RELAY_CASES_ALL = ([c[:7] + (0, 0) + c[7:] for c in RELAY_CASES] + MAND_RELAY_CASES)
 
@@ -312,6 +314,9 @@ WIDE_ANCHOR_CASES = [
     ("wide_km64", 1, 80, 200, 16, 48, 0, 0, 0, "bf16", False, 37, "gauss"),     # c = k + m = 64
     ("wide_route40", 1, 72, 160, 40, 0, 8, 0, 0, "f32", False, 38, "gauss"),    # wide route, no near-miss
     ("wide_km64_ties", 1, 64, 96, 16, 48, 0, 0, 0, "f32", False, 39, "int"),
+    # ledgers past 64 IDs: Table 3's 48 near-miss + 12 random (c = 72) and the widest (c = 128)
+    ("wide_nm48_r12_bf16", 2, 96, 256, 12, 48, 12, 0, 0, "bf16", False, 40, "gauss"),
+    ("wide_c128_f32", 1, 70, 200, 32, 32, 32, 16, 16, "f32", False, 41, "gauss"),
 ]
 
 
@@ -337,6 +342,10 @@ def test_anchor_parity_wide(case):
 WIDE_RELAY_CASES = [
     ("wide_relay_f32", 2, 128, 256, 12, 24, 12, 0, 0, "f32", False, 0.05, "gauss"),
     ("wide_relay_causal", 1, 160, 160, 12, 36, 8, 1, 2, "bf16", True, 0.04, "gauss"),
+    # c > 64: the rescore takes each row's candidates as two chunks of 64
+    ("wide_relay_nm48_r12_bf16", 2, 128, 256, 12, 48, 12, 0, 0, "bf16", False, 0.05, "gauss"),
+    ("wide_relay_c128_f32", 1, 96, 160, 32, 32, 32, 16, 16, "f32", False, 0.05, "gauss"),
+    ("wide_relay_nm48_causal", 1, 150, 150, 12, 48, 12, 0, 0, "bf16", True, 0.04, "gauss"),
     ("wide_relay_int", 1, 128, 200, 12, 24, 12, 0, 0, "f32", False, 0.0, "int"),
     ("wide_relay_route40", 1, 96, 300, 40, 8, 8, 0, 0, "bf16", False, 0.05, "gauss"),
 ]

@@ -350,3 +350,30 @@ def test_relay_layer_rows_equals_relay_layer_on_those_rows(drift_chain):
     rest = np.setdiff1d(np.arange(cfg.nq), idx)
     np.testing.assert_array_equal(part.ledger.route[0, rest], rec.ledger_in.route[0, rest])
     assert part.flags[0, rest].sum() == 0
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_wide_ledger_c72_brute_force(seed):
+    """Table 3's widest mix (48 near-miss + 12 random with k = 12: c = 72 IDs per row) on
+    integer inputs: the route is the exact top-12 and the near-miss set the next 48 under
+    (score desc, index asc) computed with Python integers, segments are ascending, the random
+    sentinels are 12 distinct chunks outside both sets, and the relay flags match Eq. 6-8
+    evaluated the same way."""
+    cfg = O.RouteConfig(heads=2, nq=12, nk=100, d=6, k=12, m=48, r=12, seed=seed)
+    q, k = synth.integer_inputs(2, 100, 6, seed=seed)
+    q = q[:, :12]
+    led = O.anchor_layer(cfg, q, k, 0)
+    assert led.route.shape == (2, 12, 12) and led.sent.shape == (2, 12, 60)
+    for h in range(2):
+        for i in range(12):
+            s = [sum(int(a) * int(b) for a, b in zip(q[h, i], k[h, j])) for j in range(100)]
+            order = sorted(range(100), key=lambda j: (-s[j], j))
+            route, nm, rnd = led.route[h, i], led.sent[h, i, :48], led.sent[h, i, 48:]
+            assert route.tolist() == sorted(order[:12])
+            assert nm.tolist() == sorted(order[12:60])
+            assert rnd.tolist() == sorted(rnd.tolist()) and len(set(rnd.tolist())) == 12
+            assert not set(rnd.tolist()) & set(order[:60])
+    q2, k2 = synth.integer_inputs(2, 100, 6, seed=seed + 100)
+    q2 = q2[:, :12]
+    res = O.relay_layer(cfg, q2, k2, 1, led)
+    np.testing.assert_array_equal(res.flags, brute_relay_flags(q2, k2, led, 0))

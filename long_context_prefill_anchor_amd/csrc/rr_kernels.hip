@@ -113,7 +113,10 @@ template <> struct Tile<bf16_t> {
 
 template <> struct Tile<float> {
     typedef float KReg[32];
-    static constexpr int NBUF = 2;        // 32-register tiles: one tile ahead
+    // 32-register tiles: one buffer (the load of the next tile follows the tile's MMA).  A
+    // second buffer made every fp32 route kernel spill 164-332 bytes per lane to scratch; fp32
+    // inputs serve the small one-head configurations, which are latency-bound either way.
+    static constexpr int NBUF = 1;
     float q[2][32];                       // k-step s: d = 32(L/32) + s
     __device__ __forceinline__ void load_q(const float* Q, int row0, int row1, int lane) {
         const int sub = lane >> 5;

@@ -37,8 +37,20 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 KERNEL_SRCS = tuple(os.path.join(ROOT, "long_context_prefill_anchor_amd", "csrc", f)
                     for f in ("rr_kernels.hip", "rr_device.h", "rr_internal.h"))
 BUILD_SCRIPT = os.path.join(ROOT, "long_context_prefill_anchor_amd", "build.py")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_route_reroute_batched_heads.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_batched_heads.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_batched_heads.txt")
 CALIB_BYTES = 256 << 20         # plain copy used to calibrate the HBM byte counters
+# MI355X: 32 shader engines of 8 compute units, 4 SIMDs each; the SQ busy counter is per engine.
+SIMDS_PER_SE = 32
+L2_REQUEST_BYTES = 128          # one L1 -> L2 read request moves a 128-byte line
+# Kernel symbols (as the profiler names them) -> keys of the profile summaries and the bench line,
+# with the mangled name the build's resource report uses.
+PROFILE_KERNELS = {"k_relay<rr::bf16_t, false>": "relay", "k_route<rr::bf16_t, false, false>": "route",
+                   "k_route<rr::bf16_t, false, true>": "reroute", "k_rescore<rr::bf16_t, 1, 1>": "rescore",
+                   "k_compact_out": "list"}
+PROFILE_SYMBOLS = {"relay": "k_relayINS_6bf16_tELb0E", "route": "k_routeINS_6bf16_tELb0ELb0E",
+                   "reroute": "k_routeINS_6bf16_tELb0ELb1E", "rescore": "k_rescoreINS_6bf16_tELi1ELi1E",
+                   "list": "k_compact_out"}
 
 
 def log(msg):
@@ -572,21 +584,150 @@ def kernel_build_hash():
     return h.hexdigest()
 
 
-def recorded_traffic(kernel):
-    """HBM bytes per launch of `kernel` (reroute / rescore / route) from the committed counter
-    summary, if it was taken on the kernel source and build script as they are now (else None)."""
+def _summary_fields(path):
+    """key: value lines of a committed profile summary, or None when it is missing or was taken
+    on another kernel source or build script than the current one."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     fields = dict(line.split(":", 1) for line in text.splitlines() if ":" in line and not line.startswith("#"))
     fields = {k.strip(): v.strip() for k, v in fields.items()}
-    if fields.get("kernel_build_sha256") != kernel_build_hash():
-        return None
+    return fields if fields.get("kernel_build_sha256") == kernel_build_hash() else None
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` (relay / route / rescore / reroute) from the committed
+    counter summary, if it was taken on the kernel source and build script as they are now (else
+    None)."""
+    fields = _summary_fields(TRAFFIC_FILE)
     try:
-        return float(fields[f"{kernel}_hbm_bytes_per_launch"])
+        return float(fields[f"{kernel}_hbm_bytes_per_launch"]) if fields else None
     except (KeyError, ValueError):
         return None
+
+
+def recorded_counters(kernel):
+    """Measured utilisation of `kernel` from the committed counter summary (same validity rule
+    as recorded_traffic): VALU and MFMA busy fractions of the SIMD cycles, LDS bank-conflict
+    share of LDS cycles, L1 -> L2 read bytes per launch."""
+    fields = _summary_fields(COUNTERS_FILE)
+    if not fields:
+        return None
+    out = {}
+    for name in ("valu_busy", "mfma_busy", "lds_bank_conflict_frac", "l2_read_bytes_per_launch",
+                 "valu_insts_per_wave", "vgprs"):
+        try:
+            out[name] = float(fields[f"{kernel}_{name}"])
+        except (KeyError, ValueError):
+            pass
+    return out or None
+
+
+def _pmc_medians(csv_path):
+    """{profile key: {counter: median over the run's dispatches}} from one rocprofv3 counter
+    collection file.  "calib_copy": the largest value any device copy dispatch shows for each
+    counter (the run's one 256 MiB copy, bench.py --calib-copy, is its largest copy)."""
+    import csv
+    vals, calib = {}, {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            value = float(row["Counter_Value"])
+            if "copyBuffer" in name and "Rect" not in name:
+                calib[row["Counter_Name"]] = max(calib.get(row["Counter_Name"], 0.0), value)
+                continue
+            key = next((v for k, v in PROFILE_KERNELS.items() if k in name), None)
+            if key is None:
+                continue
+            vals.setdefault(key, {}).setdefault(row["Counter_Name"], []).append(value)
+    out = {k: {c: float(np.median(v)) for c, v in d.items()} for k, d in vals.items()}
+    if calib:
+        out["calib_copy"] = calib
+    return out
+
+
+def summarize_profiles(out_dir, cmd_line):
+    """Write profiles/traffic_batched_heads.txt and profiles/counters_batched_heads.txt from the
+    counter runs under `out_dir` (rocprofv3 --pmc, one pass per run, each under
+    <out_dir>/<schedule>_<pass>/, schedules auto and compacted, passes util, mem, fetch, write;
+    see the command lines written into the files)."""
+    import glob
+    runs = {}
+    for f in sorted(glob.glob(os.path.join(out_dir, "*", "*counter_collection.csv"))):
+        tag = os.path.basename(os.path.dirname(f))
+        runs[tag] = _pmc_medians(f)
+    med = {}
+    for tag, per_kernel in runs.items():
+        for key, cs in per_kernel.items():
+            med.setdefault(key, {}).update(cs)
+    h = kernel_build_hash()
+    try:
+        import json
+        from long_context_prefill_anchor_amd import build as B
+        resources = json.load(open(B.RESOURCES))
+    except (OSError, ValueError):
+        resources = {}
+    calib = med.get("calib_copy", {})
+    fetch_scale = (CALIB_BYTES / 1024) / calib["FETCH_SIZE"] if calib.get("FETCH_SIZE") else None
+    write_scale = (CALIB_BYTES / 1024) / calib["WRITE_SIZE"] if calib.get("WRITE_SIZE") else None
+    head = [f"# Command (rocprofv3 under {cmd_line.split()[0]}): one run per counter pass and relay schedule,",
+            f"#   {cmd_line}",
+            "# Values are medians over every dispatch of the kernel in the run; valid only for the kernel",
+            "# source and build script with the hash below (sha256 of rr_kernels.hip, rr_device.h and",
+            "# rr_internal.h, followed by build.py).",
+            f"kernel_build_sha256: {h}"]
+    t = ["# HBM traffic per launch, batched-heads workload (32 heads x 1024 chunks, d = 64, bf16).",
+         f"# Calibration: one plain {CALIB_BYTES >> 20} MiB device copy (bench.py --calib-copy) reads and",
+         "# writes that many bytes; its FETCH_SIZE / WRITE_SIZE (KiB as counted) give the scales that",
+         "# turn counted KiB into bytes moved."] + head
+    t.append(f"fetch_scale: {fetch_scale:.4f}" if fetch_scale else "fetch_scale: none")
+    t.append(f"write_scale: {write_scale:.4f}" if write_scale else "write_scale: none")
+    c = ["# Utilisation per kernel, batched-heads workload (32 heads x 1024 chunks, d = 64, bf16).",
+         "# valu_busy  = SQ_ACTIVE_INST_VALU * 4 / (SQ_BUSY_CYCLES * 32): VALU issue cycles over SIMD",
+         "#              cycles (the active-instruction counter is in quad-cycles summed over waves, the",
+         "#              busy counter is per shader engine of 32 SIMDs);",
+         "# mfma_busy  = SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CYCLES * 32);",
+         "# lds_bank_conflict_frac = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS;",
+         "# l2_read_bytes_per_launch = TCP_TCC_READ_REQ_sum * 128 (L1 -> L2 read requests of one line);",
+         "# vgprs, scratch and occupancy from the build's resource report (librr.resources.json);",
+         "# wait_frac = SQ_WAIT_ANY / SQ_WAVE_CYCLES (wave time spent waiting on memory, LDS or barriers)."] + head
+    for key in ("relay", "route", "rescore", "reroute", "list"):
+        cs = med.get(key)
+        if not cs:
+            continue
+        if fetch_scale and "FETCH_SIZE" in cs and write_scale and "WRITE_SIZE" in cs:
+            rd, wr = cs["FETCH_SIZE"] * 1024 * fetch_scale, cs["WRITE_SIZE"] * 1024 * write_scale
+            t += [f"{key}_fetch_kib_counted: {cs['FETCH_SIZE']:.1f}", f"{key}_write_kib_counted: {cs['WRITE_SIZE']:.1f}",
+                  f"{key}_hbm_read_bytes_per_launch: {rd:.0f}", f"{key}_hbm_write_bytes_per_launch: {wr:.0f}",
+                  f"{key}_hbm_bytes_per_launch: {rd + wr:.0f}"]
+        busy = cs.get("SQ_BUSY_CYCLES")
+        if busy:
+            c.append(f"{key}_valu_busy: {cs['SQ_ACTIVE_INST_VALU'] * 4 / (busy * SIMDS_PER_SE):.4f}")
+            c.append(f"{key}_mfma_busy: {cs['SQ_VALU_MFMA_BUSY_CYCLES'] / (busy * SIMDS_PER_SE):.4f}")
+        if cs.get("SQ_WAVES"):
+            c.append(f"{key}_valu_insts_per_wave: {cs['SQ_INSTS_VALU'] / cs['SQ_WAVES']:.0f}")
+            if cs.get("SQ_INSTS_LDS") is not None:
+                c.append(f"{key}_lds_insts_per_wave: {cs['SQ_INSTS_LDS'] / cs['SQ_WAVES']:.0f}")
+        if cs.get("SQ_ACTIVE_INST_LDS"):
+            c.append(f"{key}_lds_bank_conflict_frac: {cs['SQ_LDS_BANK_CONFLICT'] / cs['SQ_ACTIVE_INST_LDS']:.4f}")
+        if cs.get("TCP_TCC_READ_REQ_sum") is not None:
+            c.append(f"{key}_l2_read_bytes_per_launch: {cs['TCP_TCC_READ_REQ_sum'] * L2_REQUEST_BYTES:.0f}")
+        if cs.get("SQ_WAVE_CYCLES") and cs.get("SQ_WAIT_ANY") is not None:
+            c.append(f"{key}_wait_frac: {cs['SQ_WAIT_ANY'] / cs['SQ_WAVE_CYCLES']:.4f}")
+        res = next((u for sym, u in resources.items() if PROFILE_SYMBOLS[key] in sym), None)
+        if res:
+            c.append(f"{key}_vgprs: {res.get('VGPRs')}")
+            c.append(f"{key}_scratch_bytes_per_lane: {res.get('ScratchSize [bytes/lane]')}")
+            c.append(f"{key}_occupancy_waves_per_simd: {res.get('Occupancy [waves/SIMD]')}")
+        for name in sorted(cs):
+            c.append(f"{key}.{name}: {cs[name]:.1f}")
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(t) + "\n")
+    with open(COUNTERS_FILE, "w") as f:
+        f.write("\n".join(c) + "\n")
+    print(TRAFFIC_FILE)
+    print(COUNTERS_FILE)
 
 
 def calib_copy():
@@ -620,9 +761,17 @@ def main():
                     help="skip the side measurements (64-head 4096-chunk causal; fixed-drift sweep; sentinel ablation)")
     ap.add_argument("--only-attention", action="store_true",
                     help="measure only the sparse attention over routed chunks and print its JSON")
+    ap.add_argument("--relay-mode", default="auto", choices=list(rr.RELAY_MODES),
+                    help="relay schedule of the headline chain (include/rr.h, rr_ledger_set_relay_mode)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ counter summaries from rocprofv3 --pmc runs under DIR and exit")
+    ap.add_argument("--profile-command", default="", help="command line recorded in the summaries")
     ap.add_argument("--calib-copy", action="store_true",
                     help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (counter calibration)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.profile_command or "rocprofv3 --pmc <counters> -- python3 bench.py")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); heads shard across GPUs "
               "with no exchange, so run one process per GPU on its own heads.", file=sys.stderr)
@@ -650,6 +799,7 @@ def main():
     log(f"[bench] generating + uploading {w.layers} layers of {H}x{n}x{d} bf16 Q and K")
     qs, ks = upload_layers(w)
     led = rr.Ledger(H, n, n, d, w.k, w.m, w.r, w.gamma, w.causal, w.dtype, w.seed)
+    led.set_relay_mode(args.relay_mode)
     full = rr.Ledger(H, n, n, d, w.k, 0, 0, w.gamma, w.causal, w.dtype, w.seed)
 
     log("[bench] quality pass (recall, reroute fraction, pair fraction)")
@@ -727,6 +877,11 @@ def main():
         "full_routing": mfma_line("k_route<bf16, full> (k=12, m=r=0)", full_flops, t_full, n_full),
         "anchor": mfma_line("k_route<bf16, full> (k=12, m=12, r=8)", full_flops, t_anc, n_anc),
     }
+    # Measured utilisation beside the roofline fractions (committed counter summary; the route
+    # kernel's figures are medians over its full-routing and anchor launches, 32 of them full
+    # routing for every 4 anchors).
+    kernels["full_routing"]["counters"] = recorded_counters("route")
+    kernels["full_routing"]["traffic"] = recorded_traffic("route")
     roofline = None
     if n_rel:
         # fused relay layer: the rescoring of every row plus the full scoring of the flagged rows
@@ -736,6 +891,7 @@ def main():
         rel["rescore_bytes"] = {"bytes": rescore_bytes, "achieved": round(ach_b, 1), "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": round(ach_b / HBM_PEAK_GBS, 4)}
         rel["traffic"] = recorded_traffic("relay")
+        rel["counters"] = recorded_counters("relay")
         kernels["relay"] = rel
         roofline = dict(rel)
     if n_resc:
@@ -743,10 +899,17 @@ def main():
         kernels["rescore"] = {"kernel": "k_rescore<bf16, 1>", "bound": "hbm", "achieved": round(ach_resc, 1),
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach_resc / HBM_PEAK_GBS, 4),
                               "per_launch": {"bytes": rescore_bytes, "avg_us": round(t_resc, 2), "launches": n_resc},
-                              "traffic": recorded_traffic("rescore")}
+                              "traffic": recorded_traffic("rescore"), "counters": recorded_counters("rescore")}
+        ctr = kernels["rescore"]["counters"]
+        if ctr and "l2_read_bytes_per_launch" in ctr:
+            # the gathers' L1 -> L2 bytes beside the algorithmic HBM bytes
+            ach_l2 = ctr["l2_read_bytes_per_launch"] / (t_resc * 1e-6) / 1e9
+            kernels["rescore"]["l2_read"] = {"bytes": ctr["l2_read_bytes_per_launch"], "achieved": round(ach_l2, 1),
+                                             "unit": "GB/s"}
     if n_rer:
         rer = mfma_line("k_route<bf16, reroute> (flagged rows)", reroute_flops, t_rer, n_rer)
         rer["traffic"] = recorded_traffic("reroute")
+        rer["counters"] = recorded_counters("reroute")
         kernels["reroute"] = rer
         if roofline is None:
             roofline = dict(rer)
@@ -828,7 +991,7 @@ def main():
         "config": {"workload": "batched_heads", "heads": H, "nq": n, "nk": n, "d": d,
                    "layers": L, "anchors": list(w.anchors), "k": w.k, "m": w.m, "r": w.r,
                    "gamma": w.gamma, "causal": w.causal, "drift": "sigma_l ~ U[0.01, 0.06), relative",
-                   "parallelism": "single GPU"},
+                   "relay_schedule": args.relay_mode, "parallelism": "single GPU"},
         "speedup_vs_full": round(float(speedup), 4),
         "recall": round(q["recall"], 6),
         "reroute_fraction": round(q["reroute_fraction"], 4),

@@ -168,12 +168,13 @@ rr_status rr_relay_layer_noalloc(const rr_config* cfg, int32_t* ids, int32_t* an
  *                       flagged rows into its first row slots (the compaction of Sections
  *                       4.1-4.2, within the block) and routes only those in full, as two 64-row
  *                       slices.  Needs k + m <= 32, c <= 32 and nk * d * (2 for bf16, 4 for fp32)
- *                       <= 128 KiB (nk <= 1024 in bf16).  Latency-bound layers take this path.
+ *                       <= 128 KiB (nk <= 1024 in bf16).  Layers that fill the GPU with
+ *                       latency-bound blocks take this path.
  *   RR_RELAY_COMPACTED  the two kernels of Section 4.2: rescoring of every row, then a reroute
  *                       grid over the layer's compacted flagged rows, 64 per block, so that the
  *                       reroute's work scales with the flagged fraction.  Large layers.
- *   RR_RELAY_AUTO       (default) fused when it fits and heads * ceil(nq / 128) <= 512, else
- *                       compacted.
+ *   RR_RELAY_AUTO       (default) fused when it fits and 128 <= heads * ceil(nq / 128) <= 512,
+ *                       else compacted.
  * Errors: RR_EINVAL for a NULL ledger or an unknown mode; RR_EUNSUPPORTED for RR_RELAY_FUSED
  * outside its limits. */
 typedef enum { RR_RELAY_AUTO = 0, RR_RELAY_FUSED = 1, RR_RELAY_COMPACTED = 2 } rr_relay_mode;

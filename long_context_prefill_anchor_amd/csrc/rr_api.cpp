@@ -162,9 +162,14 @@ void release_events(rr_ledger* L) {
     L->spare.clear();
 }
 
-// Fused relay layers serve layers of up to this many 128-row blocks (two per compute unit):
-// there the fixed latency of a reroute block, not its work, sets the time, and one launch per
-// layer that rescores from LDS and skips the threshold pass beats the two-kernel schedule.
+// Fused relay layers serve layers of FUSED_MIN_BLOCKS .. FUSED_MAX_BLOCKS 128-row blocks (half
+// to two of them per compute unit): there the fixed latency of a reroute block, not its work,
+// sets the time, and one launch per layer that rescores from LDS beats the two-kernel schedule.
+// Smaller layers leave most of the GPU idle, and a fused block's serial rescore-then-reroute
+// chain is longer than the two short launches of the compacted schedule (measured: one head of
+// 128-1024 chunks, 2-7 us per layer in favour of the compacted schedule; 32 heads x 1024 chunks,
+// 2 us in favour of the fused one).
+constexpr long long FUSED_MIN_BLOCKS = 128;
 constexpr long long FUSED_MAX_BLOCKS = 512;
 
 // Non-owning view of a ledger's device state and of the working memory a relay layer's kernels
@@ -196,7 +201,8 @@ bool fused_fits(const LedgerView& v) {
 bool use_fused(const LedgerView& v) {
     if (!fused_fits(v)) return false;
     if (v.relay_mode != RR_RELAY_AUTO) return v.relay_mode == RR_RELAY_FUSED;
-    return (long long)v.cfg.heads * ((v.cfg.nq + 127) / 128) <= FUSED_MAX_BLOCKS;
+    const long long blocks = (long long)v.cfg.heads * ((v.cfg.nq + 127) / 128);
+    return blocks >= FUSED_MIN_BLOCKS && blocks <= FUSED_MAX_BLOCKS;
 }
 
 rr::RouteArgs route_args(const LedgerView& v, const void* q, const void* k, int layer) {

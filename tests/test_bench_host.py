@@ -49,3 +49,42 @@ def test_traffic_record_needs_the_sources_it_was_taken_on(tmp_path, monkeypatch)
     assert bench.kernel_build_hash() != good
     assert bench.recorded_traffic("reroute") is None
     assert any(p.endswith("rr_device.h") for p in bench.KERNEL_SRCS)
+
+
+def test_profile_summaries_round_trip(tmp_path, monkeypatch):
+    """summarize_profiles turns rocprofv3 counter files into the committed summaries, and the
+    bench reads them back only while the kernel source hash matches."""
+    cols = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+            "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+            "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+    def write(tag, rows):
+        d = tmp_path / "runs" / tag
+        d.mkdir(parents=True)
+        lines = [",".join(cols)]
+        for kname, grid, counter, value in rows:
+            lines.append(",".join(["1", "1", "Agent 1", "1", "1", "1", str(grid), "1", f'"{kname}"', "512", "0", "0",
+                                   "254", "0", "100", counter, str(value), "0", "1"]))
+        (d / "pmc_counter_collection.csv").write_text("\n".join(lines) + "\n")
+
+    relay = "void rr::k_relay<rr::bf16_t, false>(rr::RescoreArgs, rr::RouteArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    write("auto_util", [(relay, 131072, "SQ_ACTIVE_INST_VALU", 1000.0), (relay, 131072, "SQ_BUSY_CYCLES", 100.0),
+                        (relay, 131072, "SQ_VALU_MFMA_BUSY_CYCLES", 320.0), (relay, 131072, "SQ_WAVES", 10.0),
+                        (relay, 131072, "SQ_INSTS_VALU", 900.0)])
+    write("auto_fetch", [(relay, 131072, "FETCH_SIZE", 4.0), (copy, 512, "FETCH_SIZE", 100.0),
+                         (copy, 131072, "FETCH_SIZE", (bench.CALIB_BYTES >> 10) / 2)])
+    write("auto_write", [(relay, 131072, "WRITE_SIZE", 2.0), (copy, 131072, "WRITE_SIZE", bench.CALIB_BYTES >> 10)])
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.txt"))
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(tmp_path / "counters.txt"))
+    bench.summarize_profiles(str(tmp_path / "runs"), "rocprofv3 --pmc X -- python3 bench.py")
+    # fetch counted at half the copy's bytes: scale 2; write scale 1
+    assert bench.recorded_traffic("relay") == 4.0 * 1024 * 2 + 2.0 * 1024
+    ctr = bench.recorded_counters("relay")
+    assert abs(ctr["valu_busy"] - 1000.0 * 4 / (100.0 * 32)) < 1e-4
+    assert abs(ctr["mfma_busy"] - 320.0 / (100.0 * 32)) < 1e-4
+    assert ctr["valu_insts_per_wave"] == 90.0
+    # a summary taken on other kernel sources is ignored
+    text = (tmp_path / "traffic.txt").read_text().replace(bench.kernel_build_hash(), "0" * 64)
+    (tmp_path / "traffic.txt").write_text(text)
+    assert bench.recorded_traffic("relay") is None

@@ -21,6 +21,10 @@ LIB = os.path.join(PKG, "librr.so")
 # Per-kernel register, scratch, LDS and occupancy figures of the last build (the compiler's
 # kernel-resource-usage remarks), written beside the library.
 RESOURCES = os.path.join(PKG, "librr.resources.json")
+# Measurement build: the same sources with phase timestamps compiled in (RR_PHASE_TRACE), for
+# bench.py --phase-trace; never loaded by the library's users or tests.
+PHASE_LIB = os.path.join(PKG, "librr_phase.so")
+PHASE_RESOURCES = os.path.join(PKG, "librr_phase.resources.json")
 SOURCES = ["rr_api.cpp", "rr_kernels.hip", "rr_attention.hip", "rr_wide.hip"]
 ARCH = os.environ.get("RR_OFFLOAD_ARCH", "gfx950")
 
@@ -32,7 +36,8 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, phase_trace: bool = False) -> str:
+    lib, resources = (PHASE_LIB, PHASE_RESOURCES) if phase_trace else (LIB, RESOURCES)
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            # The route kernel runs two waves per SIMD (register-bound) and is latency-bound there;
@@ -44,8 +49,10 @@ def build(verbose: bool = False) -> str:
            # per-kernel VGPRs, scratch (spills), LDS and occupancy, parsed into RESOURCES
            "-Rpass-analysis=kernel-resource-usage",
            f"-I{INCLUDE}", f"-I{CSRC}"]
+    if phase_trace:
+        cmd.append("-DRR_PHASE_TRACE")
     cmd += ["-x", "hip"] + [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd += ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -59,15 +66,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     usage = parse_resource_remarks(remarks)
-    with open(RESOURCES, "w") as f:
+    with open(resources, "w") as f:
         json.dump(usage, f, indent=1, sort_keys=True)
     if verbose:
         for name, u in sorted(usage.items()):
             print(f"  {name}: VGPRs {u.get('VGPRs')} scratch {u.get('ScratchSize [bytes/lane]')} B/lane "
                   f"occupancy {u.get('Occupancy [waves/SIMD]')} waves/SIMD", flush=True)
-    return LIB
+    return lib
 
 
 def parse_resource_remarks(lines):
@@ -89,4 +96,4 @@ def parse_resource_remarks(lines):
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, phase_trace="--phase-trace" in sys.argv[1:]))

@@ -40,6 +40,29 @@
 
 namespace rr {
 
+// Phase timestamps for measurement builds (RR_PHASE_TRACE defined; the library is built
+// without): the first lane of every wave of the first TRACE_BLOCKS blocks of a launch records
+// the 100 MHz real-time counter at fixed points of the route and relay kernels, and counts its
+// mid-stream drains; rr_debug_phase_trace / rr_debug_phase_clear (end of this file) copy the
+// tables out and clear them.  Work and results are unchanged.
+#ifdef RR_PHASE_TRACE
+constexpr int TRACE_BLOCKS = 4096, TRACE_WAVES = 8, TRACE_SLOTS = 16;
+__device__ uint64_t g_phase[TRACE_BLOCKS * TRACE_WAVES * TRACE_SLOTS];
+__device__ uint32_t g_drains[TRACE_BLOCKS * TRACE_WAVES];
+#define RR_STAMP(LB, W, K)                                                                                   \
+    do {                                                                                                     \
+        if ((threadIdx.x & 63) == 0 && (LB) >= 0 && (LB) < TRACE_BLOCKS)                                     \
+            g_phase[((size_t)(LB) * TRACE_WAVES + (W)) * TRACE_SLOTS + (K)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+#define RR_COUNT_DRAIN(LB, W)                                                                                \
+    do {                                                                                                     \
+        if ((threadIdx.x & 63) == 0 && (LB) >= 0 && (LB) < TRACE_BLOCKS) g_drains[(LB) * TRACE_WAVES + (W)] += 1; \
+    } while (0)
+#else
+#define RR_STAMP(LB, W, K) do {} while (0)
+#define RR_COUNT_DRAIN(LB, W) do {} while (0)
+#endif
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int ROWS = 64;           // rows per route block (one per lane)
@@ -426,7 +449,10 @@ constexpr int RLIST = 32;          // per-row list of drawn random sentinels (r 
 // lanes 2 and 3 the drawn chunks by index, each pair with a 16-key network per lane and one
 // bitonic exchange between the two lanes, which leaves every segment in ascending index order.
 __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&hv)[16], int slot, int sub,
-                                           int my_row, int my_qrow, int my_n, int h, unsigned char* lds) {
+                                           int my_row, int my_qrow, int my_n, int h, unsigned char* lds,
+                                           int tlb, int tw) {
+    (void)tlb;
+    (void)tw;
     const int ki = min(p.k, my_n);
     const int mi = min(p.m, my_n - ki);
     const int words = (p.nk + 31) >> 5;
@@ -449,6 +475,7 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
         }
     }
 
+    RR_STAMP(tlb, tw, 13);
     // Mandatory sentinels (Section 3.1, item 3): the sink chunks [0, sink) and the row's last
     // `recent` allowed chunks, ascending, skipping those already in the route or near-miss
     // set; marked so that the draws avoid them.  One lane walks them (sink + recent <= 32).
@@ -555,6 +582,7 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
         }
     }
     taken = dpp_i<DPP_BCAST0>(taken);                 // lane 0 holds the final count
+    RR_STAMP(tlb, tw, 14);
     if (sub == 0) {
         p.anchor[(size_t)h * p.nq + my_row] = p.layer;
         p.refreshed[(size_t)h * p.nq + my_row] = (uint8_t)p.refresh_mark;
@@ -597,6 +625,7 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
                 }
         }
     }
+    RR_STAMP(tlb, tw, 15);
     int tr, tn;
     quad_excl_sum(cr, sub, &tr);
     quad_excl_sum(cn, sub, &tn);
@@ -628,6 +657,7 @@ struct RowCtx {
     uint32_t* my_buf;
     int qslot, qsub, q_row, q_n, q_qrow;
     bool q_redo;
+    int trace_lb, trace_w;      // phase-trace block and wave (measurement builds only)
 };
 
 // Streaming selection pass from the rows' shared thresholds (sh.thr), final merge and ledger
@@ -702,6 +732,7 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
                         cnt += (hi[v] >= ts) ? 1 : 0;
                     }
                     if (__ballot(cnt >= 16)) {
+                        RR_COUNT_DRAIN(cx.trace_lb, cx.trace_w);
                         drain(top, my_buf, cnt, fresh);
                         cnt = 0;
                         const uint64_t own = pick(top, p.sel - 1);
@@ -712,20 +743,26 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
                 }
             }
         }
+        RR_STAMP(cx.trace_lb, cx.trace_w, 5);
         drain(top, my_buf, cnt, fresh);
+        RR_STAMP(cx.trace_lb, cx.trace_w, 6);
 
         // Final merge, one row per quad: wave w takes rows 16w .. 16w+15 and lane 4j + s of it
         // holds wave s's list of row 16w + j.
         uint64_t* xl = reinterpret_cast<uint64_t*>(dyn_lds);            // [SPLIT][XWAVE]: [ROWS][XSTRIDE] + pad
         __syncthreads();                                                // every buffer is drained
+        RR_STAMP(cx.trace_lb, cx.trace_w, 7);
 #pragma unroll
         for (int s = 0; s < TOPW; ++s) xl[wave * XWAVE + lane * XSTRIDE + s] = top[s];
         __syncthreads();
 #pragma unroll
         for (int s = 0; s < TOPW; ++s) top[s] = xl[qsub * XWAVE + qslot * XSTRIDE + s];
+        RR_STAMP(cx.trace_lb, cx.trace_w, 8);
         uint64_t hv[16];
         quad_merge_split(top, hv, qsub);
+        RR_STAMP(cx.trace_lb, cx.trace_w, 9);
         __syncthreads();                                                // xl is free again
+        RR_STAMP(cx.trace_lb, cx.trace_w, 10);
 
         bool emit_now = q_row >= 0;
         if constexpr (REROUTE) {
@@ -745,8 +782,10 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
                 emit_now = emit_now && cx.q_redo;
             }
         }
-        if (emit_now) emit_split(p, hv, qslot, qsub, q_row, q_qrow, q_n, h, dyn_lds);
+        if (emit_now) emit_split(p, hv, qslot, qsub, q_row, q_qrow, q_n, h, dyn_lds, cx.trace_lb, cx.trace_w);
+        RR_STAMP(cx.trace_lb, cx.trace_w, 11);
         __syncthreads();                                                // LDS free, sh.redo final
+        RR_STAMP(cx.trace_lb, cx.trace_w, 12);
     }
 }
 
@@ -793,6 +832,8 @@ __device__ __forceinline__ RowCtx<DT> row_context(const RouteArgs& p, const Rout
     cx.q_qrow = sh.qrows[cx.qslot];
     cx.q_n = (cx.q_row < 0) ? 0 : (CAUSAL ? cx.q_qrow + 1 : p.nk);
     cx.q_redo = false;
+    cx.trace_lb = -1;
+    cx.trace_w = wave;
     return cx;
 }
 
@@ -809,6 +850,7 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
     if (lb < 0) return;
     const int h = lb / G;
     const int g = lb % G;
+    RR_STAMP(lb, wave, 0);
 
     // ------------------------------------------------------------------ rows of this block
     if constexpr (REROUTE) {
@@ -993,8 +1035,11 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
         base_thr = make_key(t0, 0xFFFFFFFFu);
         __syncthreads();                                               // gm aliases the buffers
     }
+    RR_STAMP(lb, wave, 1);
     if (wave == 0) sh.thr[lane] = (my_row < 0) ? NO_PASS_KEY : base_thr;
     __syncthreads();
+    RR_STAMP(lb, wave, 2);
+    cx.trace_lb = lb;
 
     // ------------------------------------------------------------------ streaming pass
     select_and_emit<DT, CAUSAL, REROUTE>(p, sh, dyn_lds, tile, kbuf, REROUTE, cx, 0);
@@ -1482,6 +1527,7 @@ void k_relay(RescoreArgs s, RouteArgs p) {
     int32_t* sid = reinterpret_cast<int32_t*>(dyn_lds + RELAY_MAX_K_BYTES) + (size_t)wave * RELAY_RPW * 32;
     const int i0 = g2 * RELAY_ROWS + wave * RELAY_RPW;
     const int nrow = max(0, min(RELAY_RPW, p.nq - i0));
+    RR_STAMP(lb, wave, 0);
 
     // ------------------------------------------------------------------ 1. staging + rescoring
     {
@@ -1522,6 +1568,7 @@ void k_relay(RescoreArgs s, RouteArgs p) {
         }
         __builtin_amdgcn_s_waitcnt(0);                  // this wave's key chunks have landed
         __syncthreads();                                // the keys are in LDS
+        RR_STAMP(lb, wave, 1);
         float alpha, mu, beta;
         bool bad;
         rescore_rows_lds<DT, RELAY_RPW>(s, h, i0, lane, kl, sid, qv, alpha, mu, beta, bad);
@@ -1531,7 +1578,9 @@ void k_relay(RescoreArgs s, RouteArgs p) {
             rhint[wave * RELAY_RPW + lane] = bad ? -INFINITY : mu;
         }
     }
+    RR_STAMP(lb, wave, 2);
     __syncthreads();                                    // flags ready; the keys' LDS is free
+    RR_STAMP(lb, wave, 3);
 
     // ------------------------------------------------------------------ 2. compaction
     if (wave < 2) {
@@ -1568,6 +1617,7 @@ void k_relay(RescoreArgs s, RouteArgs p) {
         }
     }
     __syncthreads();
+    RR_STAMP(lb, wave, 4);
     if (nflag[0] == 0) return;                          // uniform: nothing to reroute
 
     // ------------------------------------------------------------------ 3. reroute, two slices
@@ -1575,6 +1625,8 @@ void k_relay(RescoreArgs s, RouteArgs p) {
     const int wv = wave % SPLIT;
     unsigned char* lds_s = dyn_lds + (size_t)slice * route_lds_bytes_dev(p.nk, p.c);
     RowCtx<DT> cx = row_context<DT, CAUSAL>(p, sh[slice], lds_s, h, wv, lane);
+    cx.trace_lb = lb;
+    cx.trace_w = wave;
     Tile<DT> tile;
     typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
     select_and_emit<DT, CAUSAL, true>(p, sh[slice], lds_s, tile, kbuf, false, cx, 0);
@@ -1689,3 +1741,22 @@ hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st) {
 }
 
 }  // namespace rr
+
+#ifdef RR_PHASE_TRACE
+// Measurement builds only: copy out / clear the phase tables ([block][wave][slot] timestamps,
+// [block][wave] mid-stream drain counts).  Return 0 on success.
+extern "C" int rr_debug_phase_trace(uint64_t* stamps, size_t n_stamps, uint32_t* drains, size_t n_drains) {
+    if (n_stamps > sizeof(rr::g_phase) / 8 || n_drains > sizeof(rr::g_drains) / 4) return -1;
+    if (hipMemcpyFromSymbol(stamps, HIP_SYMBOL(rr::g_phase), n_stamps * 8, 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return -1;
+    return hipMemcpyFromSymbol(drains, HIP_SYMBOL(rr::g_drains), n_drains * 4, 0, hipMemcpyDeviceToHost) ==
+                   hipSuccess ? 0 : -1;
+}
+extern "C" int rr_debug_phase_clear(void) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(rr::g_phase)) != hipSuccess) return -1;
+    if (hipMemset(p, 0, sizeof(rr::g_phase)) != hipSuccess) return -1;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(rr::g_drains)) != hipSuccess) return -1;
+    return hipMemset(p, 0, sizeof(rr::g_drains)) == hipSuccess ? 0 : -1;
+}
+#endif

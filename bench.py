@@ -741,6 +741,80 @@ def calib_copy():
     del a, b
 
 
+# Phase-trace slots (see RR_STAMP in csrc/rr_kernels.hip): what each stamp follows.
+PHASE_SLOTS = {0: "start", 1: "keys staged (relay) / first pass done (route)", 2: "rescored (relay) / threshold set (route)",
+               3: "flags ready (relay)", 4: "compacted (relay)", 5: "streaming pass done", 6: "final drain done",
+               7: "drain barrier", 8: "lists exchanged", 9: "quad merge done", 10: "merge barrier",
+               13: "bitmap built", 14: "random draws done", 15: "segments sorted", 11: "ledger written",
+               12: "end barrier"}
+
+
+def phase_trace():
+    """Per-phase durations of the route and relay kernels at the batched-heads shape, from the
+    measurement build (python -m long_context_prefill_anchor_amd.build --phase-trace): the first
+    lane of every wave stamps the 100 MHz real-time counter at fixed points; per phase, the
+    median and 90th percentile over all waves of one launch (us), the spread of each block's
+    waves at each stamp, and the waves' mid-stream drain counts."""
+    import ctypes
+    import torch
+    L = rr.lib()
+    L.rr_debug_phase_trace.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t]
+    NB, NW, NS = 4096, 8, 16
+
+    def trace(fn, nblocks, nw, chain):
+        assert L.rr_debug_phase_clear() == 0
+        torch.cuda.synchronize()
+        fn()
+        torch.cuda.synchronize()
+        st = np.zeros(NB * NW * NS, np.uint64)
+        dr = np.zeros(NB * NW, np.uint32)
+        assert L.rr_debug_phase_trace(st.ctypes.data, st.size, dr.ctypes.data, dr.size) == 0
+        t = st.reshape(NB, NW, NS)[:nblocks, :nw].astype(np.int64)
+        live = t[:, 0, 0] > 0
+        t, dr = t[live], dr.reshape(NB, NW)[:nblocks, :nw][live]
+        out = {"blocks": int(live.sum())}
+        phases = {}
+        for a, b in zip(chain[:-1], chain[1:]):
+            m = (t[:, :, a] > 0) & (t[:, :, b] > 0)
+            d = (t[:, :, b] - t[:, :, a])[m] / 100.0
+            if d.size:
+                phases[f"{PHASE_SLOTS[a]} -> {PHASE_SLOTS[b]}"] = [round(float(np.median(d)), 2),
+                                                                   round(float(np.percentile(d, 90)), 2)]
+        out["phase_us_median_p90"] = phases
+        end = t[:, :, chain[-1]]
+        ok = (end > 0).all(axis=1)
+        out["block_chain_us_median"] = round(float(np.median((end[ok].max(axis=1) - t[ok, :, 0].min(axis=1)) / 100.0)), 2)
+        out["drains_per_wave"] = {int(k): int(c) for k, c in zip(*np.unique(dr, return_counts=True))}
+        return out
+
+    w = W.batched_heads()
+    gen = synth.generate(w)
+    l0, l1 = next(gen), next(gen)
+    H, n = w.heads, w.n
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()  # noqa: E731
+    q0, k0, q1, k1 = up(l0.q), up(l0.k), up(l1.q), up(l1.k)
+    led = rr.Ledger(H, n, n, 64, w.k, w.m, w.r, 0.0, False, "bf16", w.seed)
+    full = rr.Ledger(H, n, n, 64, w.k, 0, 0, 0.0, False, "bf16", w.seed)
+    for _ in range(3):
+        led.anchor(q0, k0, 0)
+        full.anchor(q0, k0, 0)
+    route = [0, 1, 2, 5, 6, 7, 8, 9, 10, 13, 14, 15, 11, 12]
+    res = {"workload": "batched_heads, layers 0 (anchor) and 1 (relay)"}
+    res["full_routing"] = trace(lambda: full.anchor(q1, k1, 1), H * 16, 4, route)
+    res["anchor"] = trace(lambda: led.anchor(q0, k0, 0), H * 16, 4, route)
+    led.set_relay_mode("fused")
+    led.anchor(q0, k0, 0)
+    led.relay(q1, k1, 1)
+    led.anchor(q0, k0, 0)
+    res["relay_fused"] = trace(lambda: led.relay(q1, k1, 1), H * 8, 8, [0, 1, 2, 3, 4] + route[3:])
+    led.set_relay_mode("compacted")
+    led.anchor(q0, k0, 0)
+    res["reroute_compacted"] = trace(lambda: led.relay(q1, k1, 1), H * 16, 4, [0, 2] + route[3:])
+    led.close()
+    full.close()
+    return res
+
+
 def side(fn, *a, **kw):
     """A side measurement: its result, or {"error": ...} if it fails (the headline stands)."""
     try:
@@ -766,12 +840,22 @@ def main():
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ counter summaries from rocprofv3 --pmc runs under DIR and exit")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summaries")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="per-phase kernel durations from the measurement build "
+                         "(python -m long_context_prefill_anchor_amd.build --phase-trace); prints its JSON")
     ap.add_argument("--calib-copy", action="store_true",
                     help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (counter calibration)")
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.profile_command or "rocprofv3 --pmc <counters> -- python3 bench.py")
         return
+    if args.phase_trace:
+        from long_context_prefill_anchor_amd import build as B
+        if not os.path.exists(B.PHASE_LIB):
+            print(f"{B.PHASE_LIB} is missing: python -m long_context_prefill_anchor_amd.build --phase-trace",
+                  file=sys.stderr)
+            sys.exit(2)
+        rr.LIB_PATH = B.PHASE_LIB
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); heads shard across GPUs "
               "with no exchange, so run one process per GPU on its own heads.", file=sys.stderr)
@@ -789,6 +873,9 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
     rr.lib()
+    if args.phase_trace:
+        print(json.dumps({"phase_trace": phase_trace()}), flush=True)
+        return
     if args.calib_copy:
         calib_copy()
     if args.only_attention:

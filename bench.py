@@ -421,26 +421,12 @@ def sparse_attention_measure(reps=20, causal=False):
             "unique_bytes": unique}
 
 
-class LedgerGroup:
-    """Width-bucket ledgers driven as one: each call goes to every bucket in turn."""
-
-    def __init__(self, leds):
-        self.leds = leds
-
-    def anchor(self, q, k, layer):
-        for led in self.leds:
-            led.anchor(q, k, layer)
-
-    def relay(self, q, k, layer, out=None):
-        for led in self.leds:
-            led.relay(q, k, layer)
-
-
 def width_buckets(steps=3, warmup=1):
     """Query-dependent route widths through width-bucketed ledgers (Sections 4.3-4.4) on the
     headline chain: even query rows route with k = 8 (m = 12, r = 8), odd rows with k = 16
-    (m = 12, r = 4); the comparator routes every row in full at its own width.  Recall is
-    against each row's own exact top-k."""
+    (m = 12, r = 4); the comparator routes every row in full at its own width.  Both advance
+    their buckets together (rr_anchor_route_group / rr_relay_layer_group: one launch per layer
+    for all buckets).  Recall is against each row's own exact top-k."""
     import torch
     w = W.batched_heads()
     H, n = w.heads, w.n
@@ -451,26 +437,27 @@ def width_buckets(steps=3, warmup=1):
     fulls = [rr.Ledger(H, n, n, w.d, k, 0, 0, w.gamma, w.causal, w.dtype, w.seed, q_rows=rows)
              for rows, k, _, _ in specs]
     outs = [led.alloc_outputs(with_scores=False) for led in leds]
+    group, full_group = rr.LedgerGroup(leds), rr.LedgerGroup(fulls)
     recall, rerouted = 0.0, 0
     for l in range(w.layers):
-        for led, full, o in zip(leds, fulls, outs):
-            if w.is_anchor(l):
-                led.anchor(qs[l], ks[l], l)
-            else:
-                led.relay(qs[l], ks[l], l, o)
-            full.anchor(qs[l], ks[l], l)
+        if w.is_anchor(l):
+            group.anchor(qs[l], ks[l], l)
+        else:
+            group.relay(qs[l], ks[l], l, outs)
+        full_group.anchor(qs[l], ks[l], l)
         torch.cuda.synchronize()
         for led, full, o in zip(leds, fulls, outs):
             used = led.get()[0].cpu().numpy().reshape(-1, led.k)
             exact = full.get()[0].cpu().numpy().reshape(-1, led.k)
             recall += route_recall(used, exact) * led.nq / n
             rerouted += H * led.nq if w.is_anchor(l) else int(o.n_rows.cpu().numpy()[0])
-    relay_ms, full_ms, _ = time_chains(w, LedgerGroup(leds), LedgerGroup(fulls), qs, ks, steps, warmup)
+    relay_ms, full_ms, _ = time_chains(w, group, full_group, qs, ks, steps, warmup)
     relay_layers = [l for l in range(w.layers) if not w.is_anchor(l)]
     t_relay, t_full = relay_ms[:, relay_layers].sum(), full_ms.sum()
     out = {"workload": "batched_heads, two width buckets",
            "buckets": [{"rows": "even query rows", "k": 8, "m": 12, "r": 8},
                        {"rows": "odd query rows", "k": 16, "m": 12, "r": 4}],
+           "launch": "one grid per layer for both buckets (grouped calls)",
            "recall": round(recall / w.layers, 6), "reroute_fraction": round(rerouted / (H * n * w.layers), 4),
            "relay_routes_per_s": round(H * n * len(relay_layers) * steps / (t_relay / 1e3), 1),
            "speedup_vs_full": round(float((t_full / (w.layers * steps)) / (t_relay / (len(relay_layers) * steps))), 4),

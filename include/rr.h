@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define RR_ABI_VERSION 3
+#define RR_ABI_VERSION 4
 
 typedef enum {
     RR_OK = 0,
@@ -140,6 +140,29 @@ rr_status rr_anchor_route(rr_ledger* ledger, const void* q, const void* k, int32
  * anchored and `layer` is greater than the last layer it saw.  `out` may be NULL. */
 rr_status rr_relay_layer(rr_ledger* ledger, const void* q, const void* k, int32_t layer,
                          void* stream, const rr_relay_out* out);
+
+/* Width buckets (Section 4.4: rows bucketed by route width, each bucket a ledger of its own;
+ * Section 4.3: the ledger holds whatever width the policy assigns) advanced together: the
+ * anchor layer / relay layer of `n` ledgers (1 <= n <= RR_GROUP_MAX, host array of distinct
+ * ledgers) over the same Q and K, in one kernel launch where the kernels allow it instead of
+ * one launch per bucket (each of which alone would leave part of the GPU idle).  The ledgers
+ * must share heads, nk, dtype, causal, the query rows per head (nq_q) and the device; their
+ * k, m, r, sink, recent, gamma and hysteresis settings may differ.  Results are those of
+ * calling rr_anchor_route / rr_relay_layer on each ledger in turn, which is also what runs
+ * when one launch is not possible: an anchor group with a ledger of k + m > 32, a relay group
+ * in which a ledger does not fit the fused kernel or asks for RR_RELAY_COMPACTED, or, with
+ * every ledger on RR_RELAY_AUTO, a group outside 128 <= sum of heads * ceil(nq / 128) <= 512.
+ * outs: NULL, or a host array of n pointers to optional outputs (each may be NULL), indexed as
+ * the ledgers.  The relay group checks every ledger's state (as rr_relay_layer) before
+ * launching anything.  Errors: RR_EINVAL for a NULL or repeated ledger, n out of range,
+ * ledgers that differ in the shared settings, NULL q / k or layer < 0; RR_ESTATE as
+ * rr_relay_layer; RR_EDEVICE if a launch fails (every ledger of the group is then poisoned;
+ * in the one-by-one path, the failing ledger and those after it are not advanced). */
+#define RR_GROUP_MAX 4
+rr_status rr_anchor_route_group(rr_ledger* const* ledgers, int32_t n, const void* q, const void* k,
+                                int32_t layer, void* stream);
+rr_status rr_relay_layer_group(rr_ledger* const* ledgers, int32_t n, const void* q, const void* k,
+                               int32_t layer, void* stream, const rr_relay_out* const* outs);
 
 /* Allocation-free relay layer, for callers that cannot allocate (code under HIP graph capture,
  * tight serving loops, harnesses that forbid device allocation): the relay layer of

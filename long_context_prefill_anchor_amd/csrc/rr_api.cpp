@@ -266,8 +266,8 @@ rr_status scratch_for_current_device(void** out) {
 // kernel (plus the compacted-list kernel when those outputs are asked for), or the rescoring
 // kernel then the reroute of the compacted rows.  `T`: ledger whose profiling records the
 // launches (null: none).  On failure *what names the launch.
-hipError_t relay_launch(const LedgerView& v, const void* q, const void* k, int32_t layer, hipStream_t st,
-                        const rr_relay_out* out, rr_ledger* T, const char** what) {
+rr::RescoreArgs rescore_args(const LedgerView& v, const void* q, const void* k, int32_t layer,
+                             const rr_relay_out* out) {
     rr::RescoreArgs s{};
     s.qp = q;
     s.kp = k;
@@ -296,6 +296,14 @@ hipError_t relay_launch(const LedgerView& v, const void* q, const void* k, int32
     s.layer = layer;
     s.min_reuse = v.cfg.min_reuse;
     s.gamma_extra = v.cfg.gamma_extra;
+    return s;
+}
+
+bool wants_list(const rr_relay_out* out) { return out && (out->rows || out->head_counts || out->n_rows); }
+
+hipError_t relay_launch(const LedgerView& v, const void* q, const void* k, int32_t layer, hipStream_t st,
+                        const rr_relay_out* out, rr_ledger* T, const char** what) {
+    const rr::RescoreArgs s = rescore_args(v, q, k, layer, out);
     rr::RouteArgs a = route_args(v, q, k, layer);
     a.refresh_mark = 1;
     const bool bf16 = v.cfg.dtype == RR_BF16, causal = v.cfg.causal != 0;
@@ -308,7 +316,7 @@ hipError_t relay_launch(const LedgerView& v, const void* q, const void* k, int32
             *what = "relay launch";
             return e;
         }
-        if (out && (out->rows || out->head_counts || out->n_rows)) {
+        if (wants_list(out)) {
             tix = timed ? time_begin(T, RR_KERNEL_LIST, st) : -1;
             e = rr::launch_compact_out(v.bcount, v.blist, v.cfg.heads, v.cfg.nq, out->rows, out->head_counts,
                                        out->n_rows, st);
@@ -517,6 +525,131 @@ rr_status rr_relay_layer(rr_ledger* L, const void* q, const void* k, int32_t lay
     const hipError_t e = relay_launch(view_of(L), q, k, layer, st, out, L, &what);
     if (e != hipSuccess) return hip_fail(L, e, what);
     L->last_layer = layer;
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// A width-bucket group: 1 .. RR_GROUP_MAX distinct ledgers over the same Q and K (same heads,
+// nk, element type, causal mask, query rows per head and device).
+rr_status check_group(rr_ledger* const* L, int32_t n, const void* q, const void* k, int32_t layer) {
+    if (!L) return fail(RR_EINVAL, "ledgers is NULL");
+    if (n < 1 || n > RR_GROUP_MAX) return fail(RR_EINVAL, "a group holds 1 to %d ledgers (got %d)", RR_GROUP_MAX, n);
+    for (int b = 0; b < n; ++b) {
+        if (!L[b]) return fail(RR_EINVAL, "ledger %d is NULL", b);
+        for (int a = 0; a < b; ++a)
+            if (L[a] == L[b]) return fail(RR_EINVAL, "ledger %d appears twice in the group", b);
+        const rr_config& c0 = L[0]->cfg;
+        const rr_config& c = L[b]->cfg;
+        if (c.heads != c0.heads || c.nk != c0.nk || c.dtype != c0.dtype || c.causal != c0.causal ||
+            L[b]->nq_q != L[0]->nq_q || L[b]->device != L[0]->device)
+            return fail(RR_EINVAL, "ledger %d differs from ledger 0 in heads, nk, dtype, causal, query rows or device", b);
+    }
+    if (!q || !k) return fail(RR_EINVAL, "q and k must be device pointers");
+    if (layer < 0) return fail(RR_EINVAL, "layer must be >= 0 (got %d)", layer);
+    return RR_OK;
+}
+
+rr_status group_launch_failed(rr_ledger* const* L, int32_t n, hipError_t e, const char* what) {
+    for (int b = 1; b < n; ++b) L[b]->poisoned = true;
+    return hip_fail(L[0], e, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+rr_status rr_anchor_route_group(rr_ledger* const* L, int32_t n, const void* q, const void* k, int32_t layer,
+                                void* stream) {
+    const rr_status st0 = check_group(L, n, q, k, layer);
+    if (st0 != RR_OK) return st0;
+    bool one_grid = n > 1;
+    for (int b = 0; b < n; ++b) one_grid = one_grid && L[b]->sel <= 32;
+    if (!one_grid) {
+        for (int b = 0; b < n; ++b) {
+            const rr_status e = rr_anchor_route(L[b], q, k, layer, stream);
+            if (e != RR_OK) return e;
+        }
+        return ok();
+    }
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    rr::RouteGroup g{};
+    g.n = n;
+    for (int b = 0; b < n; ++b) {
+        g.p[b] = route_args(L[b], q, k, layer);
+        g.p[b].refresh_mark = 0;
+        g.off[b + 1] = g.off[b] + (L[b]->cfg.nq + rr::ROUTE_ROWS - 1) / rr::ROUTE_ROWS;
+    }
+    g.per_head = g.off[n];
+    int tix[RR_GROUP_MAX];
+    for (int b = 0; b < n; ++b) tix[b] = time_begin(L[b], RR_KERNEL_ROUTE, st);
+    const hipError_t e = rr::launch_route_group(g, L[0]->cfg.dtype == RR_BF16, L[0]->cfg.causal != 0, st);
+    for (int b = 0; b < n; ++b) time_end(L[b], tix[b], st);
+    if (e != hipSuccess) return group_launch_failed(L, n, e, "grouped anchor route launch");
+    for (int b = 0; b < n; ++b) {
+        L[b]->anchored = true;
+        L[b]->poisoned = false;
+        L[b]->last_layer = layer;
+    }
+    return ok();
+}
+
+rr_status rr_relay_layer_group(rr_ledger* const* L, int32_t n, const void* q, const void* k, int32_t layer,
+                               void* stream, const rr_relay_out* const* outs) {
+    const rr_status st0 = check_group(L, n, q, k, layer);
+    if (st0 != RR_OK) return st0;
+    for (int b = 0; b < n; ++b) {
+        if (L[b]->poisoned) return fail(RR_ESTATE, "ledger %d is poisoned by an earlier device error; anchor first", b);
+        if (!L[b]->anchored) return fail(RR_ESTATE, "ledger %d: relay layer before any anchor layer", b);
+        if (layer <= L[b]->last_layer)
+            return fail(RR_ESTATE, "ledger %d: relay layer %d is not after the last layer %d", b, layer, L[b]->last_layer);
+    }
+    // One grid when every ledger takes the fused kernel: each fits it, none asks for the
+    // compacted schedule, and either one asks for the fused one or the group's 128-row blocks
+    // are in the automatic schedule's range.
+    bool one_grid = n > 1, forced = false;
+    long long blocks = 0;
+    for (int b = 0; b < n; ++b) {
+        one_grid = one_grid && fused_fits(view_of(L[b])) && L[b]->relay_mode != RR_RELAY_COMPACTED;
+        forced = forced || L[b]->relay_mode == RR_RELAY_FUSED;
+        blocks += (long long)L[b]->cfg.heads * ((L[b]->cfg.nq + 127) / 128);
+    }
+    one_grid = one_grid && (forced || (blocks >= FUSED_MIN_BLOCKS && blocks <= FUSED_MAX_BLOCKS));
+    if (!one_grid) {
+        for (int b = 0; b < n; ++b) {
+            const rr_status e = rr_relay_layer(L[b], q, k, layer, stream, outs ? outs[b] : nullptr);
+            if (e != RR_OK) return e;
+        }
+        return ok();
+    }
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    rr::RelayGroup g{};
+    g.n = n;
+    for (int b = 0; b < n; ++b) {
+        const LedgerView v = view_of(L[b]);
+        g.s[b] = rescore_args(v, q, k, layer, outs ? outs[b] : nullptr);
+        g.p[b] = route_args(v, q, k, layer);
+        g.p[b].refresh_mark = 1;
+        g.off[b + 1] = g.off[b] + (L[b]->cfg.nq + 127) / 128;
+    }
+    g.per_head = g.off[n];
+    int tix[RR_GROUP_MAX];
+    for (int b = 0; b < n; ++b) tix[b] = time_begin(L[b], RR_KERNEL_RELAY, st);
+    hipError_t e = rr::launch_relay_group(g, L[0]->cfg.dtype == RR_BF16, L[0]->cfg.causal != 0, st);
+    for (int b = 0; b < n; ++b) time_end(L[b], tix[b], st);
+    if (e != hipSuccess) return group_launch_failed(L, n, e, "grouped relay launch");
+    for (int b = 0; b < n; ++b) {
+        const rr_relay_out* out = outs ? outs[b] : nullptr;
+        if (!wants_list(out)) continue;
+        const int t = time_begin(L[b], RR_KERNEL_LIST, st);
+        e = rr::launch_compact_out(L[b]->bcount, L[b]->blist, L[b]->cfg.heads, L[b]->cfg.nq, out->rows,
+                                   out->head_counts, out->n_rows, st);
+        time_end(L[b], t, st);
+        if (e != hipSuccess) return group_launch_failed(L, n, e, "compacted-list launch");
+    }
+    for (int b = 0; b < n; ++b) L[b]->last_layer = layer;
     return ok();
 }
 

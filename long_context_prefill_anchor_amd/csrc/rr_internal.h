@@ -62,6 +62,22 @@ struct AttnArgs {
 
 constexpr int ROUTE_ROWS = 64;   // rows per route block and per rescore block
 
+// Width-bucket ledgers over the same Q and K launched as one grid: logical blocks run head-major
+// over the group, ledger b taking blocks off[b] .. off[b + 1] - 1 of each head's per_head.
+constexpr int GROUP_MAX = 4;
+struct RouteGroup {
+    int n;                      // ledgers in the group, 1 .. GROUP_MAX
+    int per_head;               // blocks per head over all of them
+    int off[GROUP_MAX + 1];
+    RouteArgs p[GROUP_MAX];
+};
+struct RelayGroup {
+    int n, per_head;
+    int off[GROUP_MAX + 1];
+    RescoreArgs s[GROUP_MAX];
+    RouteArgs p[GROUP_MAX];
+};
+
 hipError_t launch_route(const RouteArgs& a, bool bf16, bool causal, bool reroute, hipStream_t st);
 hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st);
 // Fused relay layer: rescoring, in-block compaction and reroute of every 128-row block in one
@@ -70,6 +86,10 @@ hipError_t launch_rescore(const RescoreArgs& a, bool bf16, hipStream_t st);
 bool relay_fits(int nk, int c, int sel, bool bf16);
 hipError_t launch_relay(const RescoreArgs& s, const RouteArgs& a, bool bf16, bool causal, hipStream_t st);
 // Compacted list (ascending h*nq+i), per-head counts and total from bcount / blist.
+// Anchor routing (sel <= 32) / fused relay layers (relay_fits) of a group of ledgers that share
+// H, nk, the element type and the causal mask.
+hipError_t launch_route_group(const RouteGroup& g, bool bf16, bool causal, hipStream_t st);
+hipError_t launch_relay_group(const RelayGroup& g, bool bf16, bool causal, hipStream_t st);
 hipError_t launch_compact_out(const int32_t* bcount, const int32_t* blist, int H, int nq, int32_t* out_rows,
                               int32_t* out_head_counts, int32_t* out_n_rows, hipStream_t st);
 size_t route_lds_bytes(int nk, int c);

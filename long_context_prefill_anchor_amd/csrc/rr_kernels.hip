@@ -34,6 +34,7 @@
 // (a row that ends with fewer than k+m keys is recomputed from -inf).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <algorithm>
 
 #include "rr_device.h"
 #include "rr_internal.h"
@@ -837,20 +838,19 @@ __device__ __forceinline__ RowCtx<DT> row_context(const RouteArgs& p, const Rout
     return cx;
 }
 
+// One route block: 64 ledger rows of one head (block lb = h * G + g of the ledger's grid).
+// tlb: the block's number in phase traces.
 template <typename DT, bool CAUSAL, bool REROUTE>
-__global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2))) void k_route(RouteArgs p) {
+__device__ __forceinline__ void route_block(const RouteArgs& p, int lb, int tlb, RouteShared& sh,
+                                            unsigned char* dyn_lds) {
     typedef typename Elem<DT>::type E;
-    extern __shared__ __align__(16) unsigned char dyn_lds[];
-    __shared__ RouteShared sh;
-
+    (void)tlb;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = (p.nq + ROWS - 1) / ROWS;
-    const int lb = REROUTE ? slice_major_block(p.H, G) : xcd_block(p.H * G);
-    if (lb < 0) return;
     const int h = lb / G;
     const int g = lb % G;
-    RR_STAMP(lb, wave, 0);
+    RR_STAMP(tlb, wave, 0);
 
     // ------------------------------------------------------------------ rows of this block
     if constexpr (REROUTE) {
@@ -1035,17 +1035,58 @@ __global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2)
         base_thr = make_key(t0, 0xFFFFFFFFu);
         __syncthreads();                                               // gm aliases the buffers
     }
-    RR_STAMP(lb, wave, 1);
+    RR_STAMP(tlb, wave, 1);
     if (wave == 0) sh.thr[lane] = (my_row < 0) ? NO_PASS_KEY : base_thr;
     __syncthreads();
-    RR_STAMP(lb, wave, 2);
-    cx.trace_lb = lb;
+    RR_STAMP(tlb, wave, 2);
+    cx.trace_lb = tlb;
 
     // ------------------------------------------------------------------ streaming pass
     select_and_emit<DT, CAUSAL, REROUTE>(p, sh, dyn_lds, tile, kbuf, REROUTE, cx, 0);
     if constexpr (REROUTE) {
         if (sh.redo) redo_rows<DT, CAUSAL>(p, sh, dyn_lds, cx);         // uniform; rare
     }
+}
+
+template <typename DT, bool CAUSAL, bool REROUTE>
+__global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2))) void k_route(RouteArgs p) {
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    __shared__ RouteShared sh;
+    const int G = (p.nq + ROWS - 1) / ROWS;
+    const int lb = REROUTE ? slice_major_block(p.H, G) : xcd_block(p.H * G);
+    if (lb < 0) return;
+    route_block<DT, CAUSAL, REROUTE>(p, lb, lb, sh, dyn_lds);
+}
+
+// The block of a grouped launch (width buckets sharing Q and K): logical blocks run head-major
+// over all ledgers of the group, so one head's blocks of every bucket share an XCD (and its L2
+// copy of that head's keys).  Returns the ledger, and its own block number in *lb_out (-1 for
+// grid padding).
+template <typename A>
+__device__ __forceinline__ int group_block(int n, int per_head, const int (&off)[GROUP_MAX + 1], const A (&args)[GROUP_MAX],
+                                           int rows_per_block, int H, int* lb_out) {
+    const int lb = xcd_block(H * per_head);
+    if (lb < 0) {
+        *lb_out = -1;
+        return 0;
+    }
+    const int h = lb / per_head;
+    const int x = lb % per_head;
+    int b = 0;
+    while (b + 1 < n && x >= off[b + 1]) ++b;            // uniform
+    const int G = (args[b].nq + rows_per_block - 1) / rows_per_block;
+    *lb_out = h * G + (x - off[b]);
+    return b;
+}
+
+template <typename DT, bool CAUSAL>
+__global__ __launch_bounds__(ROWS * SPLIT) __attribute__((amdgpu_waves_per_eu(2))) void k_route_group(RouteGroup g) {
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    __shared__ RouteShared sh;
+    int lb;
+    const int b = group_block(g.n, g.per_head, g.off, g.p, ROWS, g.p[0].H, &lb);
+    if (lb < 0) return;
+    route_block<DT, CAUSAL, false>(g.p[b], lb, (int)blockIdx.x, sh, dyn_lds);
 }
 
 // ------------------------------------------------------------------------------ rescore
@@ -1501,25 +1542,33 @@ __device__ __forceinline__ void rescore_rows_lds(const RescoreArgs& p, int h, in
 // and part of the other, so the reroute runs at the occupancy of full routing (two 64-row
 // slices per compute unit) without its threshold pass, and the rescoring reads keys from LDS
 // instead of gathering them from L2.  A block without a flagged row stops after step 2.
+// Block-shared state of a fused relay block.
+struct RelayShared {
+    RouteShared sh[2];
+    uint32_t rflag[RELAY_ROWS];
+    float rhint[RELAY_ROWS];
+    int nflag[2];
+};
+
+// One fused relay block: 128 ledger rows of one head (block lb = h * G2 + g2 of the ledger's
+// grid).  tlb: the block's number in phase traces.
 template <typename DT, bool CAUSAL>
-__global__ __launch_bounds__(ROWS * RELAY_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
-void k_relay(RescoreArgs s, RouteArgs p) {
+__device__ __forceinline__ void relay_block(const RescoreArgs& s, const RouteArgs& p, int lb, int tlb,
+                                            RelayShared& rs, unsigned char* dyn_lds) {
     typedef typename Elem<DT>::type E;
     constexpr uint32_t ROW_BYTES = 64 * sizeof(E);
     constexpr int LPR = ROW_BYTES / 16;
     constexpr int KPIECES = RELAY_MAX_K_BYTES / 16 / (ROWS * RELAY_WAVES);   // 16-byte pieces per thread
-    extern __shared__ __align__(16) unsigned char dyn_lds[];
-    __shared__ RouteShared sh[2];
-    __shared__ uint32_t rflag[RELAY_ROWS];
-    __shared__ float rhint[RELAY_ROWS];
-    __shared__ int nflag[2];
+    RouteShared (&sh)[2] = rs.sh;
+    uint32_t (&rflag)[RELAY_ROWS] = rs.rflag;
+    float (&rhint)[RELAY_ROWS] = rs.rhint;
+    int (&nflag)[2] = rs.nflag;
+    (void)tlb;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G2 = (p.nq + RELAY_ROWS - 1) / RELAY_ROWS;
-    const int lb = xcd_block(p.H * G2);
-    if (lb < 0) return;
     const int h = lb / G2;
     const int g2 = lb % G2;
     const uint32_t kbytes = (uint32_t)p.nk * ROW_BYTES;
@@ -1527,7 +1576,7 @@ void k_relay(RescoreArgs s, RouteArgs p) {
     int32_t* sid = reinterpret_cast<int32_t*>(dyn_lds + RELAY_MAX_K_BYTES) + (size_t)wave * RELAY_RPW * 32;
     const int i0 = g2 * RELAY_ROWS + wave * RELAY_RPW;
     const int nrow = max(0, min(RELAY_RPW, p.nq - i0));
-    RR_STAMP(lb, wave, 0);
+    RR_STAMP(tlb, wave, 0);
 
     // ------------------------------------------------------------------ 1. staging + rescoring
     {
@@ -1568,7 +1617,7 @@ void k_relay(RescoreArgs s, RouteArgs p) {
         }
         __builtin_amdgcn_s_waitcnt(0);                  // this wave's key chunks have landed
         __syncthreads();                                // the keys are in LDS
-        RR_STAMP(lb, wave, 1);
+        RR_STAMP(tlb, wave, 1);
         float alpha, mu, beta;
         bool bad;
         rescore_rows_lds<DT, RELAY_RPW>(s, h, i0, lane, kl, sid, qv, alpha, mu, beta, bad);
@@ -1578,9 +1627,9 @@ void k_relay(RescoreArgs s, RouteArgs p) {
             rhint[wave * RELAY_RPW + lane] = bad ? -INFINITY : mu;
         }
     }
-    RR_STAMP(lb, wave, 2);
+    RR_STAMP(tlb, wave, 2);
     __syncthreads();                                    // flags ready; the keys' LDS is free
-    RR_STAMP(lb, wave, 3);
+    RR_STAMP(tlb, wave, 3);
 
     // ------------------------------------------------------------------ 2. compaction
     if (wave < 2) {
@@ -1617,7 +1666,7 @@ void k_relay(RescoreArgs s, RouteArgs p) {
         }
     }
     __syncthreads();
-    RR_STAMP(lb, wave, 4);
+    RR_STAMP(tlb, wave, 4);
     if (nflag[0] == 0) return;                          // uniform: nothing to reroute
 
     // ------------------------------------------------------------------ 3. reroute, two slices
@@ -1625,12 +1674,35 @@ void k_relay(RescoreArgs s, RouteArgs p) {
     const int wv = wave % SPLIT;
     unsigned char* lds_s = dyn_lds + (size_t)slice * route_lds_bytes_dev(p.nk, p.c);
     RowCtx<DT> cx = row_context<DT, CAUSAL>(p, sh[slice], lds_s, h, wv, lane);
-    cx.trace_lb = lb;
+    cx.trace_lb = tlb;
     cx.trace_w = wave;
     Tile<DT> tile;
     typename Tile<DT>::KReg kbuf[Tile<DT>::NBUF];
     select_and_emit<DT, CAUSAL, true>(p, sh[slice], lds_s, tile, kbuf, false, cx, 0);
     if (sh[0].redo || sh[1].redo) redo_rows<DT, CAUSAL>(p, sh[slice], lds_s, cx);    // uniform; rare
+}
+
+template <typename DT, bool CAUSAL>
+__global__ __launch_bounds__(ROWS * RELAY_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+void k_relay(RescoreArgs s, RouteArgs p) {
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    __shared__ RelayShared rs;
+    const int G2 = (p.nq + RELAY_ROWS - 1) / RELAY_ROWS;
+    const int lb = xcd_block(p.H * G2);
+    if (lb < 0) return;
+    relay_block<DT, CAUSAL>(s, p, lb, lb, rs, dyn_lds);
+}
+
+// A fused relay layer over several width-bucket ledgers in one grid (see group_block).
+template <typename DT, bool CAUSAL>
+__global__ __launch_bounds__(ROWS * RELAY_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+void k_relay_group(RelayGroup g) {
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    __shared__ RelayShared rs;
+    int lb;
+    const int b = group_block(g.n, g.per_head, g.off, g.p, RELAY_ROWS, g.p[0].H, &lb);
+    if (lb < 0) return;
+    relay_block<DT, CAUSAL>(g.s[b], g.p[b], lb, (int)blockIdx.x, rs, dyn_lds);
 }
 
 // The compacted list of a relay layer (Sections 4.1-4.2: ascending h * nq + i of the flagged
@@ -1714,6 +1786,41 @@ hipError_t launch_relay(const RescoreArgs& s, const RouteArgs& a, bool bf16, boo
     if (!relay_fits(a.nk, a.c, a.sel, bf16)) return hipErrorInvalidValue;
     if (bf16) return causal ? launch_relay_t<bf16_t, true>(s, a, st) : launch_relay_t<bf16_t, false>(s, a, st);
     return causal ? launch_relay_t<float, true>(s, a, st) : launch_relay_t<float, false>(s, a, st);
+}
+
+template <typename DT, bool CAUSAL>
+static hipError_t launch_route_group_t(const RouteGroup& g, hipStream_t st) {
+    size_t lds = 0;
+    for (int b = 0; b < g.n; ++b) lds = std::max(lds, route_lds_bytes(g.p[b].nk, g.p[b].c));
+    hipLaunchKernelGGL((k_route_group<DT, CAUSAL>), dim3(xcd_grid(g.p[0].H * g.per_head)), dim3(ROWS * SPLIT), lds,
+                       st, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_group(const RouteGroup& g, bool bf16, bool causal, hipStream_t st) {
+    if (g.n < 1 || g.n > GROUP_MAX) return hipErrorInvalidValue;
+    for (int b = 0; b < g.n; ++b)
+        if (g.p[b].sel > 32) return hipErrorInvalidValue;
+    if (bf16) return causal ? launch_route_group_t<bf16_t, true>(g, st) : launch_route_group_t<bf16_t, false>(g, st);
+    return causal ? launch_route_group_t<float, true>(g, st) : launch_route_group_t<float, false>(g, st);
+}
+
+template <typename DT, bool CAUSAL>
+static hipError_t launch_relay_group_t(const RelayGroup& g, hipStream_t st) {
+    size_t lds = 0;
+    for (int b = 0; b < g.n; ++b)
+        lds = std::max(lds, relay_lds_bytes(g.p[b].nk, g.p[b].c, sizeof(typename Elem<DT>::type) == 2));
+    hipLaunchKernelGGL((k_relay_group<DT, CAUSAL>), dim3(xcd_grid(g.p[0].H * g.per_head)), dim3(ROWS * RELAY_WAVES),
+                       lds, st, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_relay_group(const RelayGroup& g, bool bf16, bool causal, hipStream_t st) {
+    if (g.n < 1 || g.n > GROUP_MAX) return hipErrorInvalidValue;
+    for (int b = 0; b < g.n; ++b)
+        if (!relay_fits(g.p[b].nk, g.p[b].c, g.p[b].sel, bf16)) return hipErrorInvalidValue;
+    if (bf16) return causal ? launch_relay_group_t<bf16_t, true>(g, st) : launch_relay_group_t<bf16_t, false>(g, st);
+    return causal ? launch_relay_group_t<float, true>(g, st) : launch_relay_group_t<float, false>(g, st);
 }
 
 hipError_t launch_compact_out(const int32_t* bcount, const int32_t* blist, int H, int nq, int32_t* out_rows,

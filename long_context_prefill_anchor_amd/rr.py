@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "RR_OK", -1: "RR_EINVAL", -2: "RR_EUNSUPPORTED", -3: "RR_ENOM
 # Entry points declared in include/rr.h, in declaration order.
 ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_create_rows", "rr_ledger_destroy",
                 "rr_anchor_route",
-                "rr_relay_layer", "rr_relay_layer_noalloc", "rr_ledger_set_relay_mode", "rr_ledger_get",
+                "rr_relay_layer", "rr_anchor_route_group", "rr_relay_layer_group", "rr_relay_layer_noalloc",
+                "rr_ledger_set_relay_mode", "rr_ledger_get",
                 "rr_ledger_set", "rr_ledger_config",
                 "rr_ledger_get_refreshed", "rr_ledger_set_refreshed", "rr_sparse_attention",
                 "rr_ledger_profile",
@@ -31,6 +32,7 @@ ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_create_rows", 
 RR_KERNEL_ROUTE, RR_KERNEL_RESCORE, RR_KERNEL_REROUTE, RR_KERNEL_RELAY, RR_KERNEL_LIST = 0, 1, 2, 3, 4
 RR_KERNEL_KINDS = 5
 RR_RELAY_AUTO, RR_RELAY_FUSED, RR_RELAY_COMPACTED = 0, 1, 2
+RR_GROUP_MAX = 4
 RELAY_MODES = {"auto": RR_RELAY_AUTO, "fused": RR_RELAY_FUSED, "compacted": RR_RELAY_COMPACTED}
 
 
@@ -71,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.rr_ledger_destroy.restype = None
         L.rr_anchor_route.argtypes = [vp, vp, vp, i32, vp]
         L.rr_relay_layer.argtypes = [vp, vp, vp, i32, vp, P(rr_relay_out)]
+        L.rr_anchor_route_group.argtypes = [P(vp), i32, vp, vp, i32, vp]
+        L.rr_relay_layer_group.argtypes = [P(vp), i32, vp, vp, i32, vp, P(P(rr_relay_out))]
         L.rr_ledger_set_relay_mode.argtypes = [vp, i32]
         L.rr_relay_layer_noalloc.argtypes = [P(rr_config), vp, vp, vp, vp, vp, i32, vp, P(rr_relay_out)]
         L.rr_ledger_get.argtypes = [vp, vp, vp, vp, i32, vp]
@@ -165,6 +169,27 @@ def rr_relay_layer(handle, q, k, layer: int, stream=None, flags=None, rows=None,
                      _ptr(beta), _ptr(cand_scores))
     _check(lib().rr_relay_layer(handle, _ptr(q), _ptr(k), int(layer), _stream(stream),
                                 ctypes.byref(o) if out else None), "rr_relay_layer")
+
+
+def _handles(handles):
+    return (ctypes.c_void_p * max(1, len(handles)))(*[h for h in handles]), len(handles)
+
+
+def rr_anchor_route_group(handles, q, k, layer: int, stream=None) -> None:
+    arr, n = _handles(handles)
+    _check(lib().rr_anchor_route_group(arr, n, _ptr(q), _ptr(k), int(layer), _stream(stream)),
+           "rr_anchor_route_group")
+
+
+def rr_relay_layer_group(handles, q, k, layer: int, stream=None, outs=None) -> None:
+    """outs: None, or one rr_relay_out (or None) per ledger."""
+    arr, n = _handles(handles)
+    po = None
+    if outs is not None:
+        po = (ctypes.POINTER(rr_relay_out) * max(1, len(outs)))(
+            *[ctypes.pointer(o) if o is not None else ctypes.POINTER(rr_relay_out)() for o in outs])
+    _check(lib().rr_relay_layer_group(arr, n, _ptr(q), _ptr(k), int(layer), _stream(stream), po),
+           "rr_relay_layer_group")
 
 
 def rr_relay_layer_noalloc(cfg: rr_config, ids, anchor_layer, refreshed, q, k, layer: int, stream=None,
@@ -306,6 +331,12 @@ class Ledger:
             rr_relay_layer(self.handle, q, k, layer, stream, out.flags, out.rows, out.head_counts,
                            out.n_rows, out.alpha, out.beta, out.cand_scores)
 
+    def out_struct(self, out: Optional[RelayOutputs]):
+        if out is None:
+            return None
+        return rr_relay_out(_ptr(out.flags), _ptr(out.rows), _ptr(out.head_counts), _ptr(out.n_rows),
+                            _ptr(out.alpha), _ptr(out.beta), _ptr(out.cand_scores))
+
     def get(self, stream=None):
         """(route [H,nq,k], sent [H,nq,c-k], anchor [H,nq]) as device int32 tensors."""
         import torch
@@ -335,3 +366,19 @@ class Ledger:
     def set(self, route, sent, anchor, last_layer, stream=None):
         rr_ledger_set(self.handle, route, sent if self.c > self.k else None, anchor, last_layer,
                       False, stream)
+
+
+class LedgerGroup:
+    """Width-bucket ledgers (Ledger objects over the same Q and K) advanced together, one launch
+    per layer where the kernels allow it (rr_anchor_route_group / rr_relay_layer_group)."""
+
+    def __init__(self, ledgers):
+        self.ledgers = list(ledgers)
+
+    def anchor(self, q, k, layer, stream=None):
+        rr_anchor_route_group([x.handle for x in self.ledgers], q, k, layer, stream)
+
+    def relay(self, q, k, layer, outs=None, stream=None):
+        """outs: None, or one RelayOutputs (or None) per ledger."""
+        structs = None if outs is None else [x.out_struct(o) for x, o in zip(self.ledgers, outs)]
+        rr_relay_layer_group([x.handle for x in self.ledgers], q, k, layer, stream, structs)

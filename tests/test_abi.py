@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     L = rr.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert rr.rr_abi_version() == 3
+    assert rr.rr_abi_version() == 4
 
 
 def cfg(**kw):
@@ -174,6 +174,18 @@ def test_null_ledger_is_rejected_by_every_call():
     assert L.rr_ledger_kernel_times(None, None, None) == rr.RR_EINVAL
     assert "NULL" in rr.rr_last_error() or "required" in rr.rr_last_error()
     L.rr_ledger_destroy(None)     # ignored
+
+
+def test_group_calls_reject_bad_groups_before_any_launch():
+    """The width-bucket group calls check the group on the host: NULL arrays or members, sizes
+    outside 1 .. RR_GROUP_MAX (nothing is dereferenced or launched for these)."""
+    L = rr.lib()
+    none2 = (ctypes.c_void_p * 2)(None, None)
+    for fn, extra in ((L.rr_anchor_route_group, ()), (L.rr_relay_layer_group, (None,))):
+        assert fn(None, 1, 1, 1, 0, None, *extra) == rr.RR_EINVAL and "NULL" in rr.rr_last_error()
+        assert fn(none2, 0, 1, 1, 0, None, *extra) == rr.RR_EINVAL and "1 to 4" in rr.rr_last_error()
+        assert fn(none2, rr.RR_GROUP_MAX + 1, 1, 1, 0, None, *extra) == rr.RR_EINVAL
+        assert fn(none2, 2, 1, 1, 0, None, *extra) == rr.RR_EINVAL and "ledger 0 is NULL" in rr.rr_last_error()
 
 
 def test_last_error_clears_on_success():

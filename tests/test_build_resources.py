@@ -10,11 +10,12 @@ import pytest
 from long_context_prefill_anchor_amd import build as B
 
 # Kernels allowed to use scratch, with the most they may use (bytes per lane): the fp32-input
-# reroute and fused relay instantiations (fp32 operands need twice the registers of bf16 at two
-# waves per SIMD, and these two carry the reroute's redo path too; the fp32 workloads are the
-# small 128- and 256-chunk ones).  The fp32 anchor / full-routing kernel runs without scratch.
-SCRATCH_ALLOWED = {"k_routeIfLb0ELb1E": 64, "k_routeIfLb1ELb1E": 64,
-                   "k_relayIfLb0": 72, "k_relayIfLb1": 80}
+# reroute and fused relay instantiations, single and grouped (fp32 operands need twice the
+# registers of bf16 at two waves per SIMD, and these carry the reroute's redo path too; the fp32
+# workloads are the small 128- and 256-chunk ones).  The fp32 anchor / full-routing kernel runs
+# without scratch.
+SCRATCH_ALLOWED = {"k_routeIfLb0ELb1E": 64, "k_routeIfLb1ELb1E": 72,
+                   "k_relayIfLb0": 72, "k_relayIfLb1": 80, "k_relay_groupIfLb": 64}
 
 
 @pytest.fixture(scope="module")

@@ -1,0 +1,185 @@
+"""Width buckets advanced together (Section 4.4: one ledger per route width; Section 4.3): the
+group calls rr_anchor_route_group / rr_relay_layer_group, which run every bucket of a layer in
+one kernel launch, against the same ledgers advanced one call at a time (rr_anchor_route /
+rr_relay_layer, whose width-bucket results test_gpu_parity.py checks against the oracle).  The
+two must agree bit for bit: ledger IDs, anchor layers, hysteresis state, flags, alpha, beta,
+candidate scores and the compacted lists.
+
+Every test prints the case it is about to run (flushed) before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+from long_context_prefill_anchor_amd import rr, synth
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rr.lib()
+    yield
+
+
+_ALL = dict(sink=1, recent=2, min_reuse=1, gamma_extra=0.005)
+
+# name, heads, query rows, nk, dtype, causal, relay mode (group, one at a time), row split,
+# [(k, m, r)], extra options.  A one-grid group runs the fused kernel, so the ledgers it is
+# compared with are set to the fused schedule too.
+GROUP_CASES = [
+    ("two_bf16_fused", 2, 300, 256, "bf16", False, ("fused", "fused"), "random", [(8, 8, 8), (16, 12, 4)], {}),
+    ("three_f32_causal_fused", 2, 200, 200, "f32", True, ("fused", "fused"), "random",
+     [(4, 4, 6), (12, 12, 8), (6, 6, 4)], {}),
+    ("all_options_causal_fused", 2, 180, 180, "bf16", True, ("fused", "fused"), "random", [(6, 6, 4), (12, 8, 6)], _ALL),
+    # 64 heads x (128 + 128 rows): 128 blocks of 128 rows, inside the automatic one-grid range
+    ("auto_in_range_bf16", 64, 256, 256, "bf16", False, ("auto", "fused"), "parity", [(8, 12, 8), (16, 12, 4)], {}),
+    ("four_ragged_fused", 3, 260, 1000, "bf16", False, ("fused", "fused"), "random",
+     [(12, 0, 0), (8, 8, 8), (12, 12, 8), (16, 16, 0)], {}),
+    # a bucket past 32 route + near-miss entries: the group runs one ledger at a time
+    ("wide_bucket_fallback", 2, 200, 300, "bf16", False, ("auto", "auto"), "random", [(8, 8, 8), (12, 24, 8)], {}),
+    # the compacted schedule asked for: one ledger at a time as well
+    ("compacted_fallback", 2, 200, 256, "bf16", False, ("compacted", "compacted"), "random", [(8, 8, 8), (16, 12, 8)], {}),
+]
+
+
+def split_rows(nq, nb, how, seed):
+    if how == "parity":
+        assign = np.arange(nq) % nb
+    else:
+        assign = np.random.default_rng(seed).integers(0, nb, nq)
+        assign[:nb] = np.arange(nb)                     # no empty bucket
+    return [np.flatnonzero(assign == b) for b in range(nb)]
+
+
+def make_set(H, nq, nk, dtype, causal, mode, rows, widths, extra):
+    leds = []
+    for rws, (k, m, r) in zip(rows, widths):
+        led = rr.Ledger(H, nq, nk, 64, k, m, r, 0.0, causal, dtype, 71, q_rows=rws, **extra)
+        led.set_relay_mode(mode)
+        leds.append(led)
+    return leds
+
+
+def bits(t):
+    """Bitwise view of a device tensor as a host int32 array (NaN payloads compare exactly)."""
+    import torch
+    a = t.cpu()
+    if a.dtype == torch.float32:
+        a = a.view(torch.int32)
+    return a.numpy().copy()
+
+
+def assert_same_state(a: rr.Ledger, b: rr.Ledger, what):
+    for x, y, part in zip(a.get(), b.get(), ("route", "sentinels", "anchor layer")):
+        np.testing.assert_array_equal(bits(x), bits(y), err_msg=f"{what}: {part}")
+    np.testing.assert_array_equal(bits(a.get_refreshed()), bits(b.get_refreshed()), err_msg=f"{what}: refreshed")
+
+
+def assert_same_outputs(oa: rr.RelayOutputs, ob: rr.RelayOutputs, what):
+    for f in ("flags", "rows", "head_counts", "n_rows", "alpha", "beta", "cand_scores"):
+        np.testing.assert_array_equal(bits(getattr(oa, f)), bits(getattr(ob, f)), err_msg=f"{what}: {f}")
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=[c[0] for c in GROUP_CASES])
+def test_group_matches_one_ledger_at_a_time(case):
+    import torch
+    name, H, nq, nk, dtype, causal, (mode_g, mode_s), how, widths, extra = case
+    U.log(f"[group] {name} H={H} nq={nq} nk={nk} {dtype} causal={causal} modes={mode_g},{mode_s} "
+          f"buckets={widths}")
+    rows = split_rows(nq, len(widths), how, 5)
+    grouped = make_set(H, nq, nk, dtype, causal, mode_g, rows, widths, extra)
+    single = make_set(H, nq, nk, dtype, causal, mode_s, rows, widths, extra)
+    group = rr.LedgerGroup(grouped)
+    q, k = synth.gaussian_inputs(H, nq, nk, 64, seed=81, dtype=dtype)
+    layers = [(3, q, k)]
+    for j, sigma in enumerate((0.03, 0.06, 0.01)):
+        q = synth.perturb(q, sigma / 8, seed=90 + 2 * j, dtype=dtype)
+        k = synth.perturb(k, sigma / 8, seed=91 + 2 * j, dtype=dtype)
+        layers.append((4 + j, q, k))
+    for li, (layer, qn, kn) in enumerate(layers):
+        qd, kd = U.upload(qn), U.upload(kn)
+        if li == 0:
+            group.anchor(qd, kd, layer)
+            for led in single:
+                led.anchor(qd, kd, layer)
+            torch.cuda.synchronize()
+            for b, (x, y) in enumerate(zip(grouped, single)):
+                assert_same_state(x, y, f"{name} anchor, bucket {b}")
+            continue
+        outs_g = [led.alloc_outputs() for led in grouped]
+        outs_s = [led.alloc_outputs() for led in single]
+        group.relay(qd, kd, layer, outs_g)
+        for led, o in zip(single, outs_s):
+            led.relay(qd, kd, layer, o)
+        torch.cuda.synchronize()
+        flagged = [int(o.n_rows.cpu()[0]) for o in outs_g]
+        U.log(f"   layer {layer}: flagged per bucket {flagged}")
+        for b, (x, y) in enumerate(zip(grouped, single)):
+            assert_same_state(x, y, f"{name} layer {layer}, bucket {b}")
+            assert_same_outputs(outs_g[b], outs_s[b], f"{name} layer {layer}, bucket {b}")
+    for led in grouped + single:
+        led.close()
+
+
+def test_group_without_outputs_and_its_timing():
+    """Group relay without outputs (outs = NULL) leaves the same ledgers; a one-grid launch is
+    recorded once in every member's kernel timing."""
+    import torch
+    H, nq, nk = 2, 256, 256
+    U.log("[group] no outputs + timing: H=2 nq=256 nk=256 bf16 fused")
+    rows = split_rows(nq, 2, "parity", 0)
+    grouped = make_set(H, nq, nk, "bf16", False, "fused", rows, [(8, 8, 8), (12, 12, 8)], {})
+    single = make_set(H, nq, nk, "bf16", False, "fused", rows, [(8, 8, 8), (12, 12, 8)], {})
+    q0, k0 = synth.gaussian_inputs(H, nq, nk, 64, seed=3, dtype="bf16")
+    q1 = synth.perturb(q0, 0.05 / 8, seed=4, dtype="bf16")
+    k1 = synth.perturb(k0, 0.05 / 8, seed=5, dtype="bf16")
+    qd0, kd0, qd1, kd1 = U.upload(q0), U.upload(k0), U.upload(q1), U.upload(k1)
+    g = rr.LedgerGroup(grouped)
+    g.anchor(qd0, kd0, 0)
+    for led in single:
+        led.anchor(qd0, kd0, 0)
+    for led in grouped:
+        led.profile(True)
+    g.relay(qd1, kd1, 1)
+    for led in single:
+        led.relay(qd1, kd1, 1)
+    torch.cuda.synchronize()
+    for b, (x, y) in enumerate(zip(grouped, single)):
+        assert_same_state(x, y, f"no-output group, bucket {b}")
+        times = x.kernel_times()
+        assert times[rr.RR_KERNEL_RELAY][0] == 1, times
+        assert sum(n for n, _ in times) == 1, times
+    for led in grouped + single:
+        led.close()
+
+
+def test_group_state_rules():
+    """The relay group checks every member before launching: a member that was never anchored
+    fails the call and leaves the others unadvanced (they then take the layer)."""
+    import torch
+    H, nq, nk = 1, 128, 128
+    U.log("[group] state rules: H=1 nq=128 nk=128 bf16")
+    rows = split_rows(nq, 2, "parity", 0)
+    a, b = make_set(H, nq, nk, "bf16", False, "auto", rows, [(8, 8, 8), (12, 12, 8)], {})
+    q, k = synth.gaussian_inputs(H, nq, nk, 64, seed=9, dtype="bf16")
+    qd, kd = U.upload(q), U.upload(k)
+    a.anchor(qd, kd, 0)
+    with pytest.raises(rr.RRError, match="ledger 1: relay layer before any anchor layer"):
+        rr.LedgerGroup([a, b]).relay(qd, kd, 1)
+    with pytest.raises(rr.RRError, match="differs from ledger 0"):
+        other = rr.Ledger(2, nq, nk, 64, 8, 8, 8, 0.0, False, "bf16", 71)
+        try:
+            rr.LedgerGroup([a, other]).anchor(qd, kd, 0)
+        finally:
+            other.close()
+    rr.LedgerGroup([a, b]).anchor(qd, kd, 2)
+    rr.LedgerGroup([a, b]).relay(qd, kd, 3)
+    with pytest.raises(rr.RRError, match="not after the last layer"):
+        rr.LedgerGroup([a, b]).relay(qd, kd, 3)
+    torch.cuda.synchronize()
+    a.close()
+    b.close()

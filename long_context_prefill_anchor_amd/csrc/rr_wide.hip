@@ -23,9 +23,11 @@
 // already routed, random draws from Philox4x32-10 (counter = (t div 4, query row, layer,
 // head)) accepted in draw order when the chunk is still in the pool, a fill with the
 // lowest-index free chunks when the pool is not larger than r or the draw cap is reached.
-// The kernel keeps no threshold state, so anchor and reroute use it alike; in a reroute a
-// block scores its rows only if the rescore kernel flagged one of them and writes only the
-// flagged ones, and its first wave also writes those rows' entries of the compacted list.
+// The kernel keeps no threshold state, so anchor and reroute use it alike; in a reroute the
+// blocks of a head take its flagged rows in ascending order, 16 per block, from the rescore
+// kernel's per-64-row counts and lists (the compaction of Sections 4.1-4.2), so that only
+// ceil(flagged / 16) blocks per head score and select; the head's first block also writes its
+// entries of the compacted list.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -216,32 +218,6 @@ __device__ __forceinline__ void write_row(const RouteArgs& p, WideShared& sh, in
     }
 }
 
-// Reroute outputs for the block's 16 rows (wave 0): their places in the compacted list of
-// flagged rows (ascending h*nq + i) come after the flagged rows of every earlier 64-row rescore
-// block, whose counts the rescore kernel left in bcount, and after this block's earlier rows
-// of its own 64-row block.  The head's last block writes its count, the last head's the total.
-__device__ __forceinline__ void wide_outputs(const RouteArgs& p, int lane, int h, int r0) {
-    const int G = (p.nq + ROUTE_ROWS - 1) / ROUTE_ROWS;
-    const int g64 = r0 / ROUTE_ROWS;
-    int acc = 0;
-    for (int x = lane; x < h * G + g64; x += 64) acc += p.bcount[x];
-    const int before = g64 * ROUTE_ROWS + lane;           // rows of the 64-row block before r0
-    const bool fb = before < r0 && p.flags[(size_t)h * p.nq + before] != 0;
-    const int offset = wave_sum_i(acc) + __popcll(__ballot(fb));
-    const bool f = lane < WR && r0 + lane < p.nq && p.flags[(size_t)h * p.nq + r0 + lane] != 0;
-    const uint64_t m = __ballot(f);
-    if (p.out_rows && f) p.out_rows[offset + lanes_below(m, lane)] = h * p.nq + r0 + lane;
-    if (r0 + WR >= p.nq) {
-        int hc = 0;
-        for (int x = lane; x < G; x += 64) hc += p.bcount[(size_t)h * G + x];
-        const int count_h = wave_sum_i(hc);
-        if (lane == 0) {
-            if (p.out_head_counts) p.out_head_counts[h] = count_h;
-            if (p.out_n_rows && h == p.H - 1) p.out_n_rows[0] = offset + __popcll(m);
-        }
-    }
-}
-
 // One 16-row group: score table, then the ledger rows.  Called by every wave of the block.
 // Exact top-(k+m) of NR rows (block rows bi[r], query rows row[r]) from the score table, the
 // rows side by side, then each row's ledger write.
@@ -352,29 +328,30 @@ __device__ __forceinline__ void emit_rows(const RouteArgs& p, WideShared& sh, in
         write_row(p, sh, wave, lane, h, row[r], qrow[r], n[r], ki[r], mi[r], used[r], idx[r], skey[r]);
 }
 
+// One group of nrows (<= 16) ledger rows, ascending: brow is the row of block row lane % 16 (for
+// lane % 16 < nrows).  Every wave of the block calls it.
 template <typename E, bool CAUSAL, bool REROUTE>
-__device__ __forceinline__ void route_group(const RouteArgs& p, WideShared& sh, int wave, int lane, int h, int r0) {
-    const int nrows = min(WR, p.nq - r0);
-    bool want = lane < nrows;
-    if constexpr (REROUTE) want = want && p.flags[(size_t)h * p.nq + r0 + (want ? lane : 0)] != 0;
-    const uint64_t todo = __ballot(want);                 // the same in every wave
+__device__ __forceinline__ void route_group(const RouteArgs& p, WideShared& sh, int wave, int lane, int h, int brow,
+                                            int nrows) {
+    const uint64_t todo = __ballot(lane < nrows);         // the same in every wave
     if (todo == 0ull) return;                             // whole block: nothing to write
 
     // ---------------------------------------------------------------- score table
     // Keys up to the last written row's limit (query rows ascend with the block's rows).
-    const int last = r0 + 63 - __builtin_clzll(todo);
+    const int last = __builtin_amdgcn_readlane(brow, 63 - __builtin_clzll(todo));
     const int nmax = CAUSAL ? (p.qmap ? p.qmap[last] : last) + 1 : p.nk;
     const int ntile = (nmax + 15) >> 4;
     const int g = lane >> 4, c = lane & 15;
-    // A operand: block row c (rows past the ledger read its last row; their scores are unused).
-    const int arow = min(r0 + c, p.nq - 1);
+    // A operand: block row c (rows past the group read its first row; their scores are unused).
+    const int arow = (c < nrows) ? brow : __builtin_amdgcn_readlane(brow, 0);
     const E* qv = reinterpret_cast<const E*>(p.qp) + ((size_t)h * p.nq_q + (p.qmap ? p.qmap[arow] : arow)) * 64;
     const E* Kh = reinterpret_cast<const E*>(p.kp) + (size_t)h * p.nk * 64;
     int nlim[4];                                          // key limit of result rows 4g .. 4g+3
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        const int r = r0 + 4 * g + v;
-        nlim[v] = (r < p.nq) ? (CAUSAL ? (p.qmap ? p.qmap[r] : r) + 1 : p.nk) : 0;
+        const int bi = 4 * g + v;
+        const int r = __shfl(brow, bi);
+        nlim[v] = (bi < nrows) ? (CAUSAL ? (p.qmap ? p.qmap[r] : r) + 1 : p.nk) : 0;
     }
     auto put = [&](int tile, const f32x4& acc) {
         // result lane layout: key 16 tile + c, rows 4g + v
@@ -455,11 +432,56 @@ __device__ __forceinline__ void route_group(const RouteArgs& p, WideShared& sh, 
     for (int x = 0; x < WWAVES && rest != 0ull; ++x) rest &= rest - 1ull;
     if (rest != 0ull) {
         const int b1 = __builtin_ctzll(rest);
-        const int rows[2] = {r0 + b0, r0 + b1}, bis[2] = {b0, b1};
+        const int rows[2] = {__builtin_amdgcn_readlane(brow, b0), __builtin_amdgcn_readlane(brow, b1)};
+        const int bis[2] = {b0, b1};
         emit_rows<CAUSAL, REROUTE, 2>(p, sh, wave, lane, h, rows, bis);
     } else {
-        const int rows[1] = {r0 + b0}, bis[1] = {b0};
+        const int rows[1] = {__builtin_amdgcn_readlane(brow, b0)}, bis[1] = {b0};
         emit_rows<CAUSAL, REROUTE, 1>(p, sh, wave, lane, h, rows, bis);
+    }
+}
+
+// Reroute: the head's flagged rows, ascending, are ranks 0 .. count_h - 1 of the rescore
+// kernel's per-64-row counts and ascending lists (bcount [H, G], blist [H, G, 64]).  Returns
+// the row of rank `want` (-1 at or past the count) and the head's count in *count_h.
+__device__ __forceinline__ int flagged_row(const RouteArgs& p, int h, int want, int lane, int* count_h) {
+    const int G = (p.nq + ROUTE_ROWS - 1) / ROUTE_ROWS;
+    const int32_t* bc = p.bcount + (size_t)h * G;
+    const int32_t* bl = p.blist + (size_t)h * G * ROUTE_ROWS;
+    int base = 0, row = -1;
+    for (int c0 = 0; c0 < G; c0 += 64) {                  // uniform
+        const int cnt = (c0 + lane < G) ? bc[c0 + lane] : 0;
+        const int incl = wave_incl_scan_i(cnt);
+        const int nb = min(64, G - c0);
+        for (int bb = 0; bb < nb; ++bb) {
+            const int hi = base + __builtin_amdgcn_readlane(incl, bb);
+            const int lo = hi - __builtin_amdgcn_readlane(cnt, bb);
+            if (want >= lo && want < hi) row = bl[(size_t)(c0 + bb) * ROUTE_ROWS + (want - lo)];
+        }
+        base += __builtin_amdgcn_readlane(incl, 63);
+    }
+    *count_h = base;
+    return row;
+}
+
+// Reroute outputs of head h (one wave): its compacted rows (ascending h * nq + i), its count and,
+// for the last head, the layer's total.
+__device__ __forceinline__ void head_outputs(const RouteArgs& p, int h, int lane, int count_h) {
+    const int G = (p.nq + ROUTE_ROWS - 1) / ROUTE_ROWS;
+    int acc = 0;
+    for (int x = lane; x < h * G; x += 64) acc += p.bcount[x];
+    const int offset = wave_sum_i(acc);                   // flagged rows of the heads before h
+    if (lane == 0) {
+        if (p.out_head_counts) p.out_head_counts[h] = count_h;
+        if (p.out_n_rows && h == p.H - 1) p.out_n_rows[0] = offset + count_h;
+    }
+    if (p.out_rows) {
+        int run = 0;
+        for (int bb = 0; bb < G; ++bb) {                  // uniform
+            const int cb = p.bcount[(size_t)h * G + bb];
+            if (lane < cb) p.out_rows[offset + run + lane] = h * p.nq + p.blist[((size_t)h * G + bb) * ROUTE_ROWS + lane];
+            run += cb;
+        }
     }
 }
 
@@ -475,11 +497,19 @@ __global__ __launch_bounds__(64 * WWAVES) __attribute__((amdgpu_waves_per_eu(4))
     const int per_xcd = (int)gridDim.x / 8;
     const int lb = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
     if (lb >= p.H * per_head) return;                     // grid padding (whole block)
-    const int h = lb / per_head, r0 = (lb % per_head) * WR;
+    const int h = lb / per_head, b = lb % per_head;
     if constexpr (REROUTE) {
-        if (wave == 0 && (p.out_rows || p.out_head_counts || p.out_n_rows)) wide_outputs(p, lane, h, r0);
+        // Block b takes ranks 16 b .. 16 b + 15 of the head's flagged rows (compacted, so that
+        // only ceil(flagged / 16) blocks per head score and select); the rest exit.
+        int count_h;
+        const int brow = flagged_row(p, h, WR * b + (lane & 15), lane, &count_h);
+        if (b == 0 && wave == 0 && (p.out_rows || p.out_head_counts || p.out_n_rows)) head_outputs(p, h, lane, count_h);
+        if (WR * b >= count_h) return;                    // uniform
+        route_group<E, CAUSAL, REROUTE>(p, sh, wave, lane, h, brow, min(WR, count_h - WR * b));
+    } else {
+        const int r0 = b * WR;
+        route_group<E, CAUSAL, REROUTE>(p, sh, wave, lane, h, r0 + (lane & 15), min(WR, p.nq - r0));
     }
-    route_group<E, CAUSAL, REROUTE>(p, sh, wave, lane, h, r0);
 }
 
 template <typename E, bool CAUSAL, bool REROUTE>

@@ -87,7 +87,12 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(64 * AW) __attribute__((amdgpu_waves_per_eu(3))) void k_sparse_attn(AttnArgs p) {
     __shared__ __align__(16) uint16_t lk[AT * KSTR];     // K of the current chunk: [token][d]
     __shared__ __align__(16) uint16_t lv[64 * VSTR];     // V^T of the current chunk: [d][token]
-    const int blk = blockIdx.x;
+    // Workgroups go to the 8 XCDs round-robin; renumbered so that XCD x runs the contiguous
+    // range [x * per, (x + 1) * per) of query chunks, i.e. whole heads: the chunks a head's
+    // routes name then meet again in that XCD's L2 instead of in all eight.
+    const int per = (int)gridDim.x / 8;
+    const int blk = ((int)blockIdx.x % 8) * per + (int)blockIdx.x / 8;
+    if (blk >= p.H * p.nq) return;                       // grid padding
     const int h = blk / p.nq;
     const int i = blk % p.nq;
     const int x = threadIdx.x;
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(64 * AW) __attribute__((amdgpu_waves_per_eu(3))) vo
 }  // namespace
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st) {
-    const dim3 grid((unsigned)(a.H * a.nq));
+    const dim3 grid((unsigned)((a.H * a.nq + 7) / 8 * 8));   // a multiple of the 8 XCDs
     if (a.causal)
         hipLaunchKernelGGL(k_sparse_attn<true>, grid, dim3(64 * AW), 0, st, a);
     else

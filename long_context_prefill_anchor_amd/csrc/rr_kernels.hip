@@ -328,6 +328,10 @@ __device__ __forceinline__ int slice_major_block(int H, int G) {
 
 __host__ __forceinline__ int xcd_grid(int nlogical) { return (nlogical + XCDS - 1) / XCDS * XCDS; }
 
+// Words of a row's sentinel bitmap: one bit per key chunk plus a spare word, padded to a multiple
+// of four so that every row's bitmap starts 16-byte aligned (cleared with 16-byte stores).
+__host__ __device__ __forceinline__ constexpr int bitmap_words(int nk) { return ((nk + 31) / 32 + 1 + 3) & ~3; }
+
 // LDS a route block (64 rows, SPLIT waves) needs: the per-wave candidate buffers, the cross-wave
 // exchange lists, the pass-1 group maxima and the ledger-write area, which alias; rounded up to
 // 16 bytes.
@@ -335,7 +339,7 @@ __host__ __device__ __forceinline__ size_t route_lds_bytes_dev(int nk, int c) {
     const size_t cand = (size_t)SPLIT * CAP * ROWS * sizeof(uint2);
     const size_t xl = (size_t)SPLIT * XWAVE * sizeof(uint64_t);
     const size_t gm = (size_t)ROWS * GSTRIDE * sizeof(float);
-    const size_t em = (size_t)ROWS * (((nk + 31) / 32 + 1) + 32 + c + 1) * sizeof(uint32_t);
+    const size_t em = (size_t)ROWS * (bitmap_words(nk) + 32 + c + 1) * sizeof(uint32_t);
     size_t m = cand > xl ? cand : xl;
     m = m > gm ? m : gm;
     m = m > em ? m : em;
@@ -457,7 +461,7 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
     const int ki = min(p.k, my_n);
     const int mi = min(p.m, my_n - ki);
     const int words = (p.nk + 31) >> 5;
-    const int W = words + 1;
+    const int W = bitmap_words(p.nk);                 // words + 1, padded to 16 bytes
     uint32_t* bm = reinterpret_cast<uint32_t*>(lds) + (size_t)slot * (W + RLIST);
     int32_t* rlist = reinterpret_cast<int32_t*>(bm + W);
     int32_t* stage = reinterpret_cast<int32_t*>(lds) + (size_t)ROWS * (W + RLIST) + (size_t)slot * (p.c + 1);
@@ -465,7 +469,7 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
     // with sentinels need it.
     const int mw = p.sink + p.recent;
     if (p.r > 0 || mw > 0) {                          // uniform
-        for (int w = sub; w < W; w += 4) bm[w] = 0u;
+        for (int w = 4 * sub; w < W; w += 16) *reinterpret_cast<uint4*>(bm + w) = make_uint4(0u, 0u, 0u, 0u);
         if (sub < 2) {                                // lanes 0 / 1 own positions [0,16) / [16,32)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -1449,8 +1453,8 @@ constexpr uint32_t RELAY_MAX_K_BYTES = 128u << 10;  // a head's keys staged in L
 // qv[rr]: this lane's 16-byte chunk of row rr's query.  Results as rescore_rows (lane rr).
 template <typename DT, int RPW>
 __device__ __forceinline__ void rescore_rows_lds(const RescoreArgs& p, int h, int i0, int lane, const unsigned char* kl,
-                                                 const int32_t* sid, const uint4 (&qv)[RPW], float& res_alpha,
-                                                 float& res_mu, float& res_beta, bool& res_bad) {
+                                                 const int32_t* sid, const uint4 (&qv)[RPW], float* res_lds,
+                                                 float& res_alpha, float& res_mu, float& res_beta, bool& res_bad) {
     typedef typename Elem<DT>::type E;
     constexpr uint32_t ROW_BYTES = 64 * sizeof(E);
     constexpr int LPR = ROW_BYTES / 16;
@@ -1461,8 +1465,7 @@ __device__ __forceinline__ void rescore_rows_lds(const RescoreArgs& p, int h, in
     const int b0 = lane & 1;
     const int cown = cand_of_lane<LPR, 1>(lane);
     const bool ownR = cown < p.k, ownSel = cown < p.sel, ownS = cown >= p.k && cown < p.c;
-    res_alpha = res_mu = res_beta = 0.f;
-    res_bad = false;
+    uint32_t badmask = 0u;                             // bit rr: row rr has a missing route / near-miss ID
 #pragma unroll
     for (int pr = 0; pr < RPW; pr += 2) {
         float A[2], B[2];
@@ -1509,18 +1512,19 @@ __device__ __forceinline__ void rescore_rows_lds(const RescoreArgs& p, int h, in
             a = vmin2(__uint_as_float(z[0]), __uint_as_float(z[1]));
             bb = vmax2(__uint_as_float(w[0]), __uint_as_float(w[1]));
         }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const float al = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 2 * t));
-            const float mu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 2 * t + 1));
-            const float be = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bb), 2 * t));
-            const bool mine = lane == pr + t;
-            res_alpha = mine ? al : res_alpha;
-            res_mu = mine ? mu : res_mu;
-            res_beta = mine ? be : res_beta;
-            res_bad = mine ? bad[t] : res_bad;
-        }
+        // Lanes 2t and 2t + 1 hold alpha and mu of row pr + t, lane 2t its beta: straight to the
+        // wave's result slot (alpha, mu at 2 rr, 2 rr + 1; beta at 2 RPW + rr).
+        if (lane < 4) res_lds[2 * pr + lane] = a;
+        if (lane < 4 && (lane & 1) == 0) res_lds[2 * RPW + pr + (lane >> 1)] = bb;
+        badmask |= (bad[0] ? 1u : 0u) << pr;
+        badmask |= (bad[1] ? 1u : 0u) << (pr + 1);
     }
+    // The same wave wrote the slot: its LDS operations complete in order.
+    const int rr = lane < RPW ? lane : 0;
+    res_alpha = res_lds[2 * rr];
+    res_mu = res_lds[2 * rr + 1];
+    res_beta = res_lds[2 * RPW + rr];
+    res_bad = ((badmask >> rr) & 1u) != 0u;
 }
 
 // One relay layer (Sections 3.2, 4.1, 4.2) for 128 ledger rows of one head in one block of
@@ -1547,6 +1551,7 @@ struct RelayShared {
     RouteShared sh[2];
     uint32_t rflag[RELAY_ROWS];
     float rhint[RELAY_ROWS];
+    float rres[RELAY_WAVES][3 * RELAY_RPW];   // each wave's rescoring results (alpha, mu | beta)
     int nflag[2];
 };
 
@@ -1620,7 +1625,7 @@ __device__ __forceinline__ void relay_block(const RescoreArgs& s, const RouteArg
         RR_STAMP(tlb, wave, 1);
         float alpha, mu, beta;
         bool bad;
-        rescore_rows_lds<DT, RELAY_RPW>(s, h, i0, lane, kl, sid, qv, alpha, mu, beta, bad);
+        rescore_rows_lds<DT, RELAY_RPW>(s, h, i0, lane, kl, sid, qv, rs.rres[wave], alpha, mu, beta, bad);
         if (lane < RELAY_RPW) {
             const bool f = relay_decide(s, h, i0 + lane, alpha, mu, beta, bad, false);
             rflag[wave * RELAY_RPW + lane] = f ? 1u : 0u;
@@ -1771,7 +1776,7 @@ size_t relay_lds_bytes(int nk, int c, bool bf16) {
 bool relay_fits(int nk, int c, int sel, bool bf16) {
     const size_t row_bytes = bf16 ? 128 : 256;
     return sel <= 32 && c <= 32 && (size_t)nk * row_bytes <= RELAY_MAX_K_BYTES &&
-           relay_lds_bytes(nk, c, bf16) + sizeof(RouteShared) * 2 + RELAY_ROWS * 8 + 64 <= (160u << 10);
+           relay_lds_bytes(nk, c, bf16) + sizeof(RelayShared) + 64 <= (160u << 10);
 }
 
 template <typename DT, bool CAUSAL>

@@ -15,7 +15,7 @@ from long_context_prefill_anchor_amd import build as B
 # workloads are the small 128- and 256-chunk ones).  The fp32 anchor / full-routing kernel runs
 # without scratch.
 SCRATCH_ALLOWED = {"k_routeIfLb0ELb1E": 64, "k_routeIfLb1ELb1E": 72,
-                   "k_relayIfLb0": 72, "k_relayIfLb1": 80, "k_relay_groupIfLb": 64}
+                   "k_relayIfLb0": 72, "k_relayIfLb1": 80, "k_relay_groupIfLb": 72}
 
 
 @pytest.fixture(scope="module")

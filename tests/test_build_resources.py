@@ -14,8 +14,8 @@ from long_context_prefill_anchor_amd import build as B
 # registers of bf16 at two waves per SIMD, and these carry the reroute's redo path too; the fp32
 # workloads are the small 128- and 256-chunk ones).  The fp32 anchor / full-routing kernel runs
 # without scratch.
-SCRATCH_ALLOWED = {"k_routeIfLb0ELb1E": 64, "k_routeIfLb1ELb1E": 72,
-                   "k_relayIfLb0": 72, "k_relayIfLb1": 80, "k_relay_groupIfLb": 72}
+SCRATCH_ALLOWED = {"k_routeIfLb0ELb1E": 80, "k_routeIfLb1ELb1E": 80,
+                   "k_relayIfLb": 80, "k_relay_groupIfLb": 80}
 
 
 @pytest.fixture(scope="module")

@@ -176,6 +176,8 @@ def test_group_state_rules():
             rr.LedgerGroup([a, other]).anchor(qd, kd, 0)
         finally:
             other.close()
+    with pytest.raises(rr.RRError, match="appears twice"):
+        rr.LedgerGroup([a, a]).anchor(qd, kd, 0)
     rr.LedgerGroup([a, b]).anchor(qd, kd, 2)
     rr.LedgerGroup([a, b]).relay(qd, kd, 3)
     with pytest.raises(rr.RRError, match="not after the last layer"):

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define RR_ABI_VERSION 4
+#define RR_ABI_VERSION 5
 
 typedef enum {
     RR_OK = 0,
@@ -212,14 +212,30 @@ rr_status rr_ledger_set_relay_mode(rr_ledger* ledger, int32_t mode);
 rr_status rr_ledger_get(const rr_ledger* ledger, int32_t* route, int32_t* sent,
                         int32_t* anchor_layer, int32_t dst_is_host, void* stream);
 
+/* Check ledger tensors in host memory (layout of rr_ledger_get; the three tensors of Section
+ * 4.1) against the rules every routing call leaves them in, without touching the GPU: per row,
+ * each segment ascending with -1 padding only at its end; IDs inside the row's allowed chunks
+ * [0, n_i) (n_i = query row + 1 under the causal mask, else nk) and distinct across the row's
+ * segments; a full route of min(k, n_i) IDs and near-miss segment of min(m, n_i - k_i); mandatory
+ * IDs among the sink chunks or the row's last `recent` allowed chunks; min(r, pool) random IDs
+ * (Section 3.1); anchor layers within [0, last_layer].  q_rows / nq_q: NULL / ignored, or a
+ * width bucket's query rows as in rr_ledger_create_rows.  Returns RR_OK, or RR_EINVAL naming
+ * the first offending row (also for NULL tensors or a bad q_rows), RR_EINVAL /
+ * RR_EUNSUPPORTED for the configuration as rr_config_check. */
+rr_status rr_ledger_validate(const rr_config* cfg, const int32_t* q_rows, int32_t nq_q,
+                             const int32_t* route, const int32_t* sent,
+                             const int32_t* anchor_layer, int32_t last_layer);
+
 /* Replace the whole ledger (snapshot restore / replay) with the three tensors of Section 4.1:
  * route, sent and anchor_layer are required, same layout as rr_ledger_get, caller-owned and
  * only read; `last_layer` becomes the last layer seen, so the next relay call must use a
- * greater layer.  The IDs are trusted to be valid for this configuration (in range, allowed,
- * distinct per row; IDs outside [0, nk) are treated as padding by the relay rescoring, a
- * causal-violating or repeated ID is not detected).  The hysteresis state is cleared (see
- * rr_ledger_set_refreshed).  src_is_host as in rr_ledger_get.  Errors: RR_EINVAL for NULL
- * arguments or last_layer < 0; RR_EDEVICE if a copy fails (the ledger is then poisoned). */
+ * greater layer.  From host memory (src_is_host = 1) the tensors are first checked as by
+ * rr_ledger_validate and refused with RR_EINVAL, the ledger unchanged, if they break a rule;
+ * from device memory they are trusted (IDs outside [0, nk) then count as padding in the relay
+ * rescoring; a causal-violating or repeated ID is not detected).  The hysteresis state is
+ * cleared (see rr_ledger_set_refreshed).  src_is_host as in rr_ledger_get.  Errors: RR_EINVAL
+ * for NULL arguments, last_layer < 0 or host tensors that fail the check; RR_EDEVICE if a copy
+ * fails (the ledger is then poisoned). */
 rr_status rr_ledger_set(rr_ledger* ledger, const int32_t* route, const int32_t* sent,
                         const int32_t* anchor_layer, int32_t last_layer, int32_t src_is_host,
                         void* stream);

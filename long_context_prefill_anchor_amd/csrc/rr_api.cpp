@@ -3,6 +3,7 @@
 // Event-Triggered Cross-Layer Route Reuse for Efficient Dynamic Sparse Attention").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -33,6 +34,7 @@ struct rr_ledger {
     int32_t* anchor = nullptr;   // [H, nq]
     uint8_t* refreshed = nullptr; // [H, nq] hysteresis state (1 = refreshed at a relay layer)
     int32_t* qmap = nullptr;     // width bucket: [nq] query row of each ledger row (else null)
+    std::vector<int32_t> qmap_host;  // the same on the host (snapshot checks)
     int nq_q = 0;                // query rows per head of the Q handed to compute calls
     uint8_t* flags_ws = nullptr; // [H, nq]
     float* hint_ws = nullptr;    // [H, nq]
@@ -362,6 +364,67 @@ rr_status rr_config_check(const rr_config* cfg) {
 
 namespace {
 
+// Host check of ledger IDs (Section 4.1's three tensors, layout of rr_ledger_get) against the
+// rules every routing call leaves them in, row by row: each segment ascending with -1 padding
+// only at its end; IDs inside the row's allowed range [0, n_i) (n_i = query row + 1 under the
+// causal mask, else nk) and distinct across the row's segments; a full route (min(k, n_i)
+// IDs) and near-miss segment (min(m, n_i - k_i)); mandatory IDs among the sink chunks or the
+// row's last `recent` allowed chunks; min(r, pool) random IDs; anchor layers in [0, last_layer].
+rr_status check_ledger_ids(const rr_config& c, const int32_t* q_rows, const int32_t* route, const int32_t* sent,
+                           const int32_t* anchor_layer, int32_t last_layer) {
+    const int cc = c.k + c.m + c.sink + c.recent + c.r;
+    const int ns = cc - c.k;
+    const int seg_len[4] = {c.k, c.m, c.sink + c.recent, c.r};
+    const char* seg_name[4] = {"route", "near-miss", "mandatory", "random"};
+    std::vector<uint32_t> seen((size_t)c.nk, 0u);
+    uint32_t stamp = 0;
+    for (int h = 0; h < c.heads; ++h) {
+        for (int i = 0; i < c.nq; ++i) {
+            const size_t flat = (size_t)h * c.nq + i;
+            const int qrow = q_rows ? q_rows[i] : i;
+            const int n = c.causal ? qrow + 1 : c.nk;
+            const int a = anchor_layer[flat];
+            if (a < 0 || a > last_layer)
+                return fail(RR_EINVAL, "head %d row %d: anchor layer %d outside [0, %d]", h, i, a, last_layer);
+            ++stamp;
+            const int ki = std::min(c.k, n), mi = std::min(c.m, n - ki);
+            int count[4] = {0, 0, 0, 0};
+            int pos = 0;
+            for (int sg = 0; sg < 4; ++sg) {
+                int prev = -1;
+                bool padded = false;
+                for (int t = 0; t < seg_len[sg]; ++t, ++pos) {
+                    const int id = pos < c.k ? route[flat * c.k + pos] : sent[flat * ns + (pos - c.k)];
+                    if (id == -1) {
+                        padded = true;
+                        continue;
+                    }
+                    if (padded)
+                        return fail(RR_EINVAL, "head %d row %d: %s ID %d after -1 padding", h, i, seg_name[sg], id);
+                    if (id < 0 || id >= n)
+                        return fail(RR_EINVAL, "head %d row %d: %s ID %d outside the allowed chunks [0, %d)", h, i,
+                                    seg_name[sg], id, n);
+                    if (id <= prev)
+                        return fail(RR_EINVAL, "head %d row %d: %s segment not ascending (%d after %d)", h, i,
+                                    seg_name[sg], id, prev);
+                    if (seen[id] == stamp) return fail(RR_EINVAL, "head %d row %d: chunk %d appears twice", h, i, id);
+                    if (sg == 2 && !(id < c.sink || id >= n - c.recent))
+                        return fail(RR_EINVAL, "head %d row %d: mandatory ID %d is neither a sink nor a recent chunk",
+                                    h, i, id);
+                    seen[id] = stamp;
+                    prev = id;
+                    ++count[sg];
+                }
+            }
+            const int rwant = std::min(c.r, n - ki - mi - count[2]);
+            if (count[0] != ki || count[1] != mi || count[3] != rwant)
+                return fail(RR_EINVAL, "head %d row %d: %d route, %d near-miss and %d random IDs where the row holds "
+                            "%d, %d and %d", h, i, count[0], count[1], count[3], ki, mi, rwant);
+        }
+    }
+    return RR_OK;
+}
+
 // Shared by rr_ledger_create and rr_ledger_create_rows (q_rows: validated host array or null).
 rr_status create_ledger(const rr_config* cfg, const int32_t* q_rows, int32_t nq_q, rr_ledger** out) {
     rr_ledger* L = new (std::nothrow) rr_ledger;
@@ -399,8 +462,10 @@ rr_status create_ledger(const rr_config* cfg, const int32_t* q_rows, int32_t nq_
     e = hipMemset(L->anchor, 0xFF, rows * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(L->ids, 0xFF, rows * L->c * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(L->refreshed, 0, rows);
-    if (e == hipSuccess && q_rows)
+    if (e == hipSuccess && q_rows) {
         e = hipMemcpy(L->qmap, q_rows, (size_t)cfg->nq * sizeof(int32_t), hipMemcpyHostToDevice);
+        L->qmap_host.assign(q_rows, q_rows + cfg->nq);
+    }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         free_all(L);
@@ -437,6 +502,27 @@ rr_status rr_ledger_create_rows(const rr_config* cfg, const int32_t* q_rows, int
             return fail(RR_EINVAL, "q_rows must ascend strictly within [0, nq_q) (entry %d = %d)", r, q_rows[r]);
     }
     return create_ledger(cfg, q_rows, nq_q, out);
+}
+
+rr_status rr_ledger_validate(const rr_config* cfg, const int32_t* q_rows, int32_t nq_q, const int32_t* route,
+                             const int32_t* sent, const int32_t* anchor_layer, int32_t last_layer) {
+    const rr_status st = check_cfg(cfg, q_rows != nullptr);
+    if (st != RR_OK) return st;
+    const int c = cfg->k + cfg->m + cfg->sink + cfg->recent + cfg->r;
+    if (!route || !anchor_layer || (!sent && c > cfg->k))
+        return fail(RR_EINVAL, "route, sent and anchor_layer are required");
+    if (last_layer < 0) return fail(RR_EINVAL, "last_layer must be >= 0 (got %d)", last_layer);
+    if (q_rows) {
+        if (nq_q < cfg->nq || nq_q > 65536)
+            return fail(RR_EINVAL, "nq_q must be in [nq, 65536] (got %d for nq = %d)", nq_q, cfg->nq);
+        if (cfg->causal && nq_q != cfg->nk) return fail(RR_EINVAL, "causal routing needs nq_q == nk");
+        for (int r = 0; r < cfg->nq; ++r) {
+            if (q_rows[r] < 0 || q_rows[r] >= nq_q || (r > 0 && q_rows[r] <= q_rows[r - 1]))
+                return fail(RR_EINVAL, "q_rows must ascend strictly within [0, nq_q) (entry %d = %d)", r, q_rows[r]);
+        }
+    }
+    const rr_status v = check_ledger_ids(*cfg, q_rows, route, sent, anchor_layer, last_layer);
+    return v == RR_OK ? ok() : v;
 }
 
 void rr_ledger_destroy(rr_ledger* L) {
@@ -719,6 +805,11 @@ rr_status rr_ledger_set(rr_ledger* L, const int32_t* route, const int32_t* sent,
     if (!route || !anchor_layer || (!sent && (L->c - L->cfg.k) > 0))
         return fail(RR_EINVAL, "route, sent and anchor_layer are required");
     if (last_layer < 0) return fail(RR_EINVAL, "last_layer must be >= 0 (got %d)", last_layer);
+    if (src_is_host) {
+        const rr_status v = check_ledger_ids(L->cfg, L->qmap_host.empty() ? nullptr : L->qmap_host.data(), route,
+                                             sent, anchor_layer, last_layer);
+        if (v != RR_OK) return v;
+    }
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const hipMemcpyKind kind = src_is_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice;
     const size_t rows = (size_t)L->cfg.heads * L->cfg.nq;

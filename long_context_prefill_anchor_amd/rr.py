@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "RR_OK", -1: "RR_EINVAL", -2: "RR_EUNSUPPORTED", -3: "RR_ENOM
 ENTRY_POINTS = ("rr_config_check", "rr_ledger_create", "rr_ledger_create_rows", "rr_ledger_destroy",
                 "rr_anchor_route",
                 "rr_relay_layer", "rr_anchor_route_group", "rr_relay_layer_group", "rr_relay_layer_noalloc",
-                "rr_ledger_set_relay_mode", "rr_ledger_get",
+                "rr_ledger_set_relay_mode", "rr_ledger_get", "rr_ledger_validate",
                 "rr_ledger_set", "rr_ledger_config",
                 "rr_ledger_get_refreshed", "rr_ledger_set_refreshed", "rr_sparse_attention",
                 "rr_ledger_profile",
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
         L.rr_ledger_set_relay_mode.argtypes = [vp, i32]
         L.rr_relay_layer_noalloc.argtypes = [P(rr_config), vp, vp, vp, vp, vp, i32, vp, P(rr_relay_out)]
         L.rr_ledger_get.argtypes = [vp, vp, vp, vp, i32, vp]
+        L.rr_ledger_validate.argtypes = [P(rr_config), P(i32), i32, vp, vp, vp, i32]
         L.rr_ledger_set.argtypes = [vp, vp, vp, vp, i32, i32, vp]
         L.rr_ledger_config.argtypes = [vp, P(rr_config)]
         L.rr_ledger_get_refreshed.argtypes = [vp, vp, i32, vp]
@@ -110,12 +111,17 @@ def _check(status: int, where: str) -> None:
 
 
 def _ptr(x) -> Optional[int]:
-    """Device (or host) address of a tensor / raw int; None stays None."""
+    """Device (or host) address of a tensor, a contiguous NumPy array or a raw int; None stays
+    None."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
-    return x.data_ptr()
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if not x.flags["C_CONTIGUOUS"]:
+        raise ValueError("host arrays must be C-contiguous")
+    return x.ctypes.data
 
 
 def _stream(stream) -> Optional[int]:
@@ -211,6 +217,20 @@ def rr_ledger_set_relay_mode(handle, mode) -> None:
 def rr_ledger_get(handle, route, sent, anchor_layer, dst_is_host: bool, stream=None) -> None:
     _check(lib().rr_ledger_get(handle, _ptr(route), _ptr(sent), _ptr(anchor_layer),
                                int(bool(dst_is_host)), _stream(stream)), "rr_ledger_get")
+
+
+def rr_ledger_validate(cfg: rr_config, route, sent, anchor_layer, last_layer: int, q_rows=None,
+                       nq_q: int = 0) -> None:
+    """Host-memory check of ledger tensors (numpy int32 arrays, rr_ledger_get layout); raises
+    RRError naming the first offending row."""
+    import numpy as np
+    arrs = [None if x is None else np.ascontiguousarray(x, dtype=np.int32) for x in (route, sent, anchor_layer)]
+    rows = None
+    if q_rows is not None:
+        rows = (ctypes.c_int32 * len(q_rows))(*[int(x) for x in q_rows])
+    ptr = [None if a is None or a.size == 0 else a.ctypes.data for a in arrs]
+    _check(lib().rr_ledger_validate(ctypes.byref(cfg), rows, int(nq_q), ptr[0], ptr[1], ptr[2], int(last_layer)),
+           "rr_ledger_validate")
 
 
 def rr_ledger_set(handle, route, sent, anchor_layer, last_layer: int, src_is_host: bool,

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     L = rr.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert rr.rr_abi_version() == 4
+    assert rr.rr_abi_version() == 5
 
 
 def cfg(**kw):

@@ -580,6 +580,33 @@ def test_state_rules_on_device():
     led.close()
 
 
+def test_ledger_set_from_host_checks_the_ids():
+    """rr_ledger_set from host memory: an oracle ledger is taken as is (rr_ledger_get returns
+    it); a ledger with a repeated chunk is refused with RR_EINVAL and leaves the ledger as it
+    was."""
+    import torch
+    U.log("[state] rr_ledger_set from host memory: valid and repeated-chunk ledgers")
+    led, cfg = make(2, 48, 64, k=8, m=6, r=5, dtype="f32", seed=3)
+    q, k = synth.gaussian_inputs(2, 48, 64, 64, seed=1)
+    ora = O.anchor_layer(cfg, q, k, 2)
+    rr.rr_ledger_set(led.handle, ora.route, ora.sent, ora.anchor, 2, True)
+    got = U.ledger_np(led)
+    assert np.array_equal(got[0], ora.route) and np.array_equal(got[1], ora.sent)
+    assert np.array_equal(got[2], ora.anchor)
+    bad_sent = ora.sent.copy()
+    bad_sent[1, 4, 0] = ora.route[1, 4, 0]
+    bad_sent[1, 4, :6] = np.sort(bad_sent[1, 4, :6])
+    with pytest.raises(rr.RRError) as e:
+        rr.rr_ledger_set(led.handle, ora.route, np.ascontiguousarray(bad_sent), ora.anchor, 3, True)
+    assert e.value.status == rr.RR_EINVAL and "head 1 row 4" in str(e.value)
+    torch.cuda.synchronize()
+    again = U.ledger_np(led)
+    assert all(np.array_equal(a, b) for a, b in zip(got, again))
+    qd, kd = U.upload(q), U.upload(k)
+    led.relay(qd, kd, 3)                             # last layer still 2: the refused set changed nothing
+    led.close()
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("mode", RELAY_MODES)
 def test_kernel_timing_records_every_launch(mode):

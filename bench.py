@@ -418,6 +418,10 @@ def sparse_attention_measure(reps=20, causal=False):
                      "frac": round(ach_f / MFMA_BF16_PEAK_TFLOPS, 4)},
             "hbm_gathered": {"bytes": gathered, "achieved": round(ach_b, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(ach_b / HBM_PEAK_GBS, 4)},
+            # every byte moved once (Q, K, V, O): the bound a perfect reuse of routed chunks would meet
+            "hbm_unique": {"bytes": unique, "achieved": round(unique / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(unique / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "gathered_over_unique": round(gathered / unique, 2)},
             "unique_bytes": unique}
 
 

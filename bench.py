@@ -774,7 +774,17 @@ def phase_trace():
         out["phase_us_median_p90"] = phases
         end = t[:, :, chain[-1]]
         ok = (end > 0).all(axis=1)
-        out["block_chain_us_median"] = round(float(np.median((end[ok].max(axis=1) - t[ok, :, 0].min(axis=1)) / 100.0)), 2)
+        chains = (end[ok].max(axis=1) - t[ok, :, 0].min(axis=1)) / 100.0
+        out["block_chain_us_median"] = round(float(np.median(chains)), 2)
+        # spread of the blocks' chains, and of their start and end times over the launch (the
+        # launch lasts from the first start to the last end)
+        starts, ends = t[ok, :, 0].min(axis=1), end[ok].max(axis=1)
+        t0 = starts.min()
+        out["block_chain_us_p10_p90_max"] = [round(float(np.percentile(chains, 10)), 2),
+                                             round(float(np.percentile(chains, 90)), 2), round(float(chains.max()), 2)]
+        out["block_start_us_p90_max"] = [round(float(np.percentile((starts - t0) / 100.0, 90)), 2),
+                                         round(float((starts.max() - t0) / 100.0), 2)]
+        out["launch_span_us"] = round(float((ends.max() - t0) / 100.0), 2)
         out["drains_per_wave"] = {int(k): int(c) for k, c in zip(*np.unique(dr, return_counts=True))}
         return out
 

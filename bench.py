@@ -150,6 +150,27 @@ def quality_pass(w, led, full, qs, ks):
                 stride4_recall=stride4_sum / L)
 
 
+RHO_BINS = ((0.0, 0.35), (0.35, 0.5), (0.5, 0.65), (0.65, 0.8), (0.8, 1.0))
+
+
+def rho_breakdown(rho_per_layer, relay_ms, full_ms):
+    """Relay against full routing layer by layer, grouped by the layer's flagged fraction rho
+    (the chain's layers differ in drift): per bin the number of relay layers, their mean rho,
+    and the mean over those layers of each layer's median relay and full-routing time (us)."""
+    rows = [(rho, float(np.median(relay_ms[:, j])) * 1e3, float(np.median(full_ms[:, j])) * 1e3)
+            for j, rho in enumerate(rho_per_layer)]
+    out = []
+    for lo, hi in RHO_BINS:
+        sel = [x for x in rows if lo <= x[0] < hi or (hi == 1.0 and x[0] == 1.0)]
+        if not sel:
+            continue
+        r = float(np.mean([x[1] for x in sel]))
+        f = float(np.mean([x[2] for x in sel]))
+        out.append({"rho": [lo, hi], "layers": len(sel), "rho_mean": round(float(np.mean([x[0] for x in sel])), 3),
+                    "relay_layer_us": round(r, 2), "full_layer_us": round(f, 2), "speedup_vs_full": round(f / r, 4)})
+    return out
+
+
 def time_chains(w, led, full, qs, ks, steps, warmup):
     """`warmup` untimed passes, then `steps` timed passes of the relay chain and the full-routing
     chain, each layer call bracketed by events on the launch stream; returns the per-layer
@@ -932,6 +953,7 @@ def main():
     full_layer_us = float(np.median(full_ms) * 1e3)
     speedup = (t_full_layers / (L * args.steps)) / (t_relay_layers / (len(relay_layers) * args.steps))
     pairs_per_s = q["relay_pairs"] * args.steps / (t_relay_layers / 1e3)
+    relay_vs_rho = rho_breakdown(q["relay_rho_per_layer"], relay_ms[:, relay_layers], full_ms[:, relay_layers])
 
     # Per-kernel averages from the library's own launch events (same stream as the kernels).
     def avg_us(kt, kind):
@@ -1091,6 +1113,7 @@ def main():
         "relay_layer_us_median": round(relay_layer_us, 2),
         "anchor_layer_us_median": round(anchor_layer_us, 2),
         "full_layer_us_median": round(full_layer_us, 2),
+        "relay_vs_rho": relay_vs_rho,
         "roofline": roofline,
         "kernels": kernels,
         "graph": graph,

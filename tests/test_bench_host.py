@@ -88,3 +88,16 @@ def test_profile_summaries_round_trip(tmp_path, monkeypatch):
     text = (tmp_path / "traffic.txt").read_text().replace(bench.kernel_build_hash(), "0" * 64)
     (tmp_path / "traffic.txt").write_text(text)
     assert bench.recorded_traffic("relay") is None
+
+
+def test_rho_breakdown_groups_layers_by_flagged_fraction():
+    rho = [0.2, 0.3, 0.55, 0.9, 1.0]
+    relay = np.array([[10.0, 20.0, 30.0, 40.0, 50.0], [12.0, 20.0, 30.0, 40.0, 50.0]]) / 1e3   # ms, 2 steps
+    full = np.full((2, 5), 33.0) / 1e3
+    out = bench.rho_breakdown(rho, relay, full)
+    assert [b["rho"] for b in out] == [[0.0, 0.35], [0.5, 0.65], [0.8, 1.0]]
+    assert [b["layers"] for b in out] == [2, 1, 2]
+    first = out[0]
+    assert first["relay_layer_us"] == 15.5 and first["full_layer_us"] == 33.0      # medians 11 and 20
+    assert first["speedup_vs_full"] == round(33.0 / 15.5, 4) and first["rho_mean"] == 0.25
+    assert out[2]["relay_layer_us"] == 45.0

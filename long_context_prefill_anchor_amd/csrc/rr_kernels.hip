@@ -1445,6 +1445,9 @@ constexpr int RELAY_ROWS = 2 * ROWS;              // ledger rows per fused relay
 constexpr int RELAY_WAVES = 2 * SPLIT;            // its waves: two reroute slices of SPLIT waves
 constexpr int RELAY_RPW = RELAY_ROWS / RELAY_WAVES;  // rows rescored per wave
 constexpr uint32_t RELAY_MAX_K_BYTES = 128u << 10;  // a head's keys staged in LDS (1024 bf16 rows)
+// Words between two rows' staged candidate IDs: 32 IDs plus a pad, so that the 16 rows a
+// quarter-wave reads at once start in 16 different 4-bank groups (16-byte aligned rows).
+constexpr int RELAY_SID_STRIDE = 36;
 
 // Rescoring of ledger rows i0 .. i0 + nrow - 1 (nrow <= RPW) by one wave with the head's key rows
 // resident in LDS (kl: nk rows of 64 elements) and the candidate IDs staged per wave (sid: RPW
@@ -1479,12 +1482,12 @@ __device__ __forceinline__ void rescore_rows_lds(const RescoreArgs& p, int h, in
             for (int j = 0; j < NI; ++j) {
                 // Unconditional: a missing ID reads row 0, and its score is masked by `valid`
                 // below (a branch here would serialise every read behind its ID read).
-                const int id = sid[rr * 32 + RPI * j + grp];
+                const int id = sid[rr * RELAY_SID_STRIDE + RPI * j + grp];
                 const uint4 kv = *reinterpret_cast<const uint4*>(kl + (size_t)max(id, 0) * ROW_BYTES + coff);
                 part[j] = Dot<DT>::acc(qv[rr], kv, 0.f);
             }
             const float sc = reduce_scatter<LPR, 1>(part, lane);
-            const bool valid = sid[rr * 32 + cown] >= 0;        // -1 also past c
+            const bool valid = sid[rr * RELAY_SID_STRIDE + cown] >= 0;   // -1 also past c
             const float vr = (ownR && valid) ? sc : INFINITY;
             const float vsel = (ownSel && valid) ? sc : INFINITY;
             B[t] = (ownS && valid) ? sc : -INFINITY;
@@ -1525,6 +1528,119 @@ __device__ __forceinline__ void rescore_rows_lds(const RescoreArgs& p, int h, in
     res_mu = res_lds[2 * rr + 1];
     res_beta = res_lds[2 * RPW + rr];
     res_bad = ((badmask >> rr) & 1u) != 0u;
+}
+
+// The same rescoring for bf16 keys on the matrix cores (Section 3.2, Eq. 5-7).  For candidate
+// slot c, two 16x16x32 products give D[m][n] = K[id(m, c)] . Q[n] over the wave's 16 rows m, n;
+// the scores wanted are the diagonal D[n][n], which lands in register n % 4 of lane
+// n + 16 (n / 4) (lane L holds D[4 (L / 16) + v][L % 16]).  The four lanes L with L % 16 = n
+// supply row n's candidate key (A) and query (B), each a 16-byte chunk of the 64 dims per
+// product; A and B take the same chunk in the same lane, so a diagonal entry sums all 64 dims
+// whatever chunk each lane takes (off-diagonal entries mix chunks and are never read).  Lane
+// (n, g = L / 16) takes chunk relay_chunk(n, g, s) in product s: the 8 lanes n = 8a .. 8a + 7 of a
+// quarter-wave then read 8 different 16-byte columns of their 8 key rows, which fall in 8
+// different bank groups whatever the rows.  Fifteen of every sixteen products are discarded:
+// the matrix cores are otherwise idle here, and the dot products cost no vector instructions.
+// The diagonal lanes fold alpha (route), mu (route + near-miss: the reroute hint) and beta
+// (sentinels) over the slots; the other lanes' folds are never read.
+// qb[s]: this lane's query chunk relay_chunk(L % 16, L / 16, s).
+__device__ __forceinline__ constexpr int relay_chunk(int n, int g, int s) {
+    return 4 * (s ^ ((n >> 2) & 1)) + ((g + n) & 3);
+}
+
+// One pass over the 32 candidate slots, eight at a time: the key reads of the next eight slots
+// are issued before the products of the current eight (scheduling barriers keep the compiler
+// from sinking them back, which would leave one LDS round trip per slot).  The slot classes
+// (route c < k, route + near-miss c < k + m, sentinel c >= k) are compared in vector registers:
+// as scalar conditions the compiler hoisted all 96 of them and spilled them.  SCORES also writes
+// every candidate's score (a uniform choice made outside the loop).
+template <bool SCORES>
+__device__ __forceinline__ void rescore_slots_mfma(const RescoreArgs& p, const int (&id)[32], const unsigned char* kl,
+                                                   uint32_t off0, uint32_t off1, const bf16x8 (&qb)[2], int v,
+                                                   float* srow_out, float& a, float& mu, float& b, bool& bad) {
+    constexpr int GS = 8;                              // slots per group
+    int kv = p.k, selv = p.sel, cv = p.c;
+    asm volatile("" : "+v"(kv), "+v"(selv), "+v"(cv));
+    bf16x8 kb[2][GS][2];
+    auto issue = [&](int grp, int buf) {
+#pragma unroll
+        for (int j = 0; j < GS; ++j) {
+            // A missing ID reads key row 0; its score is masked by `valid`.
+            const unsigned char* kr = kl + (uint32_t)max(id[GS * grp + j], 0) * 128u;
+            kb[buf][j][0] = *reinterpret_cast<const bf16x8*>(kr + off0);
+            kb[buf][j][1] = *reinterpret_cast<const bf16x8*>(kr + off1);
+        }
+    };
+    issue(0, 0);
+#pragma unroll
+    for (int grp = 0; grp < 32 / GS; ++grp) {
+        const int buf = grp & 1;
+        if (grp + 1 < 32 / GS) issue(grp + 1, buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < GS; ++j) {
+            const int c = GS * grp + j;
+            const bool valid = id[c] >= 0;             // -1: padding, past c, outside K
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[buf][j][0], qb[0], d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[buf][j][1], qb[1], d, 0, 0, 0);
+            const float lo = (v & 1) ? d[1] : d[0];
+            const float hi = (v & 1) ? d[3] : d[2];
+            const float sc = (v & 2) ? hi : lo;
+            const bool isR = c < kv, isSel = c < selv;
+            a = vmin2(a, (isR && valid) ? sc : INFINITY);
+            mu = vmin2(mu, (isSel && valid) ? sc : INFINITY);
+            bad = bad || (isSel && !valid);
+            b = vmax2(b, (!isR && valid) ? sc : -INFINITY);   // past c the ID is -1
+            if constexpr (SCORES) {
+                if (srow_out != nullptr && c < cv) srow_out[c] = valid ? sc : __builtin_nanf("");
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int RPW>
+__device__ __forceinline__ void rescore_rows_lds_mfma(const RescoreArgs& p, int h, int i0, int lane,
+                                                      const unsigned char* kl, const int32_t* sid,
+                                                      const bf16x8 (&qb)[2], float* res_lds, float& res_alpha,
+                                                      float& res_mu, float& res_beta, bool& res_bad) {
+    static_assert(RPW == 16, "one 16x16 product per candidate slot");
+    const int n = lane & 15, g = lane >> 4, v = lane & 3;
+    const bool diag = (n >> 2) == g;
+    int id[32];
+    {
+        const int4* srow = reinterpret_cast<const int4*>(sid + n * RELAY_SID_STRIDE);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int4 x = srow[u];
+            id[4 * u] = x.x;
+            id[4 * u + 1] = x.y;
+            id[4 * u + 2] = x.z;
+            id[4 * u + 3] = x.w;
+        }
+    }
+    const uint32_t off0 = 16u * relay_chunk(n, g, 0), off1 = 16u * relay_chunk(n, g, 1);
+    float a = INFINITY, mu = INFINITY, b = -INFINITY;
+    bool bad = false;
+    if (p.cand_scores) {                                // uniform: checks only
+        float* out = (diag && i0 + n < p.nq) ? p.cand_scores + ((size_t)h * p.nq + i0 + n) * p.c : nullptr;
+        rescore_slots_mfma<true>(p, id, kl, off0, off1, qb, v, out, a, mu, b, bad);
+    } else {
+        rescore_slots_mfma<false>(p, id, kl, off0, off1, qb, v, nullptr, a, mu, b, bad);
+    }
+    if (diag) {
+        res_lds[2 * n] = a;
+        res_lds[2 * n + 1] = mu;
+        res_lds[2 * RPW + n] = b;
+    }
+    const uint64_t badmask = __ballot(diag && bad);
+    // The same wave wrote the slot: its LDS operations complete in order.
+    const int rr = lane < RPW ? lane : 0;
+    res_alpha = res_lds[2 * rr];
+    res_mu = res_lds[2 * rr + 1];
+    res_beta = res_lds[2 * RPW + rr];
+    res_bad = ((badmask >> (rr + 16 * (rr >> 2))) & 1ull) != 0ull;
 }
 
 // One relay layer (Sections 3.2, 4.1, 4.2) for 128 ledger rows of one head in one block of
@@ -1578,7 +1694,7 @@ __device__ __forceinline__ void relay_block(const RescoreArgs& s, const RouteArg
     const int g2 = lb % G2;
     const uint32_t kbytes = (uint32_t)p.nk * ROW_BYTES;
     unsigned char* kl = dyn_lds;
-    int32_t* sid = reinterpret_cast<int32_t*>(dyn_lds + RELAY_MAX_K_BYTES) + (size_t)wave * RELAY_RPW * 32;
+    int32_t* sid = reinterpret_cast<int32_t*>(dyn_lds + RELAY_MAX_K_BYTES) + (size_t)wave * RELAY_RPW * RELAY_SID_STRIDE;
     const int i0 = g2 * RELAY_ROWS + wave * RELAY_RPW;
     const int nrow = max(0, min(RELAY_RPW, p.nq - i0));
     RR_STAMP(tlb, wave, 0);
@@ -1607,25 +1723,46 @@ __device__ __forceinline__ void relay_block(const RescoreArgs& s, const RouteArg
             const int x = lane + 64 * u, rr = x / 32, c = x % 32;
             idv[u] = buf_load4(rI, (rr < nrow && c < s.c) ? (uint32_t)((i0 + rr) * s.c + c) * 4u : OOB);
         }
-        uint4 qv[RELAY_RPW];
-        const uint32_t coff = 16u * (lane % LPR);
-#pragma unroll
-        for (int rr = 0; rr < RELAY_RPW; ++rr) {
+        constexpr bool MFMA_RESCORE = sizeof(E) == 2;   // bf16: rescoring on the matrix cores
+        uint4 qv[MFMA_RESCORE ? 1 : RELAY_RPW];
+        bf16x8 qb[2];
+        if constexpr (MFMA_RESCORE) {
+            // Row L % 16, chunk relay_chunk(L % 16, L / 16, s) (see rescore_rows_lds_mfma).
+            const int rr = lane & 15;
             const int qr = s.qmap ? (rr < nrow ? s.qmap[i0 + rr] : 0) : i0 + rr;
-            qv[rr] = buf_load16(rQ, rr < nrow ? (uint32_t)qr * ROW_BYTES + coff : OOB);
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) {
+                const uint32_t off = 16u * (uint32_t)relay_chunk(rr, lane >> 4, hs);
+                const uint4 x = buf_load16(rQ, rr < nrow ? (uint32_t)qr * ROW_BYTES + off : OOB);
+                qb[hs] = __builtin_bit_cast(bf16x8, x);
+            }
+            qv[0] = make_uint4(0u, 0u, 0u, 0u);
+        } else {
+            const uint32_t coff = 16u * (lane % LPR);
+#pragma unroll
+            for (int rr = 0; rr < RELAY_RPW; ++rr) {
+                const int qr = s.qmap ? (rr < nrow ? s.qmap[i0 + rr] : 0) : i0 + rr;
+                qv[rr] = buf_load16(rQ, rr < nrow ? (uint32_t)qr * ROW_BYTES + coff : OOB);
+            }
         }
 #pragma unroll
         for (int u = 0; u < RELAY_RPW * 32 / 64; ++u) {
             const int x = lane + 64 * u, rr = x / 32, c = x % 32;
             // -1 for padding (also past c), rows outside the head and any index outside K
-            sid[x] = (rr < nrow && c < s.c && (unsigned)idv[u] < (unsigned)s.nk) ? idv[u] : -1;
+            sid[rr * RELAY_SID_STRIDE + c] = (rr < nrow && c < s.c && (unsigned)idv[u] < (unsigned)s.nk) ? idv[u] : -1;
         }
         __builtin_amdgcn_s_waitcnt(0);                  // this wave's key chunks have landed
         __syncthreads();                                // the keys are in LDS
         RR_STAMP(tlb, wave, 1);
         float alpha, mu, beta;
         bool bad;
-        rescore_rows_lds<DT, RELAY_RPW>(s, h, i0, lane, kl, sid, qv, rs.rres[wave], alpha, mu, beta, bad);
+        if constexpr (MFMA_RESCORE) {
+            (void)qv;
+            rescore_rows_lds_mfma<RELAY_RPW>(s, h, i0, lane, kl, sid, qb, rs.rres[wave], alpha, mu, beta, bad);
+        } else {
+            (void)qb;
+            rescore_rows_lds<DT, RELAY_RPW>(s, h, i0, lane, kl, sid, qv, rs.rres[wave], alpha, mu, beta, bad);
+        }
         if (lane < RELAY_RPW) {
             const bool f = relay_decide(s, h, i0 + lane, alpha, mu, beta, bad, false);
             rflag[wave * RELAY_RPW + lane] = f ? 1u : 0u;
@@ -1767,7 +1904,7 @@ hipError_t launch_route(const RouteArgs& a, bool bf16, bool causal, bool reroute
 }
 
 size_t relay_lds_bytes(int nk, int c, bool bf16) {
-    const size_t stage = RELAY_MAX_K_BYTES + (size_t)RELAY_WAVES * RELAY_RPW * 32 * sizeof(int32_t);
+    const size_t stage = RELAY_MAX_K_BYTES + (size_t)RELAY_WAVES * RELAY_RPW * RELAY_SID_STRIDE * sizeof(int32_t);
     const size_t slices = 2 * route_lds_bytes_dev(nk, c);
     (void)bf16;
     return stage > slices ? stage : slices;

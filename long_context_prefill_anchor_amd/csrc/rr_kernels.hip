@@ -471,11 +471,14 @@ __device__ __forceinline__ void emit_split(const RouteArgs& p, const uint64_t (&
     if (p.r > 0 || mw > 0) {                          // uniform
         for (int w = 4 * sub; w < W; w += 16) *reinterpret_cast<uint4*>(bm + w) = make_uint4(0u, 0u, 0u, 0u);
         if (sub < 2) {                                // lanes 0 / 1 own positions [0,16) / [16,32)
+            // Branch-free: an unused position ORs zero into word 0 (per-entry branches cost
+            // four scalar instructions and an exec round trip each).
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int pos = 16 * sub + i;
-                const uint32_t j = key_index(hv[i]);
-                if (pos < ki + mi && hv[i] != EMPTY_KEY) atomicOr(&bm[j >> 5], 1u << (j & 31));
+                const bool use = pos < ki + mi && hv[i] != EMPTY_KEY;
+                const uint32_t j = use ? key_index(hv[i]) : 0u;
+                atomicOr(&bm[j >> 5], use ? 1u << (j & 31) : 0u);
             }
         }
     }
@@ -1577,13 +1580,22 @@ __device__ __forceinline__ void rescore_slots_mfma(const RescoreArgs& p, const i
         const int buf = grp & 1;
         if (grp + 1 < 32 / GS) issue(grp + 1, buf ^ 1);
         __builtin_amdgcn_sched_barrier(0);
+        // All products of the group first, each slot in its own accumulator, so that the
+        // matrix core runs them back to back while the folds of earlier slots proceed.
+        f32x4 dd[GS];
+#pragma unroll
+        for (int j = 0; j < GS; ++j) {
+            dd[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dd[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[buf][j][0], qb[0], dd[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < GS; ++j)
+            dd[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[buf][j][1], qb[1], dd[j], 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < GS; ++j) {
             const int c = GS * grp + j;
             const bool valid = id[c] >= 0;             // -1: padding, past c, outside K
-            f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[buf][j][0], qb[0], d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[buf][j][1], qb[1], d, 0, 0, 0);
+            const f32x4 d = dd[j];
             const float lo = (v & 1) ? d[1] : d[0];
             const float hi = (v & 1) ? d[3] : d[2];
             const float sc = (v & 2) ? hi : lo;

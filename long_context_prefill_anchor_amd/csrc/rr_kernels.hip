@@ -760,14 +760,30 @@ __device__ __forceinline__ void select_and_emit(const RouteArgs& p, RouteShared&
         uint64_t* xl = reinterpret_cast<uint64_t*>(dyn_lds);            // [SPLIT][XWAVE]: [ROWS][XSTRIDE] + pad
         __syncthreads();                                                // every buffer is drained
         RR_STAMP(cx.trace_lb, cx.trace_w, 7);
+        // A block (slice) without rows has nothing to publish: no wave of it reads these lists
+        // (ntiles is 0 exactly when none of the 64 rows exists, the same in its four waves).
+        // bf16 only, as the skip below: the fp32 instantiations are at their register limit.
+        constexpr bool SKIP_EMPTY = sizeof(typename Elem<DT>::type) == 2;
+        if (!SKIP_EMPTY || ntiles > 0) {
 #pragma unroll
-        for (int s = 0; s < TOPW; ++s) xl[wave * XWAVE + lane * XSTRIDE + s] = top[s];
+            for (int s = 0; s < TOPW; ++s) xl[wave * XWAVE + lane * XSTRIDE + s] = top[s];
+        }
         __syncthreads();
-#pragma unroll
-        for (int s = 0; s < TOPW; ++s) top[s] = xl[qsub * XWAVE + qslot * XSTRIDE + s];
-        RR_STAMP(cx.trace_lb, cx.trace_w, 8);
         uint64_t hv[16];
-        quad_merge_split(top, hv, qsub);
+        // A wave whose 16 merge rows are all empty (the tail of a partly filled slice) skips
+        // the reads and the merge: it would only hold back the busy waves on its SIMD.
+        const bool any_row = !SKIP_EMPTY || __ballot(q_row >= 0) != 0ull;   // uniform over the wave
+        if (any_row) {
+#pragma unroll
+            for (int s = 0; s < TOPW; ++s) top[s] = xl[qsub * XWAVE + qslot * XSTRIDE + s];
+        }
+        RR_STAMP(cx.trace_lb, cx.trace_w, 8);
+        if (any_row) {
+            quad_merge_split(top, hv, qsub);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) hv[s] = EMPTY_KEY;
+        }
         RR_STAMP(cx.trace_lb, cx.trace_w, 9);
         __syncthreads();                                                // xl is free again
         RR_STAMP(cx.trace_lb, cx.trace_w, 10);

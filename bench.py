@@ -773,7 +773,7 @@ def phase_trace():
     L.rr_debug_phase_trace.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t]
     NB, NW, NS = 4096, 8, 16
 
-    def trace(fn, nblocks, nw, chain):
+    def trace(fn, nblocks, nw, chain, nflag=None):
         assert L.rr_debug_phase_clear() == 0
         torch.cuda.synchronize()
         fn()
@@ -783,6 +783,7 @@ def phase_trace():
         assert L.rr_debug_phase_trace(st.ctypes.data, st.size, dr.ctypes.data, dr.size) == 0
         t = st.reshape(NB, NW, NS)[:nblocks, :nw].astype(np.int64)
         live = t[:, 0, 0] > 0
+        bidx = np.nonzero(live)[0]
         t, dr = t[live], dr.reshape(NB, NW)[:nblocks, :nw][live]
         out = {"blocks": int(live.sum())}
         phases = {}
@@ -807,6 +808,17 @@ def phase_trace():
                                          round(float((starts.max() - t0) / 100.0), 2)]
         out["launch_span_us"] = round(float((ends.max() - t0) / 100.0), 2)
         out["drains_per_wave"] = {int(k): int(c) for k, c in zip(*np.unique(dr, return_counts=True))}
+        if nflag is not None:
+            # Fused relay blocks by their flagged rows: one reroute slice (<= 64) or two.
+            nf = nflag[bidx[ok]]
+            out["flagged_rows_per_block_mean"] = round(float(nf.mean()), 1)
+            for name, sel in (("one_slice", nf <= 64), ("two_slices", nf > 64)):
+                c = chains[sel]
+                out[f"{name}_blocks"] = int(sel.sum())
+                if c.size:
+                    out[f"{name}_chain_us_median_max"] = [round(float(np.median(c)), 2), round(float(c.max()), 2)]
+            if nf.std() > 0 and chains.std() > 0:
+                out["chain_vs_flagged_corr"] = round(float(np.corrcoef(nf, chains)[0, 1]), 3)
         return out
 
     w = W.batched_heads()
@@ -833,6 +845,31 @@ def phase_trace():
     led.anchor(q0, k0, 0)
     res["reroute_compacted"] = trace(lambda: led.relay(q1, k1, 1), H * 16, 4, [0, 2] + route[3:])
     led.close()
+    # The fused relay layer at fixed drifts (layer 1 after an anchor at layer 0), with each
+    # block's chain set against its flagged rows, beside full routing of the same layer.
+    by_drift = []
+    for sigma in (0.01, 0.03, 0.06):
+        wd = w.with_(name=f"phase_drift{sigma:g}", drift=(sigma, sigma))
+        g = synth.generate(wd)
+        a0, a1 = next(g), next(g)
+        qa, ka, qb, kb = up(a0.q), up(a0.k), up(a1.q), up(a1.k)
+        ld = rr.Ledger(H, n, n, 64, w.k, w.m, w.r, 0.0, False, "bf16", w.seed)
+        ld.set_relay_mode("fused")
+        outs = ld.alloc_outputs(with_scores=False)
+        ld.anchor(qa, ka, 0)
+        ld.relay(qb, kb, 1, outs)
+        torch.cuda.synchronize()
+        # flagged rows of each 128-row fused block, in the kernel's block order (h * n/128 + g)
+        nflag = outs.flags.cpu().numpy().astype(np.int64).reshape(H, n // 128, 128).sum(axis=2).reshape(-1)
+        ld.anchor(qa, ka, 0)
+        r = trace(lambda: ld.relay(qb, kb, 1), H * 8, 8, [0, 1, 2, 3, 4] + route[3:], nflag=nflag)
+        f = trace(lambda: full.anchor(qb, kb, 1), H * 16, 4, route)
+        by_drift.append({"sigma": sigma, "rho": round(float(nflag.sum()) / (H * n), 4),
+                         "relay_fused": {k: v for k, v in r.items() if k != "phase_us_median_p90"},
+                         "full_routing": {k: f[k] for k in ("block_chain_us_median", "block_chain_us_p10_p90_max",
+                                                            "launch_span_us")}})
+        ld.close()
+    res["relay_fused_by_drift"] = by_drift
     full.close()
     return res
 

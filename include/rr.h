@@ -85,7 +85,9 @@ typedef struct {
 } rr_config;
 /* c = k + m + sink + recent + r ledger IDs per row.  Limits (RR_EUNSUPPORTED beyond them):
  * d == 64, k + m <= 64 (k + m > 32 only with nk <= 1024), r <= 32, sink + recent <= 32,
- * (hence c <= 128), nk <= 4096, nq <= 65536;
+ * (hence c <= 128), nk <= 16384 (2M tokens in 128-token chunks) with the route kernel's
+ * per-block LDS within 160 KB (64 rows of nk-bit sentinel bitmaps and c-ID staging rows:
+ * c <= 86 at nk = 16384, any c up to nk = 8192), nq <= 65536;
  * heads * nq < 2^31 (RR_EINVAL).  A row with fewer allowed chunks than c gets shorter
  * segments, padded with -1. */
 

@@ -99,7 +99,14 @@ rr_status check_cfg(const rr_config* c, bool bucket) {
     if (c->k + c->m + c->sink + c->recent + c->r > 128)
         return fail(RR_EUNSUPPORTED, "k + m + sink + recent + r must be <= 128 (got %d)",
                     c->k + c->m + c->sink + c->recent + c->r);
-    if (c->nk > 4096) return fail(RR_EUNSUPPORTED, "nk must be <= 4096 (got %d)", c->nk);
+    if (c->nk > 16384) return fail(RR_EUNSUPPORTED, "nk must be <= 16384 (got %d)", c->nk);
+    {
+        const int ids = c->k + c->m + c->sink + c->recent + c->r;
+        if (!rr::route_fits(c->nk, ids))
+            return fail(RR_EUNSUPPORTED,
+                        "nk = %d with %d ledger IDs per row exceeds the route kernel's LDS (per-row sentinel "
+                        "bitmaps of nk bits and staging rows of c IDs in 160 KB)", c->nk, ids);
+    }
     if (c->nq > 65536) return fail(RR_EUNSUPPORTED, "nq must be <= 65536 (got %d)", c->nq);
     return RR_OK;
 }

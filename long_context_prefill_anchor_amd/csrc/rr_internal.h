@@ -93,6 +93,8 @@ hipError_t launch_relay_group(const RelayGroup& g, bool bf16, bool causal, hipSt
 hipError_t launch_compact_out(const int32_t* bcount, const int32_t* blist, int H, int nq, int32_t* out_rows,
                               int32_t* out_head_counts, int32_t* out_n_rows, hipStream_t st);
 size_t route_lds_bytes(int nk, int c);
+// The route kernels' LDS for nk key chunks and c ledger IDs per row fits a compute unit.
+bool route_fits(int nk, int c);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t st);
 // k + m > 32 (rr_wide.hip): one wave per row, same ledger rules; nk <= 1024.
 hipError_t launch_route_wide(const RouteArgs& a, bool bf16, bool causal, bool reroute, hipStream_t st);

@@ -355,6 +355,10 @@ struct RouteShared {
     int32_t redo;
 };
 
+// A route block's LDS (the dynamic area and its shared row state) fits a compute unit's 160 KB.
+// Past 4096 key chunks the per-row sentinel bitmaps dominate: one block per compute unit.
+bool route_fits(int nk, int c) { return route_lds_bytes_dev(nk, c) + sizeof(RouteShared) + 64 <= (160u << 10); }
+
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a > b ? b : a; }
 // keep_max ? max(a, b) : min(a, b) with one compare (the lane's choice flips the compare's mask).

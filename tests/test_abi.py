@@ -50,6 +50,10 @@ def test_config_check_accepts_every_named_workload():
     # Table 3's widest mix (48 near-miss + 12 random, c = 72) and the widest ledger (c = 128)
     assert rr.rr_config_check(cfg(k=12, m=48, r=12)) == rr.RR_OK
     assert rr.rr_config_check(cfg(k=32, m=32, r=32, sink=16, recent=16)) == rr.RR_OK
+    # long rows: 16384 key chunks (2M tokens in 128-token chunks) with up to 86 IDs per row
+    assert rr.rr_config_check(cfg(nk=16384)) == rr.RR_OK
+    assert rr.rr_config_check(cfg(nk=16384, r=32, sink=15, recent=15)) == rr.RR_OK
+    assert rr.rr_config_check(cfg(nk=8192, k=16, m=16, r=32, sink=16, recent=16)) == rr.RR_OK
 
 
 def test_config_struct_layout_matches_the_header(tmp_path):
@@ -92,7 +96,9 @@ def test_config_struct_layout_matches_the_header(tmp_path):
     (dict(k=20, m=45), rr.RR_EUNSUPPORTED, "k + m"),
     (dict(k=20, m=13, r=4, nk=2048), rr.RR_EUNSUPPORTED, "nk <= 1024"),
     (dict(r=33), rr.RR_EUNSUPPORTED, "r must"),
-    (dict(nk=8192), rr.RR_EUNSUPPORTED, "nk"),
+    (dict(nk=32768), rr.RR_EUNSUPPORTED, "nk must be <= 16384"),
+    # c = 88 IDs per row at 16384 chunks: the route block's LDS would exceed 160 KB
+    (dict(nk=16384, r=32, sink=16, recent=16), rr.RR_EUNSUPPORTED, "LDS"),
     (dict(sink=-1), rr.RR_EINVAL, "sink >= 0"),
     (dict(recent=-2), rr.RR_EINVAL, "recent >= 0"),
     (dict(sink=20, recent=13), rr.RR_EUNSUPPORTED, "sink + recent"),

@@ -45,6 +45,10 @@ ANCHOR_CASES = [
     ("int_ties_bf16_causal", 2, 150, 150, 12, 12, 8, "bf16", True, 12, "int"),
     ("int_ties_narrow", 1, 64, 200, 12, 12, 8, "f32", False, 13, "int1"),
     ("equal_keys", 2, 64, 100, 12, 12, 8, "f32", False, 14, "equal"),
+    # long rows: 8192 and 16384 key chunks (1M / 2M tokens in 128-token chunks), one route
+    # block per compute unit (the sentinel bitmaps fill the LDS)
+    ("long_keys_bf16", 1, 96, 16384, 12, 12, 8, "bf16", False, 15, "gauss"),
+    ("long_keys_f32", 1, 64, 8192, 12, 12, 8, "f32", False, 16, "gauss"),
 ]
 
 
@@ -111,6 +115,9 @@ RELAY_CASES = [
     ("relay_gather_wide", 1, 80, 1300, 16, 16, 32, "bf16", False, 0.05, "gauss"),
     # more than 64 rescore blocks per head (nq > 4096): the reroute finds its rows by scanning flags
     ("relay_many_rows", 1, 4160, 96, 12, 12, 8, "bf16", False, 0.05, "gauss"),
+    # long rows (see the anchor cases)
+    ("relay_long_keys_bf16", 1, 96, 16384, 12, 12, 8, "bf16", False, 0.05, "gauss"),
+    ("relay_long_keys_f32", 1, 64, 8192, 12, 12, 8, "f32", False, 0.05, "gauss"),
 ]
 
 
@@ -530,6 +537,30 @@ def test_full_size_causal_large_relay_sampled(mode):
     U.log(f"   sampled={rep.rows} compared={compared} flagged={flagged} excluded={rep.excluded} "
           f"max|ds|={rep.max_score_err:.2e}")
     assert compared >= 6000 and flagged > 1000
+    assert rep.excluded <= max(2, rep.rows // 50)
+    led.close()
+
+
+@pytest.mark.parametrize("mode", ["auto", "compacted"])
+def test_long_keys_causal_relay_sampled(mode):
+    """One head of 16384 causal bf16 chunks (2M tokens in 128-token chunks): GPU anchor at layer
+    0 and relay at layer 1 on every row; the oracle on sampled rows: the first 64 (rows shorter
+    than k + m), the last 64 (rows of ~16K keys, one route block per compute unit) and 400
+    random rows."""
+    w = W.causal_large().with_(name="causal_16k", heads=1, n=16384)
+    U.log(f"[long keys {mode}] 1 x 16384 causal anchor layer 0 + relay layer 1, sampled rows")
+    gen = synth.generate(w)
+    l0, l1 = next(gen), next(gen)
+    led, cfg = make(w.heads, w.n, w.n, w.k, w.m, w.r, w.dtype, True, w.seed)
+    rng = np.random.default_rng(2)
+    rows = {(0, i) for i in range(64)} | {(0, i) for i in range(w.n - 64, w.n)}
+    rows |= {(0, int(i)) for i in rng.integers(0, w.n, 400)}
+    rep = U.Report()
+    compared, flagged = U.relay_parity_sampled(led, cfg, l0.q, l0.k, l1.q, l1.k, rows, U.GAP_TOL, 1e-3, rep,
+                                               mode=mode)
+    U.log(f"   sampled={rep.rows} compared={compared} flagged={flagged} excluded={rep.excluded} "
+          f"max|ds|={rep.max_score_err:.2e}")
+    assert compared >= 400 and flagged > 50
     assert rep.excluded <= max(2, rep.rows // 50)
     led.close()
 
